@@ -1,0 +1,183 @@
+"""Benchmark of the compressed sparse attention layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one dsa_layer_decode call over one batch (compress the entry that
+completes at m, index every visible entry, Top-k, sparse attention, window
+insert) on seeded synthetic inputs already resident in HBM.  Input sets are
+rotated (three by default) so that repeated steps do not find the indexer
+keys in the 256 MB Infinity Cache.  Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "c4a DSA decode queries/s + HBM GB/s (% peak) at L=1M k=512; prefill TFLOP/s"
+PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def decode_bytes_per_query(w, nv):
+    """Algorithmic HBM bytes of one decode query: the visible indexer keys
+    (Di fp8 bytes + a 4-byte scale each), the k + W gathered latent vectors,
+    q and out, and the k selected indices."""
+    el = 2 if w.main_dtype == "bf16" else 4
+    idx_b = nv * (w.Di + (4 if w.idx_dtype == "fp8" else 0)) if w.Hi else 0
+    if w.idx_dtype == "f32":
+        idx_b = nv * w.Di * 4
+    sel = min(w.k, nv)
+    attn = (sel + min(w.W, w.m)) * w.D * el
+    return idx_b + attn + 2 * w.H * w.D * el + w.k * 4
+
+
+def build_sets(w, n_sets, device):
+    from sparse_long_context_c4a_amd import inputs as gen
+    from sparse_long_context_c4a_amd import layer as Ly
+    sets = []
+    for i in range(n_sets):
+        inp = gen.layer_inputs(w, seed=w.seed + 1000 * i)
+        st = Ly.state_from_inputs(inp, device)
+        ch = Ly.chunk_from_inputs(w, inp, device)
+        sets.append((st, ch))
+        del inp
+    return sets
+
+
+def time_layer(w, sets, steps, warmup, decode):
+    import torch
+    from sparse_long_context_c4a_amd import _lib
+    from sparse_long_context_c4a_amd import layer as Ly
+    dev = sets[0][1].x.device
+    B, T = sets[0][1].x.shape[0], sets[0][1].T
+    outs = [Ly.alloc_outputs(w, B, T, dev) for _ in sets]
+    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s) for (st, ch), o in
+            zip(sets, outs)]
+    ws_bytes = max(_lib.layer_workspace(a) for a in args)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fn = _lib.layer_decode if decode else _lib.layer_prefill
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(args[i % len(args)], ws=ws, stream=stream)
+    ev_i = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        a = args[i % len(args)]
+        a.ev_index[0], a.ev_index[1] = ev_i[i][0].cuda_event, ev_i[i][1].cuda_event
+        a.ev_attn[0], a.ev_attn[1] = ev_a[i][0].cuda_event, ev_a[i][1].cuda_event
+        fn(a, ws=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    for a in args:
+        a.ev_index[0] = a.ev_index[1] = a.ev_attn[0] = a.ev_attn[1] = None
+    st = [o[3].item() for o in outs]
+    assert all(s == 0 for s in st), f"device status {st}"
+    ms = t0.elapsed_time(t1) / steps
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev_i) / steps
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev_a) / steps
+    return ms, idx_ms, attn_ms
+
+
+def cpu_baseline(w, n_queries):
+    """The fp64 oracle on a bounded sample of the same workload: the full
+    layer step for the first n_queries sequences of one input set."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.layer import Geometry
+    from oracle.run import run_layer
+    from sparse_long_context_c4a_amd import configs, inputs as gen
+    ws = configs.shrink(w, B=n_queries)
+    inp = gen.layer_inputs(ws, seed=w.seed)
+    g = Geometry(s=w.s, S=w.S, D=w.D, r=w.r, Di=w.Di, r_idx=w.r_idx, H=w.H, Hi=w.Hi, k=w.k,
+                 W=w.W, main_dtype=w.main_dtype, idx_dtype=w.idx_dtype)
+    t = time.perf_counter()
+    run_layer(g, inp)
+    dt = time.perf_counter() - t
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_queries / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_queries} of the {w.B} decode queries of {w.name} (full layer step, "
+                      f"fp64 NumPy), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4a_decode_B4_L1M")
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer's multi-GPU "
+              "sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_long_context_c4a_amd import configs
+    from sparse_long_context_c4a_amd import _lib
+    w = configs.BY_NAME[args.workload]
+    assert w.mode == "decode"
+    dev = "cuda"
+    print(f"[bench] building {args.sets} input sets for {w.name}", file=sys.stderr, flush=True)
+    sets = build_sets(w, args.sets, dev)
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms, idx_ms, attn_ms = time_layer(w, sets, args.steps, args.warmup, decode=True)
+    nv = _lib.n_complete(w.m, w.s, w.S)
+    qps = w.B / (ms / 1e3)
+    step_bytes = w.B * decode_bytes_per_query(w, nv)
+    gbps = step_bytes / (ms / 1e3) / 1e9
+    idx_bytes = w.B * nv * (w.Di + 4)
+    idx_gbps = idx_bytes / (idx_ms / 1e3) / 1e9 if idx_ms > 0 else None
+    line = {
+        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.L, "query_pos": w.m,
+                   "n_vis": nv, "k": w.k, "window": w.W, "latent_dim": w.D, "heads": w.H,
+                   "indexer_heads": w.Hi, "indexer_dim": w.Di, "input_sets": args.sets},
+        "hbm_gbps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "alg_bytes_per_step": step_bytes,
+        "kernel_ms": {"indexer": idx_ms, "attention": attn_ms},
+        "roofline": {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": idx_gbps / PEAK_HBM_GBPS if idx_gbps else None, "traffic": None,
+                     "kernel": "k_index_fp8_stream", "alg_bytes_per_launch": idx_bytes},
+    }
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        wp = configs.C4A_PREFILL_128K
+        print("[bench] prefill chunk", file=sys.stderr, flush=True)
+        psets = build_sets(wp, 1, dev)
+        pms, pidx_ms, pattn_ms = time_layer(wp, psets, 3, 1, decode=False)
+        nvs = sum(_lib.n_complete(wp.p0 + t, wp.s, wp.S) for t in range(wp.T))
+        idx_flop = 2.0 * wp.Hi * wp.Di * nvs
+        attn_flop = 4.0 * wp.T * wp.H * (wp.k + wp.W) * wp.D
+        line["prefill"] = {"workload": wp.name, "ms_per_step": pms,
+                           "indexer_ms": pidx_ms, "attention_ms": pattn_ms,
+                           "indexer_tflops": idx_flop / (pidx_ms / 1e3) / 1e12,
+                           "indexer_frac_fp8_peak": idx_flop / (pidx_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
+                           "layer_tflops": (idx_flop + attn_flop) / (pms / 1e3) / 1e12}
+        del psets
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,286 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) compressed sparse attention library.
+ *
+ * The layer (DeepSeek V4 attention as described in the pages
+ * "DeepSeek DSA、DeepSeek V4与vLLM Hybrid KV Cache详解" [P1] and
+ * "DeepSeek V4 稀疏注意力完全解剖" [P2]) runs five steps:
+ *
+ *   S1 compress   entry j = RoPE_{s j}( sum_{i<S} softmax(z_j)_i x_{s j + i} )
+ *                 (c4a: S = 8 raw tokens at stride s = 4; c128a: S = s = 128)
+ *                 [P1] 5.2, [P2] 机制二
+ *   S2 visibility entry j is visible to query m iff s j + S - 1 < m;
+ *                 window = raw tokens [m-W, m-1]          [P2] 机制四
+ *   S3 indexer    I[m, j] = sum_h w[m,h] ReLU(q_idx[m,h] . k_idx[j])
+ *                 over the visible entries                 [P1] 4.1
+ *   S4 Top-k      keep the k highest-scoring entries       [P1] 4.2, [P2] 机制三
+ *   S5 attention  MQA over {selected entries} U {window}, K = V, one softmax,
+ *                 output rotated back by R_m^{-1}          [P1] 4.3 / 5.1,
+ *                                                          [P2] 机制一, 深潜
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major in the layout given per field.  The library never allocates,
+ *    frees or synchronises; scratch memory comes in through the workspace
+ *    argument (size from the matching *_workspace query, alignment 256 B).
+ *  - Each call validates its arguments on the host, enqueues kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream) and returns.  On a
+ *    validation failure nothing is launched.
+ *  - Per-sequence positions are device int64 arrays, so a call sequence can
+ *    be captured in a HIP graph.  Host-side bounds (max_pos_end) size the
+ *    grids; kernels clamp to them and never read or write outside the
+ *    buffers described here.  A device-side precondition that fails (a
+ *    position beyond max_pos_end, an entry beyond e_cap) sets bits in the
+ *    optional device word `status` (see DSA_DEVERR_*), or is ignored if
+ *    `status` is NULL; the affected outputs are then unspecified but all
+ *    memory accesses stay in bounds.
+ *  - Storage formats: DSA_F32 IEEE binary32; DSA_BF16 bfloat16;
+ *    DSA_FP8_E4M3 OCP fp8 e4m3fn (bias 7, max 448, no infinities) with one
+ *    fp32 scale per row (value = scale * code).
+ *  - RoPE acts on interleaved pairs of the last rope_dim dims of a vector,
+ *    pair i rotated by angle (pos + rope_pos_offset) * rope_base^(-2i/rope_dim).
+ *    rope_pos_offset shifts every rotation position and no index.
+ *  - Calls hold no global mutable state; errors are returned, never printed,
+ *    and dsa_last_error() gives a thread-local message for the last failure.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape   */
+  DSA_ERR_UNSUPPORTED = -2, /* dtype / dim combination not built, not gfx950 */
+  DSA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required       */
+  DSA_ERR_HIP = -4          /* a HIP runtime call failed                     */
+} dsa_status;
+
+typedef enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
+
+/* Bits OR-ed into the optional device status word by kernels. */
+#define DSA_DEVERR_POSITION 1u  /* a position outside [0, max_pos_end)        */
+#define DSA_DEVERR_CAPACITY 2u  /* an entry slot or n_vis beyond e_cap        */
+#define DSA_DEVERR_NO_INDEX 4u  /* no indexer but n_vis(m) > k                */
+
+/* Compressor / attention geometry. */
+typedef struct dsa_geom {
+  int32_t stride;          /* s: raw tokens between consecutive entries     */
+  int32_t span;            /* S: raw tokens mixed into one entry (S >= s)   */
+  int32_t dim;             /* D: vector length                              */
+  int32_t rope_dim;        /* r: rotary tail dims, even, 0 <= r <= D        */
+  double rope_base;        /* frequency base (> 0 when r > 0)               */
+  int64_t rope_pos_offset; /* added to every rotation position              */
+} dsa_geom;
+
+/* ---------------------------------------------------------------- S1 ----
+ * dsa_compress: write every compressed entry that completes inside a chunk
+ * of raw tokens ([P1] 5.2; [P2] 机制二 c4a diagram T0 = t0..t7, T1 = t4..t11;
+ * [P2] 融合点 1 for the fused order compress -> RMSNorm -> RoPE -> insert).
+ *
+ * For sequence b the chunk holds raw positions p0 = raw_pos0[b] ..
+ * p0 + raw_len - 1.  Entries j with p0 <= s j + S - 1 < p0 + raw_len are
+ * written, i.e. j = n_complete(p0) .. n_complete(p0 + raw_len) - 1 with
+ * n_complete(L) = max(0, floor((L - S) / s) + 1).  Entry j reads raw tokens
+ * s j .. s j + S - 1: those >= p0 from `raw`, those < p0 from `ring`.
+ * Weights: softmax over logits[b, j - n_complete(p0), 0..S-1], one scalar per
+ * raw token shared across D.  Optional RMSNorm (gamma != NULL):
+ * c <- gamma * c / sqrt(mean(c^2) + eps).  Then RoPE at position s j.
+ * FP8 output: scale = max|c| / 448 (fp32), codes round to nearest even.
+ */
+typedef struct dsa_compress_args {
+  dsa_geom geom;
+  int32_t batch;              /* B                                           */
+  const void* raw;            /* [B, raw_len, D] raw tokens, raw_dtype       */
+  dsa_dtype raw_dtype;        /* DSA_F32 or DSA_BF16                         */
+  int64_t raw_len;            /* tokens per sequence in this chunk (>= 1)    */
+  const void* ring;           /* [B, S, D] raw_dtype: the S raw tokens before
+                                 the chunk, position p at slot p mod S        */
+  const int64_t* raw_pos0;    /* device [B]: position of raw[b, 0]           */
+  const float* logits;        /* [B, logits_rows, S]                         */
+  int32_t logits_rows;        /* >= ceil(raw_len / s)                        */
+  const float* rms_gamma;     /* [D] or NULL (no RMSNorm)                    */
+  float rms_eps;
+  void* out;                  /* [B, e_cap, D] cache, entry j at slot j      */
+  dsa_dtype out_dtype;        /* DSA_F32, DSA_BF16 or DSA_FP8_E4M3           */
+  float* out_scale;           /* [B, e_cap] for FP8 output, else ignored     */
+  int64_t e_cap;              /* cache slots per sequence                    */
+  int64_t max_pos_end;        /* host bound: raw_pos0[b] + raw_len <= this   */
+  uint32_t* status;           /* optional device status word                 */
+} dsa_compress_args;
+
+dsa_status dsa_compress(const dsa_compress_args* a, void* stream);
+
+/* ------------------------------------------------------------ S2-S4 ----
+ * dsa_index_topk: lightning-indexer scores over the visible entries and
+ * Top-k selection ([P1] 4.1, 4.2; [P2] 机制三).
+ *
+ * Queries are grouped per sequence: row i = b * queries_per_seq + t belongs
+ * to sequence b and sits at position q_pos[i].  n_vis = n_complete(q_pos[i]).
+ * I[i, j] = sum_h w[i,h] * qs[i,h] * ks[b,j] * ReLU(q[i,h] . k[b,j]) for
+ * j < n_vis, where qs / ks are the fp8 scales (1 for F32).  The output holds
+ * the min(k, n_vis) entries of highest score, ties to the lower index, in no
+ * particular order, then -1 padding.  If k >= n_vis the selection is
+ * 0 .. n_vis-1 and keys may be NULL.  Scores equal to within fp32 rounding
+ * of the k-th may be exchanged with it.
+ */
+typedef struct dsa_index_args {
+  int32_t n_seqs;             /* B                                           */
+  int32_t queries_per_seq;    /* Tq (1 for decode)                           */
+  const int64_t* q_pos;       /* device [B * Tq]                             */
+  int32_t stride, span;       /* s, S of the compressor that made the keys   */
+  int32_t heads, dim;         /* Hi, Di (DSA_FP8_E4M3 needs Di == 128)       */
+  const void* q;              /* [B * Tq, Hi, Di]                            */
+  const float* q_scale;       /* [B * Tq, Hi] (FP8; NULL means 1)            */
+  const float* w;             /* [B * Tq, Hi] head weights                   */
+  const void* keys;           /* [B, e_cap, Di]                              */
+  const float* k_scale;       /* [B, e_cap] (FP8)                            */
+  dsa_dtype dtype;            /* q and keys: DSA_F32 or DSA_FP8_E4M3         */
+  int64_t e_cap;
+  int64_t max_pos_end;        /* host bound: q_pos[i] < max_pos_end          */
+  int32_t k;                  /* >= 1                                        */
+  int32_t* idx_out;           /* [B * Tq, k]                                 */
+  float* score_out;           /* [B * Tq, k] or NULL (NaN for padding)       */
+  uint32_t* status;
+  void* ev_index[2];          /* optional hipEvent_t pair recorded on the
+                                 stream right before / after the scoring
+                                 kernel (for timing it alone); NULL = none  */
+} dsa_index_args;
+
+size_t dsa_index_topk_workspace(const dsa_index_args* a);
+dsa_status dsa_index_topk(const dsa_index_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- S5 ----
+ * dsa_sparse_attn: MQA attention over the selected entries and the raw
+ * window, K = V, one joint softmax, inverse RoPE on the output ([P1] 4.3,
+ * 5.1, 5.3; [P2] 机制一, 深潜 Inverse RoPE, 机制四).
+ *
+ * Row i (sequence b, position m = q_pos[i]) attends to
+ *   { cache[b, j] : j in idx[i], j >= 0 }  U  { window vector of raw token n :
+ *   max(0, m - W) <= n <= m - 1 }.
+ * Window vectors are stored rotated: for n >= chunk_pos0[b] (if chunk_win is
+ * given) at chunk_win[b, n - chunk_pos0[b]], otherwise at window[b, n mod
+ * w_cap] (which the caller keeps current: w_cap >= W).
+ * logits = scale * (R_m q_h) . v (q rotated here if rotate_q, else taken as
+ * already rotated); out_h = R_m^{-1} sum_a softmax_a v_a; lse_h = natural-log
+ * sum of exp(logits).  An empty set gives out = 0, lse = -inf.
+ */
+typedef struct dsa_attn_args {
+  int32_t n_seqs;             /* B                                           */
+  int32_t queries_per_seq;    /* Tq                                          */
+  const int64_t* q_pos;       /* device [B * Tq]                             */
+  int32_t heads;              /* H                                           */
+  int32_t dim;                /* D (DSA_BF16 needs D == 512)                 */
+  int32_t rope_dim;
+  double rope_base;
+  int64_t rope_pos_offset;
+  dsa_dtype dtype;            /* q, cache, window, out: DSA_F32 or DSA_BF16  */
+  const void* q;              /* [B * Tq, H, D]                              */
+  int32_t rotate_q;           /* 1: rotate q at its position here            */
+  const void* cache;          /* [B, e_cap, D]                               */
+  int64_t e_cap;
+  const int32_t* idx;         /* [B * Tq, k], -1 = none                      */
+  int32_t k;
+  const void* window;         /* [B, w_cap, D]                               */
+  int32_t w_cap;
+  int32_t window_size;        /* W (<= w_cap)                                */
+  const void* chunk_win;      /* [B, chunk_len, D] or NULL                   */
+  const int64_t* chunk_pos0;  /* device [B] (with chunk_win)                 */
+  int64_t chunk_len;
+  float softmax_scale;        /* 0 -> 1 / sqrt(D)                            */
+  int64_t max_pos_end;        /* host bound: q_pos[i] < max_pos_end          */
+  void* out;                  /* [B * Tq, H, D]                              */
+  float* lse;                 /* [B * Tq, H] or NULL                         */
+  uint32_t* status;
+} dsa_attn_args;
+
+size_t dsa_sparse_attn_workspace(const dsa_attn_args* a);
+dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ layer ----
+ * dsa_layer_decode / dsa_layer_prefill: one layer step over a chunk of T raw
+ * tokens per sequence at positions p0 = pos0[b] .. p0 + T - 1 ([P2] 全景图,
+ * decode step C-E; [P1] 6.3 flowchart).  Decode is the T = 1 case.
+ *
+ *  1. S1 for every entry completing in the chunk, main (dtype) and indexer
+ *     (idx_dtype) caches, reading raw tokens before the chunk from the
+ *     compressor rings (state = last S raw tokens, [P2] 设计 2: c4a 8,
+ *     c128a 128);
+ *  2. the rings take the chunk's last S raw tokens;
+ *  3. S3/S4 for each of the T queries (entries completed earlier in the same
+ *     chunk are visible to later queries); with idx_heads == 0 every visible
+ *     entry is selected, which needs k >= n_vis (the c128a case);
+ *  4. S5 with the window [m - W, m - 1];
+ *  5. the window ring takes the chunk's rotated tokens (after attention, so
+ *     slot m mod w_cap is reused only once m's own query has run).
+ * Raw indexer tokens kx are F32 when idx_dtype is F32 and BF16 when it is
+ * FP8.  All state buffers are updated in place.
+ */
+typedef struct dsa_layer_args {
+  dsa_geom main;              /* s, S, D, r, base, offset (main + window)    */
+  int32_t heads;              /* H                                           */
+  int32_t idx_heads;          /* Hi (0: no indexer)                          */
+  int32_t idx_dim;            /* Di                                          */
+  int32_t idx_rope_dim;
+  double idx_rope_base;
+  int32_t k;
+  int32_t window_size;        /* W                                           */
+  float softmax_scale;        /* 0 -> 1/sqrt(D)                              */
+  int32_t n_seqs;             /* B                                           */
+  int32_t chunk_len;          /* T                                           */
+  const int64_t* pos0;        /* device [B]                                  */
+  int64_t max_pos_end;        /* host bound: pos0[b] + T <= max_pos_end      */
+  dsa_dtype dtype;            /* DSA_F32 or DSA_BF16                         */
+  dsa_dtype idx_dtype;        /* DSA_F32 or DSA_FP8_E4M3                     */
+  const void* x;              /* [B, T, D] raw tokens                        */
+  const void* kx;             /* [B, T, Di] raw indexer tokens               */
+  const float* logits_main;   /* [B, ceil(T/s), S]                           */
+  const float* logits_idx;    /* [B, ceil(T/s), S]                           */
+  const void* q;              /* [B, T, H, D] (not rotated)                  */
+  const void* qi;             /* [B, T, Hi, Di]                              */
+  const float* qi_scale;      /* [B, T, Hi] (FP8)                            */
+  const float* w;             /* [B, T, Hi]                                  */
+  void* main_cache;           /* [B, e_cap, D]                               */
+  void* idx_cache;            /* [B, e_cap, Di]                              */
+  float* idx_scale;           /* [B, e_cap] (FP8)                            */
+  int64_t e_cap;
+  void* main_ring;            /* [B, S, D]                                   */
+  void* idx_ring;             /* [B, S, Di]                                  */
+  void* window;               /* [B, w_cap, D]                               */
+  int32_t w_cap;
+  const float* rms_gamma;     /* [D] or NULL                                 */
+  const float* rms_gamma_idx; /* [Di] or NULL                                */
+  float rms_eps;
+  void* out;                  /* [B, T, H, D]                                */
+  float* lse;                 /* [B, T, H] or NULL                           */
+  int32_t* idx_out;           /* [B, T, k] or NULL                           */
+  uint32_t* status;
+  void* ev_index[2];          /* optional hipEvent_t pairs recorded around   */
+  void* ev_attn[2];           /* the scoring kernel and the attention kernels */
+} dsa_layer_args;
+
+size_t dsa_layer_workspace(const dsa_layer_args* a);
+dsa_status dsa_layer_decode(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream);
+dsa_status dsa_layer_prefill(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+/* 1 if `device` is a gfx950 GPU this library was built for, else 0. */
+int dsa_device_supported(int device);
+const char* dsa_version(void);
+const char* dsa_last_error(void);
+/* n_complete(L) = max(0, floor((L - S) / s) + 1): entries whose S raw tokens
+ * all lie in [0, L); also the visible-entry count of a query at position L. */
+int64_t dsa_n_complete(int64_t L, int32_t stride, int32_t span);
+/* sizeof of a struct declared here ("dsa_geom", "dsa_compress_args",
+ * "dsa_index_args", "dsa_attn_args", "dsa_layer_args"), 0 for other names.
+ * Lets a binding check its mirror of the struct layouts. */
+size_t dsa_abi_sizeof(const char* struct_name);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

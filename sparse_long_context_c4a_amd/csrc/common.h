@@ -1,0 +1,142 @@
+// Device-side helpers shared by the gfx950 kernels: storage-format
+// conversions, rotary angles, wave64 reductions, error words.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ formats
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN, overflow becomes inf.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// OCP e4m3fn code -> float (exact).
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+  if (e == 0) return __uint_as_float(sign | __float_as_uint(static_cast<float>(m) * 0x1p-9f));
+  if (e == 15 && m == 7) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// float -> OCP e4m3fn code, round to nearest even, saturating at +-448.
+// Works on the binary32 bit pattern: below 2^-6 the grid is spaced 2^-9;
+// above, the 23-bit fraction is rounded to 3 bits at bit 20.
+__device__ __forceinline__ uint32_t f32_to_fp8(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return 0x7fu;             // NaN
+  if (ua >= 0x43e80000u) return sign | 0x7eu;     // |x| >= 464 (incl. inf)
+  if (ua < 0x3c800000u) {                          // |x| < 2^-6
+    const float q = rintf(__uint_as_float(ua) * 512.0f);  // 0..8
+    return sign | static_cast<uint32_t>(q);
+  }
+  const uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) & 0xfff00000u;
+  const uint32_t ef = (r >> 23) - 120u;            // biased e4m3 exponent, 1..15
+  const uint32_t m = (r >> 20) & 7u;
+  if (ef > 15u || (ef == 15u && m == 7u)) return sign | 0x7eu;
+  return sign | (ef << 3) | m;
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_from_f32(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_from_f32<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t* p, int64_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+// --------------------------------------------------------------- RoPE
+// cos / sin of (pos * base^(-2i/r)); the product and its reduction are done
+// in fp64 so that positions near 2^20 keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cs(int64_t pos, int i, int r, double base, float* c,
+                                        float* s) {
+  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(r));
+  double sd, cd;
+  sincos(static_cast<double>(pos) * theta, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+// ------------------------------------------------------- counts / keys
+__host__ __device__ __forceinline__ int64_t n_complete(int64_t L, int s, int S) {
+  return L < S ? 0 : (L - S) / s + 1;  // L - S >= 0 here, so / is floor
+}
+
+// Monotone map float -> uint32 (larger float, larger key); -0 and +0 map to
+// the same key so that equal scores tie.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ void set_status(uint32_t* st, uint32_t bits) {
+  if (st) atomicOr(st, bits);
+}
+
+// ------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Block-wide reductions (blockDim.x a multiple of 64, <= 1024).  `red` is a
+// __shared__ float[16] scratch; all threads get the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+}  // namespace dsa

@@ -1,0 +1,46 @@
+// Host-side internals: launch helpers and the error channel behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "dsa.h"
+
+namespace dsa {
+
+dsa_status fail(dsa_status s, const char* fmt, ...);
+dsa_status hip_check(hipError_t e, const char* what);
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Kernel launchers (one per step); arguments already validated.
+dsa_status launch_compress(const dsa_compress_args& a, hipStream_t st);
+dsa_status launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// Indexer + Top-k.  Workspace layout is owned by indexer.hip.
+size_t index_topk_ws_bytes(const dsa_index_args& a);
+dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st);
+
+// Attention.
+size_t attn_ws_bytes(const dsa_attn_args& a);
+dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st);
+
+// Layer helpers: ring and window maintenance, chunk rotation.
+dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
+                              const int64_t* pos0, int B, int64_t max_pos_end, hipStream_t st);
+dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, int r, double base,
+                               int64_t off, const int64_t* pos0, int B, void* out,
+                               int64_t max_pos_end, hipStream_t st);
+dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
+                                int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
+                                hipStream_t st);
+
+inline size_t dtype_size(dsa_dtype t) {
+  return t == DSA_F32 ? 4 : t == DSA_BF16 ? 2 : 1;
+}
+
+}  // namespace dsa

@@ -1,0 +1,121 @@
+// Layer-state maintenance kernels: compressor rings, chunk rotation and the
+// window ring.
+//
+// The compressor state is the last S raw tokens of each compressor (c4a 8,
+// c128a 128: "DeepSeek V4 稀疏注意力完全解剖", 设计 2), raw position p at slot
+// p mod S.  The window keeps the rotated raw tokens R_n x_n of the last w_cap
+// positions (same page, 机制四), position n at slot n mod w_cap.
+#include "common.h"
+#include "internal.h"
+
+namespace dsa {
+namespace {
+
+__global__ void k_zero(uint32_t* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// Copy the last min(T, S) raw tokens of the chunk into the ring.  Grid:
+// (min(T, S), B); element size in 2-byte units.
+__global__ void k_ring_update(const uint16_t* __restrict__ raw, int units, int64_t T,
+                              uint16_t* __restrict__ ring, int S, const int64_t* __restrict__ pos0,
+                              int64_t max_pos_end) {
+  const int b = blockIdx.y;
+  const int64_t p0 = pos0[b];
+  if (p0 < 0 || p0 + T > max_pos_end) return;
+  const int64_t keep = T < S ? T : S;
+  const int64_t t = T - keep + blockIdx.x;  // chunk offset of the token
+  const int64_t p = p0 + t;
+  const uint16_t* src = raw + (static_cast<int64_t>(b) * T + t) * units;
+  uint16_t* dst = ring + (static_cast<int64_t>(b) * S + (p % S)) * units;
+  for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
+}
+
+// out[b, t] = R_{p0 + t + off} x[b, t] in the storage dtype.  Grid (T, B).
+template <typename T>
+__global__ void k_rotate_chunk(const T* __restrict__ x, int D, int64_t Tn, int r, double base,
+                               int64_t off, const int64_t* __restrict__ pos0, T* __restrict__ out,
+                               int64_t max_pos_end) {
+  const int b = blockIdx.y;
+  const int64_t t = blockIdx.x;
+  const int64_t p0 = pos0[b];
+  if (p0 < 0 || p0 + Tn > max_pos_end) return;
+  const int64_t o = (static_cast<int64_t>(b) * Tn + t) * D;
+  const int first_rot = (D - r) / 2;
+  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) {
+    float a0 = load_as_f32(x, o + 2 * pr), a1 = load_as_f32(x, o + 2 * pr + 1);
+    if (pr >= first_rot) {
+      float c, s;
+      rope_cs(p0 + t + off, pr - first_rot, r, base, &c, &s);
+      const float t0 = a0 * c - a1 * s, t1 = a0 * s + a1 * c;
+      a0 = t0;
+      a1 = t1;
+    }
+    store_from_f32(out, o + 2 * pr, a0);
+    store_from_f32(out, o + 2 * pr + 1, a1);
+  }
+}
+
+// Window ring takes the last min(T, w_cap) rotated chunk tokens.
+__global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int64_t T,
+                                uint16_t* __restrict__ win, int w_cap,
+                                const int64_t* __restrict__ pos0, int64_t max_pos_end) {
+  const int b = blockIdx.y;
+  const int64_t p0 = pos0[b];
+  if (p0 < 0 || p0 + T > max_pos_end) return;
+  const int64_t keep = T < w_cap ? T : w_cap;
+  const int64_t t = T - keep + blockIdx.x;
+  const int64_t n = p0 + t;
+  const uint16_t* src = rot + (static_cast<int64_t>(b) * T + t) * units;
+  uint16_t* dst = win + (static_cast<int64_t>(b) * w_cap + (n % w_cap)) * units;
+  for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
+}
+
+}  // namespace
+
+dsa_status launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  if (n == 0) return DSA_OK;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>(1024, (n + 255) / 256));
+  hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), n);
+  return hip_check(hipGetLastError(), "k_zero launch");
+}
+
+dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
+                              const int64_t* pos0, int B, int64_t max_pos_end, hipStream_t st) {
+  const int units = static_cast<int>(D * dtype_size(dt) / 2);
+  const int64_t keep = T < S ? T : S;
+  hipLaunchKernelGGL(k_ring_update, dim3(static_cast<unsigned>(keep), B), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(raw), units, T, static_cast<uint16_t*>(ring), S,
+                     pos0, max_pos_end);
+  return hip_check(hipGetLastError(), "k_ring_update launch");
+}
+
+dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, int r, double base,
+                               int64_t off, const int64_t* pos0, int B, void* out,
+                               int64_t max_pos_end, hipStream_t st) {
+  dim3 grid(static_cast<unsigned>(T), B);
+  if (dt == DSA_F32)
+    hipLaunchKernelGGL(k_rotate_chunk<float>, grid, dim3(256), 0, st, static_cast<const float*>(x),
+                       D, T, r, base, off, pos0, static_cast<float*>(out), max_pos_end);
+  else
+    hipLaunchKernelGGL(k_rotate_chunk<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), D, T, r, base, off, pos0,
+                       static_cast<uint16_t*>(out), max_pos_end);
+  return hip_check(hipGetLastError(), "k_rotate_chunk launch");
+}
+
+dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
+                                int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
+                                hipStream_t st) {
+  const int units = static_cast<int>(D * dtype_size(dt) / 2);
+  const int64_t keep = T < w_cap ? T : w_cap;
+  hipLaunchKernelGGL(k_window_update, dim3(static_cast<unsigned>(keep), B), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(rot_chunk), units, T,
+                     static_cast<uint16_t*>(win), w_cap, pos0, max_pos_end);
+  return hip_check(hipGetLastError(), "k_window_update launch");
+}
+
+}  // namespace dsa

@@ -1,0 +1,125 @@
+"""Marshalling for one layer step: torch tensors in, LayerArgs out.
+
+Holds no arithmetic of the layer; it moves the seeded inputs to the device,
+keeps the state tensors (caches, compressor rings, window ring) and fills
+the C structs of the library.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+from .configs import Workload
+
+
+def to_device(a, device="cuda"):
+    """NumPy storage array -> device tensor with the same bits (uint16 bf16
+    patterns become torch.bfloat16, fp8 codes stay uint8)."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+@dataclass
+class LayerState:
+    main_cache: torch.Tensor
+    idx_cache: torch.Tensor
+    idx_scale: torch.Tensor
+    main_ring: torch.Tensor
+    idx_ring: torch.Tensor
+    window: torch.Tensor
+    e_cap: int
+
+
+@dataclass
+class Chunk:
+    pos0: torch.Tensor      # [B] int64
+    T: int
+    x: torch.Tensor
+    kx: torch.Tensor
+    logits_main: torch.Tensor
+    logits_idx: torch.Tensor
+    q: torch.Tensor
+    qi: torch.Tensor
+    qi_scale: torch.Tensor
+    w: torch.Tensor
+
+
+def state_from_inputs(inp, device="cuda"):
+    return LayerState(main_cache=to_device(inp["main_cache"], device),
+                      idx_cache=to_device(inp["idx_cache"], device),
+                      idx_scale=to_device(inp["idx_scale"], device),
+                      main_ring=to_device(inp["main_ring"], device),
+                      idx_ring=to_device(inp["idx_ring"], device),
+                      window=to_device(inp["win_ring"], device),
+                      e_cap=int(inp["E_cap"]))
+
+
+def _pad_logits(lg, rows):
+    if lg is None:
+        return None
+    B, n, S = lg.shape
+    out = np.zeros((B, max(rows, 1), S), np.float32)
+    out[:, :n] = lg
+    return out
+
+
+def chunk_from_inputs(w: Workload, inp, device="cuda"):
+    B, T = inp["x"].shape[0], inp["T"]
+    rows = -(-T // w.s)
+    return Chunk(pos0=torch.full((B,), inp["p0"], dtype=torch.int64, device=device), T=T,
+                 x=to_device(inp["x"], device), kx=to_device(inp["kx"], device),
+                 logits_main=to_device(_pad_logits(inp["logits_main"], rows), device),
+                 logits_idx=to_device(_pad_logits(inp["logits_idx"], rows), device),
+                 q=to_device(inp["q"], device), qi=to_device(inp["qi"], device),
+                 qi_scale=to_device(inp["qi_scale"], device), w=to_device(inp["wt"], device))
+
+
+def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=None,
+               status=None, max_pos_end=None, pos_offset=0, rms_gamma=None,
+               rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0):
+    a = _lib.LayerArgs()
+    a.main = _lib.geom(w.s, w.S, w.D, w.r, w.base, pos_offset)
+    a.heads, a.idx_heads, a.idx_dim = w.H, w.Hi, w.Di
+    a.idx_rope_dim, a.idx_rope_base = w.r_idx, w.base
+    a.k, a.window_size, a.softmax_scale = w.k, w.W, softmax_scale
+    a.n_seqs, a.chunk_len = ch.x.shape[0], ch.T
+    a.pos0 = _lib.ptr(ch.pos0)
+    a.max_pos_end = max_pos_end if max_pos_end is not None else st.e_cap * w.s
+    a.dtype = _lib.DSA_F32 if w.main_dtype == "f32" else _lib.DSA_BF16
+    a.idx_dtype = _lib.DSA_F32 if w.idx_dtype == "f32" else _lib.DSA_FP8_E4M3
+    for name in ("x", "kx", "logits_main", "logits_idx", "q", "qi", "qi_scale", "w"):
+        setattr(a, name, _lib.ptr(getattr(ch, name)))
+    a.main_cache, a.idx_cache = _lib.ptr(st.main_cache), _lib.ptr(st.idx_cache)
+    a.idx_scale, a.e_cap = _lib.ptr(st.idx_scale), st.e_cap
+    a.main_ring, a.idx_ring = _lib.ptr(st.main_ring), _lib.ptr(st.idx_ring)
+    a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
+    a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps
+    a.out, a.lse, a.idx_out = _lib.ptr(out), _lib.ptr(lse), _lib.ptr(idx_out)
+    a.status = _lib.ptr(status)
+    return a
+
+
+def alloc_outputs(w: Workload, B, T, device="cuda"):
+    dt = torch.float32 if w.main_dtype == "f32" else torch.bfloat16
+    out = torch.empty((B, T, w.H, w.D), dtype=dt, device=device)
+    lse = torch.empty((B, T, w.H), dtype=torch.float32, device=device)
+    idx = torch.empty((B, T, w.k), dtype=torch.int32, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    return out, lse, idx, status
+
+
+def run(w: Workload, st: LayerState, ch: Chunk, decode=None, ws=None, **kw):
+    """One layer step; returns (out, lse, idx, status, workspace)."""
+    B, T = ch.x.shape[0], ch.T
+    out, lse, idx, status = alloc_outputs(w, B, T, ch.x.device)
+    a = layer_args(w, st, ch, out, lse, idx, status, **kw)
+    if decode is None:
+        decode = T == 1
+    fn = _lib.layer_decode if decode else _lib.layer_prefill
+    ws = fn(a, ws=ws, device=ch.x.device)
+    return out, lse, idx, status, ws

@@ -1,0 +1,193 @@
+"""GPU parity of the whole layer step (dsa_layer_decode / dsa_layer_prefill)
+against the fp64 oracle run end to end from the same seeded inputs.
+
+Small cases cover edge conditions (a fresh sequence, ragged chunks, a chunk
+split into decode steps, c128a without an indexer); the full-size cases are
+the five workloads (decode at 64K and 1M, c128a at 1M, the 4096-token
+prefill chunk), checked on every row (decode) or on sampled rows
+(prefill), in the same launch configuration the benchmark times."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa as odsa
+from oracle.run import run_layer
+from sparse_long_context_c4a_amd import configs, inputs as gen
+
+from gpu_helpers import ATOL, check_close, check_topk_row, geometry, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _layer():
+    from sparse_long_context_c4a_amd import layer as Ly
+    return Ly
+
+
+def _compare(w, inp, ores, out, lse, idx, rows=None, label=""):
+    """GPU outputs [B, T, ...] against the oracle result dict."""
+    out, lse, idx = to_np(out), lse.cpu().numpy(), idx.cpu().numpy()
+    B, T = out.shape[:2]
+    rows = range(T) if rows is None else rows
+    st = ores["states"]
+    swaps = 0
+    for b in range(B):
+        for t in rows:
+            m = inp["p0"] + t
+            nv = odsa.n_vis(m, w.s, w.S)
+            lab = f"{label} b={b} t={t} m={m}"
+            if w.Hi > 0:
+                qi = ores["qi_dec"][b][t]
+                scores = odsa.indexer_scores(qi, np.asarray(inp["wt"][b][t], np.float64),
+                                             st[b].idx_cache[:nv])
+                swaps += check_topk_row(idx[b, t], scores, w.k, lab)
+                same = set(idx[b, t][idx[b, t] >= 0].tolist()) == \
+                    set(ores["idx"][b, t][ores["idx"][b, t] >= 0].tolist())
+            else:
+                assert sorted(idx[b, t][idx[b, t] >= 0].tolist()) == list(range(nv)), lab
+                same = True
+            if same:  # outputs are only comparable on the same selection
+                check_close(out[b, t], ores["out"][b, t], ATOL[w.main_dtype], lab)
+                check_close(lse[b, t], ores["lse"][b, t], 1e-3 if w.main_dtype == "bf16" else 1e-4,
+                            lab + " lse")
+    return swaps
+
+
+def _oracle(w, inp, only=None):
+    from oracle.run import decode_store
+    g = geometry(w)
+    res = run_layer(g, inp, only=only)
+    if w.Hi > 0:
+        res["qi_dec"] = [decode_store(inp["qi"][b], w.idx_dtype,
+                                      None if inp["qi_scale"] is None else inp["qi_scale"][b])
+                         for b in range(inp["x"].shape[0])]
+    return res
+
+
+def _run_gpu(w, inp, decode=None, state=None):
+    Ly = _layer()
+    st = state or Ly.state_from_inputs(inp, DEV)
+    ch = Ly.chunk_from_inputs(w, inp, DEV)
+    out, lse, idx, status, _ = Ly.run(w, st, ch, decode=decode, max_pos_end=st.e_cap * w.s)
+    torch.cuda.synchronize()
+    assert status.item() == 0, f"device status {status.item()}"
+    return st, out, lse, idx
+
+
+SMALL = [
+    # name, workload, overrides, p0, T, state
+    ("c4a_decode_B3_L3000", configs.C4A_DECODE_64K, dict(B=3, L=3000), None, None, "random"),
+    ("c4a_decode_L20_tiny", configs.C4A_DECODE_64K, dict(B=2, L=20), None, None, "random"),
+    ("c128a_decode_B2_L5000", configs.C128A_DECODE_1M, dict(B=2, L=5000, k=64), None, None,
+     "random"),
+    ("c4a_prefill_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077), 2000, 77, "random"),
+    ("c4a_prefill_fresh_T300", configs.C4A_PREFILL_128K, dict(L=300), 0, 300, "empty"),
+    ("f32_prefill_fresh_T200", configs.TINY_C4A_F32, dict(L=200, mode="prefill"), 0, 200,
+     "empty"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_layer_small(case):
+    name, w0, over, p0, T, state = case
+    w = configs.shrink(w0, **over)
+    seed = 5000 + SMALL.index(case)
+    print(f"[dsa_layer] {name} B={w.B} p0={p0} T={T} seed={seed}", flush=True)
+    inp = gen.layer_inputs(w, seed=seed, p0=p0, T=T, state=state)
+    st, out, lse, idx = _run_gpu(w, inp)
+    ores = _oracle(w, inp)
+    _compare(w, inp, ores, out, lse, idx, label=name)
+    # the state the layer leaves behind: window ring and compressor rings
+    for b in range(w.B):
+        ring = to_np(st.main_ring[b])
+        check_close(ring, ores["states"][b].main_ring, 0.0, f"{name} main ring")
+        win = to_np(st.window[b])
+        check_close(win, ores["states"][b].win_ring, ATOL[w.main_dtype] / 4, f"{name} window")
+
+
+def test_tiny_f32_workload_prefill_then_decode():
+    """The tiny fp32 workload: a fresh sequence of 1023 raw tokens processed
+    as one prefill chunk, then the decode step at position 1023 (k = 64 of
+    254 visible entries)."""
+    w = configs.TINY_C4A_F32
+    print("[dsa_layer] tiny f32: prefill 0..1022 then decode 1023", flush=True)
+    wp = configs.shrink(w, mode="prefill")
+    inp = gen.layer_inputs(wp, seed=w.seed, p0=0, T=1024, state="empty")
+    # split the same token stream into a 1023-token chunk and a 1-token step
+    pre = {k: v for k, v in inp.items()}
+    dec = {k: v for k, v in inp.items()}
+    n_pre = odsa.n_complete(1023, 4, 8)
+    for key in ("x", "kx", "q", "qi", "wt"):
+        pre[key] = inp[key][:, :1023]
+        dec[key] = inp[key][:, 1023:]
+    pre["qi_scale"] = dec["qi_scale"] = None
+    for key in ("logits_main", "logits_idx"):
+        pre[key] = inp[key][:, :n_pre]
+        dec[key] = inp[key][:, n_pre:]
+    pre.update(T=1023, n_new=n_pre)
+    dec.update(p0=1023, T=1, j0=n_pre, n_new=inp["n_new"] - n_pre)
+    Ly = _layer()
+    st = Ly.state_from_inputs(inp, DEV)
+    _, out_p, lse_p, idx_p = _run_gpu(wp, pre, state=st)
+    _, out_d, lse_d, idx_d = _run_gpu(w, dec, state=st)
+    # oracle: the same two steps on one state
+    g = geometry(w)
+    from oracle.run import run_layer as rl
+    ores_all = rl(g, inp, only=[1022, 1023])
+    check_close(to_np(out_d)[0, 0], ores_all["out"][0, 1023], ATOL["f32"], "decode 1023")
+    check_close(to_np(out_p)[0, 1022], ores_all["out"][0, 1022], ATOL["f32"], "prefill 1022")
+    assert set(idx_d.cpu().numpy()[0, 0].tolist()) == set(ores_all["idx"][0, 1023].tolist())
+    assert odsa.n_vis(1023, 4, 8) == 254
+
+
+def test_chunked_prefill_matches_single_pass():
+    """Chunk invariance on the GPU: one 64-token chunk vs chunks of 5, 1, 1,
+    13 and 44 tokens (sizes not divisible by the stride) on the same state;
+    both against the oracle."""
+    w = configs.shrink(configs.C4A_PREFILL_128K, L=3064)
+    inp = gen.layer_inputs(w, seed=5100, p0=3000, T=64, state="random")
+    print("[dsa_layer] chunked prefill 3000..3063", flush=True)
+    Ly = _layer()
+    _, out1, lse1, idx1 = _run_gpu(w, inp)
+    st = Ly.state_from_inputs(inp, DEV)
+    outs = []
+    p = 0
+    j0 = inp["j0"]
+    for T in (5, 1, 1, 13, 44):
+        sub = dict(inp)
+        a, b = odsa.n_complete(3000 + p, 4, 8), odsa.n_complete(3000 + p + T, 4, 8)
+        for key in ("x", "kx", "q", "qi", "qi_scale", "wt"):
+            sub[key] = inp[key][:, p:p + T]
+        for key in ("logits_main", "logits_idx"):
+            sub[key] = inp[key][:, a - j0:b - j0]
+        sub.update(p0=3000 + p, T=T, j0=a, n_new=b - a)
+        _, o, _, _ = _run_gpu(w, sub, state=st, decode=(T == 1) or None)
+        outs.append(to_np(o))
+        p += T
+    got = np.concatenate(outs, axis=1)
+    check_close(got, to_np(out1), 2 * ATOL["bf16"], "chunked vs single")
+
+
+FULL = [configs.C4A_DECODE_64K, configs.C4A_DECODE_1M, configs.C128A_DECODE_1M]
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_layer_full_size_decode(w):
+    print(f"[dsa_layer_decode] {w.name} full size, seed={w.seed}", flush=True)
+    inp = gen.layer_inputs(w)
+    _, out, lse, idx = _run_gpu(w, inp)
+    ores = _oracle(w, inp)
+    swaps = _compare(w, inp, ores, out, lse, idx, label=w.name)
+    assert swaps <= 2
+
+
+def test_layer_full_size_prefill_sampled_rows():
+    w = configs.C4A_PREFILL_128K
+    print(f"[dsa_layer_prefill] {w.name} full size, seed={w.seed}", flush=True)
+    inp = gen.layer_inputs(w)
+    _, out, lse, idx = _run_gpu(w, inp)
+    rows = [0, 1, 2, 3, 4, 5, 127, 128, 1000, 2047, 3333, 4092, 4093, 4094, 4095]
+    ores = _oracle(w, inp, only=rows)
+    _compare(w, inp, ores, out, lse, idx, rows=rows, label=w.name)

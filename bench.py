@@ -67,17 +67,15 @@ def time_layer(w, sets, steps, warmup, decode):
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(args[i % len(args)], ws=ws, stream=stream)
-    ev_i = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(steps)]
-    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(steps)]
+    ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
+    ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
         a = args[i % len(args)]
-        a.ev_index[0], a.ev_index[1] = ev_i[i][0].cuda_event, ev_i[i][1].cuda_event
-        a.ev_attn[0], a.ev_attn[1] = ev_a[i][0].cuda_event, ev_a[i][1].cuda_event
+        a.ev_index[0], a.ev_index[1] = ev_i[i][0].handle, ev_i[i][1].handle
+        a.ev_attn[0], a.ev_attn[1] = ev_a[i][0].handle, ev_a[i][1].handle
         fn(a, ws=ws, stream=stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -86,8 +84,8 @@ def time_layer(w, sets, steps, warmup, decode):
     st = [o[3].item() for o in outs]
     assert all(s == 0 for s in st), f"device status {st}"
     ms = t0.elapsed_time(t1) / steps
-    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev_i) / steps
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev_a) / steps
+    idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / steps
+    attn_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_a) / steps
     return ms, idx_ms, attn_ms
 
 

@@ -214,3 +214,47 @@ def layer_prefill(args: LayerArgs, ws=None, stream=None, device="cuda"):
     _check(_lib.dsa_layer_prefill(ctypes.byref(args), ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream)))
     return ws
+
+
+# ------------------------------------------------------------- HIP events
+# Timing events that the library records on its stream (ev_index / ev_attn
+# fields) are plain hipEvent_t handles from the HIP runtime.
+_hip = None
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise ImportError("libamdhip64.so not found")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(c_vp)]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(c_f32), c_vp, c_vp]
+        _hip.hipEventDestroy.argtypes = [c_vp]
+        _hip.hipEventSynchronize.argtypes = [c_vp]
+    return _hip
+
+
+class HipEvent:
+    """A hipEvent_t owned from Python (created with timing enabled)."""
+
+    def __init__(self):
+        self.handle = c_vp()
+        if _hip_rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end):
+        ms = c_f32()
+        rc = _hip_rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)

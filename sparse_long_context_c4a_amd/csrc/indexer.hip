@@ -4,39 +4,56 @@
 //   I[i, j] = ks_j * sum_h (w_ih * qs_ih) * ReLU(q8_ih . k8_j)
 // ("DeepSeek DSA、DeepSeek V4与vLLM Hybrid KV Cache详解" 4.1: a cheap score per
 // (query, history entry), few heads, FP8).  The fp8 scales are positive, so
-// they factor out of the ReLU: the dot products run on the raw e4m3 codes.
+// they factor out of the ReLU and the dot products run on the e4m3 codes.
 //
-// Decode path (few query rows, long histories): k_index_fp8_stream streams
-// the fp8 keys from HBM once per query.  The 16 indexer heads are the M side
-// of one v_mfma_f32_16x16x128_f8f6f4 and 16 entries are its N side, so one
-// MFMA scores 16 entries; ReLU, the head weights and the head sum are a
+// Decode path (k_index_fp8_stream): the fp8 keys stream from HBM once per
+// query.  The 16 indexer heads are the M side of the matrix-core product and
+// 16 entries its N side; ReLU, the head weights and the head sum are a
 // 4-value in-lane reduce plus two cross-lane adds on the accumulator.  The
-// same pass builds a 4096-bin histogram of the scores' top 12 key bits, and
-// the last workgroup of a row picks the bin holding the k-th largest score.
-// k_topk_collect then writes every entry above that bin straight to the
-// output and gathers the bin's own entries as candidates, and
-// k_topk_final resolves the candidates exactly (radix select on
-// (score key, -index), so ties go to the lower index).
+// fp8 codes are widened to bf16 (exact: every e4m3fn value is a bf16 value)
+// and multiplied on the bf16 MFMA (4 x v_mfma_f32_16x16x32_bf16 per 16
+// entries): the gfx950 fp8 MFMA sums its 128 products with a shared
+// alignment that drops low-order bits (measured up to ~2^-13 of the largest
+// product), too coarse for Top-k near ties, while bf16 products are exact and
+// sum in fp32.
 //
-// Row path (many query rows, e.g. a prefill chunk): one workgroup per row
-// histograms, collects and resolves its own row.
+// Top-k without cross-workgroup atomics: each workgroup of 1024 entries keeps
+// the entries whose key is above t_b = (cap+1)-th largest key of the
+// workgroup (at most `cap` of them) as candidates and records t_b.  The final
+// pass selects the exact top k of the union of candidates (radix select on
+// (score key, complemented index), so ties go to the lower index) and checks
+// the certificate  k-th key >= max_b t_b : every entry left out has a key
+// below its workgroup's t_b, hence below the k-th, so the union's top k is
+// the row's top k.  If the certificate fails (adversarial score layouts,
+// massive ties) the row falls back to an exact radix select over all of its
+// scores, which the stream kernel also writes out.
+//
+// Row path (generic shapes, f32): scores go to memory and one workgroup per
+// row runs the exact radix select.
 #include "common.h"
 #include "internal.h"
 
 namespace dsa {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kBins = 4096;          // histogram on the top 12 bits of the key
+constexpr int kBins = 4096;           // row fallback histogram: top 12 key bits
 constexpr int kBinShift = 20;
-constexpr int kCtrl = 8;             // per-row control words
-constexpr int kCandCap = 8192;       // candidates resolved in LDS
-constexpr int kStreamEntries = 1024; // entries per workgroup in the stream kernel
-constexpr int kStreamThreads = 256;
+constexpr int kFinalCap = 8192;       // candidates resolved in LDS
+constexpr int kStreamEntries = 1024;  // entries per workgroup in the stream kernel
+constexpr int kThreads = 256;
 
-enum Ctrl { kDone = 0, kThrBin = 1, kAbove = 2, kAboveWritten = 3, kCandCount = 4, kBinCount = 5 };
+// Four fp8 e4m3fn codes per dword -> eight bf16 values (exact widening).
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 struct RowInfo {
   int64_t nv;
@@ -61,100 +78,244 @@ __device__ __forceinline__ RowInfo row_info(const int64_t* q_pos, int row, int s
   return r;
 }
 
-// After all workgroups of a row have added their histogram, the last one
-// finds the bin that holds the k-th largest key: count(bins > b1) < k <=
-// count(bins >= b1).  Requires blockDim.x == 256.
-__device__ void pick_threshold_bin(const uint32_t* hist, uint32_t* ctrl, int k) {
-  __shared__ uint32_t part[256];
-  __shared__ uint32_t found[3];
+// (key, complemented index): larger composite = larger score, then lower j.
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t j) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint64_t>(0xffffffffu - j);
+}
+__device__ __forceinline__ uint32_t comp_index(uint64_t c) {
+  return 0xffffffffu - static_cast<uint32_t>(c);
+}
+
+__device__ __forceinline__ void emit(int32_t* idx_row, float* score_row, uint32_t pos, uint32_t j,
+                                     float sc) {
+  idx_row[pos] = static_cast<int32_t>(j);
+  if (score_row) score_row[pos] = sc;
+}
+
+// ------------------------------------------------------- block primitives
+// 256-thread inclusive suffix sums of cnt[0..255]: the digit d with
+// sum(cnt[d+1..]) < need <= sum(cnt[d..]), the count above d, the count at
+// d and the total.  If the total is below need, d = 0xffffffff.
+struct Digit {
+  uint32_t d, above, at, total;
+};
+
+__device__ Digit find_digit(const uint32_t* cnt, uint32_t need) {
+  __shared__ uint32_t sfx[256];
+  __shared__ Digit res;
   const int t = threadIdx.x;
-  // thread t owns bins [4095 - 16 t - 15, 4095 - 16 t] (descending)
-  uint32_t local[16];
-  uint32_t sum = 0;
+  const uint32_t c = cnt[t];
+  sfx[t] = c;
+  if (t == 0) res.d = 0xffffffffu;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t add = (t + off < 256) ? sfx[t + off] : 0u;
+    __syncthreads();
+    sfx[t] += add;
+    __syncthreads();
+  }
+  const uint32_t incl = sfx[t], excl = incl - c;
+  if (excl < need && incl >= need) res = Digit{static_cast<uint32_t>(t), excl, c, 0u};
+  __syncthreads();
+  Digit r = res;
+  r.total = sfx[0];
+  __syncthreads();
+  return r;
+}
+
+// rank-th largest (1-based) of the nonzero 32-bit keys in LDS; 0 if fewer.
+__device__ uint32_t kth_largest_key(const uint32_t* keys, int n, uint32_t rank) {
+  __shared__ uint32_t cnt[256];
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, mask = 0, need = rank;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    cnt[t] = 0;
+    __syncthreads();
+    for (int i = t; i < n; i += kThreads) {
+      const uint32_t k = keys[i];
+      if (k != 0 && (k & mask) == prefix) atomicAdd(&cnt[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const Digit dg = find_digit(cnt, need);
+    if (dg.d == 0xffffffffu) return 0;
+    prefix |= dg.d << shift;
+    mask |= 255u << shift;
+    need -= dg.above;
+  }
+  return prefix;
+}
+
+// Exact top-`need` among n distinct 64-bit composites in LDS: returns the
+// smallest composite that is kept (keep every v >= result).
+__device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t need) {
+  __shared__ uint32_t cnt[256];
+  const int t = threadIdx.x;
+  uint64_t prefix = 0, mask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    cnt[t] = 0;
+    __syncthreads();
+    for (int i = t; i < n; i += kThreads) {
+      const uint64_t v = c[i];
+      if ((v & mask) == prefix) atomicAdd(&cnt[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const Digit dg = find_digit(cnt, need);
+    prefix |= static_cast<uint64_t>(dg.d) << shift;
+    mask |= static_cast<uint64_t>(255u) << shift;
+    need -= dg.above;
+    if (dg.at == need) return prefix;  // every composite with this prefix is kept
+  }
+  return prefix;
+}
+
+// Rows with n_vis <= k: every visible entry, in index order, then padding.
+__device__ void emit_all_visible(const float* srow, int64_t nv, int k, int32_t* idx_row,
+                                 float* score_row) {
+  for (int i = threadIdx.x; i < k; i += blockDim.x) {
+    if (i < nv) emit(idx_row, score_row, i, i, srow ? srow[i] : 0.f);
+    else {
+      idx_row[i] = -1;
+      if (score_row) score_row[i] = __uint_as_float(0x7fc00000u);
+    }
+  }
+}
+
+// Exact top-k of one row from its scores in global memory (nv > k):
+// histogram of the top 12 key bits -> threshold bin; entries above it go
+// straight out, the bin's entries are resolved exactly (in LDS when they
+// fit, else by streaming radix passes).  cand_s: kFinalCap u64 of LDS,
+// h_s: kBins u32 of LDS.
+__device__ void row_select_from_scores(const float* srow, int64_t nv, int k, int32_t* irow,
+                                       float* orow, uint64_t* cand_s, uint32_t* h_s) {
+  __shared__ uint32_t cnt_above, cnt_cand, out_pos;
+  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t thr_s[3];
+  __shared__ uint32_t cnt[256];
+  const int t = threadIdx.x;
+  for (int i = t; i < kBins; i += kThreads) h_s[i] = 0;
+  if (t == 0) cnt_above = cnt_cand = out_pos = 0;
+  __syncthreads();
+  for (int64_t j = t; j < nv; j += kThreads) atomicAdd(&h_s[order_key(srow[j]) >> kBinShift], 1u);
+  __syncthreads();
+  // threshold bin: suffix counts over 4096 bins, 16 per thread
+  uint32_t local[16], sum = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    local[i] = __hip_atomic_load(&hist[kBins - 1 - (16 * t + i)], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    local[i] = h_s[kBins - 1 - (16 * t + i)];
     sum += local[i];
   }
   part[t] = sum;
-  if (t == 0) found[0] = 0xffffffffu;
   __syncthreads();
-  // exclusive prefix over threads (descending bins)
   uint32_t before = 0;
   for (int i = 0; i < t; ++i) before += part[i];
   if (before < static_cast<uint32_t>(k) && before + sum >= static_cast<uint32_t>(k)) {
     uint32_t c = before;
     for (int i = 0; i < 16; ++i) {
       if (c + local[i] >= static_cast<uint32_t>(k)) {
-        found[0] = kBins - 1 - (16 * t + i);
-        found[1] = c;
-        found[2] = local[i];
+        thr_s[0] = kBins - 1 - (16 * t + i);
+        thr_s[1] = c;
+        thr_s[2] = local[i];
         break;
       }
       c += local[i];
     }
   }
   __syncthreads();
-  if (t == 0) {
-    ctrl[kThrBin] = found[0];
-    ctrl[kAbove] = found[1];
-    ctrl[kBinCount] = found[2];
+  const uint32_t thr = thr_s[0], above = thr_s[1], at = thr_s[2];
+  const bool fits = at <= static_cast<uint32_t>(kFinalCap);
+  for (int64_t j = t; j < nv; j += kThreads) {
+    const float sc = srow[j];
+    const uint32_t key = order_key(sc);
+    const uint32_t bin = key >> kBinShift;
+    if (bin > thr) {
+      const uint32_t p = atomicAdd(&cnt_above, 1u);
+      if (p < static_cast<uint32_t>(k)) emit(irow, orow, p, static_cast<uint32_t>(j), sc);
+    } else if (bin == thr && fits) {
+      const uint32_t p = atomicAdd(&cnt_cand, 1u);
+      if (p < static_cast<uint32_t>(kFinalCap)) cand_s[p] = composite(key, static_cast<uint32_t>(j));
+    }
   }
+  __syncthreads();
+  const uint32_t need = static_cast<uint32_t>(k) - above;
+  uint64_t cut;
+  if (fits) {
+    cut = kth_largest_composite(cand_s, static_cast<int>(at), need);
+  } else {
+    // streaming radix over the bin's entries, composites built on the fly
+    uint64_t prefix = static_cast<uint64_t>(thr) << (32 + kBinShift);
+    uint64_t mask = static_cast<uint64_t>(0xfffu) << (32 + kBinShift);
+    uint32_t rem = need;
+    for (int shift = 48; shift >= 0; shift -= 8) {
+      cnt[t] = 0;
+      __syncthreads();
+      for (int64_t j = t; j < nv; j += kThreads) {
+        const uint64_t v = composite(order_key(srow[j]), static_cast<uint32_t>(j));
+        if ((v & mask) == prefix) atomicAdd(&cnt[(v >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const Digit dg = find_digit(cnt, rem);
+      prefix |= static_cast<uint64_t>(dg.d) << shift;
+      mask |= static_cast<uint64_t>(255u) << shift;
+      rem -= dg.above;
+      if (dg.at == rem) break;
+    }
+    cut = prefix;
+  }
+  // emit the threshold bin's kept entries
+  if (fits) {
+    for (int i = t; i < static_cast<int>(at); i += kThreads) {
+      const uint64_t v = cand_s[i];
+      if (v >= cut) {
+        const uint32_t p = atomicAdd(&out_pos, 1u);
+        if (p < need)
+          emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+      }
+    }
+  } else {
+    for (int64_t j = t; j < nv; j += kThreads) {
+      const uint64_t v = composite(order_key(srow[j]), static_cast<uint32_t>(j));
+      if (v >= cut && (v >> (32 + kBinShift)) == thr) {
+        const uint32_t p = atomicAdd(&out_pos, 1u);
+        if (p < need) emit(irow, orow, above + p, comp_index(v), srow[j]);
+      }
+    }
+  }
+  __syncthreads();
 }
 
-// Histogram flush + last-workgroup-done detection for the split path.
-__device__ void finish_hist(uint32_t* h_s, uint32_t* hist, uint32_t* ctrl, int k) {
-  __shared__ int is_last;
-  __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
-    const uint32_t v = h_s[i];
-    if (v) atomicAdd(&hist[i], v);
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&ctrl[kDone], 1u);
-    is_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (is_last) {
-    __threadfence();
-    pick_threshold_bin(hist, ctrl, k);
-  }
-}
-
-// ---------------------------------------------------------------- fp8 MFMA
+// --------------------------------------------------- stream (decode) kernel
 // Operand layout: lane l owns entry (or head) n = l % 16 and, within the
 // 128-byte vector, bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16)
-// with g = l / 16.  A and B use the same byte-to-k assignment, so the MFMA
-// sums every one of the 128 products exactly once; each of the two 16-byte
+// with g = l / 16; MFMA c of the four takes the lane's bytes [8 c, 8 c + 8)
+// of those 32.  A and B use the same byte-to-k assignment, so the four MFMAs
+// sum every one of the 128 products exactly once; each of the two 16-byte
 // loads of a wave covers 64 contiguous bytes of 16 entries.
-template <bool kHist>
-__global__ __launch_bounds__(kStreamThreads) void k_index_fp8_stream(
+template <bool kCand>
+__global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
     const int64_t* __restrict__ q_pos, int Tq, int Hi, int s, int S, int64_t e_cap,
     int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ ctrl, int k, uint32_t* status) {
-  __shared__ uint32_t h_s[kHist ? kBins : 1];
+    uint64_t* __restrict__ cand, uint2* __restrict__ meta, int cap, uint32_t* status) {
+  __shared__ uint32_t s_key[kCand ? kStreamEntries : 1];
+  __shared__ uint32_t cand_cnt;
   const int row = blockIdx.y, b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, blockIdx.x == 0 && tid == 0);
   const int64_t nv = ri.nv;
-  if constexpr (kHist) {
-    for (int i = tid; i < kBins; i += kStreamThreads) h_s[i] = 0;
-    __syncthreads();
-  }
   const int64_t e_begin = static_cast<int64_t>(blockIdx.x) * kStreamEntries;
+  constexpr int kGroups = kStreamEntries / 4 / 16;  // 16-entry groups per wave
+  constexpr int kUnroll = 4;
   if (e_begin < nv) {
-    v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint4 qlo = {0u, 0u, 0u, 0u}, qhi = {0u, 0u, 0u, 0u};
     if (n < Hi) {
       const uint4* qp = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * Hi + n) * 128);
-      const uint4 lo = qp[g], hi = qp[4 + g];
-      a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      qlo = qp[g];
+      qhi = qp[4 + g];
     }
+    const v8bf a0 = fp8x8_to_bf16(qlo.x, qlo.y), a1 = fp8x8_to_bf16(qlo.z, qlo.w);
+    const v8bf a2 = fp8x8_to_bf16(qhi.x, qhi.y), a3 = fp8x8_to_bf16(qhi.z, qhi.w);
     float wv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -168,60 +329,79 @@ __global__ __launch_bounds__(kStreamThreads) void k_index_fp8_stream(
     const uint8_t* kb = keys + static_cast<int64_t>(b) * e_cap * 128;
     const float* ksb = k_scale + static_cast<int64_t>(b) * e_cap;
     float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-    constexpr int kGroups = kStreamEntries / 4 / 16;  // 16-entry groups per wave
-    constexpr int kUnroll = 4;
     const int64_t wbase = e_begin + wave * (kStreamEntries / 4);
 #pragma unroll 1
     for (int gi = 0; gi < kGroups; gi += kUnroll) {
-      v8i bk[kUnroll];
+      uint4 blo[kUnroll], bhi[kUnroll];
       float ks[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t ent = wbase + (gi + u) * 16 + n;
         if (ent < nv) {
           const uint4* kp = reinterpret_cast<const uint4*>(kb + ent * 128);
-          const uint4 lo = kp[g], hi = kp[4 + g];
-          bk[u] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          blo[u] = kp[g];
+          bhi[u] = kp[4 + g];
           ks[u] = ksb[ent];
         } else {
-          bk[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          blo[u] = bhi[u] = uint4{0u, 0u, 0u, 0u};
           ks[u] = 0.f;
         }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        // fp8 e4m3 x fp8 e4m3, scales unused (0) -> the plain MFMA
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bk[u], acc, 0, 0, 0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp8x8_to_bf16(blo[u].x, blo[u].y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp8x8_to_bf16(blo[u].z, blo[u].w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, fp8x8_to_bf16(bhi[u].x, bhi[u].y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, fp8x8_to_bf16(bhi[u].z, bhi[u].w), acc, 0, 0, 0);
         // lane holds rows (heads) 4g..4g+3 of column (entry) n
         float v = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
                   wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
         const float sc = v * ks[u];
-        const int64_t ent = wbase + (gi + u) * 16 + n;
-        if (g == 0 && ent < nv) {
-          srow[ent] = sc;
-          if constexpr (kHist) atomicAdd(&h_s[order_key(sc) >> kBinShift], 1u);
+        const int local = wave * (kStreamEntries / 4) + (gi + u) * 16 + n;
+        const int64_t ent = e_begin + local;
+        if (g == 0) {
+          if (ent < nv) srow[ent] = sc;
+          if constexpr (kCand) s_key[local] = ent < nv ? order_key(sc) : 0u;
         }
       }
     }
+  } else if constexpr (kCand) {
+    for (int i = tid; i < kStreamEntries; i += kThreads) s_key[i] = 0u;
   }
-  if constexpr (kHist) finish_hist(h_s, hist + static_cast<int64_t>(row) * kBins,
-                                   ctrl + static_cast<int64_t>(row) * kCtrl, k);
+  if constexpr (kCand) {
+    // workgroup candidates: keys above the (cap+1)-th largest of this block
+    if (tid == 0) cand_cnt = 0;
+    __syncthreads();
+    const uint32_t kth = kth_largest_key(s_key, kStreamEntries, static_cast<uint32_t>(cap) + 1u);
+    const uint32_t tb = kth == 0 ? 1u : kth + 1u;  // fewer than cap+1 valid keys: take all
+    uint64_t* crow = cand + (static_cast<int64_t>(row) * gridDim.x + blockIdx.x) * cap;
+    for (int i = tid; i < kStreamEntries; i += kThreads) {
+      const uint32_t key = s_key[i];
+      if (key != 0u && key >= tb) {
+        const uint32_t p = atomicAdd(&cand_cnt, 1u);
+        if (p < static_cast<uint32_t>(cap))
+          crow[p] = composite(key, static_cast<uint32_t>(e_begin + i));
+      }
+    }
+    __syncthreads();
+    if (tid == 0)
+      meta[static_cast<int64_t>(row) * gridDim.x + blockIdx.x] =
+          uint2{e_begin < nv ? tb : 0u, min(cand_cnt, static_cast<uint32_t>(cap))};
+  }
 }
 
 // ------------------------------------------------------------- generic VALU
-// Any Hi, Di; q and keys f32 or fp8.  One entry per thread.
-template <typename T, bool kHist>
-__global__ __launch_bounds__(256) void k_index_generic(
+// Any Hi, Di; q and keys f32 or fp8.  One entry per thread; scores only.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_index_generic(
     const T* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const T* __restrict__ keys, const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
     int Tq, int Hi, int Di, int s, int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end,
-    float* __restrict__ scores, int64_t ld_scores, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ ctrl, int k, uint32_t* status) {
+    float* __restrict__ scores, int64_t ld_scores, uint32_t* status) {
   extern __shared__ float q_s[];  // [Hi * Di] then [Hi] weights
-  __shared__ uint32_t h_s[kHist ? kBins : 1];
   const int row = blockIdx.y, b = row / Tq, tid = threadIdx.x;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, blockIdx.x == 0 && tid == 0);
   const int64_t nv = ri.nv;
@@ -235,8 +415,6 @@ __global__ __launch_bounds__(256) void k_index_generic(
     const int64_t o = static_cast<int64_t>(row) * Hi + h;
     w_s[h] = w[o] * ((sizeof(T) == 1 && q_scale) ? q_scale[o] : 1.0f);
   }
-  if constexpr (kHist)
-    for (int i = tid; i < kBins; i += blockDim.x) h_s[i] = 0;
   __syncthreads();
   const int64_t ent = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid;
   if (ent < nv) {
@@ -254,342 +432,181 @@ __global__ __launch_bounds__(256) void k_index_generic(
     }
     if constexpr (sizeof(T) == 1) tot *= k_scale[static_cast<int64_t>(b) * e_cap + ent];
     scores[static_cast<int64_t>(row) * ld_scores + ent] = tot;
-    if constexpr (kHist) atomicAdd(&h_s[order_key(tot) >> kBinShift], 1u);
-  }
-  if constexpr (kHist) finish_hist(h_s, hist + static_cast<int64_t>(row) * kBins,
-                                   ctrl + static_cast<int64_t>(row) * kCtrl, k);
-}
-
-// ------------------------------------------------------------------ Top-k
-__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t j) {
-  // low 20 bits of the key (the top 12 are the threshold bin), then the
-  // complemented index so that, among equal scores, the lower index wins
-  return (static_cast<uint64_t>(key & 0xfffffu) << 32) | static_cast<uint64_t>(0xffffffffu - j);
-}
-
-__device__ __forceinline__ void emit(int32_t* idx_row, float* score_row, int pos, uint32_t j,
-                                     float sc) {
-  idx_row[pos] = static_cast<int32_t>(j);
-  if (score_row) score_row[pos] = sc;
-}
-
-// Block-wide (256 threads) search: digit d such that the count of elements
-// with digit > d is < need <= count with digit >= d.  cnt[256] in LDS.
-__device__ void find_digit(const uint32_t* cnt, uint32_t need, uint32_t* out_digit,
-                           uint32_t* out_above, uint32_t* out_at) {
-  __shared__ uint32_t sfx[256];
-  const int t = threadIdx.x;
-  // inclusive suffix sum over digits 255..t
-  const uint32_t c = cnt[t];
-  sfx[t] = c;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t add = (t + off < 256) ? sfx[t + off] : 0u;
-    __syncthreads();
-    sfx[t] += add;
-    __syncthreads();
-  }
-  const uint32_t incl = sfx[t], excl = incl - c;
-  if (excl < need && incl >= need) {
-    *out_digit = t;
-    *out_above = excl;
-    *out_at = c;
-  }
-  __syncthreads();
-}
-
-// Select the `need` largest composites among the candidates of one row and
-// emit them at positions base_pos .. base_pos + need - 1.  Candidates come
-// either from an LDS array (n_lds of them) or, when they did not fit, from
-// the row's scores in global memory filtered on the threshold bin.
-// blockDim.x == 256.
-__device__ void resolve_candidates(const uint64_t* cand, int n_lds, bool from_global,
-                                   const float* srow, int64_t nv, uint32_t thr_bin, uint32_t need,
-                                   int32_t* idx_row, float* score_row, int base_pos) {
-  __shared__ uint32_t cnt[256];
-  __shared__ uint32_t dig[3];
-  __shared__ uint32_t out_pos;
-  const int t = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
-  uint32_t remaining = need;
-  bool take_all = false;
-  for (int shift = 48; shift >= 0; shift -= 8) {
-    cnt[t] = 0;
-    __syncthreads();
-    if (from_global) {
-      for (int64_t j = t; j < nv; j += 256) {
-        const uint32_t key = order_key(srow[j]);
-        if ((key >> kBinShift) != thr_bin) continue;
-        const uint64_t c = composite(key, static_cast<uint32_t>(j));
-        if ((c & mask) == prefix) atomicAdd(&cnt[(c >> shift) & 255u], 1u);
-      }
-    } else {
-      for (int i = t; i < n_lds; i += 256) {
-        const uint64_t c = cand[i];
-        if ((c & mask) == prefix) atomicAdd(&cnt[(c >> shift) & 255u], 1u);
-      }
-    }
-    __syncthreads();
-    find_digit(cnt, remaining, &dig[0], &dig[1], &dig[2]);
-    const uint32_t d = dig[0], above = dig[1], at = dig[2];
-    prefix |= static_cast<uint64_t>(d) << shift;
-    mask |= static_cast<uint64_t>(255u) << shift;
-    remaining -= above;
-    if (at == remaining) {  // every element with this prefix is in: done
-      take_all = true;
-      break;
-    }
-    __syncthreads();
-  }
-  (void)take_all;
-  // emit: composites above the prefix (on the resolved bits) or equal to it
-  if (t == 0) out_pos = 0;
-  __syncthreads();
-  auto consider = [&](uint64_t c) {
-    if ((c & mask) >= prefix) {
-      const uint32_t p = atomicAdd(&out_pos, 1u);
-      if (p >= need) return;  // cannot happen with distinct composites; keeps writes in bounds
-      const uint32_t j = 0xffffffffu - static_cast<uint32_t>(c);
-      const uint32_t key = (thr_bin << kBinShift) | static_cast<uint32_t>(c >> 32);
-      emit(idx_row, score_row, base_pos + p, j, key_to_float(key));
-    }
-  };
-  if (from_global) {
-    for (int64_t j = t; j < nv; j += 256) {
-      const uint32_t key = order_key(srow[j]);
-      if ((key >> kBinShift) == thr_bin) consider(composite(key, static_cast<uint32_t>(j)));
-    }
-  } else {
-    for (int i = t; i < n_lds; i += 256) consider(cand[i]);
-  }
-  __syncthreads();
-}
-
-// Rows with n_vis <= k: every visible entry, in index order, then padding.
-__device__ void emit_all_visible(const float* srow, int64_t nv, int k, int32_t* idx_row,
-                                 float* score_row) {
-  for (int i = threadIdx.x; i < k; i += blockDim.x) {
-    if (i < nv) emit(idx_row, score_row, i, i, srow ? srow[i] : 0.f);
-    else {
-      idx_row[i] = -1;
-      if (score_row) score_row[i] = __uint_as_float(0x7fc00000u);
-    }
   }
 }
 
-// Split path, pass 2: entries above the threshold bin go straight out; the
-// bin's own entries become candidates.
-__global__ __launch_bounds__(256) void k_topk_collect(
+// ------------------------------------------------------------ final passes
+// Candidate path: union of the workgroups' candidates, exact top k, and the
+// certificate; falls back to the full-row select when it does not hold.
+__global__ __launch_bounds__(kThreads) void k_topk_cand_final(
     const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
-    int s, int S, int64_t nv_cap, int64_t max_pos_end, uint32_t* __restrict__ ctrl,
-    uint64_t* __restrict__ cand, int32_t* __restrict__ idx_out, float* __restrict__ score_out,
-    int k) {
-  const int row = blockIdx.y;
-  const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
-  const int64_t nv = ri.nv;
-  if (nv <= k) return;
-  uint32_t* c = ctrl + static_cast<int64_t>(row) * kCtrl;
-  const uint32_t thr = c[kThrBin];
-  const float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-  int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
-  float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
-  uint64_t* crow = cand + static_cast<int64_t>(row) * kCandCap;
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < nv;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const float sc = srow[j];
-    const uint32_t key = order_key(sc);
-    const uint32_t bin = key >> kBinShift;
-    if (bin > thr) {
-      const uint32_t p = atomicAdd(&c[kAboveWritten], 1u);
-      if (p < static_cast<uint32_t>(k)) emit(irow, orow, p, static_cast<uint32_t>(j), sc);
-    } else if (bin == thr) {
-      const uint32_t p = atomicAdd(&c[kCandCount], 1u);
-      if (p < kCandCap) crow[p] = composite(key, static_cast<uint32_t>(j));
-    }
-  }
-}
-
-// Split path, pass 3: one workgroup per row resolves the threshold bin.
-__global__ __launch_bounds__(256) void k_topk_final(
-    const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
-    int s, int S, int64_t nv_cap, int64_t max_pos_end, const uint32_t* __restrict__ ctrl,
-    const uint64_t* __restrict__ cand, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, int k, uint32_t* status) {
-  __shared__ uint64_t cand_s[kCandCap];
-  const int row = blockIdx.x;
-  const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
-  const int64_t nv = ri.nv;
-  const float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-  int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
-  float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
-  if (nv <= k || scores == nullptr) {
-    if (nv > k && threadIdx.x == 0) set_status(status, DSA_DEVERR_NO_INDEX);
-    emit_all_visible(nullptr, ri.ok ? std::min<int64_t>(nv, k) : 0, k, irow, orow);
-    return;
-  }
-  const uint32_t* c = ctrl + static_cast<int64_t>(row) * kCtrl;
-  const uint32_t thr = c[kThrBin], above = c[kAbove], at = c[kBinCount];
-  const uint32_t need = static_cast<uint32_t>(k) - above;
-  const bool fits = at <= static_cast<uint32_t>(kCandCap);
-  if (fits) {
-    const uint64_t* crow = cand + static_cast<int64_t>(row) * kCandCap;
-    for (int i = threadIdx.x; i < static_cast<int>(at); i += blockDim.x) cand_s[i] = crow[i];
-  }
-  __syncthreads();
-  resolve_candidates(cand_s, fits ? static_cast<int>(at) : 0, !fits, srow, nv, thr, need, irow,
-                     orow, static_cast<int>(above));
-}
-
-// Row path: one workgroup (256 threads) per query row does all three passes.
-__global__ __launch_bounds__(256) void k_topk_rows(
-    const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
-    int s, int S, int64_t nv_cap, int64_t max_pos_end, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, int k, uint32_t* status) {
-  __shared__ uint32_t h_s[kBins];
-  __shared__ uint64_t cand_s[kCandCap];
-  __shared__ uint32_t above_cnt, cand_cnt;
+    int s, int S, int64_t nv_cap, int64_t max_pos_end, const uint64_t* __restrict__ cand,
+    const uint2* __restrict__ meta, int nb, int cap, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out, int k) {
+  __shared__ uint64_t cand_s[kFinalCap];
+  __shared__ uint32_t h_s[kBins];  // block offsets here, then the fallback histogram
+  __shared__ uint32_t part[kThreads];
+  __shared__ uint32_t tmax_s, total_s, out_pos;
   const int row = blockIdx.x, t = threadIdx.x;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
   const int64_t nv = ri.nv;
   const float* srow = scores + static_cast<int64_t>(row) * ld_scores;
   int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
   float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
-  if (nv <= k || scores == nullptr) {
-    if (nv > k && t == 0) set_status(status, DSA_DEVERR_NO_INDEX);
-    emit_all_visible(scores ? srow : nullptr, ri.ok ? std::min<int64_t>(nv, k) : 0, k, irow, orow);
+  if (nv <= k) {
+    emit_all_visible(srow, nv, k, irow, orow);
     return;
   }
-  for (int i = t; i < kBins; i += 256) h_s[i] = 0;
-  if (t == 0) above_cnt = cand_cnt = 0;
+  const uint2* mrow = meta + static_cast<int64_t>(row) * nb;
+  if (t == 0) tmax_s = total_s = out_pos = 0;
   __syncthreads();
-  for (int64_t j = t; j < nv; j += 256) atomicAdd(&h_s[order_key(srow[j]) >> kBinShift], 1u);
+  // exclusive offsets of the per-block counts (nb <= kBins) and max t_b
+  const int per = (nb + kThreads - 1) / kThreads;
+  const int b0 = min(nb, t * per), b1 = min(nb, b0 + per);
+  uint32_t sum = 0, tm = 0;
+  for (int b = b0; b < b1; ++b) {
+    const uint2 m = mrow[b];
+    sum += m.y;
+    tm = max(tm, m.x);
+  }
+  atomicMax(&tmax_s, tm);
+  part[t] = sum;
   __syncthreads();
-  __shared__ uint32_t ctrl_s[kCtrl];
-  {
-    // same search as pick_threshold_bin, on the LDS histogram
-    __shared__ uint32_t part[256];
-    uint32_t local[16];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      local[i] = h_s[kBins - 1 - (16 * t + i)];
-      sum += local[i];
+  uint32_t before = 0;
+  for (int i = 0; i < t; ++i) before += part[i];
+  for (int b = b0; b < b1; ++b) {
+    h_s[b] = before;
+    before += mrow[b].y;
+  }
+  if (t == kThreads - 1) total_s = before;
+  __syncthreads();
+  const uint32_t total = total_s, tmax = tmax_s;
+  bool ok = total >= static_cast<uint32_t>(k) && total <= static_cast<uint32_t>(kFinalCap);
+  uint64_t cut = 0;
+  if (ok) {
+    const int slots = nb * cap;
+    const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
+    for (int sl = t; sl < slots; sl += kThreads) {
+      const int b = sl / cap, i = sl % cap;
+      if (static_cast<uint32_t>(i) < mrow[b].y) cand_s[h_s[b] + i] = crow[sl];
     }
-    part[t] = sum;
     __syncthreads();
-    uint32_t before = 0;
-    for (int i = 0; i < t; ++i) before += part[i];
-    if (before < static_cast<uint32_t>(k) && before + sum >= static_cast<uint32_t>(k)) {
-      uint32_t c = before;
-      for (int i = 0; i < 16; ++i) {
-        if (c + local[i] >= static_cast<uint32_t>(k)) {
-          ctrl_s[kThrBin] = kBins - 1 - (16 * t + i);
-          ctrl_s[kAbove] = c;
-          ctrl_s[kBinCount] = local[i];
-          break;
-        }
-        c += local[i];
+    cut = kth_largest_composite(cand_s, static_cast<int>(total), static_cast<uint32_t>(k));
+    ok = static_cast<uint32_t>(cut >> 32) >= tmax;  // the certificate
+  }
+  if (ok) {
+    for (int i = t; i < static_cast<int>(total); i += kThreads) {
+      const uint64_t v = cand_s[i];
+      if (v >= cut) {
+        const uint32_t p = atomicAdd(&out_pos, 1u);
+        if (p < static_cast<uint32_t>(k))
+          emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
       }
     }
-    __syncthreads();
-  }
-  const uint32_t thr = ctrl_s[kThrBin], above = ctrl_s[kAbove], at = ctrl_s[kBinCount];
-  const bool fits = at <= static_cast<uint32_t>(kCandCap);
-  for (int64_t j = t; j < nv; j += 256) {
-    const float sc = srow[j];
-    const uint32_t key = order_key(sc);
-    const uint32_t bin = key >> kBinShift;
-    if (bin > thr) {
-      const uint32_t p = atomicAdd(&above_cnt, 1u);
-      if (p < static_cast<uint32_t>(k)) emit(irow, orow, p, static_cast<uint32_t>(j), sc);
-    } else if (bin == thr && fits) {
-      const uint32_t p = atomicAdd(&cand_cnt, 1u);
-      if (p < static_cast<uint32_t>(kCandCap)) cand_s[p] = composite(key, static_cast<uint32_t>(j));
-    }
+    return;
   }
   __syncthreads();
-  resolve_candidates(cand_s, fits ? static_cast<int>(at) : 0, !fits, srow, nv, thr,
-                     static_cast<uint32_t>(k) - above, irow, orow, static_cast<int>(above));
+  row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
 }
 
-struct WsLayout {
+// Row path: one workgroup per query row selects from the row's scores.
+__global__ __launch_bounds__(kThreads) void k_topk_rows(
+    const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
+    int s, int S, int64_t nv_cap, int64_t max_pos_end, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out, int k, uint32_t* status) {
+  __shared__ uint64_t cand_s[kFinalCap];
+  __shared__ uint32_t h_s[kBins];
+  const int row = blockIdx.x;
+  const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
+  const int64_t nv = ri.nv;
+  const float* srow = scores ? scores + static_cast<int64_t>(row) * ld_scores : nullptr;
+  int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
+  float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
+  if (nv <= k || scores == nullptr) {
+    if (nv > k && threadIdx.x == 0) set_status(status, DSA_DEVERR_NO_INDEX);
+    emit_all_visible(srow, std::min<int64_t>(nv, k), k, irow, orow);
+    return;
+  }
+  row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
+}
+
+struct Plan {
   int64_t nv_cap, ld;
-  size_t off_scores, off_hist, off_ctrl, off_cand, total;
-  bool split;
+  bool mfma, cand;
+  int nb, cap;
+  size_t off_scores, off_cand, off_meta, total;
 };
 
-WsLayout layout(const dsa_index_args& a) {
-  WsLayout L{};
+Plan plan(const dsa_index_args& a) {
+  Plan p{};
   const int64_t rows = static_cast<int64_t>(a.n_seqs) * a.queries_per_seq;
-  L.nv_cap = std::min<int64_t>(a.e_cap, n_complete(a.max_pos_end - 1, a.stride, a.span));
-  if (L.nv_cap < 0) L.nv_cap = 0;
-  L.ld = (L.nv_cap + 63) / 64 * 64;
-  L.split = a.queries_per_seq < 8 || rows < 256;
+  p.nv_cap = std::min<int64_t>(a.e_cap, n_complete(a.max_pos_end - 1, a.stride, a.span));
+  if (p.nv_cap < 0) p.nv_cap = 0;
+  p.ld = (p.nv_cap + 63) / 64 * 64;
+  p.mfma = a.keys != nullptr && a.dtype == DSA_FP8_E4M3 && a.dim == 128 && a.heads <= 16;
+  p.nb = static_cast<int>(ceil_div(p.nv_cap, kStreamEntries));
+  // candidates per workgroup: enough that the union is about 4k, at least 32
+  p.cap = static_cast<int>(std::min<int64_t>(
+      512, std::max<int64_t>(32, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nb)))));
+  p.cand = p.mfma && p.nv_cap > a.k && p.nb <= kBins;
   size_t off = 0;
-  L.off_scores = off;
-  off = align_up(off + static_cast<size_t>(rows) * L.ld * sizeof(float));
-  L.off_hist = off;
-  if (L.split) off = align_up(off + static_cast<size_t>(rows) * kBins * sizeof(uint32_t));
-  L.off_ctrl = off;
-  if (L.split) off = align_up(off + static_cast<size_t>(rows) * kCtrl * sizeof(uint32_t));
-  L.off_cand = off;
-  if (L.split) off = align_up(off + static_cast<size_t>(rows) * kCandCap * sizeof(uint64_t));
-  L.total = off;
-  return L;
+  p.off_scores = off;
+  off = align_up(off + static_cast<size_t>(rows) * p.ld * sizeof(float));
+  p.off_cand = off;
+  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nb * p.cap * sizeof(uint64_t));
+  p.off_meta = off;
+  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nb * sizeof(uint2));
+  p.total = off;
+  return p;
 }
 
 }  // namespace
 
-size_t index_topk_ws_bytes(const dsa_index_args& a) { return layout(a).total; }
+size_t index_topk_ws_bytes(const dsa_index_args& a) { return plan(a).total; }
 
 dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) {
-  const WsLayout L = layout(a);
+  const Plan P = plan(a);
   const int rows = a.n_seqs * a.queries_per_seq;
   char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base + L.off_scores);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
-  uint32_t* ctrl = reinterpret_cast<uint32_t*>(base + L.off_ctrl);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
+  float* scores = reinterpret_cast<float*>(base + P.off_scores);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + P.off_cand);
+  uint2* meta = reinterpret_cast<uint2*>(base + P.off_meta);
   const bool no_keys = a.keys == nullptr;  // only allowed when k >= every n_vis
   dsa_status rc;
-  if (L.split && !no_keys) {
-    rc = launch_zero(hist, L.off_cand - L.off_hist, st);
-    if (rc != DSA_OK) return rc;
-  }
-  if (!no_keys && L.nv_cap > 0) {
+  if (!no_keys && P.nv_cap > 0) {
     if (a.ev_index[0]) {
       rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a.ev_index[0]), st), "event record");
       if (rc != DSA_OK) return rc;
     }
-    const bool mfma = a.dtype == DSA_FP8_E4M3 && a.dim == 128 && a.heads <= 16;
-    if (mfma) {
-      dim3 grid(static_cast<unsigned>(ceil_div(L.nv_cap, kStreamEntries)), rows);
-      if (L.split)
-        hipLaunchKernelGGL(k_index_fp8_stream<true>, grid, dim3(kStreamThreads), 0, st,
+    if (P.mfma) {
+      dim3 grid(static_cast<unsigned>(P.nb), rows);
+      if (P.cand)
+        hipLaunchKernelGGL(k_index_fp8_stream<true>, grid, dim3(kThreads), 0, st,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
-                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, L.nv_cap,
-                           a.max_pos_end, scores, L.ld, hist, ctrl, a.k, a.status);
+                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
+                           a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
       else
-        hipLaunchKernelGGL(k_index_fp8_stream<false>, grid, dim3(kStreamThreads), 0, st,
+        hipLaunchKernelGGL(k_index_fp8_stream<false>, grid, dim3(kThreads), 0, st,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
-                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, L.nv_cap,
-                           a.max_pos_end, scores, L.ld, hist, ctrl, a.k, a.status);
+                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
+                           a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
     } else {
-      dim3 grid(static_cast<unsigned>(ceil_div(L.nv_cap, 256)), rows);
+      dim3 grid(static_cast<unsigned>(ceil_div(P.nv_cap, kThreads)), rows);
       const size_t shm = (static_cast<size_t>(a.heads) * a.dim + a.heads) * sizeof(float);
-#define DSA_GENERIC(T, H)                                                                       \
-  hipLaunchKernelGGL((k_index_generic<T, H>), grid, dim3(256), shm, st,                          \
-                     static_cast<const T*>(a.q), a.q_scale, a.w, static_cast<const T*>(a.keys), \
-                     a.k_scale, a.q_pos, a.queries_per_seq, a.heads, a.dim, a.stride, a.span,   \
-                     a.e_cap, L.nv_cap, a.max_pos_end, scores, L.ld, hist, ctrl, a.k, a.status)
-      if (a.dtype == DSA_F32) {
-        if (L.split) DSA_GENERIC(float, true); else DSA_GENERIC(float, false);
-      } else {
-        if (L.split) DSA_GENERIC(uint8_t, true); else DSA_GENERIC(uint8_t, false);
-      }
-#undef DSA_GENERIC
+      if (a.dtype == DSA_F32)
+        hipLaunchKernelGGL(k_index_generic<float>, grid, dim3(kThreads), shm, st,
+                           static_cast<const float*>(a.q), a.q_scale, a.w,
+                           static_cast<const float*>(a.keys), a.k_scale, a.q_pos,
+                           a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
+                           a.max_pos_end, scores, P.ld, a.status);
+      else
+        hipLaunchKernelGGL(k_index_generic<uint8_t>, grid, dim3(kThreads), shm, st,
+                           static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
+                           static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
+                           a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
+                           a.max_pos_end, scores, P.ld, a.status);
     }
     rc = hip_check(hipGetLastError(), "indexer launch");
     if (rc != DSA_OK) return rc;
@@ -598,21 +615,13 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
       if (rc != DSA_OK) return rc;
     }
   }
-  if (L.split) {
-    if (!no_keys && L.nv_cap > static_cast<int64_t>(a.k)) {
-      const unsigned cb = static_cast<unsigned>(std::min<int64_t>(64, ceil_div(L.nv_cap, 4096)));
-      hipLaunchKernelGGL(k_topk_collect, dim3(std::max(1u, cb), rows), dim3(256), 0, st, scores,
-                         L.ld, a.q_pos, a.stride, a.span, L.nv_cap, a.max_pos_end, ctrl, cand,
-                         a.idx_out, a.score_out, a.k);
-      rc = hip_check(hipGetLastError(), "k_topk_collect launch");
-      if (rc != DSA_OK) return rc;
-    }
-    hipLaunchKernelGGL(k_topk_final, dim3(rows), dim3(256), 0, st, no_keys ? nullptr : scores,
-                       L.ld, a.q_pos, a.stride, a.span, L.nv_cap, a.max_pos_end, ctrl, cand,
-                       a.idx_out, a.score_out, a.k, a.status);
+  if (P.cand && !no_keys) {
+    hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kThreads), 0, st, scores, P.ld, a.q_pos,
+                       a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nb, P.cap,
+                       a.idx_out, a.score_out, a.k);
   } else {
-    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(256), 0, st, no_keys ? nullptr : scores,
-                       L.ld, a.q_pos, a.stride, a.span, L.nv_cap, a.max_pos_end, a.idx_out,
+    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kThreads), 0, st, no_keys ? nullptr : scores,
+                       P.ld, a.q_pos, a.stride, a.span, P.nv_cap, a.max_pos_end, a.idx_out,
                        a.score_out, a.k, a.status);
   }
   return hip_check(hipGetLastError(), "top-k launch");

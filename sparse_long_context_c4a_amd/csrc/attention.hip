@@ -234,7 +234,210 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
     lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
+// ----------------------------------------------------------- MFMA path
+// bf16, D = 512, heads in groups of 64 (4 waves x 16 heads).  A workgroup
+// takes one row and a run of slots; each tile of 32 gathered vectors is
+// staged once in LDS (row-major, 1056-byte pitch) and feeds both products:
+//   S^T = K Q^T : A = 16 vectors x 32 dims (ds_read_b128 rows), B = the
+//                 wave's rotated query heads held in registers;
+//   O^T += V^T P^T : A = 16 dims x 32 vectors read with the gfx950 LDS
+//                 transpose load (ds_read_b64_tr_b16), B = P straight from
+//                 the S^T accumulator (each lane already holds, for its
+//                 head, the probabilities of the entries it multiplies).
+// K = V, so one staged copy serves both.  Online softmax per head; partial
+// runs go to k_attn_combine, single runs apply R_m^{-1} and store.
+constexpr int kMD = 512;
+constexpr int kMTile = 32;
+constexpr int kMPitch = 1056;  // bytes per staged vector (1024 + 32 of padding)
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+template <bool kFinal>
+__global__ __launch_bounds__(256) void k_attn_mfma(
+    AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
+    const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
+    float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kMTile * kMPitch];
+  __shared__ float cs_s[kMD / 2][2];
+  __shared__ int valid_s[kMTile];
+  const int row = blockIdx.y, hq = blockIdx.x, run = blockIdx.z;
+  const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, gq = lane >> 4;
+  const int64_t m = g.q_pos[row];
+  const bool ok = m >= 0 && m < g.max_pos_end;
+  if (!ok && tid == 0 && hq == 0 && run == 0) set_status(g.status, DSA_DEVERR_POSITION);
+  const int half = g.r / 2, rot0 = kMD - g.r;
+  for (int i = tid; i < half; i += 256) {
+    float c = 1.f, sn = 0.f;
+    if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+    cs_s[i][0] = c;
+    cs_s[i][1] = sn;
+  }
+  __syncthreads();
+  // query head h of this lane as the B operand: dims 32c + 8gq + (0..7)
+  const int h = hq * 64 + wave * 16 + n;
+  v8bf qb[16];
+  {
+    const uint16_t* qrow = q + (static_cast<int64_t>(row) * g.H + h) * kMD;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int d0 = 32 * c + 8 * gq;
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
+      if (rotate_q && d0 + 8 > rot0) {
+        uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int d = d0 + 2 * p;
+          if (d >= rot0) {
+            const float a0 = bf16_to_f32(static_cast<uint16_t>(wd[p] & 0xffffu));
+            const float a1 = bf16_to_f32(static_cast<uint16_t>(wd[p] >> 16));
+            const float cc = cs_s[(d - rot0) / 2][0], ss = cs_s[(d - rot0) / 2][1];
+            wd[p] = pack_bf16x2(a0 * cc - a1 * ss, a0 * ss + a1 * cc);
+          }
+        }
+        raw = uint4{wd[0], wd[1], wd[2], wd[3]};
+      }
+      qb[c] = as_v8bf(raw);
+    }
+  }
+  const int total = g.k + g.W;
+  const int a_begin = run * g.slots_per_run;
+  const int a_end = min(total, a_begin + g.slots_per_run);
+  v4f o[32];
+#pragma unroll
+  for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // staging: thread t -> vector e = t / 8 of the tile, 16-byte chunks j*8 + t%8
+  const int se = tid >> 3, sc8 = tid & 7;
+  uint4 pre[8];
+  int valid_next = 0;
+  {
+    const int a = a_begin + se;
+    const uint16_t* src = (ok && a < a_end) ? slot_ptr<uint16_t>(g, row, b, m, a, cache, window, chunk_win)
+                                            : nullptr;
+    valid_next = src != nullptr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc8] : uint4{0u, 0u, 0u, 0u};
+  }
+  for (int a0 = a_begin; a0 < a_end; a0 += kMTile) {
+    __syncthreads();  // the previous tile is no longer read
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 8 + sc8) * 16) = pre[j];
+    if (sc8 == 0) valid_s[se] = valid_next;
+    __syncthreads();
+    if (a0 + kMTile < a_end) {  // prefetch the next tile while this one computes
+      const int a = a0 + kMTile + se;
+      const uint16_t* src = (ok && a < a_end) ? slot_ptr<uint16_t>(g, row, b, m, a, cache, window, chunk_win)
+                                              : nullptr;
+      valid_next = src != nullptr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc8] : uint4{0u, 0u, 0u, 0u};
+    }
+    // S^T for vectors 0..15 (s0) and 16..31 (s1): lane holds vectors 4gq+i
+    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int off = (32 * c + 8 * gq) * 2;
+      const v8bf k0 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + n * kMPitch + off));
+      const v8bf k1 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 + n) * kMPitch + off));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = valid_s[4 * gq + i] ? s0[i] * g.scale : -INFINITY;
+      x[4 + i] = valid_s[16 + 4 * gq + i] ? s1[i] * g.scale : -INFINITY;
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (x[i] == -INFINITY) ? 0.f : expf(x[i] - m_new);
+      psum += p[i];
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    const float corr = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (__any(corr != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) o[db] *= corr;
+    }
+    const uint4 pw = uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    const v8bf pb = as_v8bf(pw);
+    // O^T += V^T P^T; transpose-load source: vector 4gq + e (and 16 + ...),
+    // dims 16 db + 4 q4 .. + 3, with e = (lane & 15) >> 2, q4 = lane & 3
+    const int te = (lane & 15) >> 2, tq = lane & 3;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* lds_base = (lds_u8*)v_lds;
+    lds_u8* r_lo = lds_base + (4 * gq + te) * kMPitch + tq * 8;
+    lds_u8* r_hi = lds_base + (16 + 4 * gq + te) * kMPitch + tq * 8;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
+      const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+    }
+  }
+  // lane holds O^T[dims 16 db + 4gq + i][head h]
+  if constexpr (kFinal) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    uint16_t* orow = out + (static_cast<int64_t>(row) * g.H + h) * kMD;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const int d = 16 * db + 4 * gq;
+      float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int dd = d + 2 * pr;
+        if (dd >= rot0) {  // R_m^{-1}
+          const float cc = cs_s[(dd - rot0) / 2][0], ss = cs_s[(dd - rot0) / 2][1];
+          const float a0 = v[2 * pr], a1 = v[2 * pr + 1];
+          v[2 * pr] = a0 * cc + a1 * ss;
+          v[2 * pr + 1] = -a0 * ss + a1 * cc;
+        }
+      }
+      *reinterpret_cast<uint2*>(orow + d) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    if (lse && gq == 0)
+      lse[static_cast<int64_t>(row) * g.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  } else {
+    const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + run) * g.H + h;
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<float4*>(part_acc + pi * kMD + 16 * db + 4 * gq) =
+          float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+    if (gq == 0) {
+      part_ml[2 * pi] = m_run;
+      part_ml[2 * pi + 1] = l_run;
+    }
+  }
+}
+
 struct Plan {
+  bool mfma;
   int slots_per_run, n_runs;
   size_t off_acc, off_ml, total;
 };
@@ -243,13 +446,25 @@ Plan plan(const dsa_attn_args& a) {
   Plan p{};
   const int64_t rows = static_cast<int64_t>(a.n_seqs) * a.queries_per_seq;
   const int total = a.k + a.window_size;
-  const int64_t hgroups = ceil_div(a.heads, kHG);
-  // enough workgroups to cover the chip (~1024), runs of at least 64 slots
-  int64_t want = ceil_div(1024, std::max<int64_t>(1, rows * hgroups));
-  int spr = static_cast<int>(ceil_div(total, std::max<int64_t>(1, want)));
-  spr = std::max(64, static_cast<int>(ceil_div(spr, kTile) * kTile));
-  p.slots_per_run = spr;
-  p.n_runs = static_cast<int>(ceil_div(total, spr));
+  p.mfma = a.dtype == DSA_BF16 && a.dim == kMD && a.heads % 64 == 0 && a.rope_dim <= kMD;
+  if (p.mfma) {
+    // about 512 workgroups over the chip, at least two tiles per run
+    const int64_t hq = a.heads / 64;
+    const int tiles = static_cast<int>(ceil_div(total, kMTile));
+    int64_t runs = ceil_div(512, std::max<int64_t>(1, rows * hq));
+    runs = std::max<int64_t>(1, std::min<int64_t>(runs, ceil_div(tiles, 2)));
+    const int tpr = static_cast<int>(ceil_div(tiles, runs));
+    p.slots_per_run = tpr * kMTile;
+    p.n_runs = static_cast<int>(ceil_div(tiles, tpr));
+  } else {
+    const int64_t hgroups = ceil_div(a.heads, kHG);
+    // enough workgroups to cover the chip (~1024), runs of at least 64 slots
+    int64_t want = ceil_div(1024, std::max<int64_t>(1, rows * hgroups));
+    int spr = static_cast<int>(ceil_div(total, std::max<int64_t>(1, want)));
+    spr = std::max(64, static_cast<int>(ceil_div(spr, kTile) * kTile));
+    p.slots_per_run = spr;
+    p.n_runs = static_cast<int>(ceil_div(total, spr));
+  }
   size_t off = 0;
   p.off_acc = off;
   if (p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * 4);
@@ -285,13 +500,32 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
-  dim3 grid(static_cast<unsigned>(ceil_div(a.heads, kHG)), rows, p.n_runs);
-  const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
-  hipLaunchKernelGGL(k_attn_generic<T>, grid, dim3(kThreads), shm, st, g,
-                     static_cast<const T*>(a.q), a.rotate_q, static_cast<const T*>(a.cache),
-                     static_cast<const T*>(a.window), static_cast<const T*>(a.chunk_win),
-                     static_cast<T*>(a.out), a.lse, part_acc, part_ml);
-  dsa_status rc = hip_check(hipGetLastError(), "k_attn_generic launch");
+  if constexpr (sizeof(T) == 2) {
+    if (p.mfma) {
+      dim3 grid(static_cast<unsigned>(a.heads / 64), rows, p.n_runs);
+      if (p.n_runs == 1)
+        hipLaunchKernelGGL(k_attn_mfma<true>, grid, dim3(256), 0, st, g,
+                           static_cast<const uint16_t*>(a.q), a.rotate_q,
+                           static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
+                           static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
+                           a.lse, part_acc, part_ml);
+      else
+        hipLaunchKernelGGL(k_attn_mfma<false>, grid, dim3(256), 0, st, g,
+                           static_cast<const uint16_t*>(a.q), a.rotate_q,
+                           static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
+                           static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
+                           a.lse, part_acc, part_ml);
+    }
+  }
+  if (!p.mfma) {
+    dim3 grid(static_cast<unsigned>(ceil_div(a.heads, kHG)), rows, p.n_runs);
+    const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
+    hipLaunchKernelGGL(k_attn_generic<T>, grid, dim3(kThreads), shm, st, g,
+                       static_cast<const T*>(a.q), a.rotate_q, static_cast<const T*>(a.cache),
+                       static_cast<const T*>(a.window), static_cast<const T*>(a.chunk_win),
+                       static_cast<T*>(a.out), a.lse, part_acc, part_ml);
+  }
+  dsa_status rc = hip_check(hipGetLastError(), "attention launch");
   if (rc != DSA_OK || p.n_runs == 1) return rc;
   hipLaunchKernelGGL(k_attn_combine<T>, dim3(a.heads, rows), dim3(256), 0, st, g, part_acc,
                      part_ml, static_cast<T*>(a.out), a.lse);

@@ -15,7 +15,7 @@ from oracle import dsa as odsa
 from oracle.run import run_layer
 from sparse_long_context_c4a_amd import configs, inputs as gen
 
-from gpu_helpers import ATOL, check_close, check_topk_row, geometry, to_np
+from gpu_helpers import ATOL, LSE_ATOL, check_close, check_topk_row, geometry, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,7 +50,7 @@ def _compare(w, inp, ores, out, lse, idx, rows=None, label=""):
                 same = True
             if same:  # outputs are only comparable on the same selection
                 check_close(out[b, t], ores["out"][b, t], ATOL[w.main_dtype], lab)
-                check_close(lse[b, t], ores["lse"][b, t], 1e-3 if w.main_dtype == "bf16" else 1e-4,
+                check_close(lse[b, t], ores["lse"][b, t], LSE_ATOL[w.main_dtype],
                             lab + " lse")
     return swaps
 

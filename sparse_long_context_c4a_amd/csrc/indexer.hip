@@ -17,16 +17,18 @@
 // product), too coarse for Top-k near ties, while bf16 products are exact and
 // sum in fp32.
 //
-// Top-k without cross-workgroup atomics: each workgroup of 1024 entries keeps
-// the entries whose key is above t_b = (cap+1)-th largest key of the
-// workgroup (at most `cap` of them) as candidates and records t_b.  The final
-// pass selects the exact top k of the union of candidates (radix select on
-// (score key, complemented index), so ties go to the lower index) and checks
-// the certificate  k-th key >= max_b t_b : every entry left out has a key
-// below its workgroup's t_b, hence below the k-th, so the union's top k is
-// the row's top k.  If the certificate fails (adversarial score layouts,
-// massive ties) the row falls back to an exact radix select over all of its
-// scores, which the stream kernel also writes out.
+// Top-k without cross-workgroup atomics: each wave (256 entries) keeps as
+// candidates the entries with key above the wave's (cap+1)-th largest, t_w
+// (found with wave-wide max reductions, no LDS and no barriers), and records
+// t_w.  The final pass checks the certificate  k-th largest candidate key >=
+// max_w t_w : every entry left out has a key below its wave's t_w, hence
+// below the k-th, so the union's top k is the row's top k.  It
+// then selects the exact top k of the union: one histogram over the
+// candidates' key range, then the threshold bin resolved on (score key,
+// complemented index), so ties go to the lower index.  If the certificate
+// fails (adversarial score layouts, massive ties) the row falls back to an
+// exact radix select over all of its scores, which the stream kernel also
+// writes out.
 //
 // Row path (generic shapes, f32): scores go to memory and one workgroup per
 // row runs the exact radix select.
@@ -40,8 +42,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kBins = 4096;           // row fallback histogram: top 12 key bits
-constexpr int kBinShift = 20;
+constexpr int kBins = 4096;           // row select histogram bins
 constexpr int kFinalCap = 8192;       // candidates resolved in LDS
 constexpr int kStreamEntries = 1024;  // entries per workgroup in the stream kernel
 constexpr int kThreads = 256;
@@ -93,83 +94,160 @@ __device__ __forceinline__ void emit(int32_t* idx_row, float* score_row, uint32_
 }
 
 // ------------------------------------------------------- block primitives
-// 256-thread inclusive suffix sums of cnt[0..255]: the digit d with
-// sum(cnt[d+1..]) < need <= sum(cnt[d..]), the count above d, the count at
-// d and the total.  If the total is below need, d = 0xffffffff.
-struct Digit {
-  uint32_t d, above, at, total;
-};
+// The selection kernels run one workgroup of kSel threads (16 wave64s) per
+// query row; every helper below assumes blockDim.x == kSel.
+constexpr int kSel = 1024;
+constexpr int kSelWaves = kSel / 64;
 
-__device__ Digit find_digit(const uint32_t* cnt, uint32_t need) {
-  __shared__ uint32_t sfx[256];
-  __shared__ Digit res;
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int o) {
+  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
+}
+
+// Block-wide max / min / sum; every thread gets the result.
+template <int kOp>  // 0 max, 1 min, 2 sum
+__device__ __forceinline__ uint32_t block_reduce_u32(uint32_t v) {
+  __shared__ uint32_t wv[kSelWaves];
   const int t = threadIdx.x;
-  const uint32_t c = cnt[t];
-  sfx[t] = c;
-  if (t == 0) res.d = 0xffffffffu;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t add = (t + off < 256) ? sfx[t + off] : 0u;
-    __syncthreads();
-    sfx[t] += add;
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t y = shfl_xor_u32(v, o);
+    v = kOp == 0 ? max(v, y) : kOp == 1 ? min(v, y) : v + y;
   }
-  const uint32_t incl = sfx[t], excl = incl - c;
-  if (excl < need && incl >= need) res = Digit{static_cast<uint32_t>(t), excl, c, 0u};
+  if ((t & 63) == 0) wv[t >> 6] = v;
   __syncthreads();
-  Digit r = res;
-  r.total = sfx[0];
+  uint32_t r = wv[0];
+#pragma unroll
+  for (int i = 1; i < kSelWaves; ++i) r = kOp == 0 ? max(r, wv[i]) : kOp == 1 ? min(r, wv[i]) : r + wv[i];
   __syncthreads();
   return r;
 }
 
-// rank-th largest (1-based) of the nonzero 32-bit keys in LDS; 0 if fewer.
-__device__ uint32_t kth_largest_key(const uint32_t* keys, int n, uint32_t rank) {
-  __shared__ uint32_t cnt[256];
-  const int t = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, need = rank;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    cnt[t] = 0;
-    __syncthreads();
-    for (int i = t; i < n; i += kThreads) {
-      const uint32_t k = keys[i];
-      if (k != 0 && (k & mask) == prefix) atomicAdd(&cnt[(k >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    const Digit dg = find_digit(cnt, need);
-    if (dg.d == 0xffffffffu) return 0;
-    prefix |= dg.d << shift;
-    mask |= 255u << shift;
-    need -= dg.above;
+// Exclusive prefix sum of one value per thread (in thread order) and the total.
+__device__ __forceinline__ uint32_t block_prefix_excl(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wsum[kSelWaves];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(x), o, 64));
+    if (l >= o) x += y;
   }
-  return prefix;
+  if (l == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t add = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    add += i < w ? wsum[i] : 0u;
+    tot += wsum[i];
+  }
+  *total = tot;
+  __syncthreads();
+  return x - v + add;
 }
 
-// Exact top-`need` among n distinct 64-bit composites in LDS: returns the
-// smallest composite that is kept (keep every v >= result).
-__device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t need) {
+// Position of this lane's item among the wave's items with `cond`, after a
+// block-wide counter: one LDS atomic per wave.
+__device__ __forceinline__ uint32_t wave_alloc(bool cond, uint32_t* ctr) {
+  const uint64_t m = __ballot(cond);
+  const int l = threadIdx.x & 63;
+  uint32_t base = 0;
+  if (l == 0 && m) base = atomicAdd(ctr, static_cast<uint32_t>(__popcll(m)));
+  base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0, 64));
+  return base + static_cast<uint32_t>(__popcll(m & ((1ull << l) - 1ull)));
+}
+
+// Smallest shift with (span >> shift) < 2^bits.
+__device__ __forceinline__ int range_shift(uint32_t span, int bits) {
+  const int used = span == 0u ? 0 : 32 - __clz(static_cast<int>(span));
+  return used > bits ? used - bits : 0;
+}
+
+// For kSel threads owning `per` consecutive bins each in descending order
+// (thread 0 the highest): the bin B with count(bins above B) < need <=
+// count(bins >= B), plus those two counts.  local[i] of thread t is bin
+// top - (per * t + i).  Requires total >= need.
+struct Bin {
+  uint32_t b, above, at;
+};
+
+template <int per>
+__device__ __forceinline__ Bin find_bin_desc(const uint32_t (&local)[per], uint32_t top,
+                                             uint32_t need) {
+  __shared__ Bin res;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) sum += local[i];
+  uint32_t total;
+  const uint32_t before = block_prefix_excl(sum, &total);
+  const int t = threadIdx.x;
+  if (before < need && before + sum >= need) {
+    uint32_t c = before;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      if (c < need && c + local[i] >= need) res = Bin{top - (per * t + i), c, local[i]};
+      c += local[i];
+    }
+  }
+  __syncthreads();
+  const Bin r = res;
+  __syncthreads();
+  return r;
+}
+
+// Keep the `need` largest of the n distinct composites in v[] (LDS): each
+// is kept iff fewer than `need` others exceed it.  For small n (one wave
+// compares every pair through LDS broadcasts); calls f(v) for the kept.
+template <typename F>
+__device__ void keep_largest_small(const uint64_t* v, int n, uint32_t need, F f) {
+  const int t = threadIdx.x;
+  if (t < n) {
+    const uint64_t x = v[t];
+    uint32_t rank = 0;
+    for (int i = 0; i < n; ++i) rank += v[i] > x ? 1u : 0u;
+    if (rank < need) f(x);
+  }
+}
+
+// Exact selection of the `need` largest of n distinct composites c[] (LDS)
+// by radix passes of 8 bits, for the rare large tie groups; returns the
+// smallest kept composite.  pred() filters which elements take part.
+template <typename P>
+__device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t need, P pred) {
   __shared__ uint32_t cnt[256];
+  __shared__ uint32_t res[3];
   const int t = threadIdx.x;
   uint64_t prefix = 0, mask = 0;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    cnt[t] = 0;
+  for (int sh = 56; sh >= 0; sh -= 8) {
+    if (t < 256) cnt[t] = 0;
     __syncthreads();
-    for (int i = t; i < n; i += kThreads) {
+    for (int i = t; i < n; i += kSel) {
       const uint64_t v = c[i];
-      if ((v & mask) == prefix) atomicAdd(&cnt[(v >> shift) & 255u], 1u);
+      if (pred(v) && (v & mask) == prefix) atomicAdd(&cnt[(v >> sh) & 255u], 1u);
     }
     __syncthreads();
-    const Digit dg = find_digit(cnt, need);
-    prefix |= static_cast<uint64_t>(dg.d) << shift;
-    mask |= static_cast<uint64_t>(255u) << shift;
-    need -= dg.above;
-    if (dg.at == need) return prefix;  // every composite with this prefix is kept
+    // digit d: count(digits > d) < need <= count(digits >= d); thread t < 256
+    // owns digit 255 - t (descending)
+    const uint32_t mine = t < 256 ? cnt[255 - t] : 0u;
+    uint32_t total;
+    const uint32_t before = block_prefix_excl(mine, &total);
+    if (t < 256 && before < need && before + mine >= need) {
+      res[0] = 255u - t;
+      res[1] = before;
+      res[2] = mine;
+    }
+    __syncthreads();
+    const uint32_t d = res[0], above = res[1], at = res[2];
+    __syncthreads();
+    prefix |= static_cast<uint64_t>(d) << sh;
+    mask |= static_cast<uint64_t>(255u) << sh;
+    need -= above;
+    if (at == need) break;  // every composite with this prefix is kept
   }
   return prefix;
 }
 
 // Rows with n_vis <= k: every visible entry, in index order, then padding.
-__device__ void emit_all_visible(const float* srow, int64_t nv, int k, int32_t* idx_row,
+__device__ __forceinline__ void emit_all_visible(const float* srow, int64_t nv, int k, int32_t* idx_row,
                                  float* score_row) {
   for (int i = threadIdx.x; i < k; i += blockDim.x) {
     if (i < nv) emit(idx_row, score_row, i, i, srow ? srow[i] : 0.f);
@@ -180,53 +258,132 @@ __device__ void emit_all_visible(const float* srow, int64_t nv, int k, int32_t* 
   }
 }
 
-// Exact top-k of one row from its scores in global memory (nv > k):
-// histogram of the top 12 key bits -> threshold bin; entries above it go
-// straight out, the bin's entries are resolved exactly (in LDS when they
-// fit, else by streaming radix passes).  cand_s: kFinalCap u64 of LDS,
-// h_s: kBins u32 of LDS.
-__device__ void row_select_from_scores(const float* srow, int64_t nv, int k, int32_t* irow,
-                                       float* orow, uint64_t* cand_s, uint32_t* h_s) {
-  __shared__ uint32_t cnt_above, cnt_cand, out_pos;
-  __shared__ uint32_t part[kThreads];
-  __shared__ uint32_t thr_s[3];
-  __shared__ uint32_t cnt[256];
+// The `k` largest (key, complemented index) composites among the n slots of
+// c[] (LDS; 0 = empty slot), emitted to positions 0..k-1 in no particular
+// order.  A 2048-bin histogram over the keys' own range finds the bin
+// holding the k-th; entries above it go out directly, the bin's entries are
+// resolved exactly.  tmp: kTmpCap u64 of LDS; hist: 2048 u32 of LDS.
+constexpr int kTmpCap = 1024;
+
+__device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n, uint32_t k, int32_t* irow,
+                                       float* orow, uint64_t* tmp, uint32_t* hist) {
+  __shared__ uint32_t pos_above, pos_bin, n_tmp;
   const int t = threadIdx.x;
-  for (int i = t; i < kBins; i += kThreads) h_s[i] = 0;
-  if (t == 0) cnt_above = cnt_cand = out_pos = 0;
-  __syncthreads();
-  for (int64_t j = t; j < nv; j += kThreads) atomicAdd(&h_s[order_key(srow[j]) >> kBinShift], 1u);
-  __syncthreads();
-  // threshold bin: suffix counts over 4096 bins, 16 per thread
-  uint32_t local[16], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    local[i] = h_s[kBins - 1 - (16 * t + i)];
-    sum += local[i];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = t; i < n; i += kSel) {
+    const uint64_t v = c[i];
+    if (v == 0) continue;
+    lo = min(lo, static_cast<uint32_t>(v >> 32));
+    hi = max(hi, static_cast<uint32_t>(v >> 32));
   }
-  part[t] = sum;
+  for (int i = t; i < 2048; i += kSel) hist[i] = 0u;
+  if (t == 0) pos_above = pos_bin = n_tmp = 0u;
+  lo = block_reduce_u32<1>(lo);  // has barriers
+  hi = block_reduce_u32<0>(hi);
+  const int shift = range_shift(hi - lo, 11);
+  for (int i = t; i < n; i += kSel) {
+    const uint64_t v = c[i];
+    if (v != 0) atomicAdd(&hist[(static_cast<uint32_t>(v >> 32) - lo) >> shift], 1u);
+  }
   __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < t; ++i) before += part[i];
-  if (before < static_cast<uint32_t>(k) && before + sum >= static_cast<uint32_t>(k)) {
-    uint32_t c = before;
-    for (int i = 0; i < 16; ++i) {
-      if (c + local[i] >= static_cast<uint32_t>(k)) {
-        thr_s[0] = kBins - 1 - (16 * t + i);
-        thr_s[1] = c;
-        thr_s[2] = local[i];
-        break;
-      }
-      c += local[i];
+  const uint32_t local[2] = {hist[2047 - 2 * t], hist[2046 - 2 * t]};
+  const Bin br = find_bin_desc<2>(local, 2047u, k);
+  const uint32_t B = br.b, above = br.above, at = br.at;
+  const bool fits = at <= static_cast<uint32_t>(kTmpCap);
+  for (int i0 = 0; i0 < n; i0 += kSel) {
+    const int i = i0 + t;
+    const uint64_t v = i < n ? c[i] : 0ull;
+    const uint32_t bin = (static_cast<uint32_t>(v >> 32) - lo) >> shift;
+    const bool up = v != 0 && bin > B;
+    const uint32_t p = wave_alloc(up, &pos_above);
+    if (up && p < above) emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+    const bool mid = v != 0 && bin == B && fits;
+    const uint32_t q = wave_alloc(mid, &n_tmp);
+    if (mid) tmp[q] = v;
+  }
+  __syncthreads();
+  const uint32_t need = k - above;
+  auto out_bin = [&](uint64_t v) {
+    const uint32_t p = atomicAdd(&pos_bin, 1u);
+    if (p < need) emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+  };
+  if (fits && at <= 64) {
+    keep_largest_small(tmp, static_cast<int>(at), need, out_bin);
+  } else if (fits) {
+    const uint64_t cut = kth_largest_composite(tmp, static_cast<int>(at), need,
+                                               [](uint64_t) { return true; });
+    for (int i = t; i < static_cast<int>(at); i += kSel)
+      if (tmp[i] >= cut) out_bin(tmp[i]);
+  } else {
+    // very many keys in one bin: radix over the bin's composites in place
+    const uint64_t bin_lo = (static_cast<uint64_t>(lo) + (static_cast<uint64_t>(B) << shift)) << 32;
+    const uint64_t khi = static_cast<uint64_t>(lo) + (static_cast<uint64_t>(B + 1u) << shift);
+    const uint64_t bin_hi = khi > 0xffffffffull ? ~0ull : (khi << 32);  // exclusive, or open
+    auto in_bin = [=](uint64_t v) {
+      return v != 0 && v >= bin_lo && (v < bin_hi || bin_hi == ~0ull);
+    };
+    const uint64_t cut = kth_largest_composite(c, n, need, in_bin);
+    for (int i = t; i < n; i += kSel)
+      if (in_bin(c[i]) && c[i] >= cut) out_bin(c[i]);
+  }
+  __syncthreads();
+}
+
+// Visit the first nv scores of a row (read as float4; ld_scores is a
+// multiple of 4 floats and entries past nv are skipped): f(j, score).
+template <typename F>
+__device__ __forceinline__ void for_row(const float* srow, int64_t nv, F f) {
+  const float4* r4 = reinterpret_cast<const float4*>(srow);
+  const int64_t n4 = (nv + 3) / 4;
+  for (int64_t i = threadIdx.x; i < n4; i += 4 * kSel) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t ii = i + u * kSel;
+      v[u] = ii < n4 ? r4[ii] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = 4 * (i + u * kSel);
+      if (j + 0 < nv) f(j + 0, v[u].x);
+      if (j + 1 < nv) f(j + 1, v[u].y);
+      if (j + 2 < nv) f(j + 2, v[u].z);
+      if (j + 3 < nv) f(j + 3, v[u].w);
     }
   }
-  __syncthreads();
-  const uint32_t thr = thr_s[0], above = thr_s[1], at = thr_s[2];
-  const bool fits = at <= static_cast<uint32_t>(kFinalCap);
-  for (int64_t j = t; j < nv; j += kThreads) {
-    const float sc = srow[j];
+}
+
+// Exact top-k of one row from its scores in global memory (nv > k): a
+// 4096-bin histogram over the row's own key range finds the bin holding the
+// k-th score; entries above it go straight out and the bin's entries are
+// resolved exactly on (key, complemented index).  cand_s: kFinalCap u64 of
+// LDS, h_s: kBins u32 of LDS.
+__device__ __forceinline__ void row_select_from_scores(const float* srow, int64_t nv, int k, int32_t* irow,
+                                       float* orow, uint64_t* cand_s, uint32_t* h_s) {
+  __shared__ uint32_t cnt_above, cnt_cand, out_pos;
+  const int t = threadIdx.x;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for_row(srow, nv, [&](int64_t, float sc) {
     const uint32_t key = order_key(sc);
-    const uint32_t bin = key >> kBinShift;
+    lo = min(lo, key);
+    hi = max(hi, key);
+  });
+  for (int i = t; i < kBins; i += kSel) h_s[i] = 0;
+  if (t == 0) cnt_above = cnt_cand = out_pos = 0;
+  lo = block_reduce_u32<1>(lo);
+  hi = block_reduce_u32<0>(hi);
+  const int shift = range_shift(hi - lo, 12);
+  for_row(srow, nv, [&](int64_t, float sc) { atomicAdd(&h_s[(order_key(sc) - lo) >> shift], 1u); });
+  __syncthreads();
+  uint32_t local[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) local[i] = h_s[kBins - 1 - (4 * t + i)];
+  const Bin br = find_bin_desc<4>(local, kBins - 1u, static_cast<uint32_t>(k));
+  const uint32_t thr = br.b, above = br.above, at = br.at;
+  const bool fits = at <= static_cast<uint32_t>(kFinalCap);
+  for_row(srow, nv, [&](int64_t j, float sc) {
+    const uint32_t key = order_key(sc);
+    const uint32_t bin = (key - lo) >> shift;
     if (bin > thr) {
       const uint32_t p = atomicAdd(&cnt_above, 1u);
       if (p < static_cast<uint32_t>(k)) emit(irow, orow, p, static_cast<uint32_t>(j), sc);
@@ -234,51 +391,65 @@ __device__ void row_select_from_scores(const float* srow, int64_t nv, int k, int
       const uint32_t p = atomicAdd(&cnt_cand, 1u);
       if (p < static_cast<uint32_t>(kFinalCap)) cand_s[p] = composite(key, static_cast<uint32_t>(j));
     }
-  }
+  });
   __syncthreads();
   const uint32_t need = static_cast<uint32_t>(k) - above;
-  uint64_t cut;
   if (fits) {
-    cut = kth_largest_composite(cand_s, static_cast<int>(at), need);
+    auto out_bin = [&](uint64_t v) {
+      const uint32_t p = atomicAdd(&out_pos, 1u);
+      if (p < need)
+        emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+    };
+    if (at <= 64) {
+      keep_largest_small(cand_s, static_cast<int>(at), need, out_bin);
+    } else {
+      const uint64_t cut = kth_largest_composite(cand_s, static_cast<int>(at), need,
+                                                 [](uint64_t) { return true; });
+      for (int i = t; i < static_cast<int>(at); i += kSel)
+        if (cand_s[i] >= cut) out_bin(cand_s[i]);
+    }
   } else {
     // streaming radix over the bin's entries, composites built on the fly
-    uint64_t prefix = static_cast<uint64_t>(thr) << (32 + kBinShift);
-    uint64_t mask = static_cast<uint64_t>(0xfffu) << (32 + kBinShift);
+    __shared__ uint32_t cnt[256];
+    __shared__ uint32_t res[3];
+    uint64_t prefix = 0, mask = 0;
     uint32_t rem = need;
-    for (int shift = 48; shift >= 0; shift -= 8) {
-      cnt[t] = 0;
+    for (int sh = 56; sh >= 0; sh -= 8) {
+      if (t < 256) cnt[t] = 0;
       __syncthreads();
-      for (int64_t j = t; j < nv; j += kThreads) {
-        const uint64_t v = composite(order_key(srow[j]), static_cast<uint32_t>(j));
-        if ((v & mask) == prefix) atomicAdd(&cnt[(v >> shift) & 255u], 1u);
+      for_row(srow, nv, [&](int64_t j, float sc) {
+        const uint32_t key = order_key(sc);
+        if (((key - lo) >> shift) != thr) return;
+        const uint64_t v = composite(key, static_cast<uint32_t>(j));
+        if ((v & mask) == prefix) atomicAdd(&cnt[(v >> sh) & 255u], 1u);
+      });
+      __syncthreads();
+      const uint32_t mine = t < 256 ? cnt[255 - t] : 0u;
+      uint32_t total;
+      const uint32_t before = block_prefix_excl(mine, &total);
+      if (t < 256 && before < rem && before + mine >= rem) {
+        res[0] = 255u - t;
+        res[1] = before;
+        res[2] = mine;
       }
       __syncthreads();
-      const Digit dg = find_digit(cnt, rem);
-      prefix |= static_cast<uint64_t>(dg.d) << shift;
-      mask |= static_cast<uint64_t>(255u) << shift;
-      rem -= dg.above;
-      if (dg.at == rem) break;
+      const uint32_t d = res[0], ab = res[1], at2 = res[2];
+      __syncthreads();
+      prefix |= static_cast<uint64_t>(d) << sh;
+      mask |= static_cast<uint64_t>(255u) << sh;
+      rem -= ab;
+      if (at2 == rem) break;
     }
-    cut = prefix;
-  }
-  // emit the threshold bin's kept entries
-  if (fits) {
-    for (int i = t; i < static_cast<int>(at); i += kThreads) {
-      const uint64_t v = cand_s[i];
+    const uint64_t cut = prefix;
+    for_row(srow, nv, [&](int64_t j, float sc) {
+      const uint32_t key = order_key(sc);
+      if (((key - lo) >> shift) != thr) return;
+      const uint64_t v = composite(key, static_cast<uint32_t>(j));
       if (v >= cut) {
         const uint32_t p = atomicAdd(&out_pos, 1u);
-        if (p < need)
-          emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+        if (p < need) emit(irow, orow, above + p, comp_index(v), sc);
       }
-    }
-  } else {
-    for (int64_t j = t; j < nv; j += kThreads) {
-      const uint64_t v = composite(order_key(srow[j]), static_cast<uint32_t>(j));
-      if (v >= cut && (v >> (32 + kBinShift)) == thr) {
-        const uint32_t p = atomicAdd(&out_pos, 1u);
-        if (p < need) emit(irow, orow, above + p, comp_index(v), srow[j]);
-      }
-    }
+    });
   }
   __syncthreads();
 }
@@ -290,15 +461,19 @@ __device__ void row_select_from_scores(const float* srow, int64_t nv, int k, int
 // of those 32.  A and B use the same byte-to-k assignment, so the four MFMAs
 // sum every one of the 128 products exactly once; each of the two 16-byte
 // loads of a wave covers 64 contiguous bytes of 16 entries.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64)));
+  return v;
+}
+
 template <bool kCand>
 __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
     const int64_t* __restrict__ q_pos, int Tq, int Hi, int s, int S, int64_t e_cap,
     int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
-    uint64_t* __restrict__ cand, uint2* __restrict__ meta, int cap, uint32_t* status) {
-  __shared__ uint32_t s_key[kCand ? kStreamEntries : 1];
-  __shared__ uint32_t cand_cnt;
+    uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, uint32_t* status) {
   const int row = blockIdx.y, b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -307,7 +482,10 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
   const int64_t e_begin = static_cast<int64_t>(blockIdx.x) * kStreamEntries;
   constexpr int kGroups = kStreamEntries / 4 / 16;  // 16-entry groups per wave
   constexpr int kUnroll = 4;
-  if (e_begin < nv) {
+  const int64_t wbase = e_begin + wave * (kStreamEntries / 4);
+  // each lane keeps the keys of the groups gi + g (one per outer step)
+  uint32_t kk[kGroups / kUnroll] = {};
+  if (wbase < nv) {
     uint4 qlo = {0u, 0u, 0u, 0u}, qhi = {0u, 0u, 0u, 0u};
     if (n < Hi) {
       const uint4* qp = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * Hi + n) * 128);
@@ -329,8 +507,7 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* kb = keys + static_cast<int64_t>(b) * e_cap * 128;
     const float* ksb = k_scale + static_cast<int64_t>(b) * e_cap;
     float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-    const int64_t wbase = e_begin + wave * (kStreamEntries / 4);
-#pragma unroll 1
+#pragma unroll
     for (int gi = 0; gi < kGroups; gi += kUnroll) {
       uint4 blo[kUnroll], bhi[kUnroll];
       float ks[kUnroll];
@@ -358,38 +535,61 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
         float v = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
                   wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
         v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        v += __shfl_xor(v, 32, 64);  // every lane of column n now holds its score
         const float sc = v * ks[u];
-        const int local = wave * (kStreamEntries / 4) + (gi + u) * 16 + n;
-        const int64_t ent = e_begin + local;
-        if (g == 0) {
-          if (ent < nv) srow[ent] = sc;
-          if constexpr (kCand) s_key[local] = ent < nv ? order_key(sc) : 0u;
-        }
+        const int64_t ent = wbase + (gi + u) * 16 + n;
+        if (g == 0 && ent < nv) srow[ent] = sc;
+        if constexpr (kCand)
+          if (u == g) kk[gi / kUnroll] = ent < nv ? order_key(sc) : 0u;
       }
     }
-  } else if constexpr (kCand) {
-    for (int i = tid; i < kStreamEntries; i += kThreads) s_key[i] = 0u;
   }
   if constexpr (kCand) {
-    // workgroup candidates: keys above the (cap+1)-th largest of this block
-    if (tid == 0) cand_cnt = 0;
-    __syncthreads();
-    const uint32_t kth = kth_largest_key(s_key, kStreamEntries, static_cast<uint32_t>(cap) + 1u);
-    const uint32_t tb = kth == 0 ? 1u : kth + 1u;  // fewer than cap+1 valid keys: take all
-    uint64_t* crow = cand + (static_cast<int64_t>(row) * gridDim.x + blockIdx.x) * cap;
-    for (int i = tid; i < kStreamEntries; i += kThreads) {
-      const uint32_t key = s_key[i];
-      if (key != 0u && key >= tb) {
-        const uint32_t p = atomicAdd(&cand_cnt, 1u);
-        if (p < static_cast<uint32_t>(cap))
-          crow[p] = composite(key, static_cast<uint32_t>(e_begin + i));
+    // wave candidates: the keys above the (cap+1)-th largest of the wave's 256
+    uint32_t work[kGroups / kUnroll];
+#pragma unroll
+    for (int i = 0; i < kGroups / kUnroll; ++i) work[i] = kk[i];
+    uint32_t next = 0;
+    for (int it = 0; it <= cap; ++it) {
+      uint32_t m = work[0];
+#pragma unroll
+      for (int i = 1; i < kGroups / kUnroll; ++i) m = max(m, work[i]);
+      m = wave_max_u32(m);
+      next = m;
+      if (m == 0u || it == cap) break;
+      // drop one instance of m (from the lowest lane that holds it)
+      bool has = false;
+#pragma unroll
+      for (int i = 0; i < kGroups / kUnroll; ++i) has |= work[i] == m;
+      const uint64_t bal = __ballot(has);
+      if (lane == __ffsll(static_cast<long long>(bal)) - 1) {
+        bool done = false;
+#pragma unroll
+        for (int i = 0; i < kGroups / kUnroll; ++i)
+          if (!done && work[i] == m) {
+            work[i] = 0u;
+            done = true;
+          }
       }
     }
-    __syncthreads();
-    if (tid == 0)
-      meta[static_cast<int64_t>(row) * gridDim.x + blockIdx.x] =
-          uint2{e_begin < nv ? tb : 0u, min(cand_cnt, static_cast<uint32_t>(cap))};
+    // threshold: strictly above the (cap+1)-th largest (1 if fewer keys)
+    const uint32_t tw = next == 0u ? 1u : (next == 0xffffffffu ? next : next + 1u);
+    const int64_t wave_id = static_cast<int64_t>(row) * (gridDim.x * 4) + blockIdx.x * 4 + wave;
+    uint64_t* crow = cand + wave_id * cap;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kGroups / kUnroll; ++i) {
+      const bool in = kk[i] != 0u && kk[i] >= tw;
+      const uint64_t bal = __ballot(in);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (in && pos < cap) {
+        const int64_t ent = wbase + (kUnroll * i + g) * 16 + n;
+        crow[pos] = composite(kk[i], static_cast<uint32_t>(ent));
+      }
+      base += __popcll(bal);
+    }
+    if (lane >= base && lane < cap) crow[lane] = 0ull;  // empty slots
+    if (lane == 0) meta[wave_id] = wbase < nv ? tw : 0u;
   }
 }
 
@@ -436,18 +636,22 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
 }
 
 // ------------------------------------------------------------ final passes
-// Candidate path: union of the workgroups' candidates, exact top k, and the
-// certificate; falls back to the full-row select when it does not hold.
-__global__ __launch_bounds__(kThreads) void k_topk_cand_final(
+// Candidate path: union of the waves' candidates (empty slots are 0), the
+// certificate, and the exact top k; falls back to the full-row select when
+// the certificate does not hold.  The candidates stay in registers (8 per
+// thread) through one combined reduction pass, one histogram pass and the
+// emit pass.
+__global__ __launch_bounds__(kSel) void k_topk_cand_final(
     const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
     int s, int S, int64_t nv_cap, int64_t max_pos_end, const uint64_t* __restrict__ cand,
-    const uint2* __restrict__ meta, int nb, int cap, int32_t* __restrict__ idx_out,
+    const uint32_t* __restrict__ meta, int nw, int cap, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out, int k) {
   __shared__ uint64_t cand_s[kFinalCap];
-  __shared__ uint32_t h_s[kBins];  // block offsets here, then the fallback histogram
-  __shared__ uint32_t part[kThreads];
-  __shared__ uint32_t tmax_s, total_s, out_pos;
-  const int row = blockIdx.x, t = threadIdx.x;
+  __shared__ uint64_t tmp_s[kTmpCap];
+  __shared__ uint32_t h_s[kBins];
+  __shared__ uint32_t red[3][kSelWaves];
+  __shared__ uint32_t pos_above, pos_bin, n_tmp;
+  const int row = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
   const int64_t nv = ri.nv;
   const float* srow = scores + static_cast<int64_t>(row) * ld_scores;
@@ -457,60 +661,97 @@ __global__ __launch_bounds__(kThreads) void k_topk_cand_final(
     emit_all_visible(srow, nv, k, irow, orow);
     return;
   }
-  const uint2* mrow = meta + static_cast<int64_t>(row) * nb;
-  if (t == 0) tmax_s = total_s = out_pos = 0;
-  __syncthreads();
-  // exclusive offsets of the per-block counts (nb <= kBins) and max t_b
-  const int per = (nb + kThreads - 1) / kThreads;
-  const int b0 = min(nb, t * per), b1 = min(nb, b0 + per);
-  uint32_t sum = 0, tm = 0;
-  for (int b = b0; b < b1; ++b) {
-    const uint2 m = mrow[b];
-    sum += m.y;
-    tm = max(tm, m.x);
-  }
-  atomicMax(&tmax_s, tm);
-  part[t] = sum;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < t; ++i) before += part[i];
-  for (int b = b0; b < b1; ++b) {
-    h_s[b] = before;
-    before += mrow[b].y;
-  }
-  if (t == kThreads - 1) total_s = before;
-  __syncthreads();
-  const uint32_t total = total_s, tmax = tmax_s;
-  bool ok = total >= static_cast<uint32_t>(k) && total <= static_cast<uint32_t>(kFinalCap);
-  uint64_t cut = 0;
-  if (ok) {
-    const int slots = nb * cap;
-    const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
-    for (int sl = t; sl < slots; sl += kThreads) {
-      const int b = sl / cap, i = sl % cap;
-      if (static_cast<uint32_t>(i) < mrow[b].y) cand_s[h_s[b] + i] = crow[sl];
+  const int slots = nw * cap;  // <= kFinalCap by construction
+  const uint32_t* mrow = meta + static_cast<int64_t>(row) * nw;
+  const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
+  constexpr int kPer = kFinalCap / kSel;
+  uint64_t v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) v[u] = t + u * kSel < slots ? crow[t + u * kSel] : 0ull;
+  uint32_t tm = 0, lo = 0xffffffffu, hi = 0u;
+  for (int b = t; b < nw; b += kSel) tm = max(tm, mrow[b]);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (v[u] != 0) {
+      lo = min(lo, static_cast<uint32_t>(v[u] >> 32));
+      hi = max(hi, static_cast<uint32_t>(v[u] >> 32));
     }
-    __syncthreads();
-    cut = kth_largest_composite(cand_s, static_cast<int>(total), static_cast<uint32_t>(k));
-    ok = static_cast<uint32_t>(cut >> 32) >= tmax;  // the certificate
+  // one combined block reduction: max t_w, min and max candidate key
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    tm = max(tm, shfl_xor_u32(tm, o));
+    lo = min(lo, shfl_xor_u32(lo, o));
+    hi = max(hi, shfl_xor_u32(hi, o));
   }
-  if (ok) {
-    for (int i = t; i < static_cast<int>(total); i += kThreads) {
-      const uint64_t v = cand_s[i];
-      if (v >= cut) {
-        const uint32_t p = atomicAdd(&out_pos, 1u);
-        if (p < static_cast<uint32_t>(k))
-          emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
-      }
+  if (l == 0) {
+    red[0][w] = tm;
+    red[1][w] = lo;
+    red[2][w] = hi;
+  }
+  for (int i = t; i < 2048; i += kSel) h_s[i] = 0u;
+  if (t == 0) pos_above = pos_bin = n_tmp = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    tm = max(tm, red[0][i]);
+    lo = min(lo, red[1][i]);
+    hi = max(hi, red[2][i]);
+  }
+  // the certificate count (at least k candidates with key >= max_w t_w) and
+  // the histogram over the candidates' key range, in one pass
+  const int shift = range_shift(hi - lo, 11);
+  uint32_t c_ge = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (v[u] != 0) {
+      const uint32_t key = static_cast<uint32_t>(v[u] >> 32);
+      c_ge += key >= tm ? 1u : 0u;
+      atomicAdd(&h_s[(key - lo) >> shift], 1u);
     }
+  const bool ok = block_reduce_u32<2>(c_ge) >= static_cast<uint32_t>(k);  // barriers
+  if (!ok) {
+    row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
     return;
   }
+  const uint32_t local[2] = {h_s[2047 - 2 * t], h_s[2046 - 2 * t]};
+  const Bin br = find_bin_desc<2>(local, 2047u, static_cast<uint32_t>(k));
+  const uint32_t B = br.b, above = br.above, at = br.at;
+  const bool fits = at <= static_cast<uint32_t>(kTmpCap);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const uint64_t x = v[u];
+    const uint32_t bin = (static_cast<uint32_t>(x >> 32) - lo) >> shift;
+    const bool up = x != 0 && bin > B;
+    const uint32_t p = wave_alloc(up, &pos_above);
+    if (up && p < above) emit(irow, orow, p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
+    const bool mid = x != 0 && bin == B;
+    const uint32_t q = wave_alloc(mid, &n_tmp);
+    if (mid && fits) tmp_s[q] = x;
+    if (!fits) cand_s[t + u * kSel] = mid ? x : 0ull;  // only the bin's members
+  }
   __syncthreads();
-  row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
+  const uint32_t need = static_cast<uint32_t>(k) - above;
+  auto out_bin = [&](uint64_t x) {
+    const uint32_t p = atomicAdd(&pos_bin, 1u);
+    if (p < need) emit(irow, orow, above + p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
+  };
+  if (fits && at <= 64) {
+    keep_largest_small(tmp_s, static_cast<int>(at), need, out_bin);
+  } else if (fits) {
+    const uint64_t cut = kth_largest_composite(tmp_s, static_cast<int>(at), need,
+                                               [](uint64_t) { return true; });
+    for (int i = t; i < static_cast<int>(at); i += kSel)
+      if (tmp_s[i] >= cut) out_bin(tmp_s[i]);
+  } else {
+    const uint64_t cut = kth_largest_composite(cand_s, kFinalCap, need,
+                                               [](uint64_t x) { return x != 0; });
+    for (int i = t; i < kFinalCap; i += kSel)
+      if (cand_s[i] != 0 && cand_s[i] >= cut) out_bin(cand_s[i]);
+  }
 }
 
 // Row path: one workgroup per query row selects from the row's scores.
-__global__ __launch_bounds__(kThreads) void k_topk_rows(
+__global__ __launch_bounds__(kSel) void k_topk_rows(
     const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
     int s, int S, int64_t nv_cap, int64_t max_pos_end, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out, int k, uint32_t* status) {
@@ -533,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void k_topk_rows(
 struct Plan {
   int64_t nv_cap, ld;
   bool mfma, cand;
-  int nb, cap;
+  int nb, nw, cap;
   size_t off_scores, off_cand, off_meta, total;
 };
 
@@ -545,17 +786,21 @@ Plan plan(const dsa_index_args& a) {
   p.ld = (p.nv_cap + 63) / 64 * 64;
   p.mfma = a.keys != nullptr && a.dtype == DSA_FP8_E4M3 && a.dim == 128 && a.heads <= 16;
   p.nb = static_cast<int>(ceil_div(p.nv_cap, kStreamEntries));
-  // candidates per workgroup: enough that the union is about 4k, at least 32
+  p.nw = 4 * p.nb;  // waves per row, 256 entries each
+  // Candidates per wave: the union holds >= 2k and fits the final LDS pass.
+  // A wave of 256 entries at 1M context holds ~0.5 of the row's top 512;
+  // more than 8 of them has probability ~3e-8 for unstructured scores.
   p.cap = static_cast<int>(std::min<int64_t>(
-      512, std::max<int64_t>(32, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nb)))));
-  p.cand = p.mfma && p.nv_cap > a.k && p.nb <= kBins;
+      32, std::max<int64_t>(8, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nw)))));
+  p.cand = p.mfma && p.nv_cap > a.k && static_cast<int64_t>(p.nw) * p.cap <= kFinalCap &&
+           static_cast<int64_t>(p.nw) * p.cap >= 2 * static_cast<int64_t>(a.k);
   size_t off = 0;
   p.off_scores = off;
   off = align_up(off + static_cast<size_t>(rows) * p.ld * sizeof(float));
   p.off_cand = off;
-  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nb * p.cap * sizeof(uint64_t));
+  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nw * p.cap * sizeof(uint64_t));
   p.off_meta = off;
-  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nb * sizeof(uint2));
+  if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nw * sizeof(uint32_t));
   p.total = off;
   return p;
 }
@@ -570,7 +815,7 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   char* base = static_cast<char*>(ws);
   float* scores = reinterpret_cast<float*>(base + P.off_scores);
   uint64_t* cand = reinterpret_cast<uint64_t*>(base + P.off_cand);
-  uint2* meta = reinterpret_cast<uint2*>(base + P.off_meta);
+  uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
   const bool no_keys = a.keys == nullptr;  // only allowed when k >= every n_vis
   dsa_status rc;
   if (!no_keys && P.nv_cap > 0) {
@@ -616,11 +861,11 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
     }
   }
   if (P.cand && !no_keys) {
-    hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kThreads), 0, st, scores, P.ld, a.q_pos,
-                       a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nb, P.cap,
+    hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
+                       a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
                        a.idx_out, a.score_out, a.k);
   } else {
-    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kThreads), 0, st, no_keys ? nullptr : scores,
+    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kSel), 0, st, no_keys ? nullptr : scores,
                        P.ld, a.q_pos, a.stride, a.span, P.nv_cap, a.max_pos_end, a.idx_out,
                        a.score_out, a.k, a.status);
   }

@@ -118,7 +118,7 @@ INDEX_CASES = [
 ]
 
 
-def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False):
+def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, boost=None):
     L = _lib()
     rows = len(positions)
     B = B if B is not None else rows // Tq
@@ -135,6 +135,9 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False):
         kc, ks, qc, qs = keys, None, q, None
     if zero_q:
         qc = np.zeros_like(qc)
+    if boost is not None:  # entries j0..j1 get 16x larger key scales (scores 16x)
+        ks = ks.copy()
+        ks[:, boost[0]:boost[1]] *= 16.0
     a = L.IndexArgs()
     qpos = torch.tensor(np.asarray(positions, np.int64), device=DEV)
     t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt), k=_tensor(kc), ks=_tensor(ks))
@@ -187,6 +190,20 @@ def test_index_topk_ties_go_to_lower_index():
         nv = odsa.n_vis(m, 4, 8)
         assert sorted(idx[i][idx[i] >= 0].tolist()) == list(range(min(512, nv)))
         assert np.all(sco[i][idx[i] >= 0] == 0.0)
+
+
+def test_index_topk_clustered_top_entries():
+    """Adversarial layout: most of the row's top-512 sit in one workgroup's
+    1024 entries, so the per-workgroup candidate certificate cannot hold and
+    the exact full-row selection must take over."""
+    positions = [200000, 150001]
+    print("[dsa_index_topk] clustered top entries (certificate fallback)", flush=True)
+    idx, sco, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2300, boost=(1024, 2048))
+    for i, m in enumerate(positions):
+        nv = odsa.n_vis(m, 4, 8)
+        scores = odsa.indexer_scores(qd[i], wt[i], kd[i][:nv])
+        assert np.sum((idx[i] >= 1024) & (idx[i] < 2048)) > 100
+        check_topk_row(idx[i], scores, 512, f"clustered row {i}")
 
 
 def test_index_topk_nothing_visible():

@@ -33,6 +33,8 @@ class Workload:
     p0: int = 0          # prefill: first position of the chunk
     T: int = 1           # prefill: chunk length
     seed: int = 0
+    w_cap: int = 0       # window ring slots (0: 2 W, so a decode step can
+                         # insert token m before attention reads [m-W, m-1])
 
     @property
     def E_cap(self):
@@ -42,7 +44,7 @@ class Workload:
 
     @property
     def W_cap(self):
-        return self.W
+        return self.w_cap if self.w_cap else 2 * self.W
 
     @property
     def m(self):

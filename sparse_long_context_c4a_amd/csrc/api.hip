@@ -249,6 +249,28 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     return fail(DSA_ERR_WORKSPACE, "dsa_layer: workspace %zu < required %zu", ws_bytes, L.total);
   L = layer_plan(a, ws);
   const int B = a->n_seqs, T = a->chunk_len;
+  char* base = static_cast<char*>(ws);
+  if (T == 1) {
+    // one token per sequence: fused prologue, indexer + Top-k, attention over
+    // the selected entries and the window ring, window insert
+    const bool early = a->w_cap > a->window_size;  // slot m mod w_cap is outside m's window
+    rc = launch_decode_prologue(*a, const_cast<int64_t*>(L.ia.q_pos), early, st);
+    if (rc != DSA_OK) return rc;
+    rc = launch_index_topk(L.ia, base + L.off_idx_ws, st);
+    if (rc != DSA_OK) return rc;
+    L.aa.chunk_win = nullptr;
+    if (a->ev_attn[0]) {
+      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[0]), st), "event record");
+      if (rc != DSA_OK) return rc;
+    }
+    rc = launch_attn(L.aa, base + L.off_attn_ws, st);
+    if (rc != DSA_OK) return rc;
+    if (a->ev_attn[1]) {
+      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[1]), st), "event record");
+      if (rc != DSA_OK) return rc;
+    }
+    return early ? DSA_OK : launch_decode_window_insert(*a, st);
+  }
   hipLaunchKernelGGL(k_row_positions, dim3((B * T + 255) / 256), dim3(256), 0, st, a->pos0, T, B,
                      const_cast<int64_t*>(L.ia.q_pos));
   rc = hip_check(hipGetLastError(), "k_row_positions launch");
@@ -302,7 +324,6 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     if (rc != DSA_OK) return rc;
   }
   // S3 + S4
-  char* base = static_cast<char*>(ws);
   rc = launch_index_topk(L.ia, base + L.off_idx_ws, st);
   if (rc != DSA_OK) return rc;
   // rotated chunk tokens: the window of the chunk's own queries, then the ring

@@ -73,15 +73,18 @@ __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t* p, int64_t i,
 }
 
 // --------------------------------------------------------------- RoPE
-// cos / sin of (pos * base^(-2i/r)); the product and its reduction are done
-// in fp64 so that positions near 2^20 keep full fp32 accuracy.
+// cos / sin of (pos * base^(-2i/r)).  The angle is formed and reduced modulo
+// 2 pi in fp64 (two-term Cody-Waite with a double-double 2 pi), so that
+// positions near 2^20 keep full accuracy; the reduced angle in [-pi, pi]
+// then goes through fp32 sincos.
 __device__ __forceinline__ void rope_cs(int64_t pos, int i, int r, double base, float* c,
                                         float* s) {
   const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(r));
-  double sd, cd;
-  sincos(static_cast<double>(pos) * theta, &sd, &cd);
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
+  const double ang = static_cast<double>(pos) * theta;
+  const double kq = rint(ang * 0.15915494309189533577);             // 1 / (2 pi)
+  double red = fma(-kq, 6.28318530717958623200, ang);                // 2 pi, high part
+  red = fma(-kq, 2.44929359829470635445e-16, red);                   // 2 pi, low part
+  sincosf(static_cast<float>(red), s, c);
 }
 
 // ------------------------------------------------------- counts / keys

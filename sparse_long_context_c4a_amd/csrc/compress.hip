@@ -1,142 +1,20 @@
-// S1: the compressor.  One workgroup per (entry slot e, sequence b).
-//
-// Entry j mixes raw tokens s*j .. s*j+S-1 with softmax weights over its S
-// logits (one weight per token, shared across the D dims), is optionally
-// RMS-normalised, rotated at position s*j (+offset) and written to slot j
-// (f32, bf16, or fp8 e4m3fn with one fp32 scale per entry).  The pages fuse
-// exactly this chain -- compress, RMSNorm, RoPE, cache insert -- into one
-// kernel ("DeepSeek V4 稀疏注意力完全解剖", 融合点 1); here each thread owns
-// one (even, odd) dim pair so the rotation stays in registers, and a raw
-// token row is read as one coalesced D-vector per step.
+// S1: the compressor kernel, one workgroup per (entry slot e, sequence b);
+// the per-entry work is compress_one (compress_impl.h).
 #include "common.h"
+#include "compress_impl.h"
 #include "internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxSpan = 256;
-constexpr int kMaxPairsPerThread = 4;  // D <= 2048
-
 template <typename RawT, int kOut>
-__global__ __launch_bounds__(kThreads) void k_compress(
+__global__ __launch_bounds__(kCompressThreads) void k_compress(
     const RawT* __restrict__ raw, const RawT* __restrict__ ring, const int64_t* __restrict__ pos0v,
     const float* __restrict__ logits, void* __restrict__ out, float* __restrict__ out_scale,
     const float* __restrict__ gamma, float eps, int64_t T, int logits_rows, int s, int S, int D,
     int r, double base, int64_t off, int64_t e_cap, int64_t max_pos_end, uint32_t* status) {
-  __shared__ float w_s[kMaxSpan];
-  __shared__ float red[16];
-  const int e = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t p0 = pos0v[b];
-  if (p0 < 0 || p0 + T > max_pos_end) {
-    if (tid == 0 && e == 0) set_status(status, DSA_DEVERR_POSITION);
-    return;
-  }
-  const int64_t j0 = n_complete(p0, s, S), j1 = n_complete(p0 + T, s, S);
-  const int64_t j = j0 + e;
-  if (j >= j1) return;  // uniform across the block
-  if (j >= e_cap) {
-    if (tid == 0) set_status(status, DSA_DEVERR_CAPACITY);
-    return;
-  }
-
-  // softmax weights of this entry
-  const float* lg = logits + (static_cast<int64_t>(b) * logits_rows + e) * S;
-  float mx = -INFINITY;
-  for (int i = tid; i < S; i += kThreads) mx = fmaxf(mx, lg[i]);
-  mx = block_max(mx, red);
-  float sum = 0.f;
-  for (int i = tid; i < S; i += kThreads) {
-    const float v = expf(lg[i] - mx);
-    w_s[i] = v;
-    sum += v;
-  }
-  sum = block_sum(sum, red);  // contains a barrier: w_s is complete
-  const float inv = 1.0f / sum;
-
-  // weighted sum; thread owns pairs (2p, 2p+1), p = tid + k*kThreads
-  const int npairs = D / 2;
-  float acc[kMaxPairsPerThread][2];
-#pragma unroll
-  for (int k = 0; k < kMaxPairsPerThread; ++k) acc[k][0] = acc[k][1] = 0.f;
-  const RawT* rawb = raw + static_cast<int64_t>(b) * T * D;
-  const RawT* ringb = ring + static_cast<int64_t>(b) * S * D;
-  for (int i = 0; i < S; ++i) {
-    const int64_t p = static_cast<int64_t>(s) * j + i;
-    const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + (p % S) * D;
-    const float wi = w_s[i] * inv;
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k) {
-      const int pr = tid + k * kThreads;
-      if (pr < npairs) {
-        acc[k][0] = fmaf(wi, load_as_f32(row, 2 * pr), acc[k][0]);
-        acc[k][1] = fmaf(wi, load_as_f32(row, 2 * pr + 1), acc[k][1]);
-      }
-    }
-  }
-
-  if (gamma) {  // RMSNorm: c <- gamma * c / sqrt(mean(c^2) + eps)
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k)
-      if (tid + k * kThreads < npairs) ss += acc[k][0] * acc[k][0] + acc[k][1] * acc[k][1];
-    ss = block_sum(ss, red);
-    const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k) {
-      const int pr = tid + k * kThreads;
-      if (pr < npairs) {
-        acc[k][0] *= gamma[2 * pr] * rs;
-        acc[k][1] *= gamma[2 * pr + 1] * rs;
-      }
-    }
-  }
-
-  // RoPE on the tail r dims at position s*j + off
-  const int first_rot_pair = (D - r) / 2;
-#pragma unroll
-  for (int k = 0; k < kMaxPairsPerThread; ++k) {
-    const int pr = tid + k * kThreads;
-    if (pr < npairs && pr >= first_rot_pair) {
-      float c, sn;
-      rope_cs(static_cast<int64_t>(s) * j + off, pr - first_rot_pair, r, base, &c, &sn);
-      const float a0 = acc[k][0], a1 = acc[k][1];
-      acc[k][0] = a0 * c - a1 * sn;
-      acc[k][1] = a0 * sn + a1 * c;
-    }
-  }
-
-  const int64_t o = (static_cast<int64_t>(b) * e_cap + j) * D;
-  if constexpr (kOut == DSA_F32 || kOut == DSA_BF16) {
-    using OT = typename std::conditional<kOut == DSA_F32, float, uint16_t>::type;
-    OT* op = static_cast<OT*>(out) + o;
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k) {
-      const int pr = tid + k * kThreads;
-      if (pr < npairs) {
-        store_from_f32(op, 2 * pr, acc[k][0]);
-        store_from_f32(op, 2 * pr + 1, acc[k][1]);
-      }
-    }
-  } else {  // fp8 e4m3fn, token-wise scale = amax / 448
-    float am = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k)
-      if (tid + k * kThreads < npairs) am = fmaxf(am, fmaxf(fabsf(acc[k][0]), fabsf(acc[k][1])));
-    am = block_max(am, red);
-    const float sc = am / 448.0f;
-    uint8_t* op = static_cast<uint8_t*>(out) + o;
-#pragma unroll
-    for (int k = 0; k < kMaxPairsPerThread; ++k) {
-      const int pr = tid + k * kThreads;
-      if (pr < npairs) {
-        const uint32_t c0 = sc > 0.f ? f32_to_fp8(acc[k][0] / sc) : 0u;
-        const uint32_t c1 = sc > 0.f ? f32_to_fp8(acc[k][1] / sc) : 0u;
-        *reinterpret_cast<uint16_t*>(op + 2 * pr) = static_cast<uint16_t>(c0 | (c1 << 8));
-      }
-    }
-    if (tid == 0) out_scale[static_cast<int64_t>(b) * e_cap + j] = sc;
-  }
+  compress_one<RawT, kOut>(blockIdx.x, blockIdx.y, raw, ring, pos0v, logits, out, out_scale, gamma,
+                           eps, T, logits_rows, s, S, D, r, base, off, e_cap, max_pos_end, status);
 }
 
 template <typename RawT>
@@ -146,7 +24,7 @@ dsa_status launch_typed(const dsa_compress_args& a, hipStream_t st) {
   const RawT* ring = static_cast<const RawT*>(a.ring);
   const dsa_geom& g = a.geom;
 #define DSA_COMPRESS_LAUNCH(OUT)                                                                  \
-  hipLaunchKernelGGL((k_compress<RawT, OUT>), grid, dim3(kThreads), 0, st, raw, ring, a.raw_pos0, \
+  hipLaunchKernelGGL((k_compress<RawT, OUT>), grid, dim3(kCompressThreads), 0, st, raw, ring, a.raw_pos0, \
                      a.logits, a.out, a.out_scale, a.rms_gamma, a.rms_eps, a.raw_len,            \
                      a.logits_rows, g.stride, g.span, g.dim, g.rope_dim, g.rope_base,            \
                      g.rope_pos_offset, a.e_cap, a.max_pos_end, a.status)
@@ -162,9 +40,9 @@ dsa_status launch_typed(const dsa_compress_args& a, hipStream_t st) {
 }  // namespace
 
 dsa_status launch_compress(const dsa_compress_args& a, hipStream_t st) {
-  if (a.geom.span > kMaxSpan) return fail(DSA_ERR_UNSUPPORTED, "span %d > %d", a.geom.span, kMaxSpan);
-  if (a.geom.dim > 2 * kThreads * kMaxPairsPerThread)
-    return fail(DSA_ERR_UNSUPPORTED, "dim %d > %d", a.geom.dim, 2 * kThreads * kMaxPairsPerThread);
+  if (a.geom.span > kCompressMaxSpan) return fail(DSA_ERR_UNSUPPORTED, "span %d > %d", a.geom.span, kCompressMaxSpan);
+  if (a.geom.dim > 2 * kCompressThreads * kCompressPairs)
+    return fail(DSA_ERR_UNSUPPORTED, "dim %d > %d", a.geom.dim, 2 * kCompressThreads * kCompressPairs);
   if (a.logits_rows == 0) return DSA_OK;
   return a.raw_dtype == DSA_F32 ? launch_typed<float>(a, st) : launch_typed<uint16_t>(a, st);
 }

@@ -39,6 +39,12 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
                                 int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
                                 hipStream_t st);
 
+// Decode (one token per sequence): fused prologue and, when the window ring
+// has no spare slot, the window insert after attention.
+dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
+                                  hipStream_t st);
+dsa_status launch_decode_window_insert(const dsa_layer_args& a, hipStream_t st);
+
 inline size_t dtype_size(dsa_dtype t) {
   return t == DSA_F32 ? 4 : t == DSA_BF16 ? 2 : 1;
 }

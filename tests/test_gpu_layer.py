@@ -80,6 +80,8 @@ SMALL = [
     # name, workload, overrides, p0, T, state
     ("c4a_decode_B3_L3000", configs.C4A_DECODE_64K, dict(B=3, L=3000), None, None, "random"),
     ("c4a_decode_L20_tiny", configs.C4A_DECODE_64K, dict(B=2, L=20), None, None, "random"),
+    ("c4a_decode_ring_eq_window", configs.C4A_DECODE_64K, dict(B=2, L=2000, w_cap=128), None,
+     None, "random"),
     ("c128a_decode_B2_L5000", configs.C128A_DECODE_1M, dict(B=2, L=5000, k=64), None, None,
      "random"),
     ("c4a_prefill_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077), 2000, 77, "random"),

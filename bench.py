@@ -153,7 +153,7 @@ def main():
         "kernel_ms": {"indexer": idx_ms, "attention": attn_ms},
         "roofline": {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": idx_gbps / PEAK_HBM_GBPS if idx_gbps else None, "traffic": None,
-                     "kernel": "k_index_fp8_stream", "alg_bytes_per_launch": idx_bytes},
+                     "kernel": "k_decode_index", "alg_bytes_per_launch": idx_bytes},
     }
     del sets
     torch.cuda.empty_cache()

@@ -254,9 +254,10 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     // one token per sequence: fused prologue, indexer + Top-k, attention over
     // the selected entries and the window ring, window insert
     const bool early = a->w_cap > a->window_size;  // slot m mod w_cap is outside m's window
-    rc = launch_decode_prologue(*a, const_cast<int64_t*>(L.ia.q_pos), early, st);
-    if (rc != DSA_OK) return rc;
-    rc = launch_index_topk(L.ia, base + L.off_idx_ws, st);
+    int64_t* qpos = const_cast<int64_t*>(L.ia.q_pos);
+    L.ia.q_pos = a->pos0;  // one query per sequence, at pos0
+    L.aa.q_pos = a->pos0;
+    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, st);
     if (rc != DSA_OK) return rc;
     L.aa.chunk_win = nullptr;
     if (a->ev_attn[0]) {

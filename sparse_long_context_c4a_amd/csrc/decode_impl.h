@@ -1,0 +1,93 @@
+// Decode-step state updates (compressor entries, rings, window insert) as a
+// device function, shared by the stand-alone prologue kernel and the fused
+// decode indexer kernel.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "compress_impl.h"
+
+namespace dsa {
+
+// Rotate raw token x (D dims of type T) at position pos and store it to dst.
+template <typename T>
+__device__ __forceinline__ void rotate_store(const T* __restrict__ x, T* __restrict__ dst, int D,
+                                             int r, double base, int64_t pos) {
+  const int first_rot = (D - r) / 2;
+  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) {
+    float a0 = load_as_f32(x, 2 * pr), a1 = load_as_f32(x, 2 * pr + 1);
+    if (pr >= first_rot) {
+      float c, sn;
+      rope_cs(pos, pr - first_rot, r, base, &c, &sn);
+      const float t0 = a0 * c - a1 * sn, t1 = a0 * sn + a1 * c;
+      a0 = t0;
+      a1 = t1;
+    }
+    store_from_f32(dst, 2 * pr, a0);
+    store_from_f32(dst, 2 * pr + 1, a1);
+  }
+}
+
+struct PrologueArgs {
+  int B, D, Di, s, S, r, r_idx, w_cap;
+  double base, idx_base;
+  int64_t off, e_cap, max_pos_end;
+  float eps;
+  bool has_idx, insert_window;
+  const int64_t* pos0;
+  const void *x, *kx;
+  const float *logits_main, *logits_idx, *gamma, *gamma_idx;
+  void *main_cache, *idx_cache, *main_ring, *idx_ring, *window;
+  float* idx_scale;
+  int64_t* qpos;
+  uint32_t* status;
+};
+
+// Decode-step prologue, one role per workgroup: role 0 writes the main entry
+// completing at m (if any), role 1 the indexer entry, role 2 puts token m
+// into the compressor rings, the row's query position, and -- when the
+// window ring has a spare slot (w_cap > W) -- the rotated token m (slot
+// m mod w_cap is not in m's window then).  For one token the ring slot
+// written (m mod S) is not one the compressor reads (it reads positions
+// m-S+1 .. m-1 from the ring and m from x), and nothing here is read by the
+// same step's indexer or attention (the new entry is not visible to m), so
+// these workgroups may run beside them.
+template <typename MainT, int kIdxOut>
+__device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueArgs a) {
+  using IdxRawT = typename std::conditional<kIdxOut == DSA_F32, float, uint16_t>::type;
+  constexpr int kMainOut = std::is_same<MainT, float>::value ? DSA_F32 : DSA_BF16;
+  if (role == 0) {
+    compress_one<MainT, kMainOut>(0, b, static_cast<const MainT*>(a.x),
+                                  static_cast<const MainT*>(a.main_ring), a.pos0, a.logits_main,
+                                  a.main_cache, nullptr, a.gamma, a.eps, 1, 1, a.s, a.S, a.D, a.r,
+                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status);
+    return;
+  }
+  if (role == 1) {
+    if (a.has_idx)
+      compress_one<IdxRawT, kIdxOut>(0, b, static_cast<const IdxRawT*>(a.kx),
+                                     static_cast<const IdxRawT*>(a.idx_ring), a.pos0, a.logits_idx,
+                                     a.idx_cache, a.idx_scale, a.gamma_idx, a.eps, 1, 1, a.s, a.S,
+                                     a.Di, a.r_idx, a.idx_base, a.off, a.e_cap, a.max_pos_end,
+                                     a.status);
+    return;
+  }
+  const int64_t m = a.pos0[b];
+  if (threadIdx.x == 0) a.qpos[b] = m;
+  if (m < 0 || m >= a.max_pos_end) return;
+  const MainT* xb = static_cast<const MainT*>(a.x) + static_cast<int64_t>(b) * a.D;
+  MainT* rb = static_cast<MainT*>(a.main_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.D;
+  for (int i = threadIdx.x; i < a.D; i += blockDim.x) rb[i] = xb[i];
+  if (a.has_idx) {
+    const IdxRawT* kb = static_cast<const IdxRawT*>(a.kx) + static_cast<int64_t>(b) * a.Di;
+    IdxRawT* ib = static_cast<IdxRawT*>(a.idx_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.Di;
+    for (int i = threadIdx.x; i < a.Di; i += blockDim.x) ib[i] = kb[i];
+  }
+  if (a.insert_window)
+    rotate_store(xb, static_cast<MainT*>(a.window) + (static_cast<int64_t>(b) * a.w_cap + m % a.w_cap) * a.D,
+                 a.D, a.r, a.base, m + a.off);
+}
+
+
+}  // namespace dsa

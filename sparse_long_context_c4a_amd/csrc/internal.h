@@ -41,6 +41,13 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 
 // Decode (one token per sequence): fused prologue and, when the window ring
 // has no spare slot, the window insert after attention.
+struct PrologueArgs;
+PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window);
+// The indexer + Top-k of a decode step with the prologue's workgroups riding
+// in the indexer's launch (or launched first when the indexer takes another
+// path).
+dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
+                                    int64_t* qpos, bool insert_window, hipStream_t st);
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
                                   hipStream_t st);
 dsa_status launch_decode_window_insert(const dsa_layer_args& a, hipStream_t st);

@@ -7,6 +7,7 @@
 // positions (same page, 机制四), position n at slot n mod w_cap.
 #include "common.h"
 #include "compress_impl.h"
+#include "decode_impl.h"
 #include "internal.h"
 
 namespace dsa {
@@ -74,82 +75,9 @@ __global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int
   for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
 }
 
-// Rotate raw token x (D dims of type T) at position pos and store it to dst.
-template <typename T>
-__device__ __forceinline__ void rotate_store(const T* __restrict__ x, T* __restrict__ dst, int D,
-                                             int r, double base, int64_t pos) {
-  const int first_rot = (D - r) / 2;
-  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) {
-    float a0 = load_as_f32(x, 2 * pr), a1 = load_as_f32(x, 2 * pr + 1);
-    if (pr >= first_rot) {
-      float c, sn;
-      rope_cs(pos, pr - first_rot, r, base, &c, &sn);
-      const float t0 = a0 * c - a1 * sn, t1 = a0 * sn + a1 * c;
-      a0 = t0;
-      a1 = t1;
-    }
-    store_from_f32(dst, 2 * pr, a0);
-    store_from_f32(dst, 2 * pr + 1, a1);
-  }
-}
-
-struct PrologueArgs {
-  int B, D, Di, s, S, r, r_idx, w_cap;
-  double base, idx_base;
-  int64_t off, e_cap, max_pos_end;
-  float eps;
-  bool has_idx, insert_window;
-  const int64_t* pos0;
-  const void *x, *kx;
-  const float *logits_main, *logits_idx, *gamma, *gamma_idx;
-  void *main_cache, *idx_cache, *main_ring, *idx_ring, *window;
-  float* idx_scale;
-  int64_t* qpos;
-  uint32_t* status;
-};
-
-// Decode-step prologue: every state update that precedes the indexer, in one
-// launch.  Blocks [0, B): the main entry completing at m (if any); [B, 2B):
-// the indexer entry; [2B, 3B): compressor rings take token m, the row's
-// query position, and -- when the window ring has a spare slot (w_cap > W)
-// -- the rotated token m (slot m mod w_cap is not in m's window then).  For
-// one token the ring slot written (m mod S) is not one the compressor reads
-// (it reads positions m-S+1 .. m-1 from the ring and m from x).
 template <typename MainT, int kIdxOut>
 __global__ __launch_bounds__(kCompressThreads) void k_decode_prologue(PrologueArgs a) {
-  using IdxRawT = typename std::conditional<kIdxOut == DSA_F32, float, uint16_t>::type;
-  constexpr int kMainOut = std::is_same<MainT, float>::value ? DSA_F32 : DSA_BF16;
-  const int role = blockIdx.x / a.B, b = blockIdx.x % a.B;
-  if (role == 0) {
-    compress_one<MainT, kMainOut>(0, b, static_cast<const MainT*>(a.x),
-                                  static_cast<const MainT*>(a.main_ring), a.pos0, a.logits_main,
-                                  a.main_cache, nullptr, a.gamma, a.eps, 1, 1, a.s, a.S, a.D, a.r,
-                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status);
-    return;
-  }
-  if (role == 1) {
-    if (a.has_idx)
-      compress_one<IdxRawT, kIdxOut>(0, b, static_cast<const IdxRawT*>(a.kx),
-                                     static_cast<const IdxRawT*>(a.idx_ring), a.pos0, a.logits_idx,
-                                     a.idx_cache, a.idx_scale, a.gamma_idx, a.eps, 1, 1, a.s, a.S,
-                                     a.Di, a.r_idx, a.idx_base, a.off, a.e_cap, a.max_pos_end,
-                                     a.status);
-    return;
-  }
-  const int64_t m = a.pos0[b];
-  if (threadIdx.x == 0) a.qpos[b] = m;
-  if (m < 0 || m >= a.max_pos_end) return;
-  const MainT* xb = static_cast<const MainT*>(a.x) + static_cast<int64_t>(b) * a.D;
-  MainT* rb = static_cast<MainT*>(a.main_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.D;
-  for (int i = threadIdx.x; i < a.D; i += blockDim.x) rb[i] = xb[i];
-  if (a.has_idx) {
-    const IdxRawT* kb = static_cast<const IdxRawT*>(a.kx) + static_cast<int64_t>(b) * a.Di;
-    IdxRawT* ib = static_cast<IdxRawT*>(a.idx_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.Di;
-    for (int i = threadIdx.x; i < a.Di; i += blockDim.x) ib[i] = kb[i];
-  }
-  if (a.insert_window)
-    rotate_store(xb, static_cast<MainT*>(a.window) + (static_cast<int64_t>(b) * a.w_cap + m % a.w_cap) * a.D,
-                 a.D, a.r, a.base, m + a.off);
+  decode_prologue_block<MainT, kIdxOut>(blockIdx.x / a.B, blockIdx.x % a.B, a);
 }
 
 // Decode-step epilogue when the window ring has no spare slot: the rotated
@@ -214,8 +142,7 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 
 namespace dsa {
 
-dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  hipStream_t st) {
+PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window) {
   PrologueArgs p{};
   p.B = a.n_seqs;
   p.D = a.main.dim;
@@ -248,6 +175,12 @@ dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool i
   p.idx_scale = a.idx_scale;
   p.qpos = qpos;
   p.status = a.status;
+  return p;
+}
+
+dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
+                                  hipStream_t st) {
+  const PrologueArgs p = make_prologue_args(a, qpos, insert_window);
   const dim3 grid(3 * a.n_seqs), block(kCompressThreads);
   if (a.dtype == DSA_F32) {
     if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);

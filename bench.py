@@ -53,6 +53,12 @@ def build_sets(w, n_sets, device):
 
 
 def time_layer(w, sets, steps, warmup, decode):
+    """Two timed passes of `steps` layer steps each, after `warmup` untimed
+    ones.  The first pass gives the step time: nothing but the layer's own
+    launches on the stream, bracketed by events.  The second pass hands the
+    library HIP events that it attaches to the dispatch packets of the
+    scoring kernel and of the attention kernels (hipExtLaunchKernel), which
+    gives their own durations on the stream they run on."""
     import torch
     from sparse_long_context_c4a_amd import _lib
     from sparse_long_context_c4a_amd import layer as Ly
@@ -67,47 +73,57 @@ def time_layer(w, sets, steps, warmup, decode):
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(args[i % len(args)], ws=ws, stream=stream)
-    ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
-    ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    for i in range(steps):
+        fn(args[i % len(args)], ws=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
+    ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
     for i in range(steps):
         a = args[i % len(args)]
         a.ev_index[0], a.ev_index[1] = ev_i[i][0].handle, ev_i[i][1].handle
         a.ev_attn[0], a.ev_attn[1] = ev_a[i][0].handle, ev_a[i][1].handle
         fn(a, ws=ws, stream=stream)
-    t1.record(stream)
     torch.cuda.synchronize()
     for a in args:
         a.ev_index[0] = a.ev_index[1] = a.ev_attn[0] = a.ev_attn[1] = None
     st = [o[3].item() for o in outs]
     assert all(s == 0 for s in st), f"device status {st}"
-    ms = t0.elapsed_time(t1) / steps
     idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / steps
     attn_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_a) / steps
     return ms, idx_ms, attn_ms
 
 
-def cpu_baseline(w, n_queries):
-    """The fp64 oracle on a bounded sample of the same workload: the full
-    layer step for the first n_queries sequences of one input set."""
+def cpu_baseline(w, min_seconds=10.0, max_sets=8):
+    """The fp64 oracle on a bounded sample of the same workload: full layer
+    steps for all w.B decode queries of successive seeded input sets, until
+    at least min_seconds of oracle time (or max_sets sets) have been spent.
+    Input generation is outside the timed part."""
     from threadpoolctl import threadpool_info
 
     from oracle.layer import Geometry
     from oracle.run import run_layer
-    from sparse_long_context_c4a_amd import configs, inputs as gen
-    ws = configs.shrink(w, B=n_queries)
-    inp = gen.layer_inputs(ws, seed=w.seed)
+    from sparse_long_context_c4a_amd import inputs as gen
     g = Geometry(s=w.s, S=w.S, D=w.D, r=w.r, Di=w.Di, r_idx=w.r_idx, H=w.H, Hi=w.Hi, k=w.k,
                  W=w.W, main_dtype=w.main_dtype, idx_dtype=w.idx_dtype)
-    t = time.perf_counter()
-    run_layer(g, inp)
-    dt = time.perf_counter() - t
+    dt, n = 0.0, 0
+    for i in range(max_sets):
+        inp = gen.layer_inputs(w, seed=w.seed + 1000 * i)
+        t = time.perf_counter()
+        run_layer(g, inp)
+        dt += time.perf_counter() - t
+        n += w.B
+        del inp
+        if dt >= min_seconds:
+            break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n_queries / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_queries} of the {w.B} decode queries of {w.name} (full layer step, "
-                      f"fp64 NumPy), {dt:.1f} s"}
+    return {"value": n / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode queries of {w.name} ({n // w.B} seeded input sets of "
+                      f"{w.B}; full layer step, fp64 NumPy), {dt:.1f} s of oracle time"}
 
 
 def main():
@@ -118,8 +134,11 @@ def main():
     ap.add_argument("--workload", default="c4a_decode_B4_L1M")
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-queries", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB three times "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer's multi-GPU "
@@ -157,6 +176,15 @@ def main():
     }
     del sets
     torch.cuda.empty_cache()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = n
+        del src, dst
     if not args.no_prefill:
         wp = configs.C4A_PREFILL_128K
         print("[bench] prefill chunk", file=sys.stderr, flush=True)
@@ -173,7 +201,7 @@ def main():
         del psets
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line))
 
 

@@ -159,7 +159,7 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
 struct LayerWs {
   dsa_index_args ia;
   dsa_attn_args aa;
-  size_t off_idx_ws, off_attn_ws, off_idx, off_rot, total;
+  size_t off_idx_ws, off_attn_ws, off_idx, off_rot, off_cs, total;
 };
 
 LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
@@ -193,6 +193,9 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   if (!a->idx_out) off = align_up(off + static_cast<size_t>(rows) * a->k * sizeof(int32_t));
   L.off_rot = off;
   off = align_up(off + static_cast<size_t>(rows) * a->main.dim * dtype_size(a->dtype));
+  // decode: the (cos, sin) table of each row's position
+  L.off_cs = off;
+  if (a->chunk_len == 1) off = align_up(off + static_cast<size_t>(rows) * a->main.rope_dim * 4);
   // q positions (one per row)
   dsa_attn_args& aa = L.aa;
   aa.n_seqs = a->n_seqs;
@@ -257,19 +260,17 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     int64_t* qpos = const_cast<int64_t*>(L.ia.q_pos);
     L.ia.q_pos = a->pos0;  // one query per sequence, at pos0
     L.aa.q_pos = a->pos0;
-    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, st);
-    if (rc != DSA_OK) return rc;
     L.aa.chunk_win = nullptr;
-    if (a->ev_attn[0]) {
-      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[0]), st), "event record");
-      if (rc != DSA_OK) return rc;
-    }
-    rc = launch_attn(L.aa, base + L.off_attn_ws, st);
+    // the prologue leaves the (cos, sin) table of m for attention
+    float* cs_tab = reinterpret_cast<float*>(base + L.off_cs);
+    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab, st);
     if (rc != DSA_OK) return rc;
-    if (a->ev_attn[1]) {
-      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[1]), st), "event record");
-      if (rc != DSA_OK) return rc;
-    }
+    AttnLaunch lx;
+    lx.ev0 = a->ev_attn[0];
+    lx.ev1 = a->ev_attn[1];
+    lx.cs_tab = cs_tab;
+    rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
+    if (rc != DSA_OK) return rc;
     return early ? DSA_OK : launch_decode_window_insert(*a, st);
   }
   hipLaunchKernelGGL(k_row_positions, dim3((B * T + 255) / 256), dim3(256), 0, st, a->pos0, T, B,
@@ -333,16 +334,11 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
                            st);
   if (rc != DSA_OK) return rc;
   // S5
-  if (a->ev_attn[0]) {
-    rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[0]), st), "event record");
-    if (rc != DSA_OK) return rc;
-  }
-  rc = launch_attn(L.aa, base + L.off_attn_ws, st);
+  AttnLaunch lx;
+  lx.ev0 = a->ev_attn[0];
+  lx.ev1 = a->ev_attn[1];
+  rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
   if (rc != DSA_OK) return rc;
-  if (a->ev_attn[1]) {
-    rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a->ev_attn[1]), st), "event record");
-    if (rc != DSA_OK) return rc;
-  }
   // window ring update after attention
   return launch_window_update(base + L.off_rot, a->dtype, a->main.dim, T, a->window, a->w_cap,
                               a->pos0, B, a->max_pos_end, st);

@@ -39,6 +39,7 @@ struct AttnGeom {
   float scale;
   int64_t max_pos_end;
   int slots_per_run, n_runs;
+  const float* cs_tab;  // optional (cos, sin) of R_m per row, r floats per row
   uint32_t* status;
 };
 
@@ -436,18 +437,355 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   }
 }
 
+// ------------------------------------------------------ decode-shaped path
+// bf16, D = 512, heads in groups of 16, few rows.  A workgroup takes one
+// row, 16 heads and a run of slots; its four waves take interleaved groups
+// of 32 slots.  Each wave gathers its own 32 vectors straight into LDS with
+// the gfx950 LDS DMA load (global_load_lds_dwordx4: one 1 KiB vector per
+// instruction, no registers on the way), computes S^T = K Q^T and
+// O^T += V^T P^T for its 16 heads exactly as the MFMA path above, and keeps
+// its own online-softmax state.  The four waves then merge in LDS.  A row
+// whose slots span several runs leaves one un-normalised partial
+// (max, sum, acc) per run, merged by k_attn_dcombine; the run-0 workgroup
+// also leaves the R_m table for it.
+constexpr int kDH = 16;                       // heads per workgroup
+constexpr int kDStep = 32;                    // vectors per wave step
+constexpr int kDWaveBytes = kDStep * kMPitch; // 33,792 B of LDS per wave
+constexpr int kDOPitch = kMD + 4;             // floats per head row when merging waves
+constexpr int kDSlotsPerIter = 4 * kDStep;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Source of slot a of row `row` given its cache index j (read by the caller
+// for a < k); nullptr if the slot is empty.
+__device__ __forceinline__ const uint16_t* dslot_ptr(const AttnGeom& g, int b, int64_t m, int a,
+                                                     int32_t j, const uint16_t* cache,
+                                                     const uint16_t* window,
+                                                     const uint16_t* chunk_win) {
+  if (a < g.k) {
+    if (j < 0 || j >= g.e_cap) return nullptr;
+    return cache + (static_cast<int64_t>(b) * g.e_cap + j) * kMD;
+  }
+  const int64_t n = m - g.W + (a - g.k);
+  if (n < 0 || n >= m) return nullptr;
+  if (chunk_win) {
+    const int64_t c0 = g.chunk_pos0[b];
+    if (n >= c0 && n - c0 < g.chunk_len)
+      return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (n - c0)) * kMD;
+  }
+  return window + (static_cast<int64_t>(b) * g.w_cap + (n % g.w_cap)) * kMD;
+}
+
+// Cache index of slot a for lane-parallel prefetch (only slots a < k have one).
+__device__ __forceinline__ int32_t dslot_index(const AttnGeom& g, int row, int a, int a_end) {
+  return (a < a_end && a < g.k) ? g.idx[static_cast<int64_t>(row) * g.k + a] : -1;
+}
+
+// Issue the LDS DMA of one wave step: lane v < 32 holds the source of
+// vector v (a stand-in vector, whose probability will be zero, for empty
+// slots).  Returns the ballot of non-empty slots.
+__device__ __forceinline__ uint64_t gather_issue(const uint16_t* src, const uint16_t* dummy,
+                                                 int lane, uint8_t* wl) {
+  const uint64_t vmask = __ballot(lane < kDStep && src != nullptr);
+  if (vmask == 0) return 0;
+  if (src == nullptr) src = dummy;
+  const uint64_t sp = reinterpret_cast<uint64_t>(src);
+  const uint32_t sp_lo = static_cast<uint32_t>(sp), sp_hi = static_cast<uint32_t>(sp >> 32);
+#pragma unroll 8
+  for (int v = 0; v < kDStep; ++v) {
+    // readlane returns int: go through uint32_t so the low word is not
+    // sign-extended into the high one
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_lo, v));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_hi, v));
+    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+    const uint8_t* gp = reinterpret_cast<const uint8_t*>(base) + lane * 16;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)gp, (lds_void_t*)(wl + v * kMPitch), 16, 0, 0);
+  }
+  return vmask;
+}
+
+// Normalise, apply R_m^{-1} and store dims 4 d4 .. 4 d4 + 3 of one head.
+__device__ __forceinline__ void store_head_dims4(float4 acc, float L, int d4, int rot0,
+                                                 const float* cs, uint16_t* orow) {
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int d = 4 * d4 + 2 * p;
+    if (d >= rot0) {
+      const float c = cs[d - rot0], s = cs[d - rot0 + 1];
+      const float a0 = v[2 * p], a1 = v[2 * p + 1];
+      v[2 * p] = a0 * c + a1 * s;
+      v[2 * p + 1] = -a0 * s + a1 * c;
+    }
+  }
+  *reinterpret_cast<uint2*>(orow + 4 * d4) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+__global__ __launch_bounds__(256) void k_attn_decode(
+    AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
+    const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
+    float* __restrict__ part_ml, float* __restrict__ cs_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t dsm[4 * kDWaveBytes];
+  __shared__ float cs_s[kMD];  // (cos, sin) of pair i at 2i, 2i+1
+  __shared__ float ml_s[4][kDH][2];
+  __shared__ float hml_s[kDH][2];
+  const int run = blockIdx.x, hg = blockIdx.y, row = blockIdx.z;
+  const int G = gridDim.y;
+  const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, gq = lane >> 4;
+  const int total = g.k + g.W;
+  const int a_begin = run * g.slots_per_run;
+  const int a_end = min(total, a_begin + g.slots_per_run);
+  int a0 = a_begin + wave * kDStep;
+  // independent loads first: the first step's cache indices, the query
+  // position, the query heads hg*16 + n (dims 32c + 8gq .. +7, the B
+  // operand) and, when given, the R_m table
+  int32_t jn = dslot_index(g, row, a0 + lane, a_end);
+  const int64_t m = g.q_pos[row];
+  const int h = hg * kDH + n;
+  uint4 qraw[16];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * g.H + h) * kMD);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qraw[c] = qrow[4 * c + gq];
+  }
+  const int half = g.r / 2, rot0 = kMD - g.r;
+  if (g.cs_tab)
+    for (int i = tid; i < 2 * half; i += 256) cs_s[i] = g.cs_tab[static_cast<int64_t>(row) * g.r + i];
+  const bool ok = m >= 0 && m < g.max_pos_end;
+  if (!ok && tid == 0 && hg == 0 && run == 0) set_status(g.status, DSA_DEVERR_POSITION);
+  uint8_t* wl = dsm + wave * kDWaveBytes;
+  const uint16_t* dummy = q + static_cast<int64_t>(row) * g.H * kMD;
+  uint64_t vmask = 0;
+  if (a0 < a_end) {
+    const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
+                              ? dslot_ptr(g, b, m, a0 + lane, jn, cache, window, chunk_win)
+                              : nullptr;
+    vmask = gather_issue(src, dummy, lane, wl);
+  }
+  if (!g.cs_tab)
+    for (int i = tid; i < half; i += 256) {
+      float c = 1.f, sn = 0.f;
+      if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+      cs_s[2 * i] = c;
+      cs_s[2 * i + 1] = sn;
+    }
+  __syncthreads();
+  if (cs_out && !g.cs_tab && run == 0 && hg == 0)
+    for (int i = tid; i < 2 * half; i += 256) cs_out[static_cast<int64_t>(row) * g.r + i] = cs_s[i];
+  v8bf qb[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int d0 = 32 * c + 8 * gq;
+    uint4 raw = qraw[c];
+    if (rotate_q && d0 + 8 > rot0) {
+      uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int d = d0 + 2 * p;
+        if (d >= rot0) {
+          const float x0 = bf16_to_f32(static_cast<uint16_t>(wd[p] & 0xffffu));
+          const float x1 = bf16_to_f32(static_cast<uint16_t>(wd[p] >> 16));
+          const float cc = cs_s[d - rot0], ss = cs_s[d - rot0 + 1];
+          wd[p] = pack_bf16x2(x0 * cc - x1 * ss, x0 * ss + x1 * cc);
+        }
+      }
+      raw = uint4{wd[0], wd[1], wd[2], wd[3]};
+    }
+    qb[c] = as_v8bf(raw);
+  }
+  v4f o[32];
+#pragma unroll
+  for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const int te = (lane & 15) >> 2, tq = lane & 3;
+  for (; a0 < a_end; a0 += kDSlotsPerIter) {
+    // next step's cache indices in flight during this step
+    const int nxt = a0 + kDSlotsPerIter;
+    jn = nxt < a_end ? dslot_index(g, row, nxt + lane, a_end) : -1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS DMA has landed
+    if (vmask != 0) {
+      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int off = (32 * c + 8 * gq) * 2;
+        const v8bf k0 = as_v8bf(*reinterpret_cast<const uint4*>(wl + n * kMPitch + off));
+        const v8bf k1 = as_v8bf(*reinterpret_cast<const uint4*>(wl + (16 + n) * kMPitch + off));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
+      }
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * g.scale : -INFINITY;
+        x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * g.scale : -INFINITY;
+      }
+      float tmax = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = (x[i] == -INFINITY) ? 0.f : expf(x[i] - m_new);
+        psum += p[i];
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      const float corr = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      if (__any(corr != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < 32; ++db) o[db] *= corr;
+      }
+      const v8bf pb = as_v8bf(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+      lds_u8* r_lo = (lds_u8*)wl + (4 * gq + te) * kMPitch + tq * 8;
+      lds_u8* r_hi = (lds_u8*)wl + (16 + 4 * gq + te) * kMPitch + tq * 8;
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
+        const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+      }
+    }
+    vmask = 0;
+    if (nxt < a_end) {
+      const uint16_t* src = (ok && nxt + lane < a_end && lane < kDStep)
+                                ? dslot_ptr(g, b, m, nxt + lane, jn, cache, window, chunk_win)
+                                : nullptr;
+      vmask = gather_issue(src, dummy, lane, wl);
+    }
+  }
+  // merge the four waves: lane holds O^T[dims 16 db + 4 gq + i][head n]
+  if (gq == 0) {
+    ml_s[wave][n][0] = m_run;
+    ml_s[wave][n][1] = l_run;
+  }
+  __syncthreads();
+  if (tid < kDH) {  // per head: the block's max and sum over its waves
+    float M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[w][tid][0]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ml_s[w][tid][0];
+      if (mw != -INFINITY) L += ml_s[w][tid][1] * expf(mw - M);
+    }
+    hml_s[tid][0] = M;
+    hml_s[tid][1] = L;
+  }
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[w][n][0]);
+    const float cw = (m_run == -INFINITY) ? 0.f : expf(m_run - M);
+    float* ow = reinterpret_cast<float*>(wl);
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<float4*>(ow + n * kDOPitch + 16 * db + 4 * gq) =
+          float4{o[db][0] * cw, o[db][1] * cw, o[db][2] * cw, o[db][3] * cw};
+  }
+  __syncthreads();
+  // thread -> dims 4 d4 .. +3 of heads hp, hp + 2, ..., hp + 14
+  const int d4 = tid & 127, hp = tid >> 7;
+  const int64_t pbase = (static_cast<int64_t>(row) * G + hg) * g.n_runs + run;
+#pragma unroll 2
+  for (int i = 0; i < kDH / 2; ++i) {
+    const int ch = hp + 2 * i;
+    const float M = hml_s[ch][0], L = hml_s[ch][1];
+    float4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 u = *reinterpret_cast<const float4*>(
+          reinterpret_cast<const float*>(dsm + w * kDWaveBytes) + ch * kDOPitch + 4 * d4);
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const int hh = hg * kDH + ch;
+    if (g.n_runs == 1) {
+      store_head_dims4(t, L, d4, rot0, cs_s, out + (static_cast<int64_t>(row) * g.H + hh) * kMD);
+      if (lse && d4 == 0)
+        lse[static_cast<int64_t>(row) * g.H + hh] = L > 0.f ? M + logf(L) : -INFINITY;
+    } else {
+      const int64_t pi = pbase * kDH + ch;
+      reinterpret_cast<float4*>(part_acc + pi * kMD)[d4] = t;
+      if (d4 == 0) {
+        part_ml[2 * pi] = M;
+        part_ml[2 * pi + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge the runs of one (row, head) pair of heads of the decode-shaped path
+// and apply R_m^{-1} (table left by the run-0 workgroup).  Thread -> head
+// 2 blockIdx.x + tid / 128, dims 4 (tid % 128) .. +3.
+__global__ __launch_bounds__(256) void k_attn_dcombine(AttnGeom g, const float* __restrict__ part_acc,
+                                                       const float* __restrict__ part_ml,
+                                                       const float* __restrict__ cs_in,
+                                                       uint16_t* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  __shared__ float cs_s[kMD];
+  const int row = blockIdx.y, tid = threadIdx.x;
+  const int h = 2 * blockIdx.x + (tid >> 7), d4 = tid & 127;
+  const int hg = h / kDH, ch = h % kDH, G = g.H / kDH;
+  const float* cs_src = g.cs_tab ? g.cs_tab : cs_in;
+  for (int i = tid; i < g.r; i += 256) cs_s[i] = cs_src[static_cast<int64_t>(row) * g.r + i];
+  const int64_t p0 = (static_cast<int64_t>(row) * G + hg) * g.n_runs;
+  float M = -INFINITY;
+  for (int r = 0; r < g.n_runs; ++r) M = fmaxf(M, part_ml[2 * ((p0 + r) * kDH + ch)]);
+  float L = 0.f;
+  float4 t = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < g.n_runs; ++r) {
+    // an empty run left max -inf, sum 0 and acc 0
+    const int64_t pi = (p0 + r) * kDH + ch;
+    const float mr = part_ml[2 * pi];
+    const float wgt = mr == -INFINITY ? 0.f : expf(mr - M);
+    L += wgt * part_ml[2 * pi + 1];
+    const float4 u = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
+    t.x = fmaf(wgt, u.x, t.x);
+    t.y = fmaf(wgt, u.y, t.y);
+    t.z = fmaf(wgt, u.z, t.z);
+    t.w = fmaf(wgt, u.w, t.w);
+  }
+  __syncthreads();
+  store_head_dims4(t, L, d4, kMD - g.r, cs_s, out + (static_cast<int64_t>(row) * g.H + h) * kMD);
+  if (lse && d4 == 0) lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
 struct Plan {
-  bool mfma;
+  bool mfma, dec;
   int slots_per_run, n_runs;
-  size_t off_acc, off_ml, total;
+  size_t off_acc, off_ml, off_cs, total;
 };
 
 Plan plan(const dsa_attn_args& a) {
   Plan p{};
   const int64_t rows = static_cast<int64_t>(a.n_seqs) * a.queries_per_seq;
-  const int total = a.k + a.window_size;
-  p.mfma = a.dtype == DSA_BF16 && a.dim == kMD && a.heads % 64 == 0 && a.rope_dim <= kMD;
-  if (p.mfma) {
+  const int total = std::max(1, a.k + a.window_size);
+  const bool bf16_512 = a.dtype == DSA_BF16 && a.dim == kMD && a.rope_dim <= kMD;
+  p.dec = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048;
+  p.mfma = !p.dec && bf16_512 && a.heads % 64 == 0;
+  if (p.dec) {
+    // about 1024 workgroups: runs of whole 128-slot iterations
+    const int64_t pairs = rows * (a.heads / kDH);
+    const int64_t iters_total = ceil_div(total, kDSlotsPerIter);
+    const int64_t rmax = std::max<int64_t>(1, ceil_div(1024, pairs));
+    const int64_t iters = ceil_div(iters_total, rmax);
+    p.slots_per_run = static_cast<int>(iters * kDSlotsPerIter);
+    p.n_runs = static_cast<int>(ceil_div(total, p.slots_per_run));
+  } else if (p.mfma) {
     // about 512 workgroups over the chip, at least two tiles per run
     const int64_t hq = a.heads / 64;
     const int tiles = static_cast<int>(ceil_div(total, kMTile));
@@ -470,12 +808,15 @@ Plan plan(const dsa_attn_args& a) {
   if (p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * 4);
   p.off_ml = off;
   if (p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * 2 * 4);
+  p.off_cs = off;
+  if (p.dec && p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * a.rope_dim * 4);
   p.total = off;
   return p;
 }
 
 template <typename T>
-dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStream_t st) {
+dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStream_t st,
+                        const AttnLaunch& lx) {
   AttnGeom g{};
   g.q_pos = a.q_pos;
   g.Tq = a.queries_per_seq;
@@ -495,40 +836,58 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.max_pos_end = a.max_pos_end;
   g.slots_per_run = p.slots_per_run;
   g.n_runs = p.n_runs;
+  g.cs_tab = lx.cs_tab;
   g.status = a.status;
   const int rows = a.n_seqs * a.queries_per_seq;
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
+  const hipEvent_t ev0 = static_cast<hipEvent_t>(lx.ev0), ev1 = static_cast<hipEvent_t>(lx.ev1);
+  const bool combine = p.n_runs > 1 && !p.dec;
   if constexpr (sizeof(T) == 2) {
-    if (p.mfma) {
+    if (p.dec) {
+      float* cs_ws = p.n_runs > 1 ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
+      dim3 grid(static_cast<unsigned>(p.n_runs), static_cast<unsigned>(a.heads / kDH), rows);
+      launch_timed(k_attn_decode, grid, dim3(256), 0, st, ev0, p.n_runs > 1 ? nullptr : ev1, g,
+                   static_cast<const uint16_t*>(a.q), a.rotate_q,
+                   static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
+                   static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out), a.lse,
+                   part_acc, part_ml, cs_ws);
+      dsa_status rc = hip_check(hipGetLastError(), "k_attn_decode launch");
+      if (rc != DSA_OK || p.n_runs == 1) return rc;
+      launch_timed(k_attn_dcombine, dim3(a.heads / 2, rows), dim3(256), 0, st, nullptr, ev1, g,
+                   static_cast<const float*>(part_acc), static_cast<const float*>(part_ml),
+                   static_cast<const float*>(cs_ws), static_cast<uint16_t*>(a.out), a.lse);
+      return hip_check(hipGetLastError(), "k_attn_dcombine launch");
+    } else if (p.mfma) {
       dim3 grid(static_cast<unsigned>(a.heads / 64), rows, p.n_runs);
       if (p.n_runs == 1)
-        hipLaunchKernelGGL(k_attn_mfma<true>, grid, dim3(256), 0, st, g,
-                           static_cast<const uint16_t*>(a.q), a.rotate_q,
-                           static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
-                           static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
-                           a.lse, part_acc, part_ml);
+        launch_timed(k_attn_mfma<true>, grid, dim3(256), 0, st, ev0, ev1, g,
+                     static_cast<const uint16_t*>(a.q), a.rotate_q,
+                     static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
+                     static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
+                     a.lse, part_acc, part_ml);
       else
-        hipLaunchKernelGGL(k_attn_mfma<false>, grid, dim3(256), 0, st, g,
-                           static_cast<const uint16_t*>(a.q), a.rotate_q,
-                           static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
-                           static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
-                           a.lse, part_acc, part_ml);
+        launch_timed(k_attn_mfma<false>, grid, dim3(256), 0, st, ev0, nullptr, g,
+                     static_cast<const uint16_t*>(a.q), a.rotate_q,
+                     static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
+                     static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
+                     a.lse, part_acc, part_ml);
     }
   }
-  if (!p.mfma) {
+  if (!p.mfma && !p.dec) {
     dim3 grid(static_cast<unsigned>(ceil_div(a.heads, kHG)), rows, p.n_runs);
     const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
-    hipLaunchKernelGGL(k_attn_generic<T>, grid, dim3(kThreads), shm, st, g,
-                       static_cast<const T*>(a.q), a.rotate_q, static_cast<const T*>(a.cache),
-                       static_cast<const T*>(a.window), static_cast<const T*>(a.chunk_win),
-                       static_cast<T*>(a.out), a.lse, part_acc, part_ml);
+    launch_timed(k_attn_generic<T>, grid, dim3(kThreads), shm, st, ev0,
+                 combine ? nullptr : ev1, g, static_cast<const T*>(a.q), a.rotate_q,
+                 static_cast<const T*>(a.cache), static_cast<const T*>(a.window),
+                 static_cast<const T*>(a.chunk_win), static_cast<T*>(a.out), a.lse, part_acc,
+                 part_ml);
   }
   dsa_status rc = hip_check(hipGetLastError(), "attention launch");
-  if (rc != DSA_OK || p.n_runs == 1) return rc;
-  hipLaunchKernelGGL(k_attn_combine<T>, dim3(a.heads, rows), dim3(256), 0, st, g, part_acc,
-                     part_ml, static_cast<T*>(a.out), a.lse);
+  if (rc != DSA_OK || !combine) return rc;
+  launch_timed(k_attn_combine<T>, dim3(a.heads, rows), dim3(256), 0, st, nullptr, ev1, g,
+               part_acc, part_ml, static_cast<T*>(a.out), a.lse);
   return hip_check(hipGetLastError(), "k_attn_combine launch");
 }
 
@@ -536,14 +895,14 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
 
 size_t attn_ws_bytes(const dsa_attn_args& a) { return plan(a).total; }
 
-dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st) {
+dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st, const AttnLaunch& lx) {
   if (a.dim > kMaxD || a.dim % 16 != 0)
     return fail(DSA_ERR_UNSUPPORTED, "attention dim %d must be a multiple of 16, <= %d", a.dim, kMaxD);
   const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
   if (shm > 160 * 1024 - 8192) return fail(DSA_ERR_UNSUPPORTED, "attention dim %d too large", a.dim);
   const Plan p = plan(a);
-  return a.dtype == DSA_F32 ? launch_typed<float>(a, p, ws, st)
-                            : launch_typed<uint16_t>(a, p, ws, st);
+  return a.dtype == DSA_F32 ? launch_typed<float>(a, p, ws, st, lx)
+                            : launch_typed<uint16_t>(a, p, ws, st, lx);
 }
 
 }  // namespace dsa

@@ -41,14 +41,18 @@ struct PrologueArgs {
   void *main_cache, *idx_cache, *main_ring, *idx_ring, *window;
   float* idx_scale;
   int64_t* qpos;
+  float* cs_tab;  // role 3: (cos, sin) of R_m, r floats per sequence
   uint32_t* status;
 };
+
+constexpr int kPrologueRoles = 4;
 
 // Decode-step prologue, one role per workgroup: role 0 writes the main entry
 // completing at m (if any), role 1 the indexer entry, role 2 puts token m
 // into the compressor rings, the row's query position, and -- when the
 // window ring has a spare slot (w_cap > W) -- the rotated token m (slot
-// m mod w_cap is not in m's window then).  For one token the ring slot
+// m mod w_cap is not in m's window then); role 3 writes the (cos, sin)
+// table of R_m for the attention's query rotation and inverse rotation.  For one token the ring slot
 // written (m mod S) is not one the compressor reads (it reads positions
 // m-S+1 .. m-1 from the ring and m from x), and nothing here is read by the
 // same step's indexer or attention (the new entry is not visible to m), so
@@ -71,6 +75,18 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
                                      a.idx_cache, a.idx_scale, a.gamma_idx, a.eps, 1, 1, a.s, a.S,
                                      a.Di, a.r_idx, a.idx_base, a.off, a.e_cap, a.max_pos_end,
                                      a.status);
+    return;
+  }
+  if (role == 3) {
+    const int64_t m = a.pos0[b];
+    const bool ok = m >= 0 && m < a.max_pos_end;
+    if (a.cs_tab)
+      for (int i = threadIdx.x; i < a.r / 2; i += blockDim.x) {
+        float c = 1.f, s = 0.f;
+        if (ok) rope_cs(m + a.off, i, a.r, a.base, &c, &s);
+        a.cs_tab[static_cast<int64_t>(b) * a.r + 2 * i] = c;
+        a.cs_tab[static_cast<int64_t>(b) * a.r + 2 * i + 1] = s;
+      }
     return;
   }
   const int64_t m = a.pos0[b];

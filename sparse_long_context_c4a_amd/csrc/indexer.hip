@@ -670,20 +670,18 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   const bool no_keys = a.keys == nullptr;  // only allowed when k >= every n_vis
   dsa_status rc;
   if (!no_keys && P.nv_cap > 0) {
-    if (a.ev_index[0]) {
-      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a.ev_index[0]), st), "event record");
-      if (rc != DSA_OK) return rc;
-    }
+    const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
+    const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);
     if (P.mfma) {
       dim3 grid(static_cast<unsigned>(P.nb), rows);
       if (P.cand)
-        hipLaunchKernelGGL(k_index_fp8_stream<true>, grid, dim3(kThreads), 0, st,
+        launch_timed(k_index_fp8_stream<true>, grid, dim3(kThreads), 0, st, e0, e1,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
                            a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
       else
-        hipLaunchKernelGGL(k_index_fp8_stream<false>, grid, dim3(kThreads), 0, st,
+        launch_timed(k_index_fp8_stream<false>, grid, dim3(kThreads), 0, st, e0, e1,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
@@ -692,13 +690,13 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
       dim3 grid(static_cast<unsigned>(ceil_div(P.nv_cap, kThreads)), rows);
       const size_t shm = (static_cast<size_t>(a.heads) * a.dim + a.heads) * sizeof(float);
       if (a.dtype == DSA_F32)
-        hipLaunchKernelGGL(k_index_generic<float>, grid, dim3(kThreads), shm, st,
+        launch_timed(k_index_generic<float>, grid, dim3(kThreads), shm, st, e0, e1,
                            static_cast<const float*>(a.q), a.q_scale, a.w,
                            static_cast<const float*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
                            a.max_pos_end, scores, P.ld, a.status);
       else
-        hipLaunchKernelGGL(k_index_generic<uint8_t>, grid, dim3(kThreads), shm, st,
+        launch_timed(k_index_generic<uint8_t>, grid, dim3(kThreads), shm, st, e0, e1,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
@@ -706,10 +704,6 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
     }
     rc = hip_check(hipGetLastError(), "indexer launch");
     if (rc != DSA_OK) return rc;
-    if (a.ev_index[1]) {
-      rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a.ev_index[1]), st), "event record");
-      if (rc != DSA_OK) return rc;
-    }
   }
   if (P.cand && !no_keys) {
     hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
@@ -724,12 +718,13 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
 }
 
 dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
-                                    int64_t* qpos, bool insert_window, hipStream_t st) {
+                                    int64_t* qpos, bool insert_window, float* cs_tab,
+                                    hipStream_t st) {
   const Plan P = plan(a);
   const bool fused = P.cand && a.keys != nullptr && P.nv_cap > 0 && a.queries_per_seq == 1 &&
                      a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16;
   if (!fused) {
-    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, st);
+    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, st);
     if (rc != DSA_OK) return rc;
     return launch_index_topk(a, ws, st);
   }
@@ -738,23 +733,15 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
   float* scores = reinterpret_cast<float*>(base + P.off_scores);
   uint64_t* cand = reinterpret_cast<uint64_t*>(base + P.off_cand);
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
-  const PrologueArgs pa = make_prologue_args(la, qpos, insert_window);
-  dsa_status rc;
-  if (a.ev_index[0]) {
-    rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a.ev_index[0]), st), "event record");
-    if (rc != DSA_OK) return rc;
-  }
-  hipLaunchKernelGGL((k_decode_index<uint16_t, DSA_FP8_E4M3>), dim3(P.nb + 3, rows), dim3(kThreads),
-                     0, st, static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-                     static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
-                     a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap,
-                     P.nb, pa, a.status);
-  rc = hip_check(hipGetLastError(), "k_decode_index launch");
+  const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab);
+  launch_timed(k_decode_index<uint16_t, DSA_FP8_E4M3>, dim3(P.nb + kPrologueRoles, rows), dim3(kThreads), 0, st,
+               static_cast<hipEvent_t>(a.ev_index[0]), static_cast<hipEvent_t>(a.ev_index[1]),
+               static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
+               static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
+               a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,
+               pa, a.status);
+  dsa_status rc = hip_check(hipGetLastError(), "k_decode_index launch");
   if (rc != DSA_OK) return rc;
-  if (a.ev_index[1]) {
-    rc = hip_check(hipEventRecord(static_cast<hipEvent_t>(a.ev_index[1]), st), "event record");
-    if (rc != DSA_OK) return rc;
-  }
   hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
                      a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
                      a.idx_out, a.score_out, a.k);

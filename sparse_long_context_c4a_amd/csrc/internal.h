@@ -1,6 +1,7 @@
 // Host-side internals: launch helpers and the error channel behind the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -14,6 +15,18 @@ namespace dsa {
 dsa_status fail(dsa_status s, const char* fmt, ...);
 dsa_status hip_check(hipError_t e, const char* what);
 
+// A kernel launch with optional timing events attached to its own dispatch
+// packet (no separate event packets, so no idle gap between kernels).
+template <typename K, typename... Args>
+void launch_timed(K kernel, dim3 grid, dim3 block, size_t shm, hipStream_t st, hipEvent_t ev0,
+                  hipEvent_t ev1, Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(shm), st, ev0, ev1, 0u,
+                          args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
+}
+
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -25,9 +38,16 @@ dsa_status launch_zero(void* p, size_t bytes, hipStream_t st);
 size_t index_topk_ws_bytes(const dsa_index_args& a);
 dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st);
 
-// Attention.
+// Attention.  Optional timing events ride on the first and last kernel's
+// dispatch.
+struct AttnLaunch {
+  void* ev0 = nullptr;
+  void* ev1 = nullptr;
+  const float* cs_tab = nullptr;  // (cos, sin) of each row's position, rope_dim floats per row
+};
 size_t attn_ws_bytes(const dsa_attn_args& a);
-dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st);
+dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st,
+                       const AttnLaunch& lx = AttnLaunch{});
 
 // Layer helpers: ring and window maintenance, chunk rotation.
 dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
@@ -42,14 +62,16 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 // Decode (one token per sequence): fused prologue and, when the window ring
 // has no spare slot, the window insert after attention.
 struct PrologueArgs;
-PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window);
+PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
+                                float* cs_tab);
 // The indexer + Top-k of a decode step with the prologue's workgroups riding
 // in the indexer's launch (or launched first when the indexer takes another
 // path).
 dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
-                                    int64_t* qpos, bool insert_window, hipStream_t st);
+                                    int64_t* qpos, bool insert_window, float* cs_tab,
+                                    hipStream_t st);
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  hipStream_t st);
+                                  float* cs_tab, hipStream_t st);
 dsa_status launch_decode_window_insert(const dsa_layer_args& a, hipStream_t st);
 
 inline size_t dtype_size(dsa_dtype t) {

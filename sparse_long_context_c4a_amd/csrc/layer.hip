@@ -142,7 +142,8 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 
 namespace dsa {
 
-PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window) {
+PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
+                                float* cs_tab) {
   PrologueArgs p{};
   p.B = a.n_seqs;
   p.D = a.main.dim;
@@ -174,14 +175,15 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
   p.window = a.window;
   p.idx_scale = a.idx_scale;
   p.qpos = qpos;
+  p.cs_tab = cs_tab;
   p.status = a.status;
   return p;
 }
 
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  hipStream_t st) {
-  const PrologueArgs p = make_prologue_args(a, qpos, insert_window);
-  const dim3 grid(3 * a.n_seqs), block(kCompressThreads);
+                                  float* cs_tab, hipStream_t st) {
+  const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab);
+  const dim3 grid(kPrologueRoles * a.n_seqs), block(kCompressThreads);
   if (a.dtype == DSA_F32) {
     if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_decode_prologue<float, DSA_FP8_E4M3>), grid, block, 0, st, p);

@@ -26,6 +26,41 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0
 
 
+# Hardware byte counters of the scoring kernel, from the committed rocprofv3
+# summary; reported only while the sources they were taken from are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_index_c4a_decode_B4_L1M.txt")
+TRAFFIC_SOURCES = ["indexer.hip", "indexer_impl.h", "decode_impl.h", "compress_impl.h",
+                   "common.h", "internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_long_context_c4a_amd", "csrc")
+    for f in TRAFFIC_SOURCES + ["../../include/dsa.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by the
+    copy calibration) from the summary file, or None if it is missing or was
+    taken from other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_hash") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def decode_bytes_per_query(w, nv):
     """Algorithmic HBM bytes of one decode query: the visible indexer keys
     (Di fp8 bytes + a 4-byte scale each), the k + W gathered latent vectors,
@@ -136,10 +171,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
                          "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer's multi-GPU "
               "sharding is a design note, not a measured path.", file=sys.stderr)
@@ -171,7 +210,8 @@ def main():
         "hbm_gbps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "alg_bytes_per_step": step_bytes,
         "kernel_ms": {"indexer": idx_ms, "attention": attn_ms},
         "roofline": {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": idx_gbps / PEAK_HBM_GBPS if idx_gbps else None, "traffic": None,
+                     "frac": idx_gbps / PEAK_HBM_GBPS if idx_gbps else None,
+                     "traffic": measured_traffic() if w.name == "c4a_decode_B4_L1M" else None,
                      "kernel": "k_decode_index", "alg_bytes_per_launch": idx_bytes},
     }
     del sets

@@ -306,8 +306,9 @@ __device__ __forceinline__ void for_row(const float* srow, int64_t nv, F f) {
 // Exact top-k of one row from its scores in global memory (nv > k): a
 // 4096-bin histogram over the row's own key range finds the bin holding the
 // k-th score; entries above it go straight out and the bin's entries are
-// resolved exactly on (key, complemented index).  cand_s: kFinalCap u64 of
-// LDS, h_s: kBins u32 of LDS.
+// resolved exactly on (key, complemented index).  cand_s: kCap u64 of LDS,
+// h_s: kBins u32 of LDS.
+template <int kCap = kFinalCap>
 __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_t nv, int k, int32_t* irow,
                                        float* orow, uint64_t* cand_s, uint32_t* h_s) {
   __shared__ uint32_t cnt_above, cnt_cand, out_pos;
@@ -330,7 +331,7 @@ __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_
   for (int i = 0; i < 4; ++i) local[i] = h_s[kBins - 1 - (4 * t + i)];
   const Bin br = find_bin_desc<4>(local, kBins - 1u, static_cast<uint32_t>(k));
   const uint32_t thr = br.b, above = br.above, at = br.at;
-  const bool fits = at <= static_cast<uint32_t>(kFinalCap);
+  const bool fits = at <= static_cast<uint32_t>(kCap);
   for_row(srow, nv, [&](int64_t j, float sc) {
     const uint32_t key = order_key(sc);
     const uint32_t bin = (key - lo) >> shift;
@@ -339,7 +340,7 @@ __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_
       if (p < static_cast<uint32_t>(k)) emit(irow, orow, p, static_cast<uint32_t>(j), sc);
     } else if (bin == thr && fits) {
       const uint32_t p = atomicAdd(&cnt_cand, 1u);
-      if (p < static_cast<uint32_t>(kFinalCap)) cand_s[p] = composite(key, static_cast<uint32_t>(j));
+      if (p < static_cast<uint32_t>(kCap)) cand_s[p] = composite(key, static_cast<uint32_t>(j));
     }
   });
   __syncthreads();
@@ -622,11 +623,567 @@ __global__ __launch_bounds__(kSel) void k_topk_rows(
   row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
 }
 
+// ------------------------------------------------------------ prefill path
+// Many query rows against one sequence's keys is a dense contraction, run on
+// the fp8 matrix cores, with an exact correction so that the selection stays
+// the exact Top-k:
+//
+//  k_pidx_prep  (one workgroup per tile of kPQ rows of one sequence): the
+//     largest nu_j = ks_j ||k8_j|| over a slice of the sequence's visible
+//     entries; approximate scores of a strided sample of the entries; per
+//     row the threshold theta (the r-th largest sampled score, rounded down
+//     to 16 key bits) and beta = eps * sum_h |w'_h| ||q8_h|| (w' = w * qs).
+//  k_pidx_main  (same tiles): approximate scores of every visible entry --
+//     one v_mfma_f32_16x16x128_f8f6f4 per row and 16 entries on the raw
+//     codes, then ReLU, head weights and head sum in f32 -- and the entries
+//     with approximate score >= theta - 2 B, B = beta * max_j nu_j, kept as
+//     candidates.
+//  k_pidx_select (one workgroup per row): exact scores of the candidates
+//     (bf16 MFMA on exactly widened codes, f32 weights, as the decode path),
+//     the certificate #{candidates with exact score >= theta - B} >= k, then
+//     the exact Top-k of the candidates.  If the certificate fails or the
+//     candidates overflow, the row is scored exactly in full and selected
+//     from its scores.
+//
+// Why the result is exact: the fp8 MFMA's error on a 128-term dot product
+// is below 2^-10 ||a|| ||b|| (its shared alignment drops low-order product
+// bits; measured below 2^-13.4 ||a|| ||b|| on heavy-tailed codes and below
+// 2^-15.8 on Gaussian ones), ReLU is 1-Lipschitz and the f32 head sum adds
+// ~2^-21 relative, so |approx - exact| <= B for every entry with
+// eps = 1e-3 >= 2^-10 + 2^-20.  A non-candidate has approx < theta - 2B,
+// hence exact < theta - B; when at least k candidates reach theta - B, the
+// k-th largest score does too and no non-candidate can be in the Top-k.
+// The sample only steers the threshold (how many candidates); the
+// certificate, not the sample, carries the guarantee.
+constexpr int kPQ = 8;             // query rows per workgroup
+constexpr int kPSample = 2048;     // sampled entries per row
+constexpr int kPCandCap = 4096;    // candidates kept per row
+constexpr float kPEps = 1.0e-3f;
+
+struct PArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* keys;
+  const float* k_scale;
+  const int64_t* q_pos;
+  int Tq, Hi, s, S, k, tiles_per_seq;
+  int64_t e_cap, nv_cap, max_pos_end;
+  float* theta;
+  float* beta;
+  float* nu_part;
+  uint32_t* cand_cnt;
+  int32_t* cand_j;
+  uint32_t* status;
+};
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8i as_v8i(uint4 lo, uint4 hi) {
+  return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+             static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+             static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
+// Sum of squares of the 16 e4m3 codes in one uint4 (exact products, f32 sum).
+__device__ __forceinline__ float fp8x16_sumsq(uint4 v) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+    s = fmaf(a[0], a[0], s);
+    s = fmaf(a[1], a[1], s);
+    s = fmaf(b[0], b[0], s);
+    s = fmaf(b[1], b[1], s);
+  }
+  return s;
+}
+
+// The tile's rows: sequence b, rows row0 .. row0 + nq - 1.
+struct PTile {
+  int b, t0, nq;
+  int64_t row0;
+};
+__device__ __forceinline__ PTile p_tile(const PArgs& a, int tile) {
+  PTile t;
+  t.b = tile / a.tiles_per_seq;
+  t.t0 = (tile % a.tiles_per_seq) * kPQ;
+  t.nq = min(kPQ, a.Tq - t.t0);
+  t.row0 = static_cast<int64_t>(t.b) * a.Tq + t.t0;
+  return t;
+}
+
+// Per-lane operands of the tile's rows for the fp8 MFMA: A_q (lane = head
+// n, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the head's 128, the
+// same byte-to-k assignment as the keys), and w'_q for heads 4g .. 4g+3.
+struct PRows {
+  v8i a[kPQ];
+  float wv[kPQ][4];
+  int64_t nv[kPQ];
+};
+__device__ __forceinline__ void p_load_rows(const PArgs& a, const PTile& t, PRows& r) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q) {
+    uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    r.nv[q] = 0;
+    if (q < t.nq) {
+      const int64_t row = t.row0 + q;
+      if (n < a.Hi) {
+        const uint4* qp = reinterpret_cast<const uint4*>(a.q + (row * a.Hi + n) * 128);
+        lo = qp[g];
+        hi = qp[4 + g];
+      }
+      const RowInfo ri = row_info(a.q_pos, static_cast<int>(row), a.s, a.S, a.nv_cap,
+                                  a.max_pos_end, nullptr, false);
+      r.nv[q] = ri.ok ? ri.nv : 0;
+    }
+    r.a[q] = as_v8i(lo, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      float wq = 0.f;
+      if (q < t.nq && h < a.Hi) {
+        const int64_t o = (t.row0 + q) * a.Hi + h;
+        wq = a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f);
+      }
+      r.wv[q][i] = wq;
+    }
+  }
+}
+
+// In-lane part of the approximate score of row q against entry n of the
+// tile whose B operand is kb: ReLU and head weights over the lane's heads
+// 4g .. 4g+3 (the 4 head groups still to be summed across lanes).
+__device__ __forceinline__ float p_partial(const PRows& r, int q, const v8i& kb) {
+  v4f c = {0.f, 0.f, 0.f, 0.f};
+  c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.a[q], kb, c, 0, 0, 0, 0, 0, 0);
+  return r.wv[q][0] * fmaxf(c[0], 0.f) + r.wv[q][1] * fmaxf(c[1], 0.f) +
+         r.wv[q][2] * fmaxf(c[2], 0.f) + r.wv[q][3] * fmaxf(c[3], 0.f);
+}
+
+// Sum four rows' partials over the 4 head groups (16-lane rows of the
+// wave) with the gfx950 lane swaps: permlane32_swap(x, y) gives
+// ([x lanes 0-31, y lanes 0-31], [x lanes 32-63, y lanes 32-63]) and
+// permlane16_swap(x, y) gives ([x r0, y r0, x r2, y r2], [x r1, y r1, x r3,
+// y r3]) for 16-lane rows r.  The result's row g holds, for entry n, the
+// full score of row kPerm[g] of the four.
+constexpr int kPerm[4] = {0, 2, 1, 3};
+__device__ __forceinline__ float p_reduce4(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float z = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // lanes 0-31: p0, 32-63: p1
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float w = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // lanes 0-31: p2, 32-63: p3
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(w), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Approximate scores (before the key scale) of all kPQ rows against the
+// tile's 16 entries: lane (g, n) of s[h] holds row 4h + kPerm[g], entry n.
+__device__ __forceinline__ void p_scores(const PRows& r, const v8i& kb, float (&s)[kPQ / 4]) {
+  // every row's product first (eight independent matrix-core ops in
+  // flight), then the ReLU / weight math
+  v4f c[kPQ];
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q)
+    c[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.a[q], kb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0, 0, 0, 0);
+  float p[kPQ];
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q)
+    p[q] = r.wv[q][0] * fmaxf(c[q][0], 0.f) + r.wv[q][1] * fmaxf(c[q][1], 0.f) +
+           r.wv[q][2] * fmaxf(c[q][2], 0.f) + r.wv[q][3] * fmaxf(c[q][3], 0.f);
+#pragma unroll
+  for (int h = 0; h < kPQ / 4; ++h) s[h] = p_reduce4(p[4 * h], p[4 * h + 1], p[4 * h + 2], p[4 * h + 3]);
+}
+
+// Value of row 4h + kPerm[g] from a per-row array (selects, no dynamic
+// register index).
+template <typename T>
+__device__ __forceinline__ T p_pick(const T (&v)[kPQ], int h, int g) {
+  const T a = v[4 * h], b = v[4 * h + 2], c = v[4 * h + 1], d = v[4 * h + 3];
+  return g == 0 ? a : g == 1 ? b : g == 2 ? c : d;
+}
+
+__global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
+  __shared__ uint32_t skey[kPQ][kPSample];
+  __shared__ uint32_t hist[kPQ][256];
+  __shared__ float fred[kThreads / 64];
+  __shared__ int64_t ired[kThreads / 64];
+  __shared__ uint32_t pick[kPQ][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const PTile t = p_tile(a, blockIdx.x);
+  // the largest n_vis over the whole sequence (sets the slices of nu)
+  int64_t nvs = 0;
+  for (int i = tid; i < a.Tq; i += kThreads) {
+    const RowInfo ri = row_info(a.q_pos, static_cast<int>(static_cast<int64_t>(t.b) * a.Tq + i),
+                                a.s, a.S, a.nv_cap, a.max_pos_end, nullptr, false);
+    if (ri.ok) nvs = max(nvs, ri.nv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nvs = max(nvs, static_cast<int64_t>(__shfl_xor(nvs, o, 64)));
+  if (lane == 0) ired[wave] = nvs;
+  __syncthreads();
+  nvs = max(max(ired[0], ired[1]), max(ired[2], ired[3]));
+  // nu over this tile's slice of [0, nvs): 4 threads per entry, 32 bytes each
+  const int tps = a.tiles_per_seq, slice = blockIdx.x % tps;
+  const int64_t per = (nvs + tps - 1) / tps;
+  const int64_t e_lo = slice * per, e_hi = min(nvs, e_lo + per);
+  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * a.e_cap * 128;
+  const float* ksb = a.k_scale + static_cast<int64_t>(t.b) * a.e_cap;
+  float nu = 0.f;
+  for (int64_t e0 = e_lo; e0 < e_hi; e0 += kThreads / 4) {
+    const int64_t e = e0 + tid / 4;
+    float ss = 0.f;
+    if (e < e_hi) {
+      const uint4* kp = reinterpret_cast<const uint4*>(kb + e * 128) + 2 * (tid & 3);
+      ss = fp8x16_sumsq(kp[0]) + fp8x16_sumsq(kp[1]);
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (e < e_hi) nu = fmaxf(nu, ksb[e] * sqrtf(ss));
+  }
+  nu = wave_max(nu);
+  if (lane == 0) fred[wave] = nu;
+  // beta per row: thread -> row tid / 32, head (tid % 32) / 2, half tid % 2
+  {
+    const int q = tid / 32, h = (tid % 32) / 2, hf = tid % 2;
+    float ss = 0.f, wabs = 0.f;
+    if (q < t.nq && h < a.Hi) {
+      const int64_t row = t.row0 + q;
+      const uint4* qp = reinterpret_cast<const uint4*>(a.q + (row * a.Hi + h) * 128) + 4 * hf;
+      ss = fp8x16_sumsq(qp[0]) + fp8x16_sumsq(qp[1]) + fp8x16_sumsq(qp[2]) + fp8x16_sumsq(qp[3]);
+      const int64_t o = row * a.Hi + h;
+      wabs = fabsf(a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f));
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    float contrib = (hf == 0) ? wabs * sqrtf(ss) : 0.f;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) contrib += __shfl_xor(contrib, o, 32);
+    if (tid % 32 == 0 && q < t.nq) a.beta[t.row0 + q] = kPEps * contrib;
+  }
+  __syncthreads();
+  if (tid == 0) a.nu_part[blockIdx.x] = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+  // approximate scores of the sampled entries j = st * i
+  PRows r;
+  p_load_rows(a, t, r);
+  int64_t nvt = 0;
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q) nvt = max(nvt, r.nv[q]);
+  const int64_t st = max<int64_t>(1, (nvt + kPSample - 1) / kPSample);
+  const int ns = static_cast<int>((nvt + st - 1) / st);
+  // sample tiles wave, wave + 4, ... with a ring of kPre tiles in flight;
+  // the loads are unconditional (clamped to a valid entry) so that the
+  // compiler can count them
+  constexpr int kPre = 4, kTiles = kPSample / 16;
+  uint4 lo[kPre], hi[kPre];
+  float ks[kPre];
+  const int64_t jmax = max<int64_t>(0, (static_cast<int64_t>(ns) - 1) * st);
+  auto load = [&](int u, int tile) {
+    const int i = tile * 16 + n;
+    const int64_t j = min<int64_t>(static_cast<int64_t>(i) * st, jmax);
+    const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
+    lo[u] = kp[g];
+    hi[u] = kp[4 + g];
+    ks[u] = ksb[j];
+  };
+  int64_t nvp[kPQ];
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q) nvp[q] = r.nv[q];
+  const int64_t nv0 = p_pick(nvp, 0, g), nv1 = p_pick(nvp, 1, g);
+  if (ns > 0) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) load(u, wave + 4 * u);
+  }
+  for (int t0 = wave; t0 < kTiles && ns > 0; t0 += 4 * kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int tile = t0 + 4 * u;
+      const v8i bk = as_v8i(lo[u], hi[u]);
+      const float ksc = ks[u];
+      load(u, min(tile + 4 * kPre, kTiles - 1));
+      if (tile >= kTiles) continue;
+      const int i = tile * 16 + n;
+      const int64_t j = static_cast<int64_t>(i) * st;
+      const bool in = i < ns;
+      float sv[kPQ / 4];
+      p_scores(r, bk, sv);
+      // lane (g, n) holds rows qa and 4 + qa, qa = kPerm[g], of entry i
+      const int qa = g == 0 ? 0 : g == 1 ? 2 : g == 2 ? 1 : 3;
+      skey[qa][i] = (in && j < nv0) ? order_key(sv[0] * ksc) : 0u;
+      skey[4 + qa][i] = (in && j < nv1) ? order_key(sv[1] * ksc) : 0u;
+    }
+  }
+  __syncthreads();
+  // theta: the r-th largest sampled key of each row, to 16 bits (two 8-bit
+  // histogram passes); 32 threads per row
+  const int q = tid / 32, l32 = tid % 32;
+  int64_t nvq = 0;  // (r.nv is a register array: no dynamic index)
+  if (q < t.nq) {
+    const RowInfo ri = row_info(a.q_pos, static_cast<int>(t.row0 + q), a.s, a.S, a.nv_cap,
+                                a.max_pos_end, nullptr, false);
+    nvq = ri.ok ? ri.nv : 0;
+  }
+  const int nsq = static_cast<int>(min<int64_t>(ns, (nvq + st - 1) / st));
+  uint32_t need = static_cast<uint32_t>(
+      min<int64_t>(nsq, (3 * static_cast<int64_t>(a.k) * nsq + 2 * nvq - 1) / (2 * max<int64_t>(nvq, 1)) + 8));
+  uint32_t prefix = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int sh = 24 - 8 * pass;
+    for (int i = l32; i < 256; i += 32) hist[q][i] = 0u;
+    if (l32 == 0) pick[q][0] = pick[q][1] = 0u;
+    __syncthreads();
+    for (int i = l32; i < kPSample; i += 32) {
+      const uint32_t key = skey[q][i];
+      if (key != 0u && (pass == 0 || (key >> 24) == prefix)) atomicAdd(&hist[q][(key >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    // lane l32 owns bins 255 - 8 l32 .. 248 - 8 l32 (descending)
+    uint32_t c[8], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c[u] = hist[q][255 - 8 * l32 - u];
+      sum += c[u];
+    }
+    uint32_t before = sum;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const uint32_t x = static_cast<uint32_t>(__shfl_up(static_cast<int>(before), o, 32));
+      if (l32 >= o) before += x;
+    }
+    before -= sum;  // exclusive
+    if (need > 0 && before < need && before + sum >= need) {
+      uint32_t acc = before;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (acc < need && acc + c[u] >= need) {
+          pick[q][0] = 255u - 8u * l32 - u;
+          pick[q][1] = acc;
+        }
+        acc += c[u];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = pick[q][0];
+    need -= pick[q][1];
+    prefix = pass == 0 ? bin : ((prefix << 8) | bin);
+    __syncthreads();
+  }
+  if (l32 == 0 && q < t.nq) {
+    const int64_t row = t.row0 + q;
+    // rows that keep every visible entry (or none) need no candidates
+    const bool sel = nvq > a.k && nsq > 0;
+    a.theta[row] = sel ? key_to_float(prefix << 16) : INFINITY;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
+  __shared__ uint32_t lcnt[kPQ];
+  __shared__ float fred[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const PTile t = p_tile(a, blockIdx.x);
+  // max nu over the sequence's slices
+  float nu = 0.f;
+  for (int i = tid; i < a.tiles_per_seq; i += kThreads)
+    nu = fmaxf(nu, a.nu_part[static_cast<int64_t>(t.b) * a.tiles_per_seq + i]);
+  nu = wave_max(nu);
+  if (lane == 0) fred[wave] = nu;
+  if (tid < kPQ) lcnt[tid] = 0u;
+  __syncthreads();
+  nu = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+  PRows r;
+  p_load_rows(a, t, r);
+  float thr[kPQ];
+  int64_t nvt = 0;
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q) {
+    thr[q] = INFINITY;
+    if (q < t.nq) thr[q] = a.theta[t.row0 + q] - 2.0f * a.beta[t.row0 + q] * nu;
+    if (thr[q] == INFINITY) r.nv[q] = 0;  // nothing to collect for this row
+    nvt = max(nvt, r.nv[q]);
+  }
+  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * a.e_cap * 128;
+  const float* ksb = a.k_scale + static_cast<int64_t>(t.b) * a.e_cap;
+  int32_t* cj = a.cand_j + t.row0 * kPCandCap;
+  const int64_t ntiles = (nvt + 15) / 16;
+  // software pipeline: a ring of kPre tiles per wave (tiles wave, wave + 4,
+  // ...) loads while the current tile's math runs; the loads are
+  // unconditional (clamped to a valid entry) so that the compiler can count
+  // them instead of draining every load before each tile
+  constexpr int kPre = 4;
+  uint4 lo[kPre], hi[kPre];
+  float ks[kPre];
+  const int64_t jmax = max<int64_t>(0, nvt - 1);
+  auto load = [&](int u, int64_t tile) {
+    const int64_t j = min<int64_t>(tile * 16 + n, jmax);
+    const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
+    lo[u] = kp[g];
+    hi[u] = kp[4 + g];
+    ks[u] = ksb[j];
+  };
+  // this lane's two output rows (4h + kPerm[g], h = 0, 1): bounds and
+  // thresholds
+  int64_t nvp[kPQ];
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q) nvp[q] = r.nv[q];
+  const int64_t nvs0 = p_pick(nvp, 0, g), nvs1 = p_pick(nvp, 1, g);
+  const float th0 = p_pick(thr, 0, g), th1 = p_pick(thr, 1, g);
+  const int qa = g == 0 ? 0 : g == 1 ? 2 : g == 2 ? 1 : 3;
+  if (ntiles > 0) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) load(u, wave + 4 * u);
+  }
+  for (int64_t t0 = wave; t0 < ntiles; t0 += 4 * kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int64_t tt = t0 + 4 * u;
+      const v8i bk = as_v8i(lo[u], hi[u]);
+      const float ksc = ks[u];
+      load(u, min<int64_t>(tt + 4 * kPre, ntiles - 1));
+      if (tt >= ntiles) continue;
+      const int64_t j = tt * 16 + n;
+      float sv[kPQ / 4];
+      p_scores(r, bk, sv);
+      const bool h0 = j < nvs0 && sv[0] * ksc >= th0;
+      const bool h1 = j < nvs1 && sv[1] * ksc >= th1;
+      if (__any(h0 || h1)) {
+        if (h0) {
+          const uint32_t p = atomicAdd(&lcnt[qa], 1u);
+          if (p < static_cast<uint32_t>(kPCandCap)) cj[qa * kPCandCap + p] = static_cast<int32_t>(j);
+        }
+        if (h1) {
+          const uint32_t p = atomicAdd(&lcnt[4 + qa], 1u);
+          if (p < static_cast<uint32_t>(kPCandCap)) cj[(4 + qa) * kPCandCap + p] = static_cast<int32_t>(j);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < t.nq) a.cand_cnt[t.row0 + tid] = lcnt[tid];
+}
+
+// Exact score (before the key scale) of entry column n for one row: A = the
+// row's heads widened to bf16, f32 head weights; same tile math as the
+// decode stream.
+__device__ __forceinline__ float p_exact(const v8bf (&aq)[4], const float (&wv)[4], uint4 blo,
+                                         uint4 bhi) {
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[0], fp8x8_to_bf16(blo.x, blo.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[1], fp8x8_to_bf16(blo.z, blo.w), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[2], fp8x8_to_bf16(bhi.x, bhi.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[3], fp8x8_to_bf16(bhi.z, bhi.w), acc, 0, 0, 0);
+  float v = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
+            wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict__ scores,
+                                                      int64_t ld_scores,
+                                                      int32_t* __restrict__ idx_out) {
+  __shared__ uint64_t cand_s[kPCandCap];
+  __shared__ uint64_t tmp_s[kTmpCap];
+  __shared__ uint32_t h_s[kBins];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int b = row / a.Tq;
+  const RowInfo ri = row_info(a.q_pos, row, a.s, a.S, a.nv_cap, a.max_pos_end, a.status, tid == 0);
+  const int64_t nv = ri.ok ? ri.nv : 0;
+  int32_t* irow = idx_out + static_cast<int64_t>(row) * a.k;
+  if (nv <= a.k) {
+    emit_all_visible(nullptr, nv, a.k, irow, nullptr);
+    return;
+  }
+  // the row's exact operands
+  v8bf aq[4];
+  float wv[4];
+  {
+    uint4 qlo = {0u, 0u, 0u, 0u}, qhi = {0u, 0u, 0u, 0u};
+    if (n < a.Hi) {
+      const uint4* qp = reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(row) * a.Hi + n) * 128);
+      qlo = qp[g];
+      qhi = qp[4 + g];
+    }
+    aq[0] = fp8x8_to_bf16(qlo.x, qlo.y);
+    aq[1] = fp8x8_to_bf16(qlo.z, qlo.w);
+    aq[2] = fp8x8_to_bf16(qhi.x, qhi.y);
+    aq[3] = fp8x8_to_bf16(qhi.z, qhi.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      wv[i] = 0.f;
+      if (h < a.Hi) {
+        const int64_t o = static_cast<int64_t>(row) * a.Hi + h;
+        wv[i] = a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f);
+      }
+    }
+  }
+  const uint8_t* kb = a.keys + static_cast<int64_t>(b) * a.e_cap * 128;
+  const float* ksb = a.k_scale + static_cast<int64_t>(b) * a.e_cap;
+  float nu = 0.f;
+  for (int i = tid; i < a.tiles_per_seq; i += kSel)
+    nu = fmaxf(nu, a.nu_part[static_cast<int64_t>(b) * a.tiles_per_seq + i]);
+  nu = __uint_as_float(block_reduce_u32<0>(__float_as_uint(nu)));  // nu >= 0: bits order as floats
+  const float cut = a.theta[row] - a.beta[row] * nu;
+  const uint32_t cnt = a.cand_cnt[row];
+  bool ok = cnt <= static_cast<uint32_t>(kPCandCap);
+  if (ok) {
+    const int32_t* cj = a.cand_j + static_cast<int64_t>(row) * kPCandCap;
+    const int ct = static_cast<int>((cnt + 15) / 16);
+    uint32_t c_ge = 0;
+    for (int tile = wave; tile < ct; tile += kSelWaves) {
+      const int i = tile * 16 + n;
+      const int64_t j = i < static_cast<int>(cnt) ? cj[i] : -1;
+      uint4 blo = {0u, 0u, 0u, 0u}, bhi = {0u, 0u, 0u, 0u};
+      float ks = 0.f;
+      if (j >= 0) {
+        const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
+        blo = kp[g];
+        bhi = kp[4 + g];
+        ks = ksb[j];
+      }
+      const float sc = p_exact(aq, wv, blo, bhi) * ks;
+      if (g == 0 && i < kPCandCap) {
+        cand_s[i] = j >= 0 ? composite(order_key(sc), static_cast<uint32_t>(j)) : 0ull;
+        c_ge += (j >= 0 && sc >= cut) ? 1u : 0u;
+      }
+    }
+    for (int i = static_cast<int>(cnt) + tid; i < ct * 16; i += kSel) cand_s[i] = 0ull;
+    ok = block_reduce_u32<2>(c_ge) >= static_cast<uint32_t>(a.k);  // barriers
+  }
+  if (ok) {
+    select_topk_composites(cand_s, static_cast<int>(cnt), static_cast<uint32_t>(a.k), irow,
+                           nullptr, tmp_s, h_s);
+    return;
+  }
+  // fallback: score the whole row exactly, then select from the scores
+  float* srow = scores + static_cast<int64_t>(row) * ld_scores;
+  for (int64_t tile = wave; tile * 16 < nv; tile += kSelWaves) {
+    const int64_t j = tile * 16 + n;
+    uint4 blo = {0u, 0u, 0u, 0u}, bhi = {0u, 0u, 0u, 0u};
+    float ks = 0.f;
+    if (j < nv) {
+      const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
+      blo = kp[g];
+      bhi = kp[4 + g];
+      ks = ksb[j];
+    }
+    const float sc = p_exact(aq, wv, blo, bhi) * ks;
+    if (g == 0 && j < nv) srow[j] = sc;
+  }
+  __syncthreads();
+  row_select_from_scores<kPCandCap>(srow, nv, a.k, irow, nullptr, cand_s, h_s);
+}
+
 struct Plan {
   int64_t nv_cap, ld;
-  bool mfma, cand;
-  int nb, nw, cap;
-  size_t off_scores, off_cand, off_meta, total;
+  bool mfma, cand, pre;
+  int nb, nw, cap, tps, tiles;
+  size_t off_scores, off_cand, off_meta, off_theta, off_beta, off_nu, off_pcnt, off_pcand, total;
 };
 
 Plan plan(const dsa_index_args& a) {
@@ -645,6 +1202,12 @@ Plan plan(const dsa_index_args& a) {
       32, std::max<int64_t>(8, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nw)))));
   p.cand = p.mfma && p.nv_cap > a.k && static_cast<int64_t>(p.nw) * p.cap <= kFinalCap &&
            static_cast<int64_t>(p.nw) * p.cap >= 2 * static_cast<int64_t>(a.k);
+  // many rows per sequence: the fp8 contraction with exact correction
+  p.pre = p.mfma && a.score_out == nullptr && rows >= 512 && a.queries_per_seq >= 64 &&
+          p.nv_cap > a.k;
+  if (p.pre) p.cand = false;
+  p.tps = static_cast<int>(ceil_div(a.queries_per_seq, kPQ));
+  p.tiles = a.n_seqs * p.tps;
   size_t off = 0;
   p.off_scores = off;
   off = align_up(off + static_cast<size_t>(rows) * p.ld * sizeof(float));
@@ -652,6 +1215,16 @@ Plan plan(const dsa_index_args& a) {
   if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nw * p.cap * sizeof(uint64_t));
   p.off_meta = off;
   if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nw * sizeof(uint32_t));
+  p.off_theta = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(rows) * sizeof(float));
+  p.off_beta = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(rows) * sizeof(float));
+  p.off_nu = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(p.tiles) * sizeof(float));
+  p.off_pcnt = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(rows) * sizeof(uint32_t));
+  p.off_pcand = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(rows) * kPCandCap * sizeof(int32_t));
   p.total = off;
   return p;
 }
@@ -669,6 +1242,41 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
   const bool no_keys = a.keys == nullptr;  // only allowed when k >= every n_vis
   dsa_status rc;
+  if (P.pre) {
+    PArgs pa{};
+    pa.q = static_cast<const uint8_t*>(a.q);
+    pa.q_scale = a.q_scale;
+    pa.w = a.w;
+    pa.keys = static_cast<const uint8_t*>(a.keys);
+    pa.k_scale = a.k_scale;
+    pa.q_pos = a.q_pos;
+    pa.Tq = a.queries_per_seq;
+    pa.Hi = a.heads;
+    pa.s = a.stride;
+    pa.S = a.span;
+    pa.k = a.k;
+    pa.tiles_per_seq = P.tps;
+    pa.e_cap = a.e_cap;
+    pa.nv_cap = P.nv_cap;
+    pa.max_pos_end = a.max_pos_end;
+    pa.theta = reinterpret_cast<float*>(base + P.off_theta);
+    pa.beta = reinterpret_cast<float*>(base + P.off_beta);
+    pa.nu_part = reinterpret_cast<float*>(base + P.off_nu);
+    pa.cand_cnt = reinterpret_cast<uint32_t*>(base + P.off_pcnt);
+    pa.cand_j = reinterpret_cast<int32_t*>(base + P.off_pcand);
+    pa.status = a.status;
+    const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
+    const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);
+    launch_timed(k_pidx_prep, dim3(P.tiles), dim3(kThreads), 0, st, e0, nullptr, pa);
+    rc = hip_check(hipGetLastError(), "k_pidx_prep launch");
+    if (rc != DSA_OK) return rc;
+    hipLaunchKernelGGL(k_pidx_main, dim3(P.tiles), dim3(kThreads), 0, st, pa);
+    rc = hip_check(hipGetLastError(), "k_pidx_main launch");
+    if (rc != DSA_OK) return rc;
+    launch_timed(k_pidx_select, dim3(rows), dim3(kSel), 0, st, nullptr, e1, pa, scores, P.ld,
+                 a.idx_out);
+    return hip_check(hipGetLastError(), "k_pidx_select launch");
+  }
   if (!no_keys && P.nv_cap > 0) {
     const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
     const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);

@@ -118,7 +118,8 @@ INDEX_CASES = [
 ]
 
 
-def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, boost=None):
+def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, boost=None,
+               want_scores=True, boost_mod=None, boost_scale=16.0):
     L = _lib()
     rows = len(positions)
     B = B if B is not None else rows // Tq
@@ -137,7 +138,10 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
         qc = np.zeros_like(qc)
     if boost is not None:  # entries j0..j1 get 16x larger key scales (scores 16x)
         ks = ks.copy()
-        ks[:, boost[0]:boost[1]] *= 16.0
+        ks[:, boost[0]:boost[1]] *= boost_scale
+    if boost_mod is not None:  # entries j = 0 mod boost_mod get 16x larger key scales
+        ks = ks.copy()
+        ks[:, ::boost_mod] *= 16.0
     a = L.IndexArgs()
     qpos = torch.tensor(np.asarray(positions, np.int64), device=DEV)
     t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt), k=_tensor(kc), ks=_tensor(ks))
@@ -150,7 +154,7 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
                                               L.ptr(t["k"]), L.ptr(t["ks"]))
     a.dtype = L.DSA_F32 if dtype == "f32" else L.DSA_FP8_E4M3
     a.e_cap, a.max_pos_end, a.k = e_cap, max_pos, k
-    a.idx_out, a.score_out, a.status = L.ptr(idx), L.ptr(sco), L.ptr(status)
+    a.idx_out, a.score_out, a.status = L.ptr(idx), L.ptr(sco) if want_scores else None, L.ptr(status)
     L.index_topk(a)
     torch.cuda.synchronize()
     assert status.item() == 0
@@ -204,6 +208,61 @@ def test_index_topk_clustered_top_entries():
         scores = odsa.indexer_scores(qd[i], wt[i], kd[i][:nv])
         assert np.sum((idx[i] >= 1024) & (idx[i] < 2048)) > 100
         check_topk_row(idx[i], scores, 512, f"clustered row {i}")
+
+
+def _check_prefill_rows(idx, kd, qd, wt, positions, Tq, k, rows, label):
+    swaps = 0
+    for i in rows:
+        b, m = i // Tq, positions[i]
+        nv = odsa.n_vis(m, 4, 8)
+        scores = odsa.indexer_scores(qd[i], wt[i], kd[b][:nv])
+        swaps += check_topk_row(idx[i], scores, k, f"{label} row {i} m={m}")
+    return swaps
+
+
+def test_index_topk_prefill_contraction():
+    """The many-rows path (fp8 MFMA scores, sampled threshold, exact
+    rescoring of the candidates): two sequences of 512 rows each, ragged
+    visibility, every 3rd row checked against the oracle."""
+    Tq = 512
+    positions = list(range(20000, 20000 + Tq)) + list(range(9001, 9001 + Tq))
+    print(f"[dsa_index_topk] prefill contraction rows={len(positions)} k=512", flush=True)
+    idx, _, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2400, B=2, Tq=Tq,
+                                    want_scores=False)
+    rows = list(range(0, len(positions), 3)) + [Tq - 1, 2 * Tq - 1]
+    swaps = _check_prefill_rows(idx, kd, qd, wt, positions, Tq, 512, rows, "contraction")
+    assert swaps <= 2
+
+
+def test_index_topk_prefill_certificate_fallback():
+    """Every 3rd entry (the entries the threshold sample reads at this n_vis)
+    scores 16x higher, so the sample overstates the k-th score, the
+    certificate fails and rows fall back to exact full scoring.  Also 9
+    heads (zero-padded on the matrix cores)."""
+    Tq = 512
+    positions = list(range(24000, 24000 + Tq))
+    print("[dsa_index_topk] prefill certificate fallback, Hi=9", flush=True)
+    idx, _, kd, qd, wt = _index_run("fp8", 9, 128, 512, positions, 2500, B=1, Tq=Tq,
+                                    want_scores=False, boost_mod=3)
+    rows = list(range(0, Tq, 16)) + [Tq - 1]
+    swaps = _check_prefill_rows(idx, kd, qd, wt, positions, Tq, 512, rows, "fallback")
+    assert swaps <= 2
+    # the boosted entries dominate the selection
+    assert np.mean(idx[rows] % 3 == 0) > 0.8
+
+
+def test_index_topk_prefill_candidate_overflow():
+    """One entry with a 10^4 larger key scale makes the error bound (and so
+    the candidate band) so wide that every visible entry is a candidate: the
+    lists overflow and every row is scored exactly in full."""
+    Tq = 256
+    positions = list(range(30000, 30000 + 2 * Tq))
+    print("[dsa_index_topk] prefill candidate overflow", flush=True)
+    idx, _, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2600, B=2, Tq=Tq,
+                                    want_scores=False, boost=(7, 8), boost_scale=1e4)
+    rows = list(range(0, 2 * Tq, 17)) + [Tq - 1, 2 * Tq - 1]
+    swaps = _check_prefill_rows(idx, kd, qd, wt, positions, Tq, 512, rows, "overflow")
+    assert swaps <= 2
 
 
 def test_index_topk_nothing_visible():

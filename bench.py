@@ -161,6 +161,29 @@ def cpu_baseline(w, min_seconds=10.0, max_sets=8):
                       f"{w.B}; full layer step, fp64 NumPy), {dt:.1f} s of oracle time"}
 
 
+def time_prefill(dev, steps=3, warmup=1):
+    """The prefill chunk workload: layer step time, indexer (+Top-k) and
+    attention kernel times, and their throughput."""
+    import torch
+    from sparse_long_context_c4a_amd import configs, _lib
+    wp = configs.C4A_PREFILL_128K
+    print("[bench] prefill chunk", file=sys.stderr, flush=True)
+    psets = build_sets(wp, 1, dev)
+    pms, pidx_ms, pattn_ms = time_layer(wp, psets, steps, warmup, decode=False)
+    nvs = sum(_lib.n_complete(wp.p0 + t, wp.s, wp.S) for t in range(wp.T))
+    idx_flop = 2.0 * wp.Hi * wp.Di * nvs
+    attn_flop = 4.0 * wp.T * wp.H * (wp.k + wp.W) * wp.D
+    del psets
+    torch.cuda.empty_cache()
+    return {"workload": wp.name, "ms_per_step": pms,
+            "indexer_ms": pidx_ms, "attention_ms": pattn_ms,
+            "indexer_tflops": idx_flop / (pidx_ms / 1e3) / 1e12,
+            "indexer_frac_fp8_peak": idx_flop / (pidx_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
+            "attention_tflops": attn_flop / (pattn_ms / 1e3) / 1e12,
+            "attention_frac_bf16_peak": attn_flop / (pattn_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "layer_tflops": (idx_flop + attn_flop) / (pms / 1e3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +194,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunk (for profiling its kernels)")
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
@@ -189,6 +214,9 @@ def main():
     w = configs.BY_NAME[args.workload]
     assert w.mode == "decode"
     dev = "cuda"
+    if args.prefill_only:
+        print(json.dumps({"prefill": time_prefill(dev)}))
+        return
     print(f"[bench] building {args.sets} input sets for {w.name}", file=sys.stderr, flush=True)
     sets = build_sets(w, args.sets, dev)
     print("[bench] timing", file=sys.stderr, flush=True)
@@ -226,19 +254,7 @@ def main():
         line["calib_copy_bytes"] = n
         del src, dst
     if not args.no_prefill:
-        wp = configs.C4A_PREFILL_128K
-        print("[bench] prefill chunk", file=sys.stderr, flush=True)
-        psets = build_sets(wp, 1, dev)
-        pms, pidx_ms, pattn_ms = time_layer(wp, psets, 3, 1, decode=False)
-        nvs = sum(_lib.n_complete(wp.p0 + t, wp.s, wp.S) for t in range(wp.T))
-        idx_flop = 2.0 * wp.Hi * wp.Di * nvs
-        attn_flop = 4.0 * wp.T * wp.H * (wp.k + wp.W) * wp.D
-        line["prefill"] = {"workload": wp.name, "ms_per_step": pms,
-                           "indexer_ms": pidx_ms, "attention_ms": pattn_ms,
-                           "indexer_tflops": idx_flop / (pidx_ms / 1e3) / 1e12,
-                           "indexer_frac_fp8_peak": idx_flop / (pidx_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
-                           "layer_tflops": (idx_flop + attn_flop) / (pms / 1e3) / 1e12}
-        del psets
+        line["prefill"] = time_prefill(dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -37,8 +37,10 @@ def sources():
 
 
 # Per-source flags.  The indexer's scores are finite for finite inputs, so
-# its ReLUs need no NaN quieting (a bare v_max_f32 instead of two).
-FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans"]}
+# its ReLUs need no NaN quieting (a bare v_max_f32 instead of two), and its
+# matrix-core results are consumed by VALU math at once, so they go to
+# VGPRs rather than to accumulation registers that must be copied out.
+FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

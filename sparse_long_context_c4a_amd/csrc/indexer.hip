@@ -781,6 +781,24 @@ __device__ __forceinline__ float p_reduce4(float p0, float p1, float p2, float p
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// The two stages of p_scores, for software pipelining across tiles: the
+// matrix-core products of every row, then ReLU, weights and head sums.
+__device__ __forceinline__ void p_products(const PRows& r, const v8i& kb, v4f (&c)[kPQ]) {
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q)
+    c[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.a[q], kb, v4f{0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ void p_finish(const PRows& r, const v4f (&c)[kPQ], float (&s)[kPQ / 4]) {
+  float p[kPQ];
+#pragma unroll
+  for (int q = 0; q < kPQ; ++q)
+    p[q] = r.wv[q][0] * fmaxf(c[q][0], 0.f) + r.wv[q][1] * fmaxf(c[q][1], 0.f) +
+           r.wv[q][2] * fmaxf(c[q][2], 0.f) + r.wv[q][3] * fmaxf(c[q][3], 0.f);
+#pragma unroll
+  for (int h = 0; h < kPQ / 4; ++h) s[h] = p_reduce4(p[4 * h], p[4 * h + 1], p[4 * h + 2], p[4 * h + 3]);
+}
+
 // Approximate scores (before the key scale) of all kPQ rows against the
 // tile's 16 entries: lane (g, n) of s[h] holds row 4h + kPerm[g], entry n.
 __device__ __forceinline__ void p_scores(const PRows& r, const v8i& kb, float (&s)[kPQ / 4]) {
@@ -905,16 +923,16 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
       const v8i bk = as_v8i(lo[u], hi[u]);
       const float ksc = ks[u];
       load(u, min(tile + 4 * kPre, kTiles - 1));
-      if (tile >= kTiles) continue;
-      const int i = tile * 16 + n;
+      const int i = tile * 16 + n;  // tile < kTiles: 16 | kTiles / 4
       const int64_t j = static_cast<int64_t>(i) * st;
       const bool in = i < ns;
       float sv[kPQ / 4];
       p_scores(r, bk, sv);
       // lane (g, n) holds rows qa and 4 + qa, qa = kPerm[g], of entry i
       const int qa = g == 0 ? 0 : g == 1 ? 2 : g == 2 ? 1 : 3;
-      skey[qa][i] = (in && j < nv0) ? order_key(sv[0] * ksc) : 0u;
-      skey[4 + qa][i] = (in && j < nv1) ? order_key(sv[1] * ksc) : 0u;
+      const uint32_t k0 = order_key(sv[0] * ksc), k1 = order_key(sv[1] * ksc);
+      skey[qa][i] = (in & (j < nv0)) ? k0 : 0u;
+      skey[4 + qa][i] = (in & (j < nv1)) ? k1 : 0u;
     }
   }
   __syncthreads();
@@ -1026,10 +1044,10 @@ __global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
   };
   // this lane's two output rows (4h + kPerm[g], h = 0, 1): bounds and
   // thresholds
-  int64_t nvp[kPQ];
+  int nvp[kPQ];
 #pragma unroll
-  for (int q = 0; q < kPQ; ++q) nvp[q] = r.nv[q];
-  const int64_t nvs0 = p_pick(nvp, 0, g), nvs1 = p_pick(nvp, 1, g);
+  for (int q = 0; q < kPQ; ++q) nvp[q] = static_cast<int>(r.nv[q]);
+  const int nvs0 = p_pick(nvp, 0, g), nvs1 = p_pick(nvp, 1, g);
   const float th0 = p_pick(thr, 0, g), th1 = p_pick(thr, 1, g);
   const int qa = g == 0 ? 0 : g == 1 ? 2 : g == 2 ? 1 : 3;
   if (ntiles > 0) {
@@ -1037,28 +1055,52 @@ __global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
     for (int u = 0; u < kPre; ++u) load(u, wave + 4 * u);
   }
   for (int64_t t0 = wave; t0 < ntiles; t0 += 4 * kPre) {
+    // kPre tiles of scores in one branch-free block (the matrix-core ops of
+    // one tile overlap the VALU work of another), then the rare appends
+    // (tiles past the end score clamped keys and are masked by j < nv)
+    uint32_t hm = 0u;  // bit 2u + h: tile u, output row h
+    float ksc[kPre];
+    v4f c[kPQ];
+    p_products(r, as_v8i(lo[0], hi[0]), c);
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      const int64_t tt = t0 + 4 * u;
-      const v8i bk = as_v8i(lo[u], hi[u]);
-      const float ksc = ks[u];
-      load(u, min<int64_t>(tt + 4 * kPre, ntiles - 1));
-      if (tt >= ntiles) continue;
-      const int64_t j = tt * 16 + n;
+      ksc[u] = ks[u];
+      // the next tile's products go to the matrix cores before this tile's
+      // VALU work, which they overlap
+      v4f cn[kPQ];
+      if (u + 1 < kPre) p_products(r, as_v8i(lo[u + 1], hi[u + 1]), cn);
+      load(u, min<int64_t>(t0 + 4 * u + 4 * kPre, ntiles - 1));
+      const int j = static_cast<int>(t0 + 4 * u) * 16 + n;
       float sv[kPQ / 4];
-      p_scores(r, bk, sv);
-      const bool h0 = j < nvs0 && sv[0] * ksc >= th0;
-      const bool h1 = j < nvs1 && sv[1] * ksc >= th1;
-      if (__any(h0 || h1)) {
-        if (h0) {
-          const uint32_t p = atomicAdd(&lcnt[qa], 1u);
-          if (p < static_cast<uint32_t>(kPCandCap)) cj[qa * kPCandCap + p] = static_cast<int32_t>(j);
-        }
-        if (h1) {
-          const uint32_t p = atomicAdd(&lcnt[4 + qa], 1u);
-          if (p < static_cast<uint32_t>(kPCandCap)) cj[(4 + qa) * kPCandCap + p] = static_cast<int32_t>(j);
-        }
+      p_finish(r, c, sv);
+      // (bitwise &: no short-circuit branches inside the block)
+      hm |= ((j < nvs0) & (sv[0] * ksc[u] >= th0)) ? (1u << (2 * u)) : 0u;
+      hm |= ((j < nvs1) & (sv[1] * ksc[u] >= th1)) ? (1u << (2 * u + 1)) : 0u;
+      if (u + 1 < kPre) {
+#pragma unroll
+        for (int q = 0; q < kPQ; ++q) c[q] = cn[q];
       }
+    }
+    // issue order: one matrix-core op, then a run of VALU work, so that the
+    // in-order wave keeps issuing VALU while each product executes
+#pragma unroll
+    for (int i = 0; i < kPQ * kPre; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    if (__any(hm != 0u)) {
+      // every slot request first, then the stores: one LDS round trip per
+      // step instead of one per request
+      uint32_t pos[2 * kPre];
+#pragma unroll
+      for (int b2 = 0; b2 < 2 * kPre; ++b2) {
+        pos[b2] = 0xffffffffu;
+        if (hm & (1u << b2)) pos[b2] = atomicAdd(&lcnt[4 * (b2 & 1) + qa], 1u);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2 * kPre; ++b2)
+        if (pos[b2] < static_cast<uint32_t>(kPCandCap))
+          cj[(4 * (b2 & 1) + qa) * kPCandCap + pos[b2]] = static_cast<int>(t0 + 4 * (b2 >> 1)) * 16 + n;
     }
   }
   __syncthreads();
@@ -1135,21 +1177,34 @@ __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict
     const int32_t* cj = a.cand_j + static_cast<int64_t>(row) * kPCandCap;
     const int ct = static_cast<int>((cnt + 15) / 16);
     uint32_t c_ge = 0;
-    for (int tile = wave; tile < ct; tile += kSelWaves) {
-      const int i = tile * 16 + n;
-      const int64_t j = i < static_cast<int>(cnt) ? cj[i] : -1;
-      uint4 blo = {0u, 0u, 0u, 0u}, bhi = {0u, 0u, 0u, 0u};
-      float ks = 0.f;
-      if (j >= 0) {
-        const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
-        blo = kp[g];
-        bhi = kp[4 + g];
-        ks = ksb[j];
+    // four tiles per step: their indices, then their keys, then the math,
+    // so that a step costs two memory round trips
+    constexpr int kU = 4;
+    for (int t0 = wave; t0 < ct; t0 += kU * kSelWaves) {
+      int64_t j[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = (t0 + u * kSelWaves) * 16 + n;
+        j[u] = i < static_cast<int>(cnt) ? cj[i] : -1;
       }
-      const float sc = p_exact(aq, wv, blo, bhi) * ks;
-      if (g == 0 && i < kPCandCap) {
-        cand_s[i] = j >= 0 ? composite(order_key(sc), static_cast<uint32_t>(j)) : 0ull;
-        c_ge += (j >= 0 && sc >= cut) ? 1u : 0u;
+      uint4 blo[kU], bhi[kU];
+      float ks[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t jj = j[u] >= 0 ? j[u] : 0;
+        const uint4* kp = reinterpret_cast<const uint4*>(kb + jj * 128);
+        blo[u] = kp[g];
+        bhi[u] = kp[4 + g];
+        ks[u] = ksb[jj];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = (t0 + u * kSelWaves) * 16 + n;
+        const float sc = p_exact(aq, wv, blo[u], bhi[u]) * ks[u];
+        if (g == 0 && i < ct * 16) {
+          cand_s[i] = j[u] >= 0 ? composite(order_key(sc), static_cast<uint32_t>(j[u])) : 0ull;
+          c_ge += (j[u] >= 0 && sc >= cut) ? 1u : 0u;
+        }
       }
     }
     for (int i = static_cast<int>(cnt) + tid; i < ct * 16; i += kSel) cand_s[i] = 0ull;

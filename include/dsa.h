@@ -36,6 +36,16 @@
  *  - Storage formats: DSA_F32 IEEE binary32; DSA_BF16 bfloat16;
  *    DSA_FP8_E4M3 OCP fp8 e4m3fn (bias 7, max 448, no infinities) with one
  *    fp32 scale per row (value = scale * code).
+ *  - Key tile layout: an FP8 cache of dim 128 (the indexer keys) is not
+ *    row-major.  Each sequence holds e_pad = ceil(e_cap / 16) * 16 entries
+ *    (allocate B * e_pad * 128 bytes) in tiles of 16 entries; tile t is 2048
+ *    bytes: 8 chunks of 16 dims, chunk c holding the 16 entries' bytes
+ *    16c .. 16c+15 in entry order.  Byte d of entry j of sequence b sits at
+ *      ((b * e_pad + 16 * (j / 16)) * 128) + (d / 16) * 256 + (j % 16) * 16 + d % 16.
+ *    This is the order in which the matrix-core operands are read, so each
+ *    load instruction of the indexer streams 1 KiB of contiguous bytes.  The
+ *    scales stay row-major [B, e_cap].  FP8 caches of other dims are
+ *    row-major.
  *  - RoPE acts on interleaved pairs of the last rope_dim dims of a vector,
  *    pair i rotated by angle (pos + rope_pos_offset) * rope_base^(-2i/rope_dim).
  *    rope_pos_offset shifts every rotation position and no index.
@@ -105,7 +115,8 @@ typedef struct dsa_compress_args {
   int32_t logits_rows;        /* >= ceil(raw_len / s)                        */
   const float* rms_gamma;     /* [D] or NULL (no RMSNorm)                    */
   float rms_eps;
-  void* out;                  /* [B, e_cap, D] cache, entry j at slot j      */
+  void* out;                  /* [B, e_cap, D] cache, entry j at slot j
+                                 (FP8 with D = 128: the key tile layout)     */
   dsa_dtype out_dtype;        /* DSA_F32, DSA_BF16 or DSA_FP8_E4M3           */
   float* out_scale;           /* [B, e_cap] for FP8 output, else ignored     */
   int64_t e_cap;              /* cache slots per sequence                    */
@@ -137,7 +148,7 @@ typedef struct dsa_index_args {
   const void* q;              /* [B * Tq, Hi, Di]                            */
   const float* q_scale;       /* [B * Tq, Hi] (FP8; NULL means 1)            */
   const float* w;             /* [B * Tq, Hi] head weights                   */
-  const void* keys;           /* [B, e_cap, Di]                              */
+  const void* keys;           /* [B, e_cap, Di]; FP8 Di = 128: tile layout   */
   const float* k_scale;       /* [B, e_cap] (FP8)                            */
   dsa_dtype dtype;            /* q and keys: DSA_F32 or DSA_FP8_E4M3         */
   int64_t e_cap;
@@ -245,7 +256,7 @@ typedef struct dsa_layer_args {
   const float* qi_scale;      /* [B, T, Hi] (FP8)                            */
   const float* w;             /* [B, T, Hi]                                  */
   void* main_cache;           /* [B, e_cap, D]                               */
-  void* idx_cache;            /* [B, e_cap, Di]                              */
+  void* idx_cache;            /* [B, e_cap, Di]; FP8 Di = 128: tile layout   */
   float* idx_scale;           /* [B, e_cap] (FP8)                            */
   int64_t e_cap;
   void* main_ring;            /* [B, S, D]                                   */

@@ -87,6 +87,29 @@ __device__ __forceinline__ void rope_cs(int64_t pos, int i, int r, double base, 
   sincosf(static_cast<float>(red), s, c);
 }
 
+// ------------------------------------------------ indexer key tile layout
+// fp8 caches of dim 128 (the indexer keys) are stored in tiles of 16
+// entries: tile t of sequence b holds entries 16t .. 16t+15 as 8 chunks of
+// 16 dims, chunk-major, each chunk the 16 entries' 16 bytes in entry order.
+// A wave that gives lane (g, n) chunk g (or 4 + g) of entry n -- the
+// matrix-core operand layout -- then reads 1 KiB of contiguous bytes per
+// load instruction.  Sequences are e_pad = ceil(e_cap / 16) * 16 entries
+// apart.
+__host__ __device__ __forceinline__ int64_t idx_e_pad(int64_t e_cap) { return (e_cap + 15) & ~int64_t{15}; }
+// Byte offset of dim d of entry j of sequence b.
+__host__ __device__ __forceinline__ int64_t idx_tile_off(int64_t b, int64_t e_pad, int64_t j, int d) {
+  return (b * e_pad + (j & ~int64_t{15})) * 128 + (d >> 4) * 256 + (j & 15) * 16 + (d & 15);
+}
+// The two 16-byte operand chunks of lane (g, n) for entry j (n = j mod 16
+// in the operand layout): chunks g and 4 + g.
+__device__ __forceinline__ void idx_load_chunks(const uint8_t* seq_keys, int64_t j, int g, uint4* lo,
+                                                uint4* hi) {
+  const uint4* t = reinterpret_cast<const uint4*>(seq_keys + (j & ~int64_t{15}) * 128);
+  const int n = static_cast<int>(j & 15);
+  *lo = t[g * 16 + n];
+  *hi = t[(4 + g) * 16 + n];
+}
+
 // ------------------------------------------------------- counts / keys
 __host__ __device__ __forceinline__ int64_t n_complete(int64_t L, int s, int S) {
   return L < S ? 0 : (L - S) / s + 1;  // L - S >= 0 here, so / is floor

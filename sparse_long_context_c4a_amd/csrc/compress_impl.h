@@ -130,14 +130,18 @@ __device__ __forceinline__ void compress_one(
       if (tid + k * kCompressThreads < npairs) am = fmaxf(am, fmaxf(fabsf(acc[k][0]), fabsf(acc[k][1])));
     am = block_max(am, red);
     const float sc = am / 448.0f;
-    uint8_t* op = static_cast<uint8_t*>(out) + o;
+    // dim 128: the 16-entry tile layout of the indexer keys; else row-major
+    const bool tiled = D == 128;
+    uint8_t* op = static_cast<uint8_t*>(out) + (tiled ? 0 : o);
+    const int64_t e_pad = idx_e_pad(e_cap);
 #pragma unroll
     for (int k = 0; k < kCompressPairs; ++k) {
       const int pr = tid + k * kCompressThreads;
       if (pr < npairs) {
         const uint32_t c0 = sc > 0.f ? f32_to_fp8(acc[k][0] / sc) : 0u;
         const uint32_t c1 = sc > 0.f ? f32_to_fp8(acc[k][1] / sc) : 0u;
-        *reinterpret_cast<uint16_t*>(op + 2 * pr) = static_cast<uint16_t>(c0 | (c1 << 8));
+        const int64_t at = tiled ? idx_tile_off(b, e_pad, j, 2 * pr) : 2 * pr;
+        *reinterpret_cast<uint16_t*>(op + at) = static_cast<uint16_t>(c0 | (c1 << 8));
       }
     }
     if (tid == 0) out_scale[static_cast<int64_t>(b) * e_cap + j] = sc;

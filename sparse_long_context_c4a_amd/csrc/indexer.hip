@@ -410,16 +410,17 @@ __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_
 // 128-byte vector, bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16)
 // with g = l / 16; MFMA c of the four takes the lane's bytes [8 c, 8 c + 8)
 // of those 32.  A and B use the same byte-to-k assignment, so the four MFMAs
-// sum every one of the 128 products exactly once; each of the two 16-byte
-// loads of a wave covers 64 contiguous bytes of 16 entries.
-template <bool kCand>
+// sum every one of the 128 products exactly once.  With the keys' tile
+// layout each of the two 16-byte loads of a wave reads 1 KiB of contiguous
+// bytes.
+template <bool kCand, int kEnt>
 __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
     const int64_t* __restrict__ q_pos, int Tq, int Hi, int s, int S, int64_t e_cap,
     int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, uint32_t* status) {
-  index_stream_block<kCand>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos,
+  index_stream_block<kCand, kEnt>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos,
                             Tq, Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand,
                             meta, cap, status);
 }
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
 // sequence per row) run the prologue roles, whose writes the indexer does not
 // read (see decode_prologue_block), so they overlap the key stream instead
 // of adding a launch and its latency in front of it.
-template <typename MainT, int kIdxOut>
+template <typename MainT, int kIdxOut, int kEnt>
 __global__ __launch_bounds__(kThreads) void k_decode_index(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb, PrologueArgs pa,
     uint32_t* status) {
   if (static_cast<int>(blockIdx.x) < nb)
-    index_stream_block<true>(blockIdx.x, nb, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos, 1,
+    index_stream_block<true, kEnt>(blockIdx.x, nb, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos, 1,
                              Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand, meta,
                              cap, status);
   else
@@ -470,13 +471,17 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
   __syncthreads();
   const int64_t ent = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid;
   if (ent < nv) {
-    const T* kr = keys + (static_cast<int64_t>(b) * e_cap + ent) * Di;
+    // fp8 keys of dim 128 use the tile layout, everything else is row-major
+    const bool tiled = sizeof(T) == 1 && Di == 128;
+    const T* kr = keys + (tiled ? 0 : (static_cast<int64_t>(b) * e_cap + ent) * Di);
+    const int64_t e_pad = idx_e_pad(e_cap);
     float tot = 0.f;
     for (int h = 0; h < Hi; ++h) {
       float d = 0.f;
       for (int i = 0; i < Di; ++i) {
         float kv;
-        if constexpr (sizeof(T) == 1) kv = fp8_to_f32(kr[i]);
+        if constexpr (sizeof(T) == 1)
+          kv = fp8_to_f32(tiled ? kr[idx_tile_off(b, e_pad, ent, i)] : kr[i]);
         else kv = kr[i];
         d = fmaf(q_s[h * Di + i], kv, d);
       }
@@ -494,10 +499,13 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
 // thread) through one combined reduction pass, one histogram pass and the
 // emit pass.
 __global__ __launch_bounds__(kSel) void k_topk_cand_final(
-    const float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
+    float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
     int s, int S, int64_t nv_cap, int64_t max_pos_end, const uint64_t* __restrict__ cand,
     const uint32_t* __restrict__ meta, int nw, int cap, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, int k) {
+    float* __restrict__ score_out, int k, const uint8_t* __restrict__ q,
+    const float* __restrict__ q_scale, const float* __restrict__ hw,
+    const uint8_t* __restrict__ keys, const float* __restrict__ k_scale, int Tq, int Hi,
+    int64_t e_cap) {
   __shared__ uint64_t cand_s[kFinalCap];
   __shared__ uint64_t tmp_s[kTmpCap];
   __shared__ uint32_t h_s[kBins];
@@ -506,10 +514,20 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   const int row = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
   const int64_t nv = ri.nv;
-  const float* srow = scores + static_cast<int64_t>(row) * ld_scores;
+  float* srow = scores + static_cast<int64_t>(row) * ld_scores;
   int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
   float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
+  const int b = row / Tq;
+  const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * 128;
+  const float* ksb = k_scale + static_cast<int64_t>(b) * e_cap;
+  v8bf aq[4];
+  float wv[4];
   if (nv <= k) {
+    if (orow) {  // the visible entries' scores (the stream kept them in registers)
+      exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
+      score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+      __syncthreads();
+    }
     emit_all_visible(srow, nv, k, irow, orow);
     return;
   }
@@ -562,6 +580,10 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     }
   const bool ok = block_reduce_u32<2>(c_ge) >= static_cast<uint32_t>(k);  // barriers
   if (!ok) {
+    // the certificate failed: score the row exactly in full, then select
+    exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
+    score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+    __syncthreads();
     row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
     return;
   }
@@ -850,15 +872,16 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
   const int tps = a.tiles_per_seq, slice = blockIdx.x % tps;
   const int64_t per = (nvs + tps - 1) / tps;
   const int64_t e_lo = slice * per, e_hi = min(nvs, e_lo + per);
-  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * a.e_cap * 128;
+  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * idx_e_pad(a.e_cap) * 128;
   const float* ksb = a.k_scale + static_cast<int64_t>(t.b) * a.e_cap;
   float nu = 0.f;
   for (int64_t e0 = e_lo; e0 < e_hi; e0 += kThreads / 4) {
     const int64_t e = e0 + tid / 4;
     float ss = 0.f;
     if (e < e_hi) {
-      const uint4* kp = reinterpret_cast<const uint4*>(kb + e * 128) + 2 * (tid & 3);
-      ss = fp8x16_sumsq(kp[0]) + fp8x16_sumsq(kp[1]);
+      const uint4* kt = reinterpret_cast<const uint4*>(kb + (e & ~int64_t{15}) * 128);
+      const int c = 2 * (tid & 3), en = static_cast<int>(e & 15);
+      ss = fp8x16_sumsq(kt[c * 16 + en]) + fp8x16_sumsq(kt[(c + 1) * 16 + en]);
     }
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
@@ -903,9 +926,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
   auto load = [&](int u, int tile) {
     const int i = tile * 16 + n;
     const int64_t j = min<int64_t>(static_cast<int64_t>(i) * st, jmax);
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
-    lo[u] = kp[g];
-    hi[u] = kp[4 + g];
+    idx_load_chunks(kb, j, g, &lo[u], &hi[u]);
     ks[u] = ksb[j];
   };
   int64_t nvp[kPQ];
@@ -1023,7 +1044,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
     if (thr[q] == INFINITY) r.nv[q] = 0;  // nothing to collect for this row
     nvt = max(nvt, r.nv[q]);
   }
-  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * a.e_cap * 128;
+  const uint8_t* kb = a.keys + static_cast<int64_t>(t.b) * idx_e_pad(a.e_cap) * 128;
   const float* ksb = a.k_scale + static_cast<int64_t>(t.b) * a.e_cap;
   int32_t* cj = a.cand_j + t.row0 * kPCandCap;
   const int64_t ntiles = (nvt + 15) / 16;
@@ -1037,9 +1058,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
   const int64_t jmax = max<int64_t>(0, nvt - 1);
   auto load = [&](int u, int64_t tile) {
     const int64_t j = min<int64_t>(tile * 16 + n, jmax);
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
-    lo[u] = kp[g];
-    hi[u] = kp[4 + g];
+    idx_load_chunks(kb, j, g, &lo[u], &hi[u]);
     ks[u] = ksb[j];
   };
   // this lane's two output rows (4h + kPerm[g], h = 0, 1): bounds and
@@ -1107,23 +1126,6 @@ __global__ __launch_bounds__(kThreads) void k_pidx_main(PArgs a) {
   if (tid < t.nq) a.cand_cnt[t.row0 + tid] = lcnt[tid];
 }
 
-// Exact score (before the key scale) of entry column n for one row: A = the
-// row's heads widened to bf16, f32 head weights; same tile math as the
-// decode stream.
-__device__ __forceinline__ float p_exact(const v8bf (&aq)[4], const float (&wv)[4], uint4 blo,
-                                         uint4 bhi) {
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[0], fp8x8_to_bf16(blo.x, blo.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[1], fp8x8_to_bf16(blo.z, blo.w), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[2], fp8x8_to_bf16(bhi.x, bhi.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[3], fp8x8_to_bf16(bhi.z, bhi.w), acc, 0, 0, 0);
-  float v = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
-            wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
 __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict__ scores,
                                                       int64_t ld_scores,
                                                       int32_t* __restrict__ idx_out) {
@@ -1164,7 +1166,7 @@ __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict
       }
     }
   }
-  const uint8_t* kb = a.keys + static_cast<int64_t>(b) * a.e_cap * 128;
+  const uint8_t* kb = a.keys + static_cast<int64_t>(b) * idx_e_pad(a.e_cap) * 128;
   const float* ksb = a.k_scale + static_cast<int64_t>(b) * a.e_cap;
   float nu = 0.f;
   for (int i = tid; i < a.tiles_per_seq; i += kSel)
@@ -1192,15 +1194,13 @@ __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t jj = j[u] >= 0 ? j[u] : 0;
-        const uint4* kp = reinterpret_cast<const uint4*>(kb + jj * 128);
-        blo[u] = kp[g];
-        bhi[u] = kp[4 + g];
+        idx_load_chunks(kb, jj, g, &blo[u], &bhi[u]);
         ks[u] = ksb[jj];
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = (t0 + u * kSelWaves) * 16 + n;
-        const float sc = p_exact(aq, wv, blo[u], bhi[u]) * ks[u];
+        const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
         if (g == 0 && i < ct * 16) {
           cand_s[i] = j[u] >= 0 ? composite(order_key(sc), static_cast<uint32_t>(j[u])) : 0ull;
           c_ge += (j[u] >= 0 && sc >= cut) ? 1u : 0u;
@@ -1222,12 +1222,10 @@ __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict
     uint4 blo = {0u, 0u, 0u, 0u}, bhi = {0u, 0u, 0u, 0u};
     float ks = 0.f;
     if (j < nv) {
-      const uint4* kp = reinterpret_cast<const uint4*>(kb + j * 128);
-      blo = kp[g];
-      bhi = kp[4 + g];
+      idx_load_chunks(kb, j, g, &blo, &bhi);
       ks = ksb[j];
     }
-    const float sc = p_exact(aq, wv, blo, bhi) * ks;
+    const float sc = exact_tile_score(aq, wv, blo, bhi) * ks;
     if (g == 0 && j < nv) srow[j] = sc;
   }
   __syncthreads();
@@ -1237,7 +1235,7 @@ __global__ __launch_bounds__(kSel) void k_pidx_select(PArgs a, float* __restrict
 struct Plan {
   int64_t nv_cap, ld;
   bool mfma, cand, pre;
-  int nb, nw, cap, tps, tiles;
+  int ent, nb, nw, cap, tps, tiles;
   size_t off_scores, off_cand, off_meta, off_theta, off_beta, off_nu, off_pcnt, off_pcand, total;
 };
 
@@ -1248,8 +1246,12 @@ Plan plan(const dsa_index_args& a) {
   if (p.nv_cap < 0) p.nv_cap = 0;
   p.ld = (p.nv_cap + 63) / 64 * 64;
   p.mfma = a.keys != nullptr && a.dtype == DSA_FP8_E4M3 && a.dim == 128 && a.heads <= 16;
-  p.nb = static_cast<int>(ceil_div(p.nv_cap, kStreamEntries));
-  p.nw = 4 * p.nb;  // waves per row, 256 entries each
+  // entries per stream workgroup (1024: at 1M context 1024 workgroups of 4
+  // waves keep every SIMD busy; 2048 halves the waves and loses more to
+  // latency than it saves in candidate extraction)
+  p.ent = 1024;
+  p.nb = static_cast<int>(ceil_div(p.nv_cap, p.ent));
+  p.nw = 4 * p.nb;  // waves per row, ent / 4 entries each
   // Candidates per wave: the union holds >= 2k and fits the final LDS pass.
   // A wave of 256 entries at 1M context holds ~0.5 of the row's top 512;
   // more than 8 of them has probability ~3e-8 for unstructured scores.
@@ -1337,18 +1339,14 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
     const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);
     if (P.mfma) {
       dim3 grid(static_cast<unsigned>(P.nb), rows);
-      if (P.cand)
-        launch_timed(k_index_fp8_stream<true>, grid, dim3(kThreads), 0, st, e0, e1,
-                           static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-                           static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
-                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
-                           a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
-      else
-        launch_timed(k_index_fp8_stream<false>, grid, dim3(kThreads), 0, st, e0, e1,
-                           static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-                           static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
-                           a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
-                           a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
+      auto go = [&](auto kern) {
+        launch_timed(kern, grid, dim3(kThreads), 0, st, e0, e1, static_cast<const uint8_t*>(a.q),
+                     a.q_scale, a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
+                     a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
+                     a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
+      };
+      if (P.cand) go(k_index_fp8_stream<true, 1024>);
+      else go(k_index_fp8_stream<false, 1024>);
     } else {
       dim3 grid(static_cast<unsigned>(ceil_div(P.nv_cap, kThreads)), rows);
       const size_t shm = (static_cast<size_t>(a.heads) * a.dim + a.heads) * sizeof(float);
@@ -1371,7 +1369,9 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   if (P.cand && !no_keys) {
     hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
                        a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
-                       a.idx_out, a.score_out, a.k);
+                       a.idx_out, a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale,
+                       a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.queries_per_seq,
+                       a.heads, a.e_cap);
   } else {
     hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kSel), 0, st, no_keys ? nullptr : scores,
                        P.ld, a.q_pos, a.stride, a.span, P.nv_cap, a.max_pos_end, a.idx_out,
@@ -1397,17 +1397,21 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
   uint64_t* cand = reinterpret_cast<uint64_t*>(base + P.off_cand);
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
   const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab);
-  launch_timed(k_decode_index<uint16_t, DSA_FP8_E4M3>, dim3(P.nb + kPrologueRoles, rows), dim3(kThreads), 0, st,
-               static_cast<hipEvent_t>(a.ev_index[0]), static_cast<hipEvent_t>(a.ev_index[1]),
-               static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-               static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
-               a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,
-               pa, a.status);
+  auto go = [&](auto kern) {
+    launch_timed(kern, dim3(P.nb + kPrologueRoles, rows), dim3(kThreads), 0, st,
+                 static_cast<hipEvent_t>(a.ev_index[0]), static_cast<hipEvent_t>(a.ev_index[1]),
+                 static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
+                 static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
+                 a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,
+                 pa, a.status);
+  };
+  go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024>);
   dsa_status rc = hip_check(hipGetLastError(), "k_decode_index launch");
   if (rc != DSA_OK) return rc;
   hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
                      a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
-                     a.idx_out, a.score_out, a.k);
+                     a.idx_out, a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale,
+                     a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, 1, a.heads, a.e_cap);
   return hip_check(hipGetLastError(), "top-k launch");
 }
 

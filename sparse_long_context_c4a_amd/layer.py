@@ -24,6 +24,37 @@ def to_device(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def idx_tiles(codes):
+    """fp8 key codes [B, E, 128] (NumPy uint8 or tensor) -> the library's
+    16-entry tile layout [B, E_pad, 128] (E_pad = E rounded up to 16): each
+    tile of 16 entries is stored chunk-major (8 chunks of 16 bytes, each the
+    16 entries' bytes of that chunk).  A pure permutation of bytes."""
+    t = codes if isinstance(codes, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(codes))
+    B, E, D = t.shape
+    assert D == 128
+    Ep = -(-E // 16) * 16
+    if Ep != E:
+        t = torch.cat([t, torch.zeros((B, Ep - E, D), dtype=t.dtype, device=t.device)], dim=1)
+    return t.reshape(B, Ep // 16, 16, 8, 16).permute(0, 1, 3, 2, 4).contiguous().reshape(B, Ep, D)
+
+
+def idx_rows(tiles, E):
+    """Inverse of idx_tiles: [B, E_pad, 128] tile layout -> [B, E, 128]."""
+    B, Ep, D = tiles.shape
+    t = tiles.reshape(B, Ep // 16, 8, 16, 16).permute(0, 1, 3, 2, 4).contiguous()
+    return t.reshape(B, Ep, D)[:, :E]
+
+
+def idx_to_device(codes, device="cuda"):
+    """Indexer keys to the device: fp8 codes of dim 128 in the tile layout,
+    anything else (f32, other dims) unchanged."""
+    if codes is None:
+        return None
+    if codes.dtype == np.uint8 and codes.ndim == 3 and codes.shape[-1] == 128:
+        return idx_tiles(codes).to(device)
+    return to_device(codes, device)
+
+
 @dataclass
 class LayerState:
     main_cache: torch.Tensor
@@ -51,7 +82,7 @@ class Chunk:
 
 def state_from_inputs(inp, device="cuda"):
     return LayerState(main_cache=to_device(inp["main_cache"], device),
-                      idx_cache=to_device(inp["idx_cache"], device),
+                      idx_cache=idx_to_device(inp["idx_cache"], device),
                       idx_scale=to_device(inp["idx_scale"], device),
                       main_ring=to_device(inp["main_ring"], device),
                       idx_ring=to_device(inp["idx_ring"], device),

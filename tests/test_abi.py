@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sparse_long_context_c4a_amd import _lib
@@ -197,3 +198,20 @@ def test_layer_without_indexer_needs_k_over_n_vis():
     assert e.value.code == -3
     a = _layer_args(chunk_len=7)
     assert _lib.layer_workspace(a) > 0
+
+
+def test_idx_tile_layout_roundtrip_and_offsets():
+    """The key tile layout helpers: a byte permutation whose inverse restores
+    the rows, and whose positions follow the documented offset formula."""
+    import torch
+    from sparse_long_context_c4a_amd.layer import idx_rows, idx_tiles
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(2, 37, 128), dtype=np.uint8)
+    t = idx_tiles(codes)
+    assert t.shape == (2, 48, 128)
+    assert np.array_equal(idx_rows(t, 37).numpy(), codes)
+    flat = t.reshape(-1).numpy()
+    e_pad = 48
+    for b, j, d in [(0, 0, 0), (0, 5, 17), (1, 36, 127), (1, 16, 64), (0, 31, 15)]:
+        off = (b * e_pad + 16 * (j // 16)) * 128 + (d // 16) * 256 + (j % 16) * 16 + d % 16
+        assert flat[off] == codes[b, j, d]

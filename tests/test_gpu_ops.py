@@ -55,7 +55,9 @@ def test_compress(case):
     gamma = (1.0 + 0.5 * rng.standard_normal(D)).astype(np.float32) if use_gamma else None
     e_cap = -(-(p0 + T) // s)
     out_t = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[odt]
-    out = torch.zeros((B, e_cap, D), dtype=out_t, device=DEV)
+    tiled = odt == "fp8" and D == 128  # indexer keys: 16-entry tile layout
+    e_rows = -(-e_cap // 16) * 16 if tiled else e_cap
+    out = torch.zeros((B, e_rows, D), dtype=out_t, device=DEV)
     scale = torch.zeros((B, e_cap), dtype=torch.float32, device=DEV)
     a = L.CompressArgs()
     a.geom = L.geom(s, S, D, r, 10000.0, 0)
@@ -72,7 +74,13 @@ def test_compress(case):
     L.compress(a)
     torch.cuda.synchronize()
     j0, j1 = odsa.n_complete(p0, s, S), odsa.n_complete(p0 + T, s, S)
-    got = out.cpu()
+    if tiled:
+        from sparse_long_context_c4a_amd.layer import idx_rows
+        rows_all = idx_rows(out, out.shape[1])
+        assert not rows_all[:, e_cap:].any().item()  # padding entries untouched
+        got = rows_all[:, :e_cap].cpu()
+    else:
+        got = out.cpu()
     sc = scale.cpu().numpy()
     # slots outside [j0, j1) are untouched
     untouched = np.ones(e_cap, bool)
@@ -144,7 +152,8 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
         ks[:, ::boost_mod] *= 16.0
     a = L.IndexArgs()
     qpos = torch.tensor(np.asarray(positions, np.int64), device=DEV)
-    t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt), k=_tensor(kc), ks=_tensor(ks))
+    from sparse_long_context_c4a_amd.layer import idx_to_device
+    t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt), k=idx_to_device(kc, DEV), ks=_tensor(ks))
     idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
     sco = torch.zeros((rows, k), dtype=torch.float32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)

@@ -127,7 +127,7 @@ INDEX_CASES = [
 
 
 def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, boost=None,
-               want_scores=True, boost_mod=None, boost_scale=16.0):
+               want_scores=True, boost_mod=None, boost_scale=16.0, boost_tile_mod=None):
     L = _lib()
     rows = len(positions)
     B = B if B is not None else rows // Tq
@@ -150,6 +150,9 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
     if boost_mod is not None:  # entries j = 0 mod boost_mod get 16x larger key scales
         ks = ks.copy()
         ks[:, ::boost_mod] *= 16.0
+    if boost_tile_mod is not None:  # entries of 16-entry tiles t = 0 mod boost_tile_mod: 16x
+        ks = ks.copy()
+        ks[:, (np.arange(ks.shape[1]) // 16) % boost_tile_mod == 0] *= 16.0
     a = L.IndexArgs()
     qpos = torch.tensor(np.asarray(positions, np.int64), device=DEV)
     from sparse_long_context_c4a_amd.layer import idx_to_device
@@ -244,20 +247,37 @@ def test_index_topk_prefill_contraction():
 
 
 def test_index_topk_prefill_certificate_fallback():
-    """Every 3rd entry (the entries the threshold sample reads at this n_vis)
-    scores 16x higher, so the sample overstates the k-th score, the
-    certificate fails and rows fall back to exact full scoring.  Also 9
-    heads (zero-padded on the matrix cores)."""
+    """Every 3rd 16-entry tile (the tiles the threshold sample reads at this
+    n_vis: ~6000 entries, 375 tiles, stride 3) scores 16x higher, so the
+    sample overstates the k-th score, the certificate fails and rows fall
+    back to exact full scoring.  Also 9 heads (zero-padded on the matrix
+    cores)."""
     Tq = 512
     positions = list(range(24000, 24000 + Tq))
     print("[dsa_index_topk] prefill certificate fallback, Hi=9", flush=True)
     idx, _, kd, qd, wt = _index_run("fp8", 9, 128, 512, positions, 2500, B=1, Tq=Tq,
-                                    want_scores=False, boost_mod=3)
+                                    want_scores=False, boost_tile_mod=3)
     rows = list(range(0, Tq, 16)) + [Tq - 1]
     swaps = _check_prefill_rows(idx, kd, qd, wt, positions, Tq, 512, rows, "fallback")
     assert swaps <= 2
     # the boosted entries dominate the selection
-    assert np.mean(idx[rows] % 3 == 0) > 0.8
+    sel = idx[rows]
+    assert np.mean((sel[sel >= 0] // 16) % 3 == 0) > 0.8
+
+
+def test_index_topk_prefill_ragged_groups():
+    """Six sequences of 100 rows (row groups of 32 and prep tiles of 8 both
+    ragged), each at its own context length, so n_vis differs between and
+    within the groups and every mask row ends in a partial tile."""
+    Tq = 100
+    starts = [7001, 15013, 3037, 40003, 22011, 12345]
+    positions = [s0 + 3 * i for s0 in starts for i in range(Tq)]
+    print("[dsa_index_topk] prefill ragged groups rows=600", flush=True)
+    idx, _, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2700, B=6, Tq=Tq,
+                                    want_scores=False)
+    rows = list(range(0, len(positions), 7)) + [Tq - 1, 2 * Tq - 1, 6 * Tq - 1]
+    swaps = _check_prefill_rows(idx, kd, qd, wt, positions, Tq, 512, rows, "ragged")
+    assert swaps <= 2
 
 
 def test_index_topk_prefill_candidate_overflow():

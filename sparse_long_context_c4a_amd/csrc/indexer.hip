@@ -735,6 +735,7 @@ struct PArgs {
   float* nu_part;
   float* kappa_part;
   uint16_t* masks;
+  uint8_t* keys_rm;  // [B, nv_cap, 128] fp8 keys, one 128-byte run per entry
   uint32_t* status;
 };
 
@@ -895,7 +896,12 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
     if (e < e_hi) {
       const uint4* kt = reinterpret_cast<const uint4*>(kb + (e & ~int64_t{15}) * 128);
       const int c = 2 * (tid & 3), en = static_cast<int>(e & 15);
-      ss = fp8x16_sumsq(kt[c * 16 + en]) + fp8x16_sumsq(kt[(c + 1) * 16 + en]);
+      const uint4 x0 = kt[c * 16 + en], x1 = kt[(c + 1) * 16 + en];
+      ss = fp8x16_sumsq(x0) + fp8x16_sumsq(x1);
+      // the entry-contiguous copy the selection gathers from
+      uint4* rm = reinterpret_cast<uint4*>(a.keys_rm + (static_cast<int64_t>(t.b) * a.nv_cap + e) * 128);
+      rm[c] = x0;
+      rm[c + 1] = x1;
     }
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
@@ -1392,6 +1398,7 @@ __global__ __launch_bounds__(kPSelT) void k_pidx_select(PArgs a, float* __restri
   float wv[4];
   exact_row_operands(a.q, a.q_scale, a.w, row, a.Hi, aq, wv);
   const uint8_t* kb = a.keys + static_cast<int64_t>(b) * idx_e_pad(a.e_cap) * 128;
+  const uint8_t* krm = a.keys_rm + static_cast<int64_t>(b) * a.nv_cap * 128;
   const float* ksb = a.k_scale + static_cast<int64_t>(b) * a.e_cap;
   bool ok = cnt <= static_cast<uint32_t>(kPCandCap) && theta < INFINITY;
   if (ok) {
@@ -1412,7 +1419,9 @@ __global__ __launch_bounds__(kPSelT) void k_pidx_select(PArgs a, float* __restri
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t jj = j[u] >= 0 ? j[u] : 0;
-        idx_load_chunks(kb, jj, g, &blo[u], &bhi[u]);
+        const uint4* rm = reinterpret_cast<const uint4*>(krm + jj * 128);
+        blo[u] = rm[g];
+        bhi[u] = rm[4 + g];
         ks[u] = ksb[jj];
       }
 #pragma unroll
@@ -1443,7 +1452,8 @@ struct Plan {
   int64_t nv_cap, ld, ld_t;
   bool mfma, cand, pre;
   int ent, nb, nw, cap, tps, tiles, rg_per_seq, rg_total, nsplit, tps_split;
-  size_t off_scores, off_cand, off_meta, off_theta, off_beta, off_nu, off_kappa, off_masks, total;
+  size_t off_scores, off_cand, off_meta, off_theta, off_beta, off_nu, off_kappa, off_masks, off_krm,
+      total;
 };
 
 Plan plan(const dsa_index_args& a) {
@@ -1501,6 +1511,8 @@ Plan plan(const dsa_index_args& a) {
   if (p.pre) off = align_up(off + static_cast<size_t>(p.tiles) * sizeof(float));
   p.off_masks = off;
   if (p.pre) off = align_up(off + static_cast<size_t>(rows) * p.ld_t * sizeof(uint16_t));
+  p.off_krm = off;
+  if (p.pre) off = align_up(off + static_cast<size_t>(a.n_seqs) * p.nv_cap * 128);
   p.total = off;
   return p;
 }
@@ -1544,6 +1556,7 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
     pa.nu_part = reinterpret_cast<float*>(base + P.off_nu);
     pa.kappa_part = reinterpret_cast<float*>(base + P.off_kappa);
     pa.masks = reinterpret_cast<uint16_t*>(base + P.off_masks);
+    pa.keys_rm = reinterpret_cast<uint8_t*>(base + P.off_krm);
     pa.status = a.status;
     const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
     const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);

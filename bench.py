@@ -29,8 +29,8 @@ PEAK_BF16_TFLOPS = 2500.0
 # Hardware byte counters of the scoring kernel, from the committed rocprofv3
 # summary; reported only while the sources they were taken from are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_index_c4a_decode_B4_L1M.txt")
-TRAFFIC_SOURCES = ["indexer.hip", "indexer_impl.h", "decode_impl.h", "compress_impl.h",
-                   "common.h", "internal.h"]
+TRAFFIC_SOURCES = ["indexer.hip", "indexer_impl.h", "select_impl.h", "decode_impl.h",
+                   "compress_impl.h", "common.h", "internal.h"]
 
 
 def kernel_source_hash():

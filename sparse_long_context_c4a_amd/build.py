@@ -40,7 +40,8 @@ def sources():
 # its ReLUs need no NaN quieting (a bare v_max_f32 instead of two), and its
 # matrix-core results are consumed by VALU math at once, so they go to
 # VGPRs rather than to accumulation registers that must be copied out.
-FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_INDEXER_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"indexer.hip": _INDEXER_FLAGS, "prefill_index.hip": _INDEXER_FLAGS}
 
 
 def _compile(src):

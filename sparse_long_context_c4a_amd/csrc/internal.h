@@ -38,6 +38,14 @@ dsa_status launch_zero(void* p, size_t bytes, hipStream_t st);
 size_t index_topk_ws_bytes(const dsa_index_args& a);
 dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st);
 
+// Indexer + Top-k for many rows per sequence (prefill): whether it applies,
+// its workspace beyond the shared per-row scores (rows x ld floats, the
+// fallback buffer), and its launch.  Owned by prefill_index.hip.
+bool prefill_index_applies(const dsa_index_args& a, int64_t nv_cap);
+size_t prefill_index_ws_bytes(const dsa_index_args& a, int64_t nv_cap);
+dsa_status launch_prefill_index_topk(const dsa_index_args& a, int64_t nv_cap, float* scores,
+                                     int64_t ld, void* ws, hipStream_t st);
+
 // Attention.  Optional timing events ride on the first and last kernel's
 // dispatch.
 struct AttnLaunch {

@@ -250,6 +250,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
 constexpr int kMD = 512;
 constexpr int kMTile = 32;
 constexpr int kMPitch = 1056;  // bytes per staged vector (1024 + 32 of padding)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 10.0f;  // log2 headroom of the lazily raised running max
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -318,6 +321,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const float scale2 = g.scale * kLog2e;
   // staging: thread t -> vector e = t / 8 of the tile, 16-byte chunks j*8 + t%8
   const int se = tid >> 3, sc8 = tid & 7;
   uint4 pre[8];
@@ -357,36 +361,41 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
     }
+    // logits in log2 units; the running max is raised lazily: the weights
+    // exp2(x - m_run) may reach 2^kLazy before the accumulators are
+    // rescaled, so most tiles need no rescale (the result is the same, the
+    // weights are only kept below 2^kLazy)
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = valid_s[4 * gq + i] ? s0[i] * g.scale : -INFINITY;
-      x[4 + i] = valid_s[16 + 4 * gq + i] ? s1[i] * g.scale : -INFINITY;
+      x[i] = valid_s[4 * gq + i] ? s0[i] * scale2 : -INFINITY;
+      x[4 + i] = valid_s[16 + 4 * gq + i] ? s1[i] * scale2 : -INFINITY;
     }
     float tmax = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
+    if (__any(tmax > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 32; ++db) o[db] *= corr;
+    }
     float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = (x[i] == -INFINITY) ? 0.f : expf(x[i] - m_new);
+      p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
       psum += p[i];
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    const float corr = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (__any(corr != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < 32; ++db) o[db] *= corr;
-    }
-    const uint4 pw = uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    const v8bf pb = as_v8bf(pw);
+    l_run += psum;
+    const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
+                     static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
+                     static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
     // O^T += V^T P^T; transpose-load source: vector 4gq + e (and 16 + ...),
     // dims 16 db + 4 q4 .. + 3, with e = (lane & 15) >> 2, q4 = lane & 3
     const int te = (lane & 15) >> 2, tq = lane & 3;
@@ -423,7 +432,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       *reinterpret_cast<uint2*>(orow + d) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
     if (lse && gq == 0)
-      lse[static_cast<int64_t>(row) * g.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+      lse[static_cast<int64_t>(row) * g.H + h] =
+          l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + run) * g.H + h;
 #pragma unroll
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       *reinterpret_cast<float4*>(part_acc + pi * kMD + 16 * db + 4 * gq) =
           float4{o[db][0], o[db][1], o[db][2], o[db][3]};
     if (gq == 0) {
-      part_ml[2 * pi] = m_run;
+      part_ml[2 * pi] = m_run * kLn2;  // natural-log units for the merge
       part_ml[2 * pi + 1] = l_run;
     }
   }

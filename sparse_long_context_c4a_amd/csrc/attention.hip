@@ -611,6 +611,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const float scale2 = g.scale * kLog2e;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const int te = (lane & 15) >> 2, tq = lane & 3;
   for (; a0 < a_end; a0 += kDSlotsPerIter) {
@@ -628,35 +629,38 @@ __global__ __launch_bounds__(256) void k_attn_decode(
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
       }
+      // log2 units, lazily raised running max (as in k_attn_mfma)
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * g.scale : -INFINITY;
-        x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * g.scale : -INFINITY;
+        x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * scale2 : -INFINITY;
+        x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * scale2 : -INFINITY;
       }
       float tmax = x[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
+      if (__any(tmax > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= corr;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) o[db] *= corr;
+      }
       float p[8], psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = (x[i] == -INFINITY) ? 0.f : expf(x[i] - m_new);
+        p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
         psum += p[i];
       }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
-      const float corr = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-      l_run = l_run * corr + psum;
-      m_run = m_new;
-      if (__any(corr != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < 32; ++db) o[db] *= corr;
-      }
-      const v8bf pb = as_v8bf(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+      l_run += psum;
+      const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
+                       static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
+                       static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
       lds_u8* r_lo = (lds_u8*)wl + (4 * gq + te) * kMPitch + tq * 8;
       lds_u8* r_hi = (lds_u8*)wl + (16 + 4 * gq + te) * kMPitch + tq * 8;
 #pragma unroll
@@ -675,7 +679,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(
       vmask = gather_issue(src, dummy, lane, wl);
     }
   }
-  // merge the four waves: lane holds O^T[dims 16 db + 4 gq + i][head n]
+  // merge the four waves (natural-log units from here on): lane holds
+  // O^T[dims 16 db + 4 gq + i][head n]
+  m_run *= kLn2;
   if (gq == 0) {
     ml_s[wave][n][0] = m_run;
     ml_s[wave][n][1] = l_run;

@@ -253,6 +253,7 @@ constexpr int kMPitch = 1056;  // bytes per staged vector (1024 + 32 of padding)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 10.0f;  // log2 headroom of the lazily raised running max
+constexpr int kMRunSlots = 2048;  // slots per run of the MFMA path (indices held in LDS)
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kMTile * kMPitch];
   __shared__ float cs_s[kMD / 2][2];
   __shared__ int valid_s[kMTile];
+  __shared__ int32_t idx_s[kMRunSlots];  // the run's cache indices
   const int row = blockIdx.y, hq = blockIdx.x, run = blockIdx.z;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
@@ -281,6 +283,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   const bool ok = m >= 0 && m < g.max_pos_end;
   if (!ok && tid == 0 && hq == 0 && run == 0) set_status(g.status, DSA_DEVERR_POSITION);
   const int half = g.r / 2, rot0 = kMD - g.r;
+  const int total = g.k + g.W;
+  const int a_begin = run * g.slots_per_run;
+  const int a_end = min(total, a_begin + g.slots_per_run);
+  // the run's cache indices once, so that a tile's gather is one memory
+  // round trip (slots_per_run <= kMRunSlots by the plan)
+  for (int a = a_begin + tid; a < min(a_end, g.k); a += 256)
+    idx_s[a - a_begin] = g.idx[static_cast<int64_t>(row) * g.k + a];
+  const int64_t c0 = chunk_win ? g.chunk_pos0[b] : 0;
   for (int i = tid; i < half; i += 256) {
     float c = 1.f, sn = 0.f;
     if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
@@ -314,9 +324,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       qb[c] = as_v8bf(raw);
     }
   }
-  const int total = g.k + g.W;
-  const int a_begin = run * g.slots_per_run;
-  const int a_end = min(total, a_begin + g.slots_per_run);
+  auto src_of = [&](int a) -> const uint16_t* {
+    if (!ok || a >= a_end) return nullptr;
+    if (a < g.k) {
+      const int32_t j = idx_s[a - a_begin];
+      if (j < 0 || j >= g.e_cap) return nullptr;
+      return cache + (static_cast<int64_t>(b) * g.e_cap + j) * kMD;
+    }
+    const int64_t nn = m - g.W + (a - g.k);
+    if (nn < 0 || nn >= m) return nullptr;
+    if (chunk_win && nn >= c0 && nn - c0 < g.chunk_len)
+      return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (nn - c0)) * kMD;
+    return window + (static_cast<int64_t>(b) * g.w_cap + (nn % g.w_cap)) * kMD;
+  };
   v4f o[32];
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -327,9 +347,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   uint4 pre[8];
   int valid_next = 0;
   {
-    const int a = a_begin + se;
-    const uint16_t* src = (ok && a < a_end) ? slot_ptr<uint16_t>(g, row, b, m, a, cache, window, chunk_win)
-                                            : nullptr;
+    const uint16_t* src = src_of(a_begin + se);
     valid_next = src != nullptr;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -343,9 +361,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     if (sc8 == 0) valid_s[se] = valid_next;
     __syncthreads();
     if (a0 + kMTile < a_end) {  // prefetch the next tile while this one computes
-      const int a = a0 + kMTile + se;
-      const uint16_t* src = (ok && a < a_end) ? slot_ptr<uint16_t>(g, row, b, m, a, cache, window, chunk_win)
-                                              : nullptr;
+      const uint16_t* src = src_of(a0 + kMTile + se);
       valid_next = src != nullptr;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -807,6 +823,7 @@ Plan plan(const dsa_attn_args& a) {
     const int tiles = static_cast<int>(ceil_div(total, kMTile));
     int64_t runs = ceil_div(512, std::max<int64_t>(1, rows * hq));
     runs = std::max<int64_t>(1, std::min<int64_t>(runs, ceil_div(tiles, 2)));
+    runs = std::max<int64_t>(runs, ceil_div(tiles, kMRunSlots / kMTile));  // indices fit LDS
     const int tpr = static_cast<int>(ceil_div(tiles, runs));
     p.slots_per_run = tpr * kMTile;
     p.n_runs = static_cast<int>(ceil_div(tiles, tpr));

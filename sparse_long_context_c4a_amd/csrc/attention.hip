@@ -236,9 +236,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
 }
 
 // ----------------------------------------------------------- MFMA path
-// bf16, D = 512, heads in groups of 64 (4 waves x 16 heads).  A workgroup
-// takes one row and a run of slots; each tile of 32 gathered vectors is
-// staged once in LDS (row-major, 1056-byte pitch) and feeds both products:
+// bf16, D = 512, heads in groups of 64.  A workgroup takes one row and a run
+// of slots; each tile of 32 gathered vectors is staged once in LDS
+// (row-major, 1056-byte pitch) and feeds both products:
 //   S^T = K Q^T : A = 16 vectors x 32 dims (ds_read_b128 rows), B = the
 //                 wave's rotated query heads held in registers;
 //   O^T += V^T P^T : A = 16 dims x 32 vectors read with the gfx950 LDS
@@ -266,8 +266,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
+// Eight waves: wave w takes heads 16 (w % 4) .. +15 and dims 256 (w / 4) ..
+// +255, so each wave holds half a head group's query and output registers
+// (two waves per SIMD rather than one).  The logits are summed over the two
+// dim halves through LDS (the two partners add the same two partial sums,
+// so both see identical logits and probabilities); each wave then
+// accumulates its half of the dims.  The run's cache indices are read into
+// LDS once, so each tile's gather is one memory round trip; the next tile is
+// gathered into registers while one computes.
 template <bool kFinal>
-__global__ __launch_bounds__(256) void k_attn_mfma(
+__global__ __launch_bounds__(512) void k_attn_mfma8(
     AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
     const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
@@ -275,10 +283,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[kMTile * kMPitch];
   __shared__ float cs_s[kMD / 2][2];
   __shared__ int valid_s[kMTile];
-  __shared__ int32_t idx_s[kMRunSlots];  // the run's cache indices
+  __shared__ int32_t idx_s[kMRunSlots];
+  __shared__ v4f spart[8][2][64];  // each wave's partial logits
   const int row = blockIdx.y, hq = blockIdx.x, run = blockIdx.z;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, gq = lane >> 4;
+  const int n = lane & 15, gq = lane >> 4, hgw = wave & 3, dh = wave >> 2;
   const int64_t m = g.q_pos[row];
   const bool ok = m >= 0 && m < g.max_pos_end;
   if (!ok && tid == 0 && hq == 0 && run == 0) set_status(g.status, DSA_DEVERR_POSITION);
@@ -286,26 +295,25 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   const int total = g.k + g.W;
   const int a_begin = run * g.slots_per_run;
   const int a_end = min(total, a_begin + g.slots_per_run);
-  // the run's cache indices once, so that a tile's gather is one memory
-  // round trip (slots_per_run <= kMRunSlots by the plan)
-  for (int a = a_begin + tid; a < min(a_end, g.k); a += 256)
+  for (int a = a_begin + tid; a < min(a_end, g.k); a += 512)
     idx_s[a - a_begin] = g.idx[static_cast<int64_t>(row) * g.k + a];
   const int64_t c0 = chunk_win ? g.chunk_pos0[b] : 0;
-  for (int i = tid; i < half; i += 256) {
+  for (int i = tid; i < half; i += 512) {
     float c = 1.f, sn = 0.f;
     if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
     cs_s[i][0] = c;
     cs_s[i][1] = sn;
   }
   __syncthreads();
-  // query head h of this lane as the B operand: dims 32c + 8gq + (0..7)
-  const int h = hq * 64 + wave * 16 + n;
-  v8bf qb[16];
+  // query head h as the B operand, this wave's dim half: chunks c = 8 dh +
+  // cc, dims 32 c + 8 gq + (0..7)
+  const int h = hq * 64 + hgw * 16 + n;
+  v8bf qb[8];
   {
     const uint16_t* qrow = q + (static_cast<int64_t>(row) * g.H + h) * kMD;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int d0 = 32 * c + 8 * gq;
+    for (int cc = 0; cc < 8; ++cc) {
+      const int d0 = 32 * (8 * dh + cc) + 8 * gq;
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
       if (rotate_q && d0 + 8 > rot0) {
         uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -315,13 +323,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
           if (d >= rot0) {
             const float a0 = bf16_to_f32(static_cast<uint16_t>(wd[p] & 0xffffu));
             const float a1 = bf16_to_f32(static_cast<uint16_t>(wd[p] >> 16));
-            const float cc = cs_s[(d - rot0) / 2][0], ss = cs_s[(d - rot0) / 2][1];
-            wd[p] = pack_bf16x2(a0 * cc - a1 * ss, a0 * ss + a1 * cc);
+            const float cc2 = cs_s[(d - rot0) / 2][0], ss = cs_s[(d - rot0) / 2][1];
+            wd[p] = pack_bf16x2(a0 * cc2 - a1 * ss, a0 * ss + a1 * cc2);
           }
         }
         raw = uint4{wd[0], wd[1], wd[2], wd[3]};
       }
-      qb[c] = as_v8bf(raw);
+      qb[cc] = as_v8bf(raw);
     }
   }
   auto src_of = [&](int a) -> const uint16_t* {
@@ -337,50 +345,56 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (nn - c0)) * kMD;
     return window + (static_cast<int64_t>(b) * g.w_cap + (nn % g.w_cap)) * kMD;
   };
-  v4f o[32];
+  v4f o[16];
 #pragma unroll
-  for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 16; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float scale2 = g.scale * kLog2e;
-  // staging: thread t -> vector e = t / 8 of the tile, 16-byte chunks j*8 + t%8
-  const int se = tid >> 3, sc8 = tid & 7;
-  uint4 pre[8];
+  // staging: thread t -> vector t / 16 of the tile, 16-byte chunks 16 j + t % 16
+  const int se = tid >> 4, sc = tid & 15;
+  uint4 pre[4];
   int valid_next = 0;
   {
     const uint16_t* src = src_of(a_begin + se);
     valid_next = src != nullptr;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc8] : uint4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j)
+      pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 16 + sc] : uint4{0u, 0u, 0u, 0u};
   }
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const int te = (lane & 15) >> 2, tq = lane & 3;
   for (int a0 = a_begin; a0 < a_end; a0 += kMTile) {
     __syncthreads();  // the previous tile is no longer read
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 8 + sc8) * 16) = pre[j];
-    if (sc8 == 0) valid_s[se] = valid_next;
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 16 + sc) * 16) = pre[j];
+    if (sc == 0) valid_s[se] = valid_next;
     __syncthreads();
     if (a0 + kMTile < a_end) {  // prefetch the next tile while this one computes
       const uint16_t* src = src_of(a0 + kMTile + se);
       valid_next = src != nullptr;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc8] : uint4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j)
+        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 16 + sc] : uint4{0u, 0u, 0u, 0u};
     }
-    // S^T for vectors 0..15 (s0) and 16..31 (s1): lane holds vectors 4gq+i
+    // partial S^T over this wave's dims, vectors 0..15 (s0) and 16..31 (s1)
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int off = (32 * c + 8 * gq) * 2;
+    for (int cc = 0; cc < 8; ++cc) {
+      const int off = (32 * (8 * dh + cc) + 8 * gq) * 2;
       const v8bf k0 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + n * kMPitch + off));
       const v8bf k1 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 + n) * kMPitch + off));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[cc], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[cc], s1, 0, 0, 0);
     }
-    // logits in log2 units; the running max is raised lazily: the weights
-    // exp2(x - m_run) may reach 2^kLazy before the accumulators are
-    // rescaled, so most tiles need no rescale (the result is the same, the
-    // weights are only kept below 2^kLazy)
+    spart[wave][0][lane] = s0;
+    spart[wave][1][lane] = s1;
+    __syncthreads();
+    s0 += spart[wave ^ 4][0][lane];
+    s1 += spart[wave ^ 4][1][lane];
+    // log2 units; the running max is raised lazily: the weights
+    // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
+    // so most tiles need no rescale
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -398,7 +412,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       l_run *= corr;
       m_run = m_new;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) o[db] *= corr;
+      for (int db = 0; db < 16; ++db) o[db] *= corr;
     }
     float p[8], psum = 0.f;
 #pragma unroll
@@ -412,51 +426,48 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
                      static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
                      static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
-    // O^T += V^T P^T; transpose-load source: vector 4gq + e (and 16 + ...),
-    // dims 16 db + 4 q4 .. + 3, with e = (lane & 15) >> 2, q4 = lane & 3
-    const int te = (lane & 15) >> 2, tq = lane & 3;
-    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    // O^T += V^T P^T over this wave's dims
     lds_u8* lds_base = (lds_u8*)v_lds;
-    lds_u8* r_lo = lds_base + (4 * gq + te) * kMPitch + tq * 8;
-    lds_u8* r_hi = lds_base + (16 + 4 * gq + te) * kMPitch + tq * 8;
+    lds_u8* r_lo = lds_base + (4 * gq + te) * kMPitch + tq * 8 + dh * 512;
+    lds_u8* r_hi = lds_base + (16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
+    for (int db = 0; db < 16; ++db) {
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
       const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
     }
   }
-  // lane holds O^T[dims 16 db + 4gq + i][head h]
+  // lane holds O^T[dims 256 dh + 16 db + 4 gq + i][head h]
   if constexpr (kFinal) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     uint16_t* orow = out + (static_cast<int64_t>(row) * g.H + h) * kMD;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const int d = 16 * db + 4 * gq;
+    for (int db = 0; db < 16; ++db) {
+      const int d = 256 * dh + 16 * db + 4 * gq;
       float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int dd = d + 2 * pr;
         if (dd >= rot0) {  // R_m^{-1}
-          const float cc = cs_s[(dd - rot0) / 2][0], ss = cs_s[(dd - rot0) / 2][1];
+          const float cc2 = cs_s[(dd - rot0) / 2][0], ss = cs_s[(dd - rot0) / 2][1];
           const float a0 = v[2 * pr], a1 = v[2 * pr + 1];
-          v[2 * pr] = a0 * cc + a1 * ss;
-          v[2 * pr + 1] = -a0 * ss + a1 * cc;
+          v[2 * pr] = a0 * cc2 + a1 * ss;
+          v[2 * pr + 1] = -a0 * ss + a1 * cc2;
         }
       }
       *reinterpret_cast<uint2*>(orow + d) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
-    if (lse && gq == 0)
+    if (lse && gq == 0 && dh == 0)
       lse[static_cast<int64_t>(row) * g.H + h] =
           l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + run) * g.H + h;
 #pragma unroll
-    for (int db = 0; db < 32; ++db)
-      *reinterpret_cast<float4*>(part_acc + pi * kMD + 16 * db + 4 * gq) =
+    for (int db = 0; db < 16; ++db)
+      *reinterpret_cast<float4*>(part_acc + pi * kMD + 256 * dh + 16 * db + 4 * gq) =
           float4{o[db][0], o[db][1], o[db][2], o[db][3]};
-    if (gq == 0) {
+    if (gq == 0 && dh == 0) {
       part_ml[2 * pi] = m_run * kLn2;  // natural-log units for the merge
       part_ml[2 * pi + 1] = l_run;
     }
@@ -645,7 +656,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
       }
-      // log2 units, lazily raised running max (as in k_attn_mfma)
+      // log2 units; the running max is raised lazily: the weights
+    // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
+    // so most tiles need no rescale
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -895,13 +908,13 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
     } else if (p.mfma) {
       dim3 grid(static_cast<unsigned>(a.heads / 64), rows, p.n_runs);
       if (p.n_runs == 1)
-        launch_timed(k_attn_mfma<true>, grid, dim3(256), 0, st, ev0, ev1, g,
+        launch_timed(k_attn_mfma8<true>, grid, dim3(512), 0, st, ev0, ev1, g,
                      static_cast<const uint16_t*>(a.q), a.rotate_q,
                      static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                      static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
                      a.lse, part_acc, part_ml);
       else
-        launch_timed(k_attn_mfma<false>, grid, dim3(256), 0, st, ev0, nullptr, g,
+        launch_timed(k_attn_mfma8<false>, grid, dim3(512), 0, st, ev0, nullptr, g,
                      static_cast<const uint16_t*>(a.q), a.rotate_q,
                      static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                      static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),

@@ -253,7 +253,8 @@ constexpr int kMPitch = 1056;  // bytes per staged vector (1024 + 32 of padding)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 10.0f;  // log2 headroom of the lazily raised running max
-constexpr int kMRunSlots = 2048;  // slots per run of the MFMA path (indices held in LDS)
+constexpr int kMRunSlots = 2048;
+constexpr int kT8 = 64;  // vectors per staged tile of the eight-wave kernel  // slots per run of the MFMA path (indices held in LDS)
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -280,11 +281,11 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
     const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
     float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kMTile * kMPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kT8 * kMPitch];
   __shared__ float cs_s[kMD / 2][2];
-  __shared__ int valid_s[kMTile];
+  __shared__ int valid_s[kT8];
   __shared__ int32_t idx_s[kMRunSlots];
-  __shared__ v4f spart[8][2][64];  // each wave's partial logits
+  __shared__ v4f spart[8][kT8 / 16][64];  // each wave's partial logits
   const int row = blockIdx.y, hq = blockIdx.x, run = blockIdx.z;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4, hgw = wave & 3, dh = wave >> 2;
@@ -350,60 +351,64 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
   for (int db = 0; db < 16; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float scale2 = g.scale * kLog2e;
-  // staging: thread t -> vector t / 16 of the tile, 16-byte chunks 16 j + t % 16
-  const int se = tid >> 4, sc = tid & 15;
-  uint4 pre[4];
+  // staging: thread t -> vector t / 8 of the tile, 16-byte chunks 8 j + t % 8
+  const int se = tid >> 3, sc = tid & 7;
+  uint4 pre[8];
   int valid_next = 0;
   {
     const uint16_t* src = src_of(a_begin + se);
     valid_next = src != nullptr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 16 + sc] : uint4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 8; ++j)
+      pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc] : uint4{0u, 0u, 0u, 0u};
   }
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const int te = (lane & 15) >> 2, tq = lane & 3;
-  for (int a0 = a_begin; a0 < a_end; a0 += kMTile) {
+  constexpr int kNB = kT8 / 16;  // 16-vector blocks per tile
+  for (int a0 = a_begin; a0 < a_end; a0 += kT8) {
     __syncthreads();  // the previous tile is no longer read
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 16 + sc) * 16) = pre[j];
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 8 + sc) * 16) = pre[j];
     if (sc == 0) valid_s[se] = valid_next;
     __syncthreads();
-    if (a0 + kMTile < a_end) {  // prefetch the next tile while this one computes
-      const uint16_t* src = src_of(a0 + kMTile + se);
+    if (a0 + kT8 < a_end) {  // prefetch the next tile while this one computes
+      const uint16_t* src = src_of(a0 + kT8 + se);
       valid_next = src != nullptr;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 16 + sc] : uint4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 8; ++j)
+        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc] : uint4{0u, 0u, 0u, 0u};
     }
-    // partial S^T over this wave's dims, vectors 0..15 (s0) and 16..31 (s1)
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // partial S^T over this wave's dims: block i holds vectors 16 i .. +15
+    v4f sv[kNB];
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) sv[i] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const int off = (32 * (8 * dh + cc) + 8 * gq) * 2;
-      const v8bf k0 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + n * kMPitch + off));
-      const v8bf k1 = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 + n) * kMPitch + off));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[cc], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[cc], s1, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) {
+        const v8bf kv = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 * i + n) * kMPitch + off));
+        sv[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[cc], sv[i], 0, 0, 0);
+      }
     }
-    spart[wave][0][lane] = s0;
-    spart[wave][1][lane] = s1;
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) spart[wave][i][lane] = sv[i];
     __syncthreads();
-    s0 += spart[wave ^ 4][0][lane];
-    s1 += spart[wave ^ 4][1][lane];
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) sv[i] += spart[wave ^ 4][i][lane];
     // log2 units; the running max is raised lazily: the weights
     // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
     // so most tiles need no rescale
-    float x[8];
+    float x[4 * kNB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = valid_s[4 * gq + i] ? s0[i] * scale2 : -INFINITY;
-      x[4 + i] = valid_s[16 + 4 * gq + i] ? s1[i] * scale2 : -INFINITY;
-    }
+    for (int i = 0; i < kNB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[4 * i + e] = valid_s[16 * i + 4 * gq + e] ? sv[i][e] * scale2 : -INFINITY;
     float tmax = x[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    for (int i = 1; i < 4 * kNB; ++i) tmax = fmaxf(tmax, x[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     if (__any(tmax > m_run + kLazy)) {
@@ -414,28 +419,33 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
 #pragma unroll
       for (int db = 0; db < 16; ++db) o[db] *= corr;
     }
-    float p[8], psum = 0.f;
+    float p[4 * kNB], psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 * kNB; ++i) {
       p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
       psum += p[i];
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
-    const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
-                     static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
-                     static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
-    // O^T += V^T P^T over this wave's dims
-    lds_u8* lds_base = (lds_u8*)v_lds;
-    lds_u8* r_lo = lds_base + (4 * gq + te) * kMPitch + tq * 8 + dh * 512;
-    lds_u8* r_hi = lds_base + (16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
+    // O^T += V^T P^T over this wave's dims, 32 vectors per product: P of
+    // blocks 2 u and 2 u + 1 is the B operand
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
-      const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+    for (int u = 0; u < kNB / 2; ++u) {
+      const v8bf pb = {static_cast<__bf16>(p[8 * u + 0]), static_cast<__bf16>(p[8 * u + 1]),
+                       static_cast<__bf16>(p[8 * u + 2]), static_cast<__bf16>(p[8 * u + 3]),
+                       static_cast<__bf16>(p[8 * u + 4]), static_cast<__bf16>(p[8 * u + 5]),
+                       static_cast<__bf16>(p[8 * u + 6]), static_cast<__bf16>(p[8 * u + 7])};
+      lds_u8* lds_base = (lds_u8*)v_lds;
+      lds_u8* r_lo = lds_base + (32 * u + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
+      lds_u8* r_hi = lds_base + (32 * u + 16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
+        const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+      }
     }
   }
   // lane holds O^T[dims 256 dh + 16 db + 4 gq + i][head h]

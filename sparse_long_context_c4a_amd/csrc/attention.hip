@@ -41,6 +41,7 @@ struct AttnGeom {
   int slots_per_run, n_runs;
   const float* cs_tab;  // optional (cos, sin) of R_m per row, r floats per row
   uint32_t* status;
+  int rows;
 };
 
 // Source of slot a of row `row`; nullptr if the slot is empty.
@@ -486,23 +487,29 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
 
 // ------------------------------------------------------ decode-shaped path
 // bf16, D = 512, heads in groups of 16, few rows.  A workgroup takes one
-// row, 16 heads and a run of slots; its four waves take interleaved groups
-// of 32 slots.  Each wave gathers its own 32 vectors straight into LDS with
-// the gfx950 LDS DMA load (global_load_lds_dwordx4: one 1 KiB vector per
-// instruction, no registers on the way), computes S^T = K Q^T and
-// O^T += V^T P^T for its 16 heads exactly as the MFMA path above, and keeps
-// its own online-softmax state.  The four waves then merge in LDS.  A row
+// row, 16 heads and a run of slots; its kDecWaves waves take interleaved
+// groups of 32 slots.  Each wave gathers its own 32 vectors (16 bytes per
+// lane of each, through registers into its LDS tile), computes S^T = K Q^T
+// and O^T += V^T P^T for its 16 heads exactly as the MFMA path above, and
+// keeps its own online-softmax state.  The waves then merge in LDS.  A row
 // whose slots span several runs leaves one un-normalised partial
-// (max, sum, acc) per run, merged by k_attn_dcombine; the run-0 workgroup
-// also leaves the R_m table for it.
+// (max, sum, acc) per run, merged by k_attn_dcombine with the R_m table the
+// run-0 workgroup leaves.  (Merging in the same launch by the last workgroup
+// to arrive needs agent-scope release/acquire fences, whose L2 write-back
+// and invalidate cost more than the second launch.)
+//
+// Workgroup order: the head groups of one (row, run) read the same vectors,
+// so they are placed on one XCD (workgroup ids congruent mod 8; the
+// dispatcher deals ids round-robin over the 8 XCDs) and share its L2: a
+// block of 8 G ids holds 8 (row, run) pairs x G head groups.
 constexpr int kDH = 16;                       // heads per workgroup
 constexpr int kDStep = 32;                    // vectors per wave step
 constexpr int kDWaveBytes = kDStep * kMPitch; // 33,792 B of LDS per wave
 constexpr int kDOPitch = kMD + 4;             // floats per head row when merging waves
-constexpr int kDSlotsPerIter = 4 * kDStep;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+#ifndef DSA_DEC_WAVES
+#define DSA_DEC_WAVES 4
+#endif
+constexpr int kDecWaves = DSA_DEC_WAVES;      // waves (32-slot steps) per workgroup
 
 // Source of slot a of row `row` given its cache index j (read by the caller
 // for a < k); nullptr if the slot is empty.
@@ -529,27 +536,35 @@ __device__ __forceinline__ int32_t dslot_index(const AttnGeom& g, int row, int a
   return (a < a_end && a < g.k) ? g.idx[static_cast<int64_t>(row) * g.k + a] : -1;
 }
 
-// Issue the LDS DMA of one wave step: lane v < 32 holds the source of
-// vector v (a stand-in vector, whose probability will be zero, for empty
-// slots).  Returns the ballot of non-empty slots.
-__device__ __forceinline__ uint64_t gather_issue(const uint16_t* src, const uint16_t* dummy,
-                                                 int lane, uint8_t* wl) {
+// Load one wave step's vectors into registers: lane l holds bytes
+// [16 l, 16 l + 16) of vector v < 32 in stg[v] (a stand-in vector, whose
+// probability will be zero, for empty slots).  Plain loads: at a few
+// workgroups per chip the LDS DMA load takes about twice as long to land as
+// these do.  Returns the ballot of non-empty slots.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t gather_load(const uint16_t* src, const uint16_t* dummy,
+                                                int lane, u32x4 (&stg)[kDStep]) {
   const uint64_t vmask = __ballot(lane < kDStep && src != nullptr);
   if (vmask == 0) return 0;
   if (src == nullptr) src = dummy;
   const uint64_t sp = reinterpret_cast<uint64_t>(src);
   const uint32_t sp_lo = static_cast<uint32_t>(sp), sp_hi = static_cast<uint32_t>(sp >> 32);
-#pragma unroll 8
+#pragma unroll
   for (int v = 0; v < kDStep; ++v) {
-    // readlane returns int: go through uint32_t so the low word is not
-    // sign-extended into the high one
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_lo, v));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_hi, v));
     const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
-    const uint8_t* gp = reinterpret_cast<const uint8_t*>(base) + lane * 16;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)gp, (lds_void_t*)(wl + v * kMPitch), 16, 0, 0);
+    typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+    stg[v] = *reinterpret_cast<g_u32x4*>(base + static_cast<uint64_t>(lane) * 16);
   }
   return vmask;
+}
+
+// Write the staged vectors to the wave's LDS tile (vector v at row v).
+__device__ __forceinline__ void gather_store(const u32x4 (&stg)[kDStep], int lane, uint8_t* wl) {
+#pragma unroll
+  for (int v = 0; v < kDStep; ++v) *reinterpret_cast<u32x4*>(wl + v * kMPitch + lane * 16) = stg[v];
 }
 
 // Normalise, apply R_m^{-1} and store dims 4 d4 .. 4 d4 + 3 of one head.
@@ -570,17 +585,24 @@ __device__ __forceinline__ void store_head_dims4(float4 acc, float L, int d4, in
   *reinterpret_cast<uint2*>(orow + 4 * d4) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-__global__ __launch_bounds__(256) void k_attn_decode(
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_decode(
     AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
     const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
     float* __restrict__ part_ml, float* __restrict__ cs_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t dsm[4 * kDWaveBytes];
+  constexpr int NT = NW * 64, kSlotsPerIter = NW * kDStep;
+  constexpr int kQPer = kDH * 64 / NT;  // 16-byte pieces of the query tile per thread
+  __shared__ __attribute__((aligned(16))) uint8_t dsm[NW * kDWaveBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q_s[kDH * kMPitch];  // rotated q, head n at row n
   __shared__ float cs_s[kMD];  // (cos, sin) of pair i at 2i, 2i+1
-  __shared__ float ml_s[4][kDH][2];
+  __shared__ float ml_s[NW][kDH][2];
   __shared__ float hml_s[kDH][2];
-  const int run = blockIdx.x, hg = blockIdx.y, row = blockIdx.z;
-  const int G = gridDim.y;
+  const int G = g.H / kDH;
+  const int id = blockIdx.x;
+  const int pair = 8 * (id / (8 * G)) + (id & 7), hg = (id >> 3) % G;
+  if (pair >= g.rows * g.n_runs) return;
+  const int row = pair / g.n_runs, run = pair % g.n_runs;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
   const int total = g.k + g.W;
@@ -588,33 +610,36 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   const int a_end = min(total, a_begin + g.slots_per_run);
   int a0 = a_begin + wave * kDStep;
   // independent loads first: the first step's cache indices, the query
-  // position, the query heads hg*16 + n (dims 32c + 8gq .. +7, the B
-  // operand) and, when given, the R_m table
+  // position, the 16 heads' query rows (piece c = tid + NT i: head c / 64,
+  // dims 8 (c % 64) .. +7) and, when given, the R_m table
   int32_t jn = dslot_index(g, row, a0 + lane, a_end);
   const int64_t m = g.q_pos[row];
-  const int h = hg * kDH + n;
-  uint4 qraw[16];
+  uint4 qraw[kQPer];
   {
-    const uint4* qrow = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * g.H + h) * kMD);
+    const uint4* qrows = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * g.H + hg * kDH) * kMD);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qraw[c] = qrow[4 * c + gq];
+    for (int i = 0; i < kQPer; ++i) qraw[i] = qrows[tid + NT * i];
   }
   const int half = g.r / 2, rot0 = kMD - g.r;
-  if (g.cs_tab)
-    for (int i = tid; i < 2 * half; i += 256) cs_s[i] = g.cs_tab[static_cast<int64_t>(row) * g.r + i];
   const bool ok = m >= 0 && m < g.max_pos_end;
   if (!ok && tid == 0 && hg == 0 && run == 0) set_status(g.status, DSA_DEVERR_POSITION);
   uint8_t* wl = dsm + wave * kDWaveBytes;
   const uint16_t* dummy = q + static_cast<int64_t>(row) * g.H * kMD;
-  uint64_t vmask = 0;
+  // the first step's gather goes out before the set-up below; later steps
+  // load at the top of their iteration
+  uint64_t vmask0 = 0;
+  u32x4 stg0[kDStep];
   if (a0 < a_end) {
     const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
                               ? dslot_ptr(g, b, m, a0 + lane, jn, cache, window, chunk_win)
                               : nullptr;
-    vmask = gather_issue(src, dummy, lane, wl);
+    vmask0 = gather_load(src, dummy, lane, stg0);
   }
+  // (after the gather: its loads wait on every load issued before them)
+  if (g.cs_tab)
+    for (int i = tid; i < 2 * half; i += NT) cs_s[i] = g.cs_tab[static_cast<int64_t>(row) * g.r + i];
   if (!g.cs_tab)
-    for (int i = tid; i < half; i += 256) {
+    for (int i = tid; i < half; i += NT) {
       float c = 1.f, sn = 0.f;
       if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
       cs_s[2 * i] = c;
@@ -622,12 +647,11 @@ __global__ __launch_bounds__(256) void k_attn_decode(
     }
   __syncthreads();
   if (cs_out && !g.cs_tab && run == 0 && hg == 0)
-    for (int i = tid; i < 2 * half; i += 256) cs_out[static_cast<int64_t>(row) * g.r + i] = cs_s[i];
-  v8bf qb[16];
+    for (int i = tid; i < 2 * half; i += NT) cs_out[static_cast<int64_t>(row) * g.r + i] = cs_s[i];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int d0 = 32 * c + 8 * gq;
-    uint4 raw = qraw[c];
+  for (int i = 0; i < kQPer; ++i) {
+    const int c = tid + NT * i, d0 = 8 * (c & 63);
+    uint4 raw = qraw[i];
     if (rotate_q && d0 + 8 > rot0) {
       uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -642,8 +666,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(
       }
       raw = uint4{wd[0], wd[1], wd[2], wd[3]};
     }
-    qb[c] = as_v8bf(raw);
+    *reinterpret_cast<uint4*>(q_s + (c >> 6) * kMPitch + 2 * d0) = raw;
   }
+  __syncthreads();
   v4f o[32];
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -651,20 +676,22 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   const float scale2 = g.scale * kLog2e;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const int te = (lane & 15) >> 2, tq = lane & 3;
-  for (; a0 < a_end; a0 += kDSlotsPerIter) {
-    // next step's cache indices in flight during this step
-    const int nxt = a0 + kDSlotsPerIter;
-    jn = nxt < a_end ? dslot_index(g, row, nxt + lane, a_end) : -1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS DMA has landed
+  // one step: the staged vectors to the wave's tile, logits, online softmax,
+  // weighted sum
+  auto step = [&](const u32x4 (&stg)[kDStep], uint64_t vmask) {
     if (vmask != 0) {
+      // each wave reads only its own tile, so no barrier: LDS operations of
+      // one wave complete in order
+      gather_store(stg, lane, wl);
       v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         const int off = (32 * c + 8 * gq) * 2;
         const v8bf k0 = as_v8bf(*reinterpret_cast<const uint4*>(wl + n * kMPitch + off));
         const v8bf k1 = as_v8bf(*reinterpret_cast<const uint4*>(wl + (16 + n) * kMPitch + off));
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c], s1, 0, 0, 0);
+        const v8bf qb = as_v8bf(*reinterpret_cast<const uint4*>(q_s + n * kMPitch + off));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb, s1, 0, 0, 0);
       }
       // log2 units; the running max is raised lazily: the weights
     // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
@@ -710,15 +737,23 @@ __global__ __launch_bounds__(256) void k_attn_decode(
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
       }
     }
-    vmask = 0;
-    if (nxt < a_end) {
-      const uint16_t* src = (ok && nxt + lane < a_end && lane < kDStep)
-                                ? dslot_ptr(g, b, m, nxt + lane, jn, cache, window, chunk_win)
+  };
+  if (a0 < a_end) {
+    // next step's cache indices in flight during this step
+    jn = a0 + kSlotsPerIter < a_end ? dslot_index(g, row, a0 + kSlotsPerIter + lane, a_end) : -1;
+    step(stg0, vmask0);
+    for (a0 += kSlotsPerIter; a0 < a_end; a0 += kSlotsPerIter) {
+      u32x4 stg[kDStep];
+      const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
+                                ? dslot_ptr(g, b, m, a0 + lane, jn, cache, window, chunk_win)
                                 : nullptr;
-      vmask = gather_issue(src, dummy, lane, wl);
+      const uint64_t vmask = gather_load(src, dummy, lane, stg);
+      const int nxt = a0 + kSlotsPerIter;
+      jn = nxt < a_end ? dslot_index(g, row, nxt + lane, a_end) : -1;
+      step(stg, vmask);
     }
   }
-  // merge the four waves (natural-log units from here on): lane holds
+  // merge the NW waves (natural-log units from here on): lane holds
   // O^T[dims 16 db + 4 gq + i][head n]
   m_run *= kLn2;
   if (gq == 0) {
@@ -729,9 +764,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   if (tid < kDH) {  // per head: the block's max and sum over its waves
     float M = -INFINITY, L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[w][tid][0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_s[w][tid][0]);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = ml_s[w][tid][0];
       if (mw != -INFINITY) L += ml_s[w][tid][1] * expf(mw - M);
     }
@@ -741,7 +776,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[w][n][0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_s[w][n][0]);
     const float cw = (m_run == -INFINITY) ? 0.f : expf(m_run - M);
     float* ow = reinterpret_cast<float*>(wl);
 #pragma unroll
@@ -750,16 +785,15 @@ __global__ __launch_bounds__(256) void k_attn_decode(
           float4{o[db][0] * cw, o[db][1] * cw, o[db][2] * cw, o[db][3] * cw};
   }
   __syncthreads();
-  // thread -> dims 4 d4 .. +3 of heads hp, hp + 2, ..., hp + 14
-  const int d4 = tid & 127, hp = tid >> 7;
+  // thread -> dims 4 d4 .. +3 of heads ch = (tid + NT i) / 128
   const int64_t pbase = (static_cast<int64_t>(row) * G + hg) * g.n_runs + run;
 #pragma unroll 2
-  for (int i = 0; i < kDH / 2; ++i) {
-    const int ch = hp + 2 * i;
+  for (int it = tid; it < 128 * kDH; it += NT) {
+    const int d4 = it & 127, ch = it >> 7;
     const float M = hml_s[ch][0], L = hml_s[ch][1];
     float4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float4 u = *reinterpret_cast<const float4*>(
           reinterpret_cast<const float*>(dsm + w * kDWaveBytes) + ch * kDOPitch + 4 * d4);
       t.x += u.x;
@@ -784,35 +818,63 @@ __global__ __launch_bounds__(256) void k_attn_decode(
 }
 
 // Merge the runs of one (row, head) pair of heads of the decode-shaped path
-// and apply R_m^{-1} (table left by the run-0 workgroup).  Thread -> head
-// 2 blockIdx.x + tid / 128, dims 4 (tid % 128) .. +3.
-__global__ __launch_bounds__(256) void k_attn_dcombine(AttnGeom g, const float* __restrict__ part_acc,
+// and apply R_m^{-1} (table left by the run-0 workgroup).  Workgroup ->
+// (head blockIdx.x, row blockIdx.y), thread -> dims 4 tid .. +3.  The
+// partials of up to kCombR runs are loaded together (one memory round
+// trip), then merged with a running log-sum-exp; longer rows take several
+// such rounds.
+constexpr int kCombR = 16;
+
+__global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const float* __restrict__ cs_in,
                                                        uint16_t* __restrict__ out,
                                                        float* __restrict__ lse) {
   __shared__ float cs_s[kMD];
   const int row = blockIdx.y, tid = threadIdx.x;
-  const int h = 2 * blockIdx.x + (tid >> 7), d4 = tid & 127;
+  const int h = blockIdx.x, d4 = tid;
   const int hg = h / kDH, ch = h % kDH, G = g.H / kDH;
   const float* cs_src = g.cs_tab ? g.cs_tab : cs_in;
-  for (int i = tid; i < g.r; i += 256) cs_s[i] = cs_src[static_cast<int64_t>(row) * g.r + i];
+  for (int i = tid; i < g.r; i += 128) cs_s[i] = cs_src[static_cast<int64_t>(row) * g.r + i];
   const int64_t p0 = (static_cast<int64_t>(row) * G + hg) * g.n_runs;
-  float M = -INFINITY;
-  for (int r = 0; r < g.n_runs; ++r) M = fmaxf(M, part_ml[2 * ((p0 + r) * kDH + ch)]);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float4 t = {0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < g.n_runs; ++r) {
-    // an empty run left max -inf, sum 0 and acc 0
-    const int64_t pi = (p0 + r) * kDH + ch;
-    const float mr = part_ml[2 * pi];
-    const float wgt = mr == -INFINITY ? 0.f : expf(mr - M);
-    L += wgt * part_ml[2 * pi + 1];
-    const float4 u = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
-    t.x = fmaf(wgt, u.x, t.x);
-    t.y = fmaf(wgt, u.y, t.y);
-    t.z = fmaf(wgt, u.z, t.z);
-    t.w = fmaf(wgt, u.w, t.w);
+  for (int r0 = 0; r0 < g.n_runs; r0 += kCombR) {
+    float mr[kCombR], lr[kCombR];
+    float4 u[kCombR];
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      // an empty run left max -inf, sum 0 and acc 0; runs past the end are empty
+      mr[q] = -INFINITY;
+      lr[q] = 0.f;
+      u[q] = float4{0.f, 0.f, 0.f, 0.f};
+      if (r0 + q < g.n_runs) {
+        const int64_t pi = (p0 + r0 + q) * kDH + ch;
+        mr[q] = part_ml[2 * pi];
+        lr[q] = part_ml[2 * pi + 1];
+        u[q] = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) Mn = fmaxf(Mn, mr[q]);
+    if (Mn == -INFINITY) continue;
+    const float c = M == -INFINITY ? 0.f : expf(M - Mn);
+    L *= c;
+    t.x *= c;
+    t.y *= c;
+    t.z *= c;
+    t.w *= c;
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      const float wgt = mr[q] == -INFINITY ? 0.f : expf(mr[q] - Mn);
+      L = fmaf(wgt, lr[q], L);
+      t.x = fmaf(wgt, u[q].x, t.x);
+      t.y = fmaf(wgt, u[q].y, t.y);
+      t.z = fmaf(wgt, u[q].z, t.z);
+      t.w = fmaf(wgt, u[q].w, t.w);
+    }
+    M = Mn;
   }
   __syncthreads();
   store_head_dims4(t, L, d4, kMD - g.r, cs_s, out + (static_cast<int64_t>(row) * g.H + h) * kMD);
@@ -833,12 +895,12 @@ Plan plan(const dsa_attn_args& a) {
   p.dec = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048;
   p.mfma = !p.dec && bf16_512 && a.heads % 64 == 0;
   if (p.dec) {
-    // about 1024 workgroups: runs of whole 128-slot iterations
+    // about 1024 workgroups: runs of whole NW x 32-slot iterations
     const int64_t pairs = rows * (a.heads / kDH);
-    const int64_t iters_total = ceil_div(total, kDSlotsPerIter);
+    const int64_t iters_total = ceil_div(total, kDecWaves * kDStep);
     const int64_t rmax = std::max<int64_t>(1, ceil_div(1024, pairs));
     const int64_t iters = ceil_div(iters_total, rmax);
-    p.slots_per_run = static_cast<int>(iters * kDSlotsPerIter);
+    p.slots_per_run = static_cast<int>(iters * kDecWaves * kDStep);
     p.n_runs = static_cast<int>(ceil_div(total, p.slots_per_run));
   } else if (p.mfma) {
     // about 512 workgroups over the chip, at least two tiles per run
@@ -895,6 +957,7 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.cs_tab = lx.cs_tab;
   g.status = a.status;
   const int rows = a.n_seqs * a.queries_per_seq;
+  g.rows = rows;
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
@@ -903,15 +966,17 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   if constexpr (sizeof(T) == 2) {
     if (p.dec) {
       float* cs_ws = p.n_runs > 1 ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
-      dim3 grid(static_cast<unsigned>(p.n_runs), static_cast<unsigned>(a.heads / kDH), rows);
-      launch_timed(k_attn_decode, grid, dim3(256), 0, st, ev0, p.n_runs > 1 ? nullptr : ev1, g,
+      const int64_t G = a.heads / kDH, pairs = static_cast<int64_t>(rows) * p.n_runs;
+      const dim3 grid(static_cast<unsigned>(ceil_div(pairs, 8) * 8 * G));
+      launch_timed(k_attn_decode<kDecWaves>, grid, dim3(kDecWaves * 64), 0, st, ev0,
+                   p.n_runs > 1 ? nullptr : ev1, g,
                    static_cast<const uint16_t*>(a.q), a.rotate_q,
                    static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                    static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out), a.lse,
                    part_acc, part_ml, cs_ws);
       dsa_status rc = hip_check(hipGetLastError(), "k_attn_decode launch");
       if (rc != DSA_OK || p.n_runs == 1) return rc;
-      launch_timed(k_attn_dcombine, dim3(a.heads / 2, rows), dim3(256), 0, st, nullptr, ev1, g,
+      launch_timed(k_attn_dcombine, dim3(a.heads, rows), dim3(128), 0, st, nullptr, ev1, g,
                    static_cast<const float*>(part_acc), static_cast<const float*>(part_ml),
                    static_cast<const float*>(cs_ws), static_cast<uint16_t*>(a.out), a.lse);
       return hip_check(hipGetLastError(), "k_attn_dcombine launch");

@@ -151,6 +151,17 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   __shared__ uint32_t red[3][kSelWaves];
   __shared__ uint32_t pos_above, pos_bin, n_tmp;
   const int row = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
+  // the candidates and wave thresholds do not depend on the row's position:
+  // their loads go out with the position's, one memory round trip for all
+  const int slots = nw * cap;  // <= kFinalCap by construction
+  const uint32_t* mrow = meta + static_cast<int64_t>(row) * nw;
+  const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
+  constexpr int kPer = kFinalCap / kSel;
+  uint64_t v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) v[u] = t + u * kSel < slots ? crow[t + u * kSel] : 0ull;
+  uint32_t tm = 0;
+  for (int b = t; b < nw; b += kSel) tm = max(tm, mrow[b]);
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
   const int64_t nv = ri.nv;
   float* srow = scores + static_cast<int64_t>(row) * ld_scores;
@@ -170,15 +181,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     emit_all_visible(srow, nv, k, irow, orow);
     return;
   }
-  const int slots = nw * cap;  // <= kFinalCap by construction
-  const uint32_t* mrow = meta + static_cast<int64_t>(row) * nw;
-  const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
-  constexpr int kPer = kFinalCap / kSel;
-  uint64_t v[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = t + u * kSel < slots ? crow[t + u * kSel] : 0ull;
-  uint32_t tm = 0, lo = 0xffffffffu, hi = 0u;
-  for (int b = t; b < nw; b += kSel) tm = max(tm, mrow[b]);
+  uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (v[u] != 0) {
@@ -230,17 +233,37 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   const Bin br = find_bin_desc<2>(local, 2047u, static_cast<uint32_t>(k));
   const uint32_t B = br.b, above = br.above, at = br.at;
   const bool fits = at <= static_cast<uint32_t>(kTmpCap);
+  // places for the wave's entries above the bin and in it: the ballots of
+  // all kPer values first, then one LDS counter update per kind and wave
+  uint64_t bu[kPer], bm[kPer];
+  uint32_t nu = 0, nm = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const uint32_t bin = (static_cast<uint32_t>(v[u] >> 32) - lo) >> shift;
+    bu[u] = __ballot(v[u] != 0 && bin > B);
+    bm[u] = __ballot(v[u] != 0 && bin == B);
+    nu += static_cast<uint32_t>(__popcll(bu[u]));
+    nm += static_cast<uint32_t>(__popcll(bm[u]));
+  }
+  uint32_t pu = 0, pm = 0;
+  if (l == 0) {
+    if (nu) pu = atomicAdd(&pos_above, nu);
+    if (nm) pm = atomicAdd(&n_tmp, nm);
+  }
+  pu = static_cast<uint32_t>(__shfl(static_cast<int>(pu), 0, 64));
+  pm = static_cast<uint32_t>(__shfl(static_cast<int>(pm), 0, 64));
+  const uint64_t below = (1ull << l) - 1ull;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const uint64_t x = v[u];
-    const uint32_t bin = (static_cast<uint32_t>(x >> 32) - lo) >> shift;
-    const bool up = x != 0 && bin > B;
-    const uint32_t p = wave_alloc(up, &pos_above);
+    const bool up = (bu[u] >> l) & 1ull, mid = (bm[u] >> l) & 1ull;
+    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu[u] & below));
     if (up && p < above) emit(irow, orow, p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
-    const bool mid = x != 0 && bin == B;
-    const uint32_t q = wave_alloc(mid, &n_tmp);
+    const uint32_t q = pm + static_cast<uint32_t>(__popcll(bm[u] & below));
     if (mid && fits) tmp_s[q] = x;
     if (!fits) cand_s[t + u * kSel] = mid ? x : 0ull;  // only the bin's members
+    pu += static_cast<uint32_t>(__popcll(bu[u]));
+    pm += static_cast<uint32_t>(__popcll(bm[u]));
   }
   __syncthreads();
   const uint32_t need = static_cast<uint32_t>(k) - above;

@@ -78,7 +78,8 @@ constexpr int kMTargetWGs = 768;                     // three per compute unit
 constexpr int kMScaleOne = 127;                      // E8M0 code of 1
 constexpr int kPSelT = 256;                          // select threads per row
 constexpr int kPCandCap = 3072;                      // candidates held in LDS
-constexpr int kPTmpCap = 512;
+constexpr int kPTmpCap = 256;                        // threshold-bin members held in LDS
+// (select's LDS stays under 40 KiB, so four rows run per compute unit)
 
 struct PArgs {
   const uint8_t* q;
@@ -690,7 +691,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kPSelT) void k_pidx_select(PArgs a, float* __restrict__ scores,
+__global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_pidx_select(PArgs a, float* __restrict__ scores,
                                                         int64_t ld_scores,
                                                         int32_t* __restrict__ idx_out) {
   __shared__ uint64_t cand_s[kPCandCap];
@@ -764,9 +765,10 @@ __global__ __launch_bounds__(kPSelT) void k_pidx_select(PArgs a, float* __restri
   if (ok) {
     const int ct = static_cast<int>((cnt + 15) / 16);
     uint32_t c_ge = 0;
-    // four tiles per step: their indices, then their keys, then the math,
-    // so that a step costs two memory round trips
-    constexpr int kU = 4;
+    // six tiles per step: their indices, then their keys, then the math,
+    // so that a step costs one memory round trip (the indices are in LDS);
+    // six keeps the kernel within 128 VGPRs (four waves per SIMD)
+    constexpr int kU = 6;
     for (int t0 = wave; t0 < ct; t0 += kU * kW) {
       int64_t j[kU];
 #pragma unroll

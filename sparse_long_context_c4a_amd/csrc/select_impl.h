@@ -216,16 +216,41 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
   const Bin br = find_bin_desc<kPer, NT>(local, 2047u, k);
   const uint32_t B = br.b, above = br.above, at = br.at;
   const bool fits = at <= static_cast<uint32_t>(kTmp);
-  for (int i0 = 0; i0 < n; i0 += NT) {
-    const int i = i0 + t;
+  // places: count the wave's entries above the bin and in it over all of
+  // its passes, take them with one LDS counter update per kind, then emit
+  const int l = t & 63;
+  const uint64_t below = (1ull << l) - 1ull;
+  auto classify = [&](int i, bool* up, bool* mid) {
     const uint64_t v = i < n ? c[i] : 0ull;
     const uint32_t bin = (static_cast<uint32_t>(v >> 32) - lo) >> shift;
-    const bool up = v != 0 && bin > B;
-    const uint32_t p = wave_alloc(up, &pos_above);
+    *up = v != 0 && bin > B;
+    *mid = v != 0 && bin == B && fits;
+    return v;
+  };
+  uint32_t nu = 0, nm = 0;
+  for (int i0 = 0; i0 < n; i0 += NT) {
+    bool up, mid;
+    classify(i0 + t, &up, &mid);
+    nu += static_cast<uint32_t>(__popcll(__ballot(up)));
+    nm += static_cast<uint32_t>(__popcll(__ballot(mid)));
+  }
+  uint32_t pu = 0, pm = 0;
+  if (l == 0) {
+    if (nu) pu = atomicAdd(&pos_above, nu);
+    if (nm) pm = atomicAdd(&n_tmp, nm);
+  }
+  pu = static_cast<uint32_t>(__shfl(static_cast<int>(pu), 0, 64));
+  pm = static_cast<uint32_t>(__shfl(static_cast<int>(pm), 0, 64));
+  for (int i0 = 0; i0 < n; i0 += NT) {
+    bool up, mid;
+    const uint64_t v = classify(i0 + t, &up, &mid);
+    const uint64_t bu = __ballot(up), bm = __ballot(mid);
+    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu & below));
     if (up && p < above) emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
-    const bool mid = v != 0 && bin == B && fits;
-    const uint32_t q = wave_alloc(mid, &n_tmp);
+    const uint32_t q = pm + static_cast<uint32_t>(__popcll(bm & below));
     if (mid) tmp[q] = v;
+    pu += static_cast<uint32_t>(__popcll(bu));
+    pm += static_cast<uint32_t>(__popcll(bm));
   }
   __syncthreads();
   const uint32_t need = k - above;

@@ -256,13 +256,10 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const uint64_t x = v[u];
-    const bool up = (bu[u] >> l) & 1ull, mid = (bm[u] >> l) & 1ull;
-    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu[u] & below));
-    if (up && p < above) emit(irow, orow, p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
+    const bool mid = (bm[u] >> l) & 1ull;
     const uint32_t q = pm + static_cast<uint32_t>(__popcll(bm[u] & below));
     if (mid && fits) tmp_s[q] = x;
     if (!fits) cand_s[t + u * kSel] = mid ? x : 0ull;  // only the bin's members
-    pu += static_cast<uint32_t>(__popcll(bu[u]));
     pm += static_cast<uint32_t>(__popcll(bm[u]));
   }
   __syncthreads();
@@ -283,6 +280,16 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
                                                [](uint64_t x) { return x != 0; });
     for (int i = t; i < kFinalCap; i += kSel)
       if (cand_s[i] != 0 && cand_s[i] >= cut) out_bin(cand_s[i]);
+  }
+  // the entries above the bin go out last, after every barrier: a barrier
+  // waits for the workgroup's outstanding global stores
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const uint64_t x = v[u];
+    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu[u] & below));
+    if (((bu[u] >> l) & 1ull) && p < above)
+      emit(irow, orow, p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
+    pu += static_cast<uint32_t>(__popcll(bu[u]));
   }
 }
 

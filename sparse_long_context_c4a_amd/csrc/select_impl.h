@@ -184,7 +184,9 @@ __device__ __forceinline__ void emit_all_visible(const float* srow, int64_t nv, 
 // c[] (LDS; 0 = empty slot), emitted to positions 0..k-1 in no particular
 // order.  A 2048-bin histogram over the keys' own range finds the bin
 // holding the k-th; entries above it go out directly, the bin's entries are
-// resolved exactly.  tmp: kTmp u64 of LDS; hist: 2048 u32 of LDS.
+// resolved exactly.  tmp: kTmp u64 of LDS; hist: 2048 u32 of LDS.  Ends
+// without a barrier (its last stores are the emits): a caller that goes on
+// to reuse c, tmp or hist synchronises first.
 constexpr int kTmpCap = 1024;
 
 template <int NT = kSel, int kTmp = kTmpCap>
@@ -244,12 +246,9 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
   for (int i0 = 0; i0 < n; i0 += NT) {
     bool up, mid;
     const uint64_t v = classify(i0 + t, &up, &mid);
-    const uint64_t bu = __ballot(up), bm = __ballot(mid);
-    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu & below));
-    if (up && p < above) emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+    const uint64_t bm = __ballot(mid);
     const uint32_t q = pm + static_cast<uint32_t>(__popcll(bm & below));
     if (mid) tmp[q] = v;
-    pu += static_cast<uint32_t>(__popcll(bu));
     pm += static_cast<uint32_t>(__popcll(bm));
   }
   __syncthreads();
@@ -277,7 +276,16 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
     for (int i = t; i < n; i += NT)
       if (in_bin(c[i]) && c[i] >= cut) out_bin(c[i]);
   }
-  __syncthreads();
+  // the entries above the bin go out last, after every barrier: a barrier
+  // waits for the workgroup's outstanding global stores
+  for (int i0 = 0; i0 < n; i0 += NT) {
+    bool up, mid;
+    const uint64_t v = classify(i0 + t, &up, &mid);
+    const uint64_t bu = __ballot(up);
+    const uint32_t p = pu + static_cast<uint32_t>(__popcll(bu & below));
+    if (up && p < above) emit(irow, orow, p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+    pu += static_cast<uint32_t>(__popcll(bu));
+  }
 }
 
 // Visit the first nv scores of a row (read as float4; ld_scores is a

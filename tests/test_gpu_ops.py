@@ -311,6 +311,12 @@ ATTN_CASES = [
     ("bf16_chunk_window", "bf16", 64, 512, 64, 128, 1, 40, list(range(2000, 2040)), 1.0, 1, True),
     ("f32_odd_heads", "f32", 20, 64, 16, 16, 2, 1, [500, 40], 0.7, 1, False),
     ("bf16_empty_set", "bf16", 64, 512, 64, 32, 1, 1, [0], 0.0, 1, False),
+    # more than 512 rows of 64 heads take the matrix-core path: one run per
+    # row, and (k + W > 2048 slots) two runs merged by the combine kernel
+    ("bf16_mfma_rows520", "bf16", 64, 512, 64, 512, 1, 520, list(range(20000, 20520)), 0.95, 1,
+     True),
+    ("bf16_mfma_two_runs", "bf16", 64, 512, 64, 2048, 1, 520, list(range(20000, 20520)), 0.95, 1,
+     False),
 ]
 
 
@@ -350,7 +356,10 @@ def test_sparse_attn(case):
     L.sparse_attn(a)
     torch.cuda.synchronize()
     got, gl = to_np(out), lse.cpu().numpy()
-    for i, m in enumerate(positions):
+    # every row of the small cases; first, last and spread rows of the large
+    check = range(rows) if rows <= 64 else sorted({0, 1, 17, rows // 2, rows - 2, rows - 1})
+    for i in check:
+        m = positions[i]
         b = i // Tq
         ent = decode_store(cache[b], dt)
         wv = decode_store(win[b], dt)

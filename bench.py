@@ -128,7 +128,9 @@ def time_layer(w, sets, steps, warmup, decode):
         a.ev_index[0] = a.ev_index[1] = a.ev_attn[0] = a.ev_attn[1] = None
     st = [o[3].item() for o in outs]
     assert all(s == 0 for s in st), f"device status {st}"
-    idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / steps
+    # (a workload without an indexer, k >= every n_vis, never records the
+    # indexer's events)
+    idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / steps if w.Hi else None
     attn_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_a) / steps
     return ms, idx_ms, attn_ms
 
@@ -225,8 +227,17 @@ def main():
     qps = w.B / (ms / 1e3)
     step_bytes = w.B * decode_bytes_per_query(w, nv)
     gbps = step_bytes / (ms / 1e3) / 1e9
-    idx_bytes = w.B * nv * (w.Di + 4)
-    idx_gbps = idx_bytes / (idx_ms / 1e3) / 1e9 if idx_ms > 0 else None
+    if w.Hi:
+        # the dominant kernel: the indexer's stream over the visible keys
+        kern, kbytes, kms = "k_decode_index", w.B * nv * (w.Di + 4), idx_ms
+    else:
+        # no indexer (the selection is every visible entry): the attention
+        # kernels' gather of the n_vis + W vectors, q and out
+        el = 2 if w.main_dtype == "bf16" else 4
+        kern = "k_attn_decode+k_attn_dcombine"
+        kbytes = w.B * ((min(w.k, nv) + min(w.W, w.m)) * w.D * el + 2 * w.H * w.D * el)
+        kms = attn_ms
+    kgbps = kbytes / (kms / 1e3) / 1e9 if kms else None
     line = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -237,10 +248,10 @@ def main():
                    "indexer_heads": w.Hi, "indexer_dim": w.Di, "input_sets": args.sets},
         "hbm_gbps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS, "alg_bytes_per_step": step_bytes,
         "kernel_ms": {"indexer": idx_ms, "attention": attn_ms},
-        "roofline": {"bound": "hbm", "achieved": idx_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": idx_gbps / PEAK_HBM_GBPS if idx_gbps else None,
+        "roofline": {"bound": "hbm", "achieved": kgbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": kgbps / PEAK_HBM_GBPS if kgbps else None,
                      "traffic": measured_traffic() if w.name == "c4a_decode_B4_L1M" else None,
-                     "kernel": "k_decode_index", "alg_bytes_per_launch": idx_bytes},
+                     "kernel": kern, "alg_bytes_per_launch": kbytes},
     }
     del sets
     torch.cuda.empty_cache()

@@ -22,6 +22,29 @@ constexpr int kCompressThreads = 256;
 constexpr int kCompressMaxSpan = 256;
 constexpr int kCompressPairs = 4;  // D <= 2048
 
+// Dims 2 pr and 2 pr + 1 of a raw token row as one load (a 32-bit word of
+// two bf16, or two f32), widened to f32 when used.
+template <typename T>
+struct PairWord;
+template <>
+struct PairWord<uint16_t> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ type load(const uint16_t* row, int pr) {
+    return *reinterpret_cast<const uint32_t*>(row + 2 * pr);
+  }
+  static __device__ __forceinline__ float first(type v) { return __uint_as_float(v << 16); }
+  static __device__ __forceinline__ float second(type v) { return __uint_as_float(v & 0xffff0000u); }
+};
+template <>
+struct PairWord<float> {
+  typedef float2 type;
+  static __device__ __forceinline__ type load(const float* row, int pr) {
+    return *reinterpret_cast<const float2*>(row + 2 * pr);
+  }
+  static __device__ __forceinline__ float first(type v) { return v.x; }
+  static __device__ __forceinline__ float second(type v) { return v.y; }
+};
+
 template <typename RawT, int kOut>
 __device__ __forceinline__ void compress_one(
     int e, int b, const RawT* __restrict__ raw, const RawT* __restrict__ ring,
@@ -66,16 +89,46 @@ __device__ __forceinline__ void compress_one(
   for (int k = 0; k < kCompressPairs; ++k) acc[k][0] = acc[k][1] = 0.f;
   const RawT* rawb = raw + static_cast<int64_t>(b) * T * D;
   const RawT* ringb = ring + static_cast<int64_t>(b) * S * D;
-  for (int i = 0; i < S; ++i) {
-    const int64_t p = static_cast<int64_t>(s) * j + i;
-    const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + (p % S) * D;
-    const float wi = w_s[i] * inv;
+  if (npairs <= kCompressThreads) {
+    // one dim pair per thread (D <= 512): 16 tokens per round, their loads
+    // all out before the first is used (unconditional: past the span the
+    // last token is re-read with weight 0; ring slots stepped in 32 bits),
+    // so a span of S tokens costs about S / 16 memory round trips (one per
+    // token would make the 128-token c128a entry latency-bound)
+    constexpr int kTok = 16;
+    using PW = PairWord<RawT>;
+    const int pr = tid < npairs ? tid : 0;
+    const int64_t pj = static_cast<int64_t>(s) * j;  // the entry's first raw position
+    const int ring0 = static_cast<int>(pj % S);
+    for (int i0 = 0; i0 < S; i0 += kTok) {
+      typename PW::type xw[kTok];
 #pragma unroll
-    for (int k = 0; k < kCompressPairs; ++k) {
-      const int pr = tid + k * kCompressThreads;
-      if (pr < npairs) {
-        acc[k][0] = fmaf(wi, load_as_f32(row, 2 * pr), acc[k][0]);
-        acc[k][1] = fmaf(wi, load_as_f32(row, 2 * pr + 1), acc[k][1]);
+      for (int u = 0; u < kTok; ++u) {
+        const int i = min(i0 + u, S - 1);
+        const int64_t p = pj + i;
+        const int slot = ring0 + i < S ? ring0 + i : ring0 + i - S;
+        const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + static_cast<int64_t>(slot) * D;
+        xw[u] = PW::load(row, pr);
+      }
+#pragma unroll
+      for (int u = 0; u < kTok; ++u) {
+        const float wi = i0 + u < S ? w_s[i0 + u] * inv : 0.f;
+        acc[0][0] = fmaf(wi, PW::first(xw[u]), acc[0][0]);
+        acc[0][1] = fmaf(wi, PW::second(xw[u]), acc[0][1]);
+      }
+    }
+  } else {
+    for (int i = 0; i < S; ++i) {
+      const int64_t p = static_cast<int64_t>(s) * j + i;
+      const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + (p % S) * D;
+      const float wi = w_s[i] * inv;
+#pragma unroll
+      for (int k = 0; k < kCompressPairs; ++k) {
+        const int pr = tid + k * kCompressThreads;
+        if (pr < npairs) {
+          acc[k][0] = fmaf(wi, load_as_f32(row, 2 * pr), acc[k][0]);
+          acc[k][1] = fmaf(wi, load_as_f32(row, 2 * pr + 1), acc[k][1]);
+        }
       }
     }
   }

@@ -21,8 +21,8 @@ namespace {
 //     ||k8_j|| over a slice of the sequence's entries (the slice's largest
 //     value); per row the error scale beta (below) and the threshold theta,
 //     the r-th largest approximate score over a sample of whole 16-entry
-//     tiles (r = 2k scaled to the sample, plus 8), rounded down to 16 key
-//     bits.
+//     tiles (r = 2k scaled to the sample, plus 8), rounded down to a 2^-16
+//     fraction of the row's sampled key range.
 //  k_pidx_main  (one workgroup per kMRows rows and a range of entry tiles;
 //     the range's keys pass through LDS once for all of those rows): per
 //     row and 16-entry tile, the fp8 MFMA with an E8M0 scale of 2^-9 gives
@@ -349,8 +349,11 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
     }
   }
   __syncthreads();
-  // theta: the r-th largest sampled key of each row, to 16 bits (two 8-bit
-  // histogram passes); 32 threads per row.  A valid key is never 0.
+  // theta: the r-th largest sampled key of each row, rounded down to a
+  // 2^-16 fraction of the row's own key range [lo, hi] (two 8-bit histogram
+  // passes over (key - lo), so the bins spread over the keys present rather
+  // than over the few exponents they share); 32 threads per row.  A valid
+  // key is never 0.
   const int q = tid / 32, l32 = tid % 32;
   int64_t nvq = 0;  // (r.nv is a register array: no dynamic index)
   if (q < t.nq) {
@@ -358,21 +361,41 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
                                 a.max_pos_end, nullptr, false);
     nvq = ri.ok ? ri.nv : 0;
   }
-  uint32_t nsq = 0;
-  for (int i = l32; i < kPSample; i += 32) nsq += skey[q][i] != 0u ? 1u : 0u;
+  uint32_t nsq = 0, klo = 0xffffffffu, khi = 0u;
+  for (int i = l32; i < kPSample; i += 32) {
+    const uint32_t key = skey[q][i];
+    if (key != 0u) {
+      ++nsq;
+      klo = min(klo, key);
+      khi = max(khi, key);
+    }
+  }
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) nsq += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nsq), o, 32));
+  for (int o = 16; o > 0; o >>= 1) {
+    nsq += static_cast<uint32_t>(__shfl_xor(static_cast<int>(nsq), o, 32));
+    klo = min(klo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(klo), o, 32)));
+    khi = max(khi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(khi), o, 32)));
+  }
   uint32_t need = static_cast<uint32_t>(min<int64_t>(
       nsq, (2 * static_cast<int64_t>(a.k) * nsq + nvq - 1) / max<int64_t>(nvq, 1) + 8));
-  uint32_t prefix = 0;
+  // pass 0 bins (key - lo) >> s0, pass 1 the next (up to) 8 bits below
+  const int s0 = nsq > 0 ? range_shift(khi - klo, 8) : 0;
+  const int s1 = max(0, s0 - 8);
+  uint32_t base = 0;  // (key - lo) of theta, bins resolved so far
+  // (both passes run in every row: the barriers are workgroup-wide; a row
+  // whose range fits 8 bits is resolved by pass 0 and skips pass 1's work)
   for (int pass = 0; pass < 2; ++pass) {
-    const int sh = 24 - 8 * pass;
+    const int sh = pass == 0 ? s0 : s1;
+    const uint32_t bmask = pass == 0 ? 255u : (1u << (s0 - s1)) - 1u;
+    const bool work = pass == 0 || s0 > 0;
     for (int i = l32; i < 256; i += 32) hist[q][i] = 0u;
     if (l32 == 0) pick[q][0] = pick[q][1] = 0u;
     __syncthreads();
-    for (int i = l32; i < kPSample; i += 32) {
+    for (int i = l32; i < kPSample && work; i += 32) {
       const uint32_t key = skey[q][i];
-      if (key != 0u && (pass == 0 || (key >> 24) == prefix)) atomicAdd(&hist[q][(key >> sh) & 255u], 1u);
+      if (key == 0u) continue;
+      const uint32_t d = key - klo;
+      if (pass == 0 || (d >> s0) == (base >> s0)) atomicAdd(&hist[q][(d >> sh) & bmask], 1u);
     }
     __syncthreads();
     // lane l32 owns bins 255 - 8 l32 .. 248 - 8 l32 (descending)
@@ -389,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
       if (l32 >= o) before += x;
     }
     before -= sum;  // exclusive
-    if (need > 0 && before < need && before + sum >= need) {
+    if (work && need > 0 && before < need && before + sum >= need) {
       uint32_t acc = before;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -401,16 +424,15 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
       }
     }
     __syncthreads();
-    const uint32_t bin = pick[q][0];
+    base += pick[q][0] << sh;
     need -= pick[q][1];
-    prefix = pass == 0 ? bin : ((prefix << 8) | bin);
     __syncthreads();
   }
   if (l32 == 0 && q < t.nq) {
     const int64_t row = t.row0 + q;
     // rows that keep every visible entry (or none) need no candidates
     const bool sel = nvq > a.k && nsq > 0;
-    a.theta[row] = sel ? key_to_float(prefix << 16) : INFINITY;
+    a.theta[row] = sel ? key_to_float(klo + base) : INFINITY;
   }
 }
 

@@ -234,7 +234,7 @@ def main():
         # no indexer (the selection is every visible entry): the attention
         # kernels' gather of the n_vis + W vectors, q and out
         el = 2 if w.main_dtype == "bf16" else 4
-        kern = "k_attn_decode+k_attn_dcombine"
+        kern = "attention+combine"
         kbytes = w.B * ((min(w.k, nv) + min(w.W, w.m)) * w.D * el + 2 * w.H * w.D * el)
         kms = attn_ms
     kgbps = kbytes / (kms / 1e3) / 1e9 if kms else None

@@ -892,7 +892,10 @@ Plan plan(const dsa_attn_args& a) {
   const int64_t rows = static_cast<int64_t>(a.n_seqs) * a.queries_per_seq;
   const int total = std::max(1, a.k + a.window_size);
   const bool bf16_512 = a.dtype == DSA_BF16 && a.dim == kMD && a.rope_dim <= kMD;
-  p.dec = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048;
+  // few rows take the 16-head decode kernel, unless a row's set is long
+  // (c128a: every visible entry), where staging each vector once for all
+  // 64 heads of the matrix-core kernel saves the four-fold gather
+  p.dec = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048 && total < 4096;
   p.mfma = !p.dec && bf16_512 && a.heads % 64 == 0;
   if (p.dec) {
     // about 1024 workgroups: runs of whole NW x 32-slot iterations

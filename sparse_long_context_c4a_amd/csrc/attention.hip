@@ -906,10 +906,13 @@ Plan plan(const dsa_attn_args& a) {
     p.slots_per_run = static_cast<int>(iters * kDecWaves * kDStep);
     p.n_runs = static_cast<int>(ceil_div(total, p.slots_per_run));
   } else if (p.mfma) {
-    // about 512 workgroups over the chip, at least two tiles per run
+    // about 256 workgroups, one per compute unit (the kernel's LDS admits
+    // one), at least two tiles per run: splitting a row further multiplies
+    // the partials the combine reads (c128a decode, 16 rows of 8320 slots:
+    // 89 us per step at 256, 110 at 512, 164 at 1024, 106 at 128)
     const int64_t hq = a.heads / 64;
     const int tiles = static_cast<int>(ceil_div(total, kMTile));
-    int64_t runs = ceil_div(512, std::max<int64_t>(1, rows * hq));
+    int64_t runs = ceil_div(256, std::max<int64_t>(1, rows * hq));
     runs = std::max<int64_t>(1, std::min<int64_t>(runs, ceil_div(tiles, 2)));
     runs = std::max<int64_t>(runs, ceil_div(tiles, kMRunSlots / kMTile));  // indices fit LDS
     const int tpr = static_cast<int>(ceil_div(tiles, runs));

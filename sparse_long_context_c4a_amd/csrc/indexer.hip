@@ -64,11 +64,14 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
                             meta, cap, status);
 }
 
-// A decode step's indexer with the step's state updates riding along: blocks
-// x < nb stream the keys of row y; blocks nb, nb+1, nb+2 of row y (one
-// sequence per row) run the prologue roles, whose writes the indexer does not
-// read (see decode_prologue_block), so they overlap the key stream instead
-// of adding a launch and its latency in front of it.
+// A decode step's indexer with the step's state updates riding along: the
+// first kPrologueRoles x rows workgroups run the prologue roles (role id %
+// kPrologueRoles of sequence id / kPrologueRoles), whose writes the indexer
+// does not read (see decode_prologue_block), so they overlap the key stream
+// instead of adding a launch and its latency in front of it; they come
+// first so that they are dispatched with the first wave of workgroups, not
+// after the stream has freed compute units.  The rest stream the keys: nb
+// workgroups per row.
 template <typename MainT, int kIdxOut, int kEnt>
 __global__ __launch_bounds__(kThreads) void k_decode_index(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -77,12 +80,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb, PrologueArgs pa,
     uint32_t* status) {
-  if (static_cast<int>(blockIdx.x) < nb)
-    index_stream_block<true, kEnt>(blockIdx.x, nb, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos, 1,
-                             Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand, meta,
-                             cap, status);
-  else
-    decode_prologue_block<MainT, kIdxOut>(blockIdx.x - nb, blockIdx.y, pa);
+  const int id = static_cast<int>(blockIdx.x), npro = pa.B * kPrologueRoles;
+  if (id < npro) {
+    decode_prologue_block<MainT, kIdxOut>(id % kPrologueRoles, id / kPrologueRoles, pa);
+  } else {
+    const int sid = id - npro;
+    index_stream_block<true, kEnt>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale, q_pos, 1,
+                                   Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand,
+                                   meta, cap, status);
+  }
 }
 
 // ------------------------------------------------------------- generic VALU
@@ -435,7 +441,7 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
   const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab);
   auto go = [&](auto kern) {
-    launch_timed(kern, dim3(P.nb + kPrologueRoles, rows), dim3(kThreads), 0, st,
+    launch_timed(kern, dim3((P.nb + kPrologueRoles) * rows), dim3(kThreads), 0, st,
                  static_cast<hipEvent_t>(a.ev_index[0]), static_cast<hipEvent_t>(a.ev_index[1]),
                  static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                  static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,

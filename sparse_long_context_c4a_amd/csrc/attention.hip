@@ -881,6 +881,75 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
   if (lse && d4 == 0) lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
+// Merge the runs of one (row, head) of the matrix-core path (partials
+// (row, run, head)) and apply R_m^{-1}: workgroup -> (head blockIdx.x, row
+// blockIdx.y), thread -> dims 4 tid .. +3, up to kCombR runs' partials
+// loaded per memory round trip.  The (cos, sin) of R_m come from the
+// step's table when the caller has one, else are computed here.
+__global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* __restrict__ part_acc,
+                                                       const float* __restrict__ part_ml,
+                                                       uint16_t* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  __shared__ float cs_s[kMD];
+  const int row = blockIdx.y, h = blockIdx.x, tid = threadIdx.x, d4 = tid;
+  const int64_t m = g.q_pos[row];
+  const bool ok = m >= 0 && m < g.max_pos_end;
+  for (int i = tid; i < g.r / 2; i += 128) {
+    float c = 1.f, sn = 0.f;
+    if (g.cs_tab) {
+      c = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * i];
+      sn = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * i + 1];
+    } else if (ok) {
+      rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+    }
+    cs_s[2 * i] = c;
+    cs_s[2 * i + 1] = sn;
+  }
+  const int64_t p0 = static_cast<int64_t>(row) * g.n_runs;
+  float M = -INFINITY, L = 0.f;
+  float4 t = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < g.n_runs; r0 += kCombR) {
+    float mr[kCombR], lr[kCombR];
+    float4 u[kCombR];
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      // an empty run left max -inf, sum 0 and acc 0; runs past the end are empty
+      mr[q] = -INFINITY;
+      lr[q] = 0.f;
+      u[q] = float4{0.f, 0.f, 0.f, 0.f};
+      if (r0 + q < g.n_runs) {
+        const int64_t pi = (p0 + r0 + q) * g.H + h;
+        mr[q] = part_ml[2 * pi];
+        lr[q] = part_ml[2 * pi + 1];
+        u[q] = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) Mn = fmaxf(Mn, mr[q]);
+    if (Mn == -INFINITY) continue;
+    const float c = M == -INFINITY ? 0.f : expf(M - Mn);
+    L *= c;
+    t.x *= c;
+    t.y *= c;
+    t.z *= c;
+    t.w *= c;
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      const float wgt = mr[q] == -INFINITY ? 0.f : expf(mr[q] - Mn);
+      L = fmaf(wgt, lr[q], L);
+      t.x = fmaf(wgt, u[q].x, t.x);
+      t.y = fmaf(wgt, u[q].y, t.y);
+      t.z = fmaf(wgt, u[q].z, t.z);
+      t.w = fmaf(wgt, u[q].w, t.w);
+    }
+    M = Mn;
+  }
+  __syncthreads();
+  store_head_dims4(t, L, d4, kMD - g.r, cs_s, out + (static_cast<int64_t>(row) * g.H + h) * kMD);
+  if (lse && d4 == 0) lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
 struct Plan {
   bool mfma, dec;
   int slots_per_run, n_runs;
@@ -972,7 +1041,7 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
   const hipEvent_t ev0 = static_cast<hipEvent_t>(lx.ev0), ev1 = static_cast<hipEvent_t>(lx.ev1);
-  const bool combine = p.n_runs > 1 && !p.dec;
+  const bool combine = p.n_runs > 1 && !p.dec && !p.mfma;
   if constexpr (sizeof(T) == 2) {
     if (p.dec) {
       float* cs_ws = p.n_runs > 1 ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
@@ -998,12 +1067,19 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
                      static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                      static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
                      a.lse, part_acc, part_ml);
-      else
+      else {
         launch_timed(k_attn_mfma8<false>, grid, dim3(512), 0, st, ev0, nullptr, g,
                      static_cast<const uint16_t*>(a.q), a.rotate_q,
                      static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                      static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out),
                      a.lse, part_acc, part_ml);
+        dsa_status rc = hip_check(hipGetLastError(), "k_attn_mfma8 launch");
+        if (rc != DSA_OK) return rc;
+        launch_timed(k_attn_mcombine, dim3(a.heads, rows), dim3(128), 0, st, nullptr, ev1, g,
+                     static_cast<const float*>(part_acc), static_cast<const float*>(part_ml),
+                     static_cast<uint16_t*>(a.out), a.lse);
+        return hip_check(hipGetLastError(), "k_attn_mcombine launch");
+      }
     }
   }
   if (!p.mfma && !p.dec) {

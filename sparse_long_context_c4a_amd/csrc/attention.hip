@@ -506,10 +506,10 @@ constexpr int kDH = 16;                       // heads per workgroup
 constexpr int kDStep = 32;                    // vectors per wave step
 constexpr int kDWaveBytes = kDStep * kMPitch; // 33,792 B of LDS per wave
 constexpr int kDOPitch = kMD + 4;             // floats per head row when merging waves
-#ifndef DSA_DEC_WAVES
-#define DSA_DEC_WAVES 4
-#endif
-constexpr int kDecWaves = DSA_DEC_WAVES;      // waves (32-slot steps) per workgroup
+// waves (32-slot steps) per workgroup: measured at the c4a decode B=4
+// workload, 4 (80 workgroups) beat 2 (160) and 1 (320, whose partials make
+// the combine four times longer)
+constexpr int kDecWaves = 4;
 
 // Source of slot a of row `row` given its cache index j (read by the caller
 // for a < k); nullptr if the slot is empty.

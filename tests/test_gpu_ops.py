@@ -38,6 +38,10 @@ COMPRESS_CASES = [
     ("c4a_ragged_rmsnorm", 4, 8, 512, 64, "bf16", "bf16", 3, 37, 1001, True),
     ("c4a_ragged_fp8_rmsnorm", 4, 8, 128, 16, "bf16", "fp8", 2, 13, 4094, True),
     ("c4a_no_entry", 4, 8, 64, 0, "f32", "f32", 1, 3, 4, False),
+    # wider than 512 dims (several dim pairs per thread) and a c128a chunk
+    # whose first entry mixes ring and new raw tokens
+    ("c4a_wide_d1024", 4, 8, 1024, 64, "bf16", "bf16", 1, 40, 1002, False),
+    ("c128a_chunk_ring_and_raw", 128, 128, 512, 64, "bf16", "bf16", 1, 300, 1000, False),
 ]
 
 

@@ -233,11 +233,18 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const PTile t = p_tile(a, blockIdx.x);
   // the largest n_vis over the whole sequence (sets the slices of nu)
+  // (eight positions per thread and round, their loads out together)
   int64_t nvs = 0;
-  for (int i = tid; i < a.Tq; i += kThreads) {
-    const RowInfo ri = row_info(a.q_pos, static_cast<int>(static_cast<int64_t>(t.b) * a.Tq + i),
-                                a.s, a.S, a.nv_cap, a.max_pos_end, nullptr, false);
-    if (ri.ok) nvs = max(nvs, ri.nv);
+  for (int i0 = tid; i0 < a.Tq; i0 += 8 * kThreads) {
+    int64_t mp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kThreads;
+      mp[u] = i < a.Tq ? a.q_pos[static_cast<int64_t>(t.b) * a.Tq + i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (mp[u] >= 0 && mp[u] < a.max_pos_end) nvs = max(nvs, min(a.nv_cap, n_complete(mp[u], a.s, a.S)));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nvs = max(nvs, static_cast<int64_t>(__shfl_xor(nvs, o, 64)));
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
   for (int t0 = wave; t0 < kPSampleTiles && ns_t > 0; t0 += 4 * kPre) {
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      const int ti = t0 + 4 * u;  // < kPSampleTiles: 16 | kPSampleTiles / 4
+      const int ti = t0 + 4 * u;  // < kPSampleTiles: 4 kPre divides kPSampleTiles
       const v8i bk = as_v8i(lo[u], hi[u]);
       const float ksc = ks[u];
       load(u, min(ti + 4 * kPre, kPSampleTiles - 1));
@@ -362,6 +369,7 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
     nvq = ri.ok ? ri.nv : 0;
   }
   uint32_t nsq = 0, klo = 0xffffffffu, khi = 0u;
+#pragma unroll 8
   for (int i = l32; i < kPSample; i += 32) {
     const uint32_t key = skey[q][i];
     if (key != 0u) {
@@ -391,11 +399,14 @@ __global__ __launch_bounds__(kThreads) void k_pidx_prep(PArgs a) {
     for (int i = l32; i < 256; i += 32) hist[q][i] = 0u;
     if (l32 == 0) pick[q][0] = pick[q][1] = 0u;
     __syncthreads();
-    for (int i = l32; i < kPSample && work; i += 32) {
-      const uint32_t key = skey[q][i];
-      if (key == 0u) continue;
-      const uint32_t d = key - klo;
-      if (pass == 0 || (d >> s0) == (base >> s0)) atomicAdd(&hist[q][(d >> sh) & bmask], 1u);
+    if (work) {
+#pragma unroll 8
+      for (int i = l32; i < kPSample; i += 32) {
+        const uint32_t key = skey[q][i];
+        const uint32_t d = key - klo;
+        if (key != 0u && (pass == 0 || (d >> s0) == (base >> s0)))
+          atomicAdd(&hist[q][(d >> sh) & bmask], 1u);
+      }
     }
     __syncthreads();
     // lane l32 owns bins 255 - 8 l32 .. 248 - 8 l32 (descending)

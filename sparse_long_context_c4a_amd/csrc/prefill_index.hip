@@ -514,6 +514,38 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   const int b = rg / a.rg_per_seq, r0 = (rg % a.rg_per_seq) * kMRows;
   const int nq = min(kMRows, a.Tq - r0);
   const int64_t row0 = static_cast<int64_t>(b) * a.Tq + r0;
+  const int wr0 = wave * kMR;  // the wave's rows wr0 .. wr0 + 7 of the workgroup
+  // every load of the set-up that depends on no other goes out first (one
+  // memory round trip instead of a chain of four): the wave's rows' query
+  // codes, their head weights (all heads of row n for lanes n < kMR) and the
+  // thresholds and error scales of rows 4 (g & 1) + i (lanes g < 2); rows
+  // past the group read row 0 of it and are masked below
+  uint4 qlo_r[kMR], qhi_r[kMR];
+#pragma unroll
+  for (int q = 0; q < kMR; ++q) {
+    const int64_t rq = row0 + (wr0 + q < nq ? wr0 + q : 0);
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + (rq * a.Hi + (n < a.Hi ? n : 0)) * 128);
+    qlo_r[q] = qp[g];
+    qhi_r[q] = qp[4 + g];
+  }
+  float wl_r[4];  // heads 4g .. 4g+3 of row n (lanes n < kMR)
+  {
+    const int64_t rq = row0 + (n < kMR && wr0 + n < nq ? wr0 + n : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      const int64_t o = rq * a.Hi + (h < a.Hi ? h : 0);
+      wl_r[i] = a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f);
+    }
+  }
+  float th_r[4], be_r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qd = 4 * (g & 1) + i;
+    const int64_t rq = row0 + (wr0 + qd < nq ? wr0 + qd : 0);
+    th_r[i] = a.theta[rq];
+    be_r[i] = a.beta[rq];
+  }
   // nu_max and kappa = max_j ||k8_j|| of the sequence; the workgroup's
   // largest n_vis
   float nu = 0.f, kap = 0.f;
@@ -572,8 +604,6 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   float rks0, rks1;
   gload(0, rk0, rks0);
   gload(min(1, nst - 1), rk1, rks1);
-  // the wave's rows wr0 .. wr0 + 7 of the workgroup
-  const int wr0 = wave * kMR;
   // stage-1 operands: lane = head n, chunks g and 4 + g of each row, and the
   // E8M0 code of 2^-c for head n: 2^c >= 2 ||q8_n|| kappa (with a margin for
   // the f32 norms), so |2^-c q8_n . k8_j| <= 1/2 (1 + 2^-10) for every entry
@@ -584,9 +614,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   for (int q = 0; q < kMR; ++q) {
     uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
     if (wr0 + q < nq && n < a.Hi) {
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((row0 + wr0 + q) * a.Hi + n) * 128);
-      lo = qp[g];
-      hi = qp[4 + g];
+      lo = qlo_r[q];
+      hi = qhi_r[q];
     }
     A[q] = as_v8i(lo, hi);
     float ss = fp8x16_sumsq(lo) + fp8x16_sumsq(hi);
@@ -606,26 +635,24 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   // |w'_h 2^c_h| in [2^14, 2^15)
   int e_row = 0;
   v8h a2m = {};
-  if (n < kMR) {
-    const int qr = wr0 + n;
-    float wmax = 0.f, wq[4] = {0.f, 0.f, 0.f, 0.f};
-    int cq[4] = {0, 0, 0, 0};
-    if (qr < nq) {
-      const int64_t o = (row0 + qr) * a.Hi;
+  // the row's largest |w'_h 2^c_h|: lane (g, n) takes heads 4g .. 4g+3 of
+  // row n, then the max over the four head groups (lanes n, n+16, n+32, n+48)
+  float wmax = 0.f, wq[4] = {0.f, 0.f, 0.f, 0.f};
+  int cq[4] = {0, 0, 0, 0};
+  if (n < kMR && wr0 + n < nq) {
 #pragma unroll
-      for (int h = 0; h < 16; ++h)  // (all loads in flight at once; Hi <= 16)
-        if (h < a.Hi)
-          wmax = fmaxf(wmax, ldexpf(fabsf(a.w[o + h] * (a.q_scale ? a.q_scale[o + h] : 1.0f)),
-                                    csh[wave][n][h]));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        if (h < a.Hi) {
-          wq[i] = a.w[o + h] * (a.q_scale ? a.q_scale[o + h] : 1.0f);
-          cq[i] = csh[wave][n][h];
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      if (h < a.Hi) {  // (Hi <= 16)
+        wq[i] = wl_r[i];
+        cq[i] = csh[wave][n][h];
+        wmax = fmaxf(wmax, ldexpf(fabsf(wq[i]), cq[i]));
       }
     }
+  }
+  wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
+  wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
+  if (n < kMR) {
     if (wmax > 0.f && wmax <= 3.0e38f) {
       int ex;
       frexpf(wmax, &ex);  // wmax = f 2^ex, f in [0.5, 1)
@@ -653,8 +680,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
     thr[i] = INFINITY;
     g0[i] = 0.f;
     if (g < 2 && wr0 + qd < nq) {
-      const float th = a.theta[row0 + wr0 + qd];
-      const double be = static_cast<double>(a.beta[row0 + wr0 + qd]);
+      const float th = th_r[i];
+      const double be = static_cast<double>(be_r[i]);
       if (th < INFINITY) {
         const double bn = be * nu;
         double d = static_cast<double>(th) - bn;

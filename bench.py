@@ -6,7 +6,10 @@ A step is one dsa_layer_decode call over one batch (compress the entry that
 completes at m, index every visible entry, Top-k, sparse attention, window
 insert) on seeded synthetic inputs already resident in HBM.  Input sets are
 rotated (three by default) so that repeated steps do not find the indexer
-keys in the 256 MB Infinity Cache.  Prints one JSON line.
+keys in the 256 MB Infinity Cache.  Prints one JSON line: the headline c4a
+decode (B=4, L=1M) as the value, the prefill chunk under "prefill", the
+other decode workloads under "workloads" (--no-extra skips them) and the
+oracle's rate on a bounded sample under "cpu_baseline".
 """
 
 import argparse
@@ -186,6 +189,25 @@ def time_prefill(dev, steps=3, warmup=1):
             "layer_tflops": (idx_flop + attn_flop) / (pms / 1e3) / 1e12}
 
 
+def time_decode_workload(w, dev, steps, warmup, n_sets):
+    """Step time and throughput of one more decode workload (reported beside
+    the headline; each is also a parity-test case)."""
+    import torch
+    from sparse_long_context_c4a_amd import _lib
+    print(f"[bench] decode workload {w.name}", file=sys.stderr, flush=True)
+    sets = build_sets(w, n_sets, dev)
+    ms, idx_ms, attn_ms = time_layer(w, sets, steps, warmup, decode=True)
+    del sets
+    torch.cuda.empty_cache()
+    nv = _lib.n_complete(w.m, w.s, w.S)
+    step_bytes = w.B * decode_bytes_per_query(w, nv)
+    gbps = step_bytes / (ms / 1e3) / 1e9
+    return {"queries_per_s": w.B / (ms / 1e3), "ms_per_step": ms, "batch": w.B, "context": w.L,
+            "k": w.k, "n_vis": nv, "alg_bytes_per_step": step_bytes, "hbm_gbps": gbps,
+            "hbm_frac": gbps / PEAK_HBM_GBPS,
+            "kernel_ms": {"indexer": idx_ms, "attention": attn_ms}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +218,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other decode workloads (reported under 'workloads')")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill chunk (for profiling its kernels)")
     ap.add_argument("--print-source-hash", action="store_true")
@@ -266,6 +290,10 @@ def main():
         del src, dst
     if not args.no_prefill:
         line["prefill"] = time_prefill(dev)
+    if not args.no_extra and w.name == "c4a_decode_B4_L1M":
+        line["workloads"] = {
+            x.name: time_decode_workload(x, dev, args.steps, args.warmup, args.sets)
+            for x in configs.ALL if x.mode == "decode" and x.name != w.name}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -119,14 +119,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(
 #pragma unroll
   for (int i = 0; i < kMaxD / 16; ++i) acc[i] = 0.f;
   float run_max = -INFINITY, run_sum = 0.f;
+  static_assert(kThreads == 16 * kTile, "one 16-thread group per staged vector");
   for (int a0 = a_begin; a0 < a_end; a0 += kTile) {
     __syncthreads();
-    for (int e = 0; e < kTile; ++e) {
+    {
+      // stage the tile: thread group e = tid / 16 fetches vector e (its slot's
+      // index, then its D values, 16 threads side by side), so a tile costs
+      // two memory round trips
+      const int e = tid / 16, dl = tid % 16;
       const int a = a0 + e;
       const T* src = (ok && a < a_end) ? slot_ptr<T>(g, row, b, m, a, cache, window, chunk_win)
                                        : nullptr;
-      if (tid == 0) valid_s[e] = src != nullptr;
-      for (int d = tid; d < D; d += kThreads) v_s[e * D + d] = src ? load_as_f32(src, d) : 0.f;
+      if (dl == 0) valid_s[e] = src != nullptr;
+#pragma unroll 8
+      for (int d = dl; d < D; d += 16) v_s[e * D + d] = src ? load_as_f32(src, d) : 0.f;
     }
     __syncthreads();
     // logits: thread (h_loc, sub) -> head h_loc, vector sub
@@ -190,7 +196,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(
   }
 }
 
-// Merge the runs of one (row, head) and apply R_m^{-1}.
+// Merge the runs of one (row, head) and apply R_m^{-1}: thread -> dim pairs
+// tid and tid + 256 (D <= 1024), the partials of up to kGCombR runs loaded
+// per memory round trip, merged with a running log-sum-exp.
+constexpr int kGCombR = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* __restrict__ part_acc,
                                                       const float* __restrict__ part_ml,
@@ -198,34 +208,67 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
   const int row = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   const int64_t m = g.q_pos[row];
   const bool ok = m >= 0 && m < g.max_pos_end;
-  float M = -INFINITY;
-  for (int r = 0; r < g.n_runs; ++r)
-    M = fmaxf(M, part_ml[2 * ((static_cast<int64_t>(row) * g.n_runs + r) * g.H + h)]);
-  float L = 0.f;
-  for (int r = 0; r < g.n_runs; ++r) {
-    const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + r) * g.H + h;
-    const float mr = part_ml[2 * pi];
-    if (mr != -INFINITY) L += part_ml[2 * pi + 1] * expf(mr - M);
+  const int D = g.D, first_rot = (D - g.r) / 2, npairs = D / 2;
+  const int64_t p0 = static_cast<int64_t>(row) * g.n_runs;
+  float M = -INFINITY, L = 0.f;
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  for (int r0 = 0; r0 < g.n_runs; r0 += kGCombR) {
+    float mr[kGCombR], lr[kGCombR], u[kGCombR][2][2];
+#pragma unroll
+    for (int q = 0; q < kGCombR; ++q) {
+      // an empty run left max -inf, sum 0 and acc 0; runs past the end are empty
+      mr[q] = -INFINITY;
+      lr[q] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) u[q][k][0] = u[q][k][1] = 0.f;
+      if (r0 + q < g.n_runs) {
+        const int64_t pi = (p0 + r0 + q) * g.H + h;
+        mr[q] = part_ml[2 * pi];
+        lr[q] = part_ml[2 * pi + 1];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pr = tid + 256 * k;
+          if (pr < npairs) {
+            u[q][k][0] = part_acc[pi * D + 2 * pr];
+            u[q][k][1] = part_acc[pi * D + 2 * pr + 1];
+          }
+        }
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int q = 0; q < kGCombR; ++q) Mn = fmaxf(Mn, mr[q]);
+    if (Mn == -INFINITY) continue;
+    const float c = M == -INFINITY ? 0.f : expf(M - Mn);
+    L *= c;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      acc[k][0] *= c;
+      acc[k][1] *= c;
+    }
+#pragma unroll
+    for (int q = 0; q < kGCombR; ++q) {
+      const float wgt = mr[q] == -INFINITY ? 0.f : expf(mr[q] - Mn);
+      L = fmaf(wgt, lr[q], L);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        acc[k][0] = fmaf(wgt, u[q][k][0], acc[k][0]);
+        acc[k][1] = fmaf(wgt, u[q][k][1], acc[k][1]);
+      }
+    }
+    M = Mn;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const int D = g.D, first_rot = (D - g.r) / 2;
   const int64_t o = (static_cast<int64_t>(row) * g.H + h) * D;
-  for (int pr = tid; pr < D / 2; pr += blockDim.x) {
-    float a0 = 0.f, a1 = 0.f;
-    for (int r = 0; r < g.n_runs; ++r) {
-      const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + r) * g.H + h;
-      const float mr = part_ml[2 * pi];
-      if (mr == -INFINITY) continue;
-      const float wgt = expf(mr - M);
-      a0 = fmaf(wgt, part_acc[pi * D + 2 * pr], a0);
-      a1 = fmaf(wgt, part_acc[pi * D + 2 * pr + 1], a1);
-    }
-    a0 *= inv;
-    a1 *= inv;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int pr = tid + 256 * k;
+    if (pr >= npairs) continue;
+    float a0 = acc[k][0] * inv, a1 = acc[k][1] * inv;
     if (pr >= first_rot && ok) {
-      float c, s;
-      rope_cs(m + g.off, pr - first_rot, g.r, g.base, &c, &s);
-      const float t0 = a0 * c + a1 * s, t1 = -a0 * s + a1 * c;
+      float c, sn;
+      rope_cs(m + g.off, pr - first_rot, g.r, g.base, &c, &sn);
+      const float t0 = a0 * c + a1 * sn, t1 = -a0 * sn + a1 * c;
       a0 = t0;
       a1 = t1;
     }
@@ -993,10 +1036,11 @@ Plan plan(const dsa_attn_args& a) {
     p.n_runs = static_cast<int>(ceil_div(tiles, tpr));
   } else {
     const int64_t hgroups = ceil_div(a.heads, kHG);
-    // enough workgroups to cover the chip (~1024), runs of at least 64 slots
+    // enough workgroups to cover the chip (~1024), runs of whole 16-slot
+    // tiles (a few rows: one tile per run, so the runs run side by side)
     int64_t want = ceil_div(1024, std::max<int64_t>(1, rows * hgroups));
     int spr = static_cast<int>(ceil_div(total, std::max<int64_t>(1, want)));
-    spr = std::max(64, static_cast<int>(ceil_div(spr, kTile) * kTile));
+    spr = std::max(kTile, static_cast<int>(ceil_div(spr, kTile) * kTile));
     p.slots_per_run = spr;
     p.n_runs = static_cast<int>(ceil_div(total, spr));
   }

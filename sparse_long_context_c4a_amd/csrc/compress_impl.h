@@ -22,27 +22,35 @@ constexpr int kCompressThreads = 256;
 constexpr int kCompressMaxSpan = 256;
 constexpr int kCompressPairs = 4;  // D <= 2048
 
-// Dims 2 pr and 2 pr + 1 of a raw token row as one load (a 32-bit word of
-// two bf16, or two f32), widened to f32 when used.
+// Dims 8 c .. 8 c + 7 of a raw token row in one or two 16-byte loads (eight
+// bf16, or two float4), widened to f32 when used.
 template <typename T>
-struct PairWord;
+struct Dim8;
 template <>
-struct PairWord<uint16_t> {
-  typedef uint32_t type;
-  static __device__ __forceinline__ type load(const uint16_t* row, int pr) {
-    return *reinterpret_cast<const uint32_t*>(row + 2 * pr);
+struct Dim8<uint16_t> {
+  typedef uint4 type;
+  static __device__ __forceinline__ type load(const uint16_t* row, int c) {
+    return reinterpret_cast<const uint4*>(row)[c];
   }
-  static __device__ __forceinline__ float first(type v) { return __uint_as_float(v << 16); }
-  static __device__ __forceinline__ float second(type v) { return __uint_as_float(v & 0xffff0000u); }
+  static __device__ __forceinline__ float at(const type& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
 };
 template <>
-struct PairWord<float> {
-  typedef float2 type;
-  static __device__ __forceinline__ type load(const float* row, int pr) {
-    return *reinterpret_cast<const float2*>(row + 2 * pr);
+struct Dim8<float> {
+  struct type {
+    float4 lo, hi;
+  };
+  static __device__ __forceinline__ type load(const float* row, int c) {
+    const float4* r = reinterpret_cast<const float4*>(row) + 2 * c;
+    return type{r[0], r[1]};
   }
-  static __device__ __forceinline__ float first(type v) { return v.x; }
-  static __device__ __forceinline__ float second(type v) { return v.y; }
+  static __device__ __forceinline__ float at(const type& v, int e) {
+    const float4& h = e < 4 ? v.lo : v.hi;
+    const int k = e & 3;
+    return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+  }
 };
 
 template <typename RawT, int kOut>
@@ -54,6 +62,7 @@ __device__ __forceinline__ void compress_one(
     int64_t max_pos_end, uint32_t* status) {
   __shared__ float w_s[kCompressMaxSpan];
   __shared__ float red[16];
+  __shared__ float red8[kCompressThreads * 8];  // token groups' partial sums
   const int tid = threadIdx.x;
   const int64_t p0 = pos0v[b];
   if (p0 < 0 || p0 + T > max_pos_end) {
@@ -89,32 +98,55 @@ __device__ __forceinline__ void compress_one(
   for (int k = 0; k < kCompressPairs; ++k) acc[k][0] = acc[k][1] = 0.f;
   const RawT* rawb = raw + static_cast<int64_t>(b) * T * D;
   const RawT* ringb = ring + static_cast<int64_t>(b) * S * D;
-  if (npairs <= kCompressThreads) {
-    // one dim pair per thread (D <= 512): 16 tokens per round, their loads
-    // all out before the first is used (unconditional: past the span the
-    // last token is re-read with weight 0; ring slots stepped in 32 bits),
-    // so a span of S tokens costs about S / 16 memory round trips (one per
-    // token would make the 128-token c128a entry latency-bound)
-    constexpr int kTok = 16;
-    using PW = PairWord<RawT>;
-    const int pr = tid < npairs ? tid : 0;
+  if (D % 8 == 0 && D / 8 <= kCompressThreads) {
+    // 16-byte loads: thread (group gr, column c) sums dims 8c .. 8c+7 over
+    // the tokens i = gr (mod ngrp) -- a token row is D/8 threads wide, and
+    // the ngrp = 256 / (D/8) groups split the span -- kTok tokens per round
+    // with all of their loads out before the first is used (unconditional:
+    // past the span the last token is re-read with weight 0); the groups'
+    // sums then meet in LDS.  (Four-byte loads, one dim pair per thread,
+    // made the 128-token c128a entry bound by the load instruction rate.)
+    constexpr int kTok = 8;
+    using DV = Dim8<RawT>;
+    const int tpr = D / 8, ngrp = kCompressThreads / tpr;
+    const int gr = tid / tpr, c = tid % tpr;
     const int64_t pj = static_cast<int64_t>(s) * j;  // the entry's first raw position
     const int ring0 = static_cast<int>(pj % S);
-    for (int i0 = 0; i0 < S; i0 += kTok) {
-      typename PW::type xw[kTok];
+    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (gr < ngrp) {
+      for (int i0 = gr; i0 < S; i0 += ngrp * kTok) {
+        typename DV::type xw[kTok];
 #pragma unroll
-      for (int u = 0; u < kTok; ++u) {
-        const int i = min(i0 + u, S - 1);
-        const int64_t p = pj + i;
-        const int slot = ring0 + i < S ? ring0 + i : ring0 + i - S;
-        const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + static_cast<int64_t>(slot) * D;
-        xw[u] = PW::load(row, pr);
+        for (int u = 0; u < kTok; ++u) {
+          const int i = min(i0 + u * ngrp, S - 1);
+          const int64_t p = pj + i;
+          const int slot = ring0 + i < S ? ring0 + i : ring0 + i - S;
+          const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + static_cast<int64_t>(slot) * D;
+          xw[u] = DV::load(row, c);
+        }
+#pragma unroll
+        for (int u = 0; u < kTok; ++u) {
+          const float wi = i0 + u * ngrp < S ? w_s[i0 + u * ngrp] * inv : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a8[e] = fmaf(wi, DV::at(xw[u], e), a8[e]);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kTok; ++u) {
-        const float wi = i0 + u < S ? w_s[i0 + u] * inv : 0.f;
-        acc[0][0] = fmaf(wi, PW::first(xw[u]), acc[0][0]);
-        acc[0][1] = fmaf(wi, PW::second(xw[u]), acc[0][1]);
+      for (int e = 0; e < 8; ++e) red8[gr * D + 8 * c + e] = a8[e];
+    }
+    __syncthreads();
+    // back to the layout below: thread owns pairs tid + 256 k
+#pragma unroll
+    for (int k = 0; k < kCompressPairs; ++k) {
+      const int pr = tid + k * kCompressThreads;
+      if (pr < npairs) {
+        float x0 = 0.f, x1 = 0.f;
+        for (int g2 = 0; g2 < ngrp; ++g2) {
+          x0 += red8[g2 * D + 2 * pr];
+          x1 += red8[g2 * D + 2 * pr + 1];
+        }
+        acc[k][0] = x0;
+        acc[k][1] = x1;
       }
     }
   } else {

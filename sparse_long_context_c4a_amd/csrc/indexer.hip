@@ -162,10 +162,18 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   const int slots = nw * cap;  // <= kFinalCap by construction
   const uint32_t* mrow = meta + static_cast<int64_t>(row) * nw;
   const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
+  // two candidates per 16-byte load: v[2 i + h] is slot 2 t + 2 kSel i + h
+  // (slots is even: cap >= 8; the row's start is 16-byte aligned)
   constexpr int kPer = kFinalCap / kSel;
   uint64_t v[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = t + u * kSel < slots ? crow[t + u * kSel] : 0ull;
+  for (int i = 0; i < kPer / 2; ++i) {
+    const int sl = 2 * t + 2 * kSel * i;
+    uint4 w = {0u, 0u, 0u, 0u};
+    if (sl < slots) w = *reinterpret_cast<const uint4*>(crow + sl);
+    v[2 * i] = static_cast<uint64_t>(w.x) | (static_cast<uint64_t>(w.y) << 32);
+    v[2 * i + 1] = static_cast<uint64_t>(w.z) | (static_cast<uint64_t>(w.w) << 32);
+  }
   uint32_t tm = 0;
   for (int b = t; b < nw; b += kSel) tm = max(tm, mrow[b]);
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);

@@ -179,6 +179,11 @@ dsa_status dsa_index_topk(const dsa_index_args* a, void* ws, size_t ws_bytes, vo
  * logits = scale * (R_m q_h) . v (q rotated here if rotate_q, else taken as
  * already rotated); out_h = R_m^{-1} sum_a softmax_a v_a; lse_h = natural-log
  * sum of exp(logits).  An empty set gives out = 0, lse = -inf.
+ * With out_fp8 = 1 the output is stored token-wise in fp8, fused with the
+ * R_m^{-1} epilogue ([P2] 融合点 2; the scale rule is the decode KV's
+ * token-wise one, [P2] 第三层): per (row, head) sigma = max_d |out_h[d]| / 448
+ * (f32, into out_scale), out = e4m3fn codes of out_h / sigma rounded to
+ * nearest even; sigma = 0 gives zero codes.
  */
 typedef struct dsa_attn_args {
   int32_t n_seqs;             /* B                                           */
@@ -207,6 +212,8 @@ typedef struct dsa_attn_args {
   void* out;                  /* [B * Tq, H, D]                              */
   float* lse;                 /* [B * Tq, H] or NULL                         */
   uint32_t* status;
+  int32_t out_fp8;            /* 0: out is dtype; 1: out is fp8 codes        */
+  float* out_scale;           /* [B * Tq, H] (out_fp8)                       */
 } dsa_attn_args;
 
 size_t dsa_sparse_attn_workspace(const dsa_attn_args* a);
@@ -272,6 +279,8 @@ typedef struct dsa_layer_args {
   uint32_t* status;
   void* ev_index[2];          /* optional hipEvent_t pairs recorded around   */
   void* ev_attn[2];           /* the scoring kernel and the attention kernels */
+  int32_t out_fp8;            /* 1: out as fp8 codes + out_scale (see S5)    */
+  float* out_scale;           /* [B, T, H] (out_fp8)                         */
 } dsa_layer_args;
 
 size_t dsa_layer_workspace(const dsa_layer_args* a);

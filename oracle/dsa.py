@@ -221,6 +221,18 @@ def sparse_attention(q_rot, vecs, m_pos, r, base, scale):
     return rope_inverse(o, m_pos, r, base), lse
 
 
+def quantize_fp8_heads(out):
+    """fp8 attention output ([P2] 融合点 2: the inverse RoPE and the fp8
+    quantisation that feeds the o_lora projection fused in one pass).  The
+    pages give no scale rule for this tensor; the reading taken is the decode
+    KV's token-wise one ([P2] 第三层), one scale per (query, head) vector:
+    each row of ``out`` [H, D] goes through ``quantize_fp8_entry``.
+    Returns (codes uint8 [H, D], sigma float64 [H])."""
+    out = np.asarray(out, np.float64)
+    q = [quantize_fp8_entry(v) for v in out]
+    return np.stack([c for c, _ in q]), np.array([sg for _, sg in q], np.float64)
+
+
 def gather_set(m, idx, entries, window_vec, W):
     """The attention set A(m): the selected compressed entries (idx >= 0) and
     the window tokens n in [m-W, m-1] ([P2] 机制四; [P1] flowchart: Top-k

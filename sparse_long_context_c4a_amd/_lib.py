@@ -60,7 +60,7 @@ class AttnArgs(ctypes.Structure):
                 ("window", c_vp), ("w_cap", c_i32), ("window_size", c_i32),
                 ("chunk_win", c_vp), ("chunk_pos0", c_vp), ("chunk_len", c_i64),
                 ("softmax_scale", c_f32), ("max_pos_end", c_i64), ("out", c_vp),
-                ("lse", c_vp), ("status", c_vp)]
+                ("lse", c_vp), ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp)]
 
 
 class LayerArgs(ctypes.Structure):
@@ -74,7 +74,8 @@ class LayerArgs(ctypes.Structure):
                 ("idx_scale", c_vp), ("e_cap", c_i64), ("main_ring", c_vp), ("idx_ring", c_vp),
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
-                ("status", c_vp), ("ev_index", c_vp * 2), ("ev_attn", c_vp * 2)]
+                ("status", c_vp), ("ev_index", c_vp * 2), ("ev_attn", c_vp * 2),
+                ("out_fp8", c_i32), ("out_scale", c_vp)]
 
 
 EXPORTS = {

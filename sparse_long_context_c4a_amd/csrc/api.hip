@@ -116,6 +116,8 @@ dsa_status validate_attn(const dsa_attn_args* a) {
           "dsa_sparse_attn: chunk_win needs chunk_pos0 and chunk_len >= 1");
   REQUIRE(a->k + a->window_size >= 1, "dsa_sparse_attn: empty attention set");
   REQUIRE(a->max_pos_end >= 1, "dsa_sparse_attn: max_pos_end < 1");
+  REQUIRE(a->out_fp8 == 0 || a->out_fp8 == 1, "dsa_sparse_attn: out_fp8 must be 0 or 1");
+  REQUIRE(!a->out_fp8 || a->out_scale, "dsa_sparse_attn: out_fp8 needs out_scale");
   return DSA_OK;
 }
 
@@ -136,6 +138,8 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
           (long long)ceil_div(a->max_pos_end, a->main.stride));
   REQUIRE(a->w_cap >= a->window_size && a->w_cap >= 1, "dsa_layer: w_cap < window_size");
   REQUIRE(a->max_pos_end >= a->chunk_len, "dsa_layer: max_pos_end < chunk_len");
+  REQUIRE(a->out_fp8 == 0 || a->out_fp8 == 1, "dsa_layer: out_fp8 must be 0 or 1");
+  REQUIRE(!a->out_fp8 || a->out_scale, "dsa_layer: out_fp8 needs out_scale");
   if (a->idx_heads > 0) {
     REQUIRE(a->idx_dim >= 2 && a->idx_dim % 2 == 0, "dsa_layer: idx_dim must be even");
     REQUIRE(a->idx_rope_dim >= 0 && a->idx_rope_dim <= a->idx_dim && a->idx_rope_dim % 2 == 0,
@@ -220,6 +224,8 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   aa.max_pos_end = a->max_pos_end;
   aa.out = a->out;
   aa.lse = a->lse;
+  aa.out_fp8 = a->out_fp8;
+  aa.out_scale = a->out_scale;
   aa.status = a->status;
   L.off_attn_ws = off;
   off = align_up(off + attn_ws_bytes(aa));

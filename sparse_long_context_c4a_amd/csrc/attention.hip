@@ -42,6 +42,10 @@ struct AttnGeom {
   const float* cs_tab;  // optional (cos, sin) of R_m per row, r floats per row
   uint32_t* status;
   int rows;
+  // true: the attention kernel writes the final output (one run per row and
+  // a bf16 / f32 output); false: it leaves partials for a combine kernel
+  bool direct;
+  float* out_scale;  // fp8 output: one scale per (row, head), else nullptr
 };
 
 // Source of slot a of row `row`; nullptr if the slot is empty.
@@ -64,8 +68,30 @@ __device__ __forceinline__ const T* slot_ptr(const AttnGeom& g, int row, int b, 
   return window + (static_cast<int64_t>(b) * g.w_cap + (n % g.w_cap)) * g.D;
 }
 
+// Largest value of x over the workgroup's NT threads (every thread calls it
+// once; red holds one float per wave).
+template <int NT>
+__device__ __forceinline__ float block_max(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// Token-wise fp8 output of one head ([P2] 融合点 2, with the quantisation of
+// the decode KV): scale = max|o| / 448 over the head's D dims, code =
+// e4m3fn(o / scale) rounded to nearest even; an all-zero head gets scale 0
+// and zero codes.
+__device__ __forceinline__ uint32_t fp8_code(float v, float sc) {
+  return sc > 0.f ? f32_to_fp8(v / sc) : 0u;
+}
+
 // Generic (any D <= 1024, f32 or bf16) attention run.  Output: either the
-// final rotated result (n_runs == 1) or an un-normalised partial
+// final rotated result (g.direct) or an un-normalised partial
 // (max, sum, acc[D]) per head for k_attn_combine.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_attn_generic(
@@ -165,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(
   }
   const int h = hg * kHG + h_loc;
   const bool hv = h < g.H;
-  if (g.n_runs == 1) {
+  if (g.direct) {
     const float inv = run_sum > 0.f ? 1.0f / run_sum : 0.f;
     const int64_t o = (static_cast<int64_t>(row) * g.H + h) * D;
     __syncthreads();
@@ -204,7 +230,9 @@ constexpr int kGCombR = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* __restrict__ part_acc,
                                                       const float* __restrict__ part_ml,
-                                                      T* __restrict__ out, float* __restrict__ lse) {
+                                                      void* __restrict__ out_v,
+                                                      float* __restrict__ lse) {
+  __shared__ float red[4];
   const int row = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   const int64_t m = g.q_pos[row];
   const bool ok = m >= 0 && m < g.max_pos_end;
@@ -260,6 +288,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const int64_t o = (static_cast<int64_t>(row) * g.H + h) * D;
+  float v[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int pr = tid + 256 * k;
@@ -272,8 +301,31 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
       a0 = t0;
       a1 = t1;
     }
-    store_from_f32(out, o + 2 * pr, a0);
-    store_from_f32(out, o + 2 * pr + 1, a1);
+    v[k][0] = a0;
+    v[k][1] = a1;
+  }
+  if (g.out_scale) {
+    const float am = block_max<256>(
+        fmaxf(fmaxf(fabsf(v[0][0]), fabsf(v[0][1])), fmaxf(fabsf(v[1][0]), fabsf(v[1][1]))), red);
+    const float sc = am / 448.0f;
+    uint8_t* out = static_cast<uint8_t*>(out_v);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pr = tid + 256 * k;
+      if (pr < npairs)
+        *reinterpret_cast<uint16_t*>(out + o + 2 * pr) =
+            static_cast<uint16_t>(fp8_code(v[k][0], sc) | (fp8_code(v[k][1], sc) << 8));
+    }
+    if (tid == 0) g.out_scale[static_cast<int64_t>(row) * g.H + h] = sc;
+  } else {
+    T* out = static_cast<T*>(out_v);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pr = tid + 256 * k;
+      if (pr >= npairs) continue;
+      store_from_f32(out, o + 2 * pr, v[k][0]);
+      store_from_f32(out, o + 2 * pr + 1, v[k][1]);
+    }
   }
   if (lse && tid == 0)
     lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
@@ -610,11 +662,14 @@ __device__ __forceinline__ void gather_store(const u32x4 (&stg)[kDStep], int lan
   for (int v = 0; v < kDStep; ++v) *reinterpret_cast<u32x4*>(wl + v * kMPitch + lane * 16) = stg[v];
 }
 
-// Normalise, apply R_m^{-1} and store dims 4 d4 .. 4 d4 + 3 of one head.
-__device__ __forceinline__ void store_head_dims4(float4 acc, float L, int d4, int rot0,
-                                                 const float* cs, uint16_t* orow) {
+// Normalise and apply R_m^{-1} to dims 4 d4 .. 4 d4 + 3 of one head.
+__device__ __forceinline__ void head_dims4(float4 acc, float L, int d4, int rot0, const float* cs,
+                                           float (&v)[4]) {
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  v[0] = acc.x * inv;
+  v[1] = acc.y * inv;
+  v[2] = acc.z * inv;
+  v[3] = acc.w * inv;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int d = 4 * d4 + 2 * p;
@@ -625,7 +680,27 @@ __device__ __forceinline__ void store_head_dims4(float4 acc, float L, int d4, in
       v[2 * p + 1] = -a0 * s + a1 * c;
     }
   }
+}
+
+__device__ __forceinline__ void store_head_dims4(float4 acc, float L, int d4, int rot0,
+                                                 const float* cs, uint16_t* orow) {
+  float v[4];
+  head_dims4(acc, L, d4, rot0, cs, v);
   *reinterpret_cast<uint2*>(orow + 4 * d4) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// The same as fp8 codes with the head's scale: the 128 threads of the
+// workgroup each hold 4 of the head's 512 dims and all call it.
+__device__ __forceinline__ void store_head_dims4_fp8(float4 acc, float L, int d4, int rot0,
+                                                     const float* cs, uint8_t* orow, float* scale,
+                                                     float* red) {
+  float v[4];
+  head_dims4(acc, L, d4, rot0, cs, v);
+  const float am = block_max<128>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))), red);
+  const float sc = am / 448.0f;
+  *reinterpret_cast<uint32_t*>(orow + 4 * d4) = fp8_code(v[0], sc) | (fp8_code(v[1], sc) << 8) |
+                                                (fp8_code(v[2], sc) << 16) | (fp8_code(v[3], sc) << 24);
+  if (d4 == 0) *scale = sc;
 }
 
 template <int NW>
@@ -845,7 +920,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
       t.w += u.w;
     }
     const int hh = hg * kDH + ch;
-    if (g.n_runs == 1) {
+    if (g.direct) {
       store_head_dims4(t, L, d4, rot0, cs_s, out + (static_cast<int64_t>(row) * g.H + hh) * kMD);
       if (lse && d4 == 0)
         lse[static_cast<int64_t>(row) * g.H + hh] = L > 0.f ? M + logf(L) : -INFINITY;
@@ -871,9 +946,10 @@ constexpr int kCombR = 16;
 __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const float* __restrict__ cs_in,
-                                                       uint16_t* __restrict__ out,
+                                                       void* __restrict__ out,
                                                        float* __restrict__ lse) {
   __shared__ float cs_s[kMD];
+  __shared__ float red[2];
   const int row = blockIdx.y, tid = threadIdx.x;
   const int h = blockIdx.x, d4 = tid;
   const int hg = h / kDH, ch = h % kDH, G = g.H / kDH;
@@ -920,7 +996,12 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
     M = Mn;
   }
   __syncthreads();
-  store_head_dims4(t, L, d4, kMD - g.r, cs_s, out + (static_cast<int64_t>(row) * g.H + h) * kMD);
+  const int64_t oh = static_cast<int64_t>(row) * g.H + h;
+  if (g.out_scale)
+    store_head_dims4_fp8(t, L, d4, kMD - g.r, cs_s, static_cast<uint8_t*>(out) + oh * kMD,
+                         g.out_scale + oh, red);
+  else
+    store_head_dims4(t, L, d4, kMD - g.r, cs_s, static_cast<uint16_t*>(out) + oh * kMD);
   if (lse && d4 == 0) lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
@@ -931,9 +1012,10 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
 // step's table when the caller has one, else are computed here.
 __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
-                                                       uint16_t* __restrict__ out,
+                                                       void* __restrict__ out,
                                                        float* __restrict__ lse) {
   __shared__ float cs_s[kMD];
+  __shared__ float red[2];
   const int row = blockIdx.y, h = blockIdx.x, tid = threadIdx.x, d4 = tid;
   const int64_t m = g.q_pos[row];
   const bool ok = m >= 0 && m < g.max_pos_end;
@@ -989,12 +1071,18 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
     M = Mn;
   }
   __syncthreads();
-  store_head_dims4(t, L, d4, kMD - g.r, cs_s, out + (static_cast<int64_t>(row) * g.H + h) * kMD);
+  const int64_t oh = static_cast<int64_t>(row) * g.H + h;
+  if (g.out_scale)
+    store_head_dims4_fp8(t, L, d4, kMD - g.r, cs_s, static_cast<uint8_t*>(out) + oh * kMD,
+                         g.out_scale + oh, red);
+  else
+    store_head_dims4(t, L, d4, kMD - g.r, cs_s, static_cast<uint16_t*>(out) + oh * kMD);
   if (lse && d4 == 0) lse[static_cast<int64_t>(row) * g.H + h] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 struct Plan {
   bool mfma, dec;
+  bool part;  // partials and a combine launch (several runs, or an fp8 output)
   int slots_per_run, n_runs;
   size_t off_acc, off_ml, off_cs, total;
 };
@@ -1044,13 +1132,14 @@ Plan plan(const dsa_attn_args& a) {
     p.slots_per_run = spr;
     p.n_runs = static_cast<int>(ceil_div(total, spr));
   }
+  p.part = p.n_runs > 1 || a.out_fp8;
   size_t off = 0;
   p.off_acc = off;
-  if (p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * 4);
+  if (p.part) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * 4);
   p.off_ml = off;
-  if (p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * 2 * 4);
+  if (p.part) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * 2 * 4);
   p.off_cs = off;
-  if (p.dec && p.n_runs > 1) off = align_up(off + static_cast<size_t>(rows) * a.rope_dim * 4);
+  if (p.dec && p.part) off = align_up(off + static_cast<size_t>(rows) * a.rope_dim * 4);
   p.total = off;
   return p;
 }
@@ -1081,31 +1170,33 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.status = a.status;
   const int rows = a.n_seqs * a.queries_per_seq;
   g.rows = rows;
+  g.direct = !p.part;
+  g.out_scale = a.out_fp8 ? a.out_scale : nullptr;
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
   const hipEvent_t ev0 = static_cast<hipEvent_t>(lx.ev0), ev1 = static_cast<hipEvent_t>(lx.ev1);
-  const bool combine = p.n_runs > 1 && !p.dec && !p.mfma;
+  const bool combine = p.part && !p.dec && !p.mfma;
   if constexpr (sizeof(T) == 2) {
     if (p.dec) {
-      float* cs_ws = p.n_runs > 1 ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
+      float* cs_ws = p.part ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
       const int64_t G = a.heads / kDH, pairs = static_cast<int64_t>(rows) * p.n_runs;
       const dim3 grid(static_cast<unsigned>(ceil_div(pairs, 8) * 8 * G));
       launch_timed(k_attn_decode<kDecWaves>, grid, dim3(kDecWaves * 64), 0, st, ev0,
-                   p.n_runs > 1 ? nullptr : ev1, g,
+                   p.part ? nullptr : ev1, g,
                    static_cast<const uint16_t*>(a.q), a.rotate_q,
                    static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                    static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out), a.lse,
                    part_acc, part_ml, cs_ws);
       dsa_status rc = hip_check(hipGetLastError(), "k_attn_decode launch");
-      if (rc != DSA_OK || p.n_runs == 1) return rc;
+      if (rc != DSA_OK || !p.part) return rc;
       launch_timed(k_attn_dcombine, dim3(a.heads, rows), dim3(128), 0, st, nullptr, ev1, g,
                    static_cast<const float*>(part_acc), static_cast<const float*>(part_ml),
-                   static_cast<const float*>(cs_ws), static_cast<uint16_t*>(a.out), a.lse);
+                   static_cast<const float*>(cs_ws), a.out, a.lse);
       return hip_check(hipGetLastError(), "k_attn_dcombine launch");
     } else if (p.mfma) {
       dim3 grid(static_cast<unsigned>(a.heads / 64), rows, p.n_runs);
-      if (p.n_runs == 1)
+      if (!p.part)
         launch_timed(k_attn_mfma8<true>, grid, dim3(512), 0, st, ev0, ev1, g,
                      static_cast<const uint16_t*>(a.q), a.rotate_q,
                      static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
@@ -1121,7 +1212,7 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
         if (rc != DSA_OK) return rc;
         launch_timed(k_attn_mcombine, dim3(a.heads, rows), dim3(128), 0, st, nullptr, ev1, g,
                      static_cast<const float*>(part_acc), static_cast<const float*>(part_ml),
-                     static_cast<uint16_t*>(a.out), a.lse);
+                     a.out, a.lse);
         return hip_check(hipGetLastError(), "k_attn_mcombine launch");
       }
     }
@@ -1138,7 +1229,8 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   dsa_status rc = hip_check(hipGetLastError(), "attention launch");
   if (rc != DSA_OK || !combine) return rc;
   launch_timed(k_attn_combine<T>, dim3(a.heads, rows), dim3(256), 0, st, nullptr, ev1, g,
-               part_acc, part_ml, static_cast<T*>(a.out), a.lse);
+               static_cast<const float*>(part_acc), static_cast<const float*>(part_ml), a.out,
+               a.lse);
   return hip_check(hipGetLastError(), "k_attn_combine launch");
 }
 

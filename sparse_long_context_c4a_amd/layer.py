@@ -112,7 +112,7 @@ def chunk_from_inputs(w: Workload, inp, device="cuda"):
 
 def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=None,
                status=None, max_pos_end=None, pos_offset=0, rms_gamma=None,
-               rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0):
+               rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0, out_scale=None):
     a = _lib.LayerArgs()
     a.main = _lib.geom(w.s, w.S, w.D, w.r, w.base, pos_offset)
     a.heads, a.idx_heads, a.idx_dim = w.H, w.Hi, w.Di
@@ -131,12 +131,16 @@ def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=No
     a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
     a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps
     a.out, a.lse, a.idx_out = _lib.ptr(out), _lib.ptr(lse), _lib.ptr(idx_out)
+    if out_scale is not None:  # fp8 output codes in out, one scale per (b, t, head)
+        a.out_fp8, a.out_scale = 1, _lib.ptr(out_scale)
     a.status = _lib.ptr(status)
     return a
 
 
-def alloc_outputs(w: Workload, B, T, device="cuda"):
+def alloc_outputs(w: Workload, B, T, device="cuda", out_fp8=False):
     dt = torch.float32 if w.main_dtype == "f32" else torch.bfloat16
+    if out_fp8:
+        dt = torch.uint8
     out = torch.empty((B, T, w.H, w.D), dtype=dt, device=device)
     lse = torch.empty((B, T, w.H), dtype=torch.float32, device=device)
     idx = torch.empty((B, T, w.k), dtype=torch.int32, device=device)
@@ -144,13 +148,15 @@ def alloc_outputs(w: Workload, B, T, device="cuda"):
     return out, lse, idx, status
 
 
-def run(w: Workload, st: LayerState, ch: Chunk, decode=None, ws=None, **kw):
-    """One layer step; returns (out, lse, idx, status, workspace)."""
+def run(w: Workload, st: LayerState, ch: Chunk, decode=None, ws=None, out_fp8=False, **kw):
+    """One layer step; returns (out, lse, idx, status, workspace).  With
+    out_fp8 the output is stored as fp8 codes and out is (codes, scales)."""
     B, T = ch.x.shape[0], ch.T
-    out, lse, idx, status = alloc_outputs(w, B, T, ch.x.device)
-    a = layer_args(w, st, ch, out, lse, idx, status, **kw)
+    out, lse, idx, status = alloc_outputs(w, B, T, ch.x.device, out_fp8)
+    osc = torch.empty((B, T, w.H), dtype=torch.float32, device=ch.x.device) if out_fp8 else None
+    a = layer_args(w, st, ch, out, lse, idx, status, out_scale=osc, **kw)
     if decode is None:
         decode = T == 1
     fn = _lib.layer_decode if decode else _lib.layer_prefill
     ws = fn(a, ws=ws, device=ch.x.device)
-    return out, lse, idx, status, ws
+    return (out, osc) if out_fp8 else out, lse, idx, status, ws

@@ -69,3 +69,28 @@ def check_close(gpu, ref, atol, label=""):
     err = np.max(np.abs(gpu[fin] - ref[fin])) if fin.any() else 0.0
     assert err <= atol, f"{label}: max abs err {err:.3e} > {atol:.1e}"
     return err
+
+
+def check_fp8_heads(codes, scales, ref, err, label=""):
+    """fp8 output of one row ([H, D] codes, [H] scales) against the oracle's
+    values ref [H, D]: each scale is max|ref_h| / 448 within err / 448 (err =
+    the attention's own absolute error before rounding), each decoded value
+    within half an e4m3fn grid step (taken at |ref| + err, the larger binade
+    the kernel's value can fall in) plus err; an all-zero head gives scale 0
+    and zero codes."""
+    from oracle import codecs as oc
+    from oracle import dsa as odsa
+    codes = np.asarray(codes)
+    gsc = np.asarray(scales, np.float64)
+    ref = np.asarray(ref, np.float64)
+    _, osig = odsa.quantize_fp8_heads(ref)
+    assert np.all(np.abs(gsc - osig) <= err / 448.0 + 1e-6 * osig), f"{label}: scales"
+    deq = oc.fp8_decode(codes) * gsc[:, None]
+    gs = np.maximum(gsc[:, None], 1e-300)
+    x = np.where(gsc[:, None] > 0, (np.abs(ref) + err) / gs, 0.0)
+    step = np.where(x < 2 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(x, 1e-300))) - 3))
+    tol = (0.5 + 1e-3) * step * gsc[:, None] + err
+    bad = np.abs(deq - ref) - tol
+    assert np.all(bad <= 0), f"{label}: fp8 output off by {np.max(bad):.3e} beyond the bound"
+    zero = ~np.any(ref, axis=1)
+    assert not codes[zero].any() and not gsc[zero].any(), f"{label}: zero heads"

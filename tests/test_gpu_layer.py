@@ -15,7 +15,8 @@ from oracle import dsa as odsa
 from oracle.run import run_layer
 from sparse_long_context_c4a_amd import configs, inputs as gen
 
-from gpu_helpers import ATOL, LSE_ATOL, check_close, check_topk_row, geometry, to_np
+from gpu_helpers import (ATOL, LSE_ATOL, check_close, check_fp8_heads, check_topk_row,
+                         geometry, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -89,6 +90,39 @@ SMALL = [
     ("f32_prefill_fresh_T200", configs.TINY_C4A_F32, dict(L=200, mode="prefill"), 0, 200,
      "empty"),
 ]
+
+
+@pytest.mark.parametrize("name", ["c4a_decode_B3_L3000", "c128a_decode_B2_L5000",
+                                  "c4a_prefill_ragged_T77"])
+def test_layer_fp8_out(name):
+    """The layer with its output stored as fp8 (fused with the inverse
+    rotation): decoded against the oracle's output, rows with the oracle's
+    selection."""
+    case = next(c for c in SMALL if c[0] == name)
+    _, w0, over, p0, T, state = case
+    w = configs.shrink(w0, **over)
+    seed = 5000 + SMALL.index(case)
+    print(f"[dsa_layer fp8 out] {name} B={w.B} p0={p0} T={T} seed={seed}", flush=True)
+    inp = gen.layer_inputs(w, seed=seed, p0=p0, T=T, state=state)
+    Ly = _layer()
+    st = Ly.state_from_inputs(inp, DEV)
+    ch = Ly.chunk_from_inputs(w, inp, DEV)
+    (codes, osc), lse, idx, status, _ = Ly.run(w, st, ch, out_fp8=True,
+                                               max_pos_end=st.e_cap * w.s)
+    torch.cuda.synchronize()
+    assert status.item() == 0, f"device status {status.item()}"
+    ores = _oracle(w, inp)
+    codes, osc, idx = codes.cpu().numpy(), osc.cpu().numpy(), idx.cpu().numpy()
+    checked = 0
+    for b in range(w.B):
+        for t in range(codes.shape[1]):
+            sel = set(idx[b, t][idx[b, t] >= 0].tolist())
+            if sel != set(ores["idx"][b, t][ores["idx"][b, t] >= 0].tolist()):
+                continue  # outputs are only comparable on the same selection
+            check_fp8_heads(codes[b, t], osc[b, t], ores["out"][b, t], ATOL[w.main_dtype],
+                            f"{name} b={b} t={t}")
+            checked += 1
+    assert checked >= codes.shape[0] * codes.shape[1] // 2
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])

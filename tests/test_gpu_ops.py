@@ -12,7 +12,7 @@ from oracle import dsa as odsa
 from oracle.run import decode_store
 from sparse_long_context_c4a_amd import inputs as gen
 
-from gpu_helpers import ATOL, LSE_ATOL, check_close, check_topk_row, to_np
+from gpu_helpers import ATOL, LSE_ATOL, check_close, check_fp8_heads, check_topk_row, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -315,6 +315,9 @@ ATTN_CASES = [
     ("bf16_chunk_window", "bf16", 64, 512, 64, 128, 1, 40, list(range(2000, 2040)), 1.0, 1, True),
     ("f32_odd_heads", "f32", 20, 64, 16, 16, 2, 1, [500, 40], 0.7, 1, False),
     ("bf16_empty_set", "bf16", 64, 512, 64, 32, 1, 1, [0], 0.0, 1, False),
+    # no compressed entries at all (k = 0): one run of the window, the second
+    # row's window only partly filled
+    ("bf16_window_only", "bf16", 64, 512, 64, 0, 2, 1, [3000, 60], 1.0, 1, False),
     # more than 512 rows of 64 heads take the matrix-core path: one run per
     # row, and (k + W > 2048 slots) two runs merged by the combine kernel
     ("bf16_mfma_rows520", "bf16", 64, 512, 64, 512, 1, 520, list(range(20000, 20520)), 0.95, 1,
@@ -326,12 +329,27 @@ ATTN_CASES = [
 
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
 def test_sparse_attn(case):
+    _attn_case(case, fp8_out=False)
+
+
+# fp8 output (fused with the inverse rotation in the epilogue): the decode
+# path with several runs and with one, the matrix-core path, the generic path
+FP8_OUT_CASES = ["bf16_decode_mixed", "bf16_window_only", "bf16_empty_set", "bf16_mfma_rows520",
+                 "f32_tiny", "f32_odd_heads"]
+
+
+@pytest.mark.parametrize("name", FP8_OUT_CASES)
+def test_sparse_attn_fp8_out(name):
+    _attn_case(next(c for c in ATTN_CASES if c[0] == name), fp8_out=True)
+
+
+def _attn_case(case, fp8_out):
     name, dt, H, D, r, k, B, Tq, positions, fill, rotq, use_chunk = case
     L = _lib()
     seed = 3000 + ATTN_CASES.index(case)
     W, w_cap = 128, 128
     rows = B * Tq
-    print(f"[dsa_sparse_attn] {name} rows={rows} k={k} seed={seed}", flush=True)
+    print(f"[dsa_sparse_attn] {name} rows={rows} k={k} seed={seed} fp8_out={fp8_out}", flush=True)
     rng = np.random.Generator(np.random.PCG64(seed))
     e_cap = max(64, -(-(max(positions) + 1) // 4))
     cache = gen.draw(rng, (B, e_cap, D), dt)
@@ -347,6 +365,9 @@ def test_sparse_attn(case):
     cpos = torch.full((B,), p0, dtype=torch.int64, device=DEV)
     out = torch.zeros((rows, H, D), dtype=torch.float32 if dt == "f32" else torch.bfloat16,
                       device=DEV)
+    if fp8_out:
+        out = torch.zeros((rows, H, D), dtype=torch.uint8, device=DEV)
+        osc = torch.full((rows, H), -1.0, dtype=torch.float32, device=DEV)
     lse = torch.zeros((rows, H), dtype=torch.float32, device=DEV)
     a = L.AttnArgs()
     a.n_seqs, a.queries_per_seq, a.q_pos, a.heads, a.dim = B, Tq, L.ptr(qpos), H, D
@@ -357,9 +378,15 @@ def test_sparse_attn(case):
     a.chunk_win, a.chunk_pos0, a.chunk_len = L.ptr(ch), L.ptr(cpos), Tq if use_chunk else 0
     a.softmax_scale, a.max_pos_end = 0.0, max(positions) + 1
     a.out, a.lse = L.ptr(out), L.ptr(lse)
+    if fp8_out:
+        a.out_fp8, a.out_scale = 1, L.ptr(osc)
     L.sparse_attn(a)
     torch.cuda.synchronize()
-    got, gl = to_np(out), lse.cpu().numpy()
+    gl = lse.cpu().numpy()
+    if fp8_out:
+        codes, gsc = out.cpu().numpy(), osc.cpu().numpy().astype(np.float64)
+    else:
+        got = to_np(out)
     # every row of the small cases; first, last and spread rows of the large
     check = range(rows) if rows <= 64 else sorted({0, 1, 17, rows // 2, rows - 2, rows - 1})
     for i in check:
@@ -378,5 +405,8 @@ def test_sparse_attn(case):
         if rotq:
             qq = odsa.rope_rotate(qq, m, r, 10000.0)
         ref, rl = odsa.sparse_attention(qq, vecs, m, r, 10000.0, 1 / np.sqrt(D))
-        check_close(got[i], ref, ATOL[dt], f"{name} row {i}")
         check_close(gl[i], rl, LSE_ATOL[dt], f"{name} lse row {i}")
+        if fp8_out:
+            check_fp8_heads(codes[i], gsc[i], ref, ATOL[dt], f"{name} fp8 row {i}")
+        else:
+            check_close(got[i], ref, ATOL[dt], f"{name} row {i}")

@@ -168,3 +168,26 @@ def test_softmax_scale_is_one_over_sqrt_d():
     # "DeepSeek DSA、DeepSeek V4与vLLM Hybrid KV Cache详解" 2: softmax(Q K^T / sqrt(d)) V
     assert _geom(D=512).tau == 1 / np.sqrt(512)
     assert _geom(D=128, scale=0.5).tau == 0.5
+
+
+def test_fp8_output_is_nearest_code_per_head():
+    """The fp8 output of each head is, element by element, the nearest of the
+    255 finite e4m3fn values times the head's scale max|o| / 448 (brute force
+    over every code), and an all-zero head gives scale 0 and zero codes."""
+    from oracle import codecs
+    rng = np.random.default_rng(11)
+    out = rng.standard_normal((4, 40)) * np.array([[0.02], [1.0], [37.0], [0.0]])
+    codes, sig = dsa.quantize_fp8_heads(out)
+    assert codes.shape == out.shape and codes.dtype == np.uint8 and sig.shape == (4,)
+    grid = codecs.fp8_decode(np.arange(256, dtype=np.uint8))
+    finite = np.isfinite(grid)
+    for h in range(3):
+        assert sig[h] == float(np.float32(np.abs(out[h]).max() / 448.0))
+        for d in range(out.shape[1]):
+            x = out[h, d] / sig[h]
+            dist = np.where(finite, np.abs(grid - x), np.inf)
+            best = np.flatnonzero(dist == dist.min())
+            assert codes[h, d] in best, (h, d, x)
+        # the largest magnitude maps to the top of the grid
+        assert np.abs(codecs.fp8_decode(codes[h])).max() == 448.0
+    assert sig[3] == 0.0 and not codes[3].any()

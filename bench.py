@@ -8,8 +8,9 @@ insert) on seeded synthetic inputs already resident in HBM.  Input sets are
 rotated (three by default) so that repeated steps do not find the indexer
 keys in the 256 MB Infinity Cache.  Prints one JSON line: the headline c4a
 decode (B=4, L=1M) as the value, the prefill chunk under "prefill", the
-other decode workloads under "workloads" (--no-extra skips them) and the
-oracle's rate on a bounded sample under "cpu_baseline".
+other decode workloads under "workloads" (--no-extra skips them; there also
+the headline step with its output stored as fp8) and the oracle's rate on a
+bounded sample under "cpu_baseline".
 """
 
 import argparse
@@ -90,21 +91,24 @@ def build_sets(w, n_sets, device):
     return sets
 
 
-def time_layer(w, sets, steps, warmup, decode):
+def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
     """Two timed passes of `steps` layer steps each, after `warmup` untimed
     ones.  The first pass gives the step time: nothing but the layer's own
     launches on the stream, bracketed by events.  The second pass hands the
     library HIP events that it attaches to the dispatch packets of the
     scoring kernel and of the attention kernels (hipExtLaunchKernel), which
-    gives their own durations on the stream they run on."""
+    gives their own durations on the stream they run on.  With out_fp8 the
+    layer stores its output as fp8 codes with one scale per (row, head)."""
     import torch
     from sparse_long_context_c4a_amd import _lib
     from sparse_long_context_c4a_amd import layer as Ly
     dev = sets[0][1].x.device
     B, T = sets[0][1].x.shape[0], sets[0][1].T
-    outs = [Ly.alloc_outputs(w, B, T, dev) for _ in sets]
-    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s) for (st, ch), o in
-            zip(sets, outs)]
+    outs = [Ly.alloc_outputs(w, B, T, dev, out_fp8) for _ in sets]
+    scs = [torch.empty((B, T, w.H), dtype=torch.float32, device=dev) if out_fp8 else None
+           for _ in sets]
+    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s, out_scale=sc)
+            for (st, ch), o, sc in zip(sets, outs, scs)]
     ws_bytes = max(_lib.layer_workspace(a) for a in args)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     fn = _lib.layer_decode if decode else _lib.layer_prefill
@@ -277,6 +281,14 @@ def main():
                      "traffic": measured_traffic() if w.name == "c4a_decode_B4_L1M" else None,
                      "kernel": kern, "alg_bytes_per_launch": kbytes},
     }
+    extra = {}
+    if not args.no_extra and w.name == "c4a_decode_B4_L1M":
+        # the same step with the output stored as fp8 (scale per row and head)
+        print("[bench] timing with fp8 output", file=sys.stderr, flush=True)
+        ms8, _, attn8 = time_layer(w, sets, args.steps, args.warmup, decode=True, out_fp8=True)
+        extra[w.name + "_fp8_out"] = {"queries_per_s": w.B / (ms8 / 1e3), "ms_per_step": ms8,
+                                      "batch": w.B, "context": w.L, "k": w.k,
+                                      "kernel_ms": {"attention": attn8}}
     del sets
     torch.cuda.empty_cache()
     if args.calib_copy_mib:
@@ -294,6 +306,7 @@ def main():
         line["workloads"] = {
             x.name: time_decode_workload(x, dev, args.steps, args.warmup, args.sets)
             for x in configs.ALL if x.mode == "decode" and x.name != w.name}
+        line["workloads"].update(extra)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

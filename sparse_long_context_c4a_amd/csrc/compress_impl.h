@@ -59,7 +59,10 @@ __device__ __forceinline__ void compress_one(
     const int64_t* __restrict__ pos0v, const float* __restrict__ logits, void* __restrict__ out,
     float* __restrict__ out_scale, const float* __restrict__ gamma, float eps, int64_t T,
     int logits_rows, int s, int S, int D, int r, double base, int64_t off, int64_t e_cap,
-    int64_t max_pos_end, uint32_t* status) {
+    int64_t max_pos_end, uint32_t* status, int d0 = 0, int dn = -1) {
+  // dims d0 .. d0 + dn - 1 only (dn = -1: all D); a slice is a multiple of 8
+  // dims and needs neither gamma nor fp8 output, which take the whole vector
+  if (dn < 0) dn = D;
   __shared__ float w_s[kCompressMaxSpan];
   __shared__ float red[16];
   __shared__ float red8[kCompressThreads * 8];  // token groups' partial sums
@@ -91,14 +94,14 @@ __device__ __forceinline__ void compress_one(
   sum = block_sum(sum, red);  // contains a barrier: w_s is complete
   const float inv = 1.0f / sum;
 
-  // weighted sum; thread owns pairs (2p, 2p+1), p = tid + k*kCompressThreads
-  const int npairs = D / 2;
+  // weighted sum; thread owns pairs (2p, 2p+1) of the slice, p = tid + k*kCompressThreads
+  const int npairs = dn / 2, pr0 = d0 / 2;
   float acc[kCompressPairs][2];
 #pragma unroll
   for (int k = 0; k < kCompressPairs; ++k) acc[k][0] = acc[k][1] = 0.f;
   const RawT* rawb = raw + static_cast<int64_t>(b) * T * D;
   const RawT* ringb = ring + static_cast<int64_t>(b) * S * D;
-  if (D % 8 == 0 && D / 8 <= kCompressThreads) {
+  if (dn % 8 == 0 && d0 % 8 == 0 && dn / 8 <= kCompressThreads) {
     // 16-byte loads: thread (group gr, column c) sums dims 8c .. 8c+7 over
     // the tokens i = gr (mod ngrp) -- a token row is D/8 threads wide, and
     // the ngrp = 256 / (D/8) groups split the span -- kTok tokens per round
@@ -108,7 +111,7 @@ __device__ __forceinline__ void compress_one(
     // made the 128-token c128a entry bound by the load instruction rate.)
     constexpr int kTok = 8;
     using DV = Dim8<RawT>;
-    const int tpr = D / 8, ngrp = kCompressThreads / tpr;
+    const int tpr = dn / 8, ngrp = kCompressThreads / tpr;
     const int gr = tid / tpr, c = tid % tpr;
     const int64_t pj = static_cast<int64_t>(s) * j;  // the entry's first raw position
     const int ring0 = static_cast<int>(pj % S);
@@ -122,7 +125,7 @@ __device__ __forceinline__ void compress_one(
           const int64_t p = pj + i;
           const int slot = ring0 + i < S ? ring0 + i : ring0 + i - S;
           const RawT* row = (p >= p0) ? rawb + (p - p0) * D : ringb + static_cast<int64_t>(slot) * D;
-          xw[u] = DV::load(row, c);
+          xw[u] = DV::load(row + d0, c);
         }
 #pragma unroll
         for (int u = 0; u < kTok; ++u) {
@@ -132,7 +135,7 @@ __device__ __forceinline__ void compress_one(
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red8[gr * D + 8 * c + e] = a8[e];
+      for (int e = 0; e < 8; ++e) red8[gr * dn + 8 * c + e] = a8[e];
     }
     __syncthreads();
     // back to the layout below: thread owns pairs tid + 256 k
@@ -142,8 +145,8 @@ __device__ __forceinline__ void compress_one(
       if (pr < npairs) {
         float x0 = 0.f, x1 = 0.f;
         for (int g2 = 0; g2 < ngrp; ++g2) {
-          x0 += red8[g2 * D + 2 * pr];
-          x1 += red8[g2 * D + 2 * pr + 1];
+          x0 += red8[g2 * dn + 2 * pr];
+          x1 += red8[g2 * dn + 2 * pr + 1];
         }
         acc[k][0] = x0;
         acc[k][1] = x1;
@@ -158,8 +161,8 @@ __device__ __forceinline__ void compress_one(
       for (int k = 0; k < kCompressPairs; ++k) {
         const int pr = tid + k * kCompressThreads;
         if (pr < npairs) {
-          acc[k][0] = fmaf(wi, load_as_f32(row, 2 * pr), acc[k][0]);
-          acc[k][1] = fmaf(wi, load_as_f32(row, 2 * pr + 1), acc[k][1]);
+          acc[k][0] = fmaf(wi, load_as_f32(row, d0 + 2 * pr), acc[k][0]);
+          acc[k][1] = fmaf(wi, load_as_f32(row, d0 + 2 * pr + 1), acc[k][1]);
         }
       }
     }
@@ -176,8 +179,8 @@ __device__ __forceinline__ void compress_one(
     for (int k = 0; k < kCompressPairs; ++k) {
       const int pr = tid + k * kCompressThreads;
       if (pr < npairs) {
-        acc[k][0] *= gamma[2 * pr] * rs;
-        acc[k][1] *= gamma[2 * pr + 1] * rs;
+        acc[k][0] *= gamma[d0 + 2 * pr] * rs;
+        acc[k][1] *= gamma[d0 + 2 * pr + 1] * rs;
       }
     }
   }
@@ -187,9 +190,9 @@ __device__ __forceinline__ void compress_one(
 #pragma unroll
   for (int k = 0; k < kCompressPairs; ++k) {
     const int pr = tid + k * kCompressThreads;
-    if (pr < npairs && pr >= first_rot_pair) {
+    if (pr < npairs && pr0 + pr >= first_rot_pair) {
       float c, sn;
-      rope_cs(static_cast<int64_t>(s) * j + off, pr - first_rot_pair, r, base, &c, &sn);
+      rope_cs(static_cast<int64_t>(s) * j + off, pr0 + pr - first_rot_pair, r, base, &c, &sn);
       const float a0 = acc[k][0], a1 = acc[k][1];
       acc[k][0] = a0 * c - a1 * sn;
       acc[k][1] = a0 * sn + a1 * c;
@@ -204,8 +207,8 @@ __device__ __forceinline__ void compress_one(
     for (int k = 0; k < kCompressPairs; ++k) {
       const int pr = tid + k * kCompressThreads;
       if (pr < npairs) {
-        store_from_f32(op, 2 * pr, acc[k][0]);
-        store_from_f32(op, 2 * pr + 1, acc[k][1]);
+        store_from_f32(op, d0 + 2 * pr, acc[k][0]);
+        store_from_f32(op, d0 + 2 * pr + 1, acc[k][1]);
       }
     }
   } else {  // fp8 e4m3fn, token-wise scale = amax / 448
@@ -225,7 +228,7 @@ __device__ __forceinline__ void compress_one(
       if (pr < npairs) {
         const uint32_t c0 = sc > 0.f ? f32_to_fp8(acc[k][0] / sc) : 0u;
         const uint32_t c1 = sc > 0.f ? f32_to_fp8(acc[k][1] / sc) : 0u;
-        const int64_t at = tiled ? idx_tile_off(b, e_pad, j, 2 * pr) : 2 * pr;
+        const int64_t at = tiled ? idx_tile_off(b, e_pad, j, d0 + 2 * pr) : d0 + 2 * pr;
         *reinterpret_cast<uint16_t*>(op + at) = static_cast<uint16_t>(c0 | (c1 << 8));
       }
     }

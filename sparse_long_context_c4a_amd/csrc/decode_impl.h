@@ -45,29 +45,51 @@ struct PrologueArgs {
   uint32_t* status;
 };
 
-constexpr int kPrologueRoles = 4;
+// Workgroups of the prologue: kSlices for the main entry, then three.
+template <int kSlices>
+constexpr int prologue_roles() { return kSlices + 3; }
+// The prologue riding in the indexer's launch keeps the main entry in one
+// workgroup (c4a: 8 raw tokens); the stand-alone prologue (c128a: 128 raw
+// tokens of 1 KiB) splits it by dims over four, which puts the loads of the
+// whole span in flight at once (c128a decode: 11.6 -> 7.7 us per launch;
+// eight slices measured the same).  An RMSNorm needs the whole vector, so with
+// gamma (or dims that do not split into 8-dim groups) the first slice does
+// it all.
+constexpr int kPrologueRoles = prologue_roles<1>();
+constexpr int kStandaloneSlices = 4;
 
-// Decode-step prologue, one role per workgroup: role 0 writes the main entry
-// completing at m (if any), role 1 the indexer entry, role 2 puts token m
-// into the compressor rings, the row's query position, and -- when the
-// window ring has a spare slot (w_cap > W) -- the rotated token m (slot
-// m mod w_cap is not in m's window then); role 3 writes the (cos, sin)
-// table of R_m for the attention's query rotation and inverse rotation.  For one token the ring slot
-// written (m mod S) is not one the compressor reads (it reads positions
-// m-S+1 .. m-1 from the ring and m from x), and nothing here is read by the
-// same step's indexer or attention (the new entry is not visible to m), so
-// these workgroups may run beside them.
-template <typename MainT, int kIdxOut>
+// Decode-step prologue, one role per workgroup: roles 0 .. kSlices-1
+// write (their dims of) the main entry completing at m (if any); the next
+// role the indexer entry; the next puts token m into the compressor rings,
+// the row's query position, and -- when the window ring has a spare slot
+// (w_cap > W) -- the rotated token m (slot m mod w_cap is not in m's window
+// then); the last writes the (cos, sin) table of R_m for the attention's
+// query rotation and inverse rotation.  For one token the ring slot written
+// (m mod S) is not one the compressor reads (it reads positions m-S+1 ..
+// m-1 from the ring and m from x), and nothing here is read by the same
+// step's indexer or attention (the new entry is not visible to m), so these
+// workgroups may run beside them.
+template <typename MainT, int kIdxOut, int kSlices>
 __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueArgs a) {
   using IdxRawT = typename std::conditional<kIdxOut == DSA_F32, float, uint16_t>::type;
   constexpr int kMainOut = std::is_same<MainT, float>::value ? DSA_F32 : DSA_BF16;
-  if (role == 0) {
+  if (kSlices == 1 ? role == 0 : static_cast<unsigned>(role) < static_cast<unsigned>(kSlices)) {
+    int d0 = 0, dn = -1;  // all dims
+    if constexpr (kSlices > 1) {
+      const bool split = a.gamma == nullptr && a.D % (8 * kSlices) == 0;
+      if (!split && role > 0) return;
+      if (split) {
+        dn = a.D / kSlices;
+        d0 = role * dn;
+      }
+    }
     compress_one<MainT, kMainOut>(0, b, static_cast<const MainT*>(a.x),
                                   static_cast<const MainT*>(a.main_ring), a.pos0, a.logits_main,
                                   a.main_cache, nullptr, a.gamma, a.eps, 1, 1, a.s, a.S, a.D, a.r,
-                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status);
+                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status, d0, dn);
     return;
   }
+  role -= kSlices - 1;  // 1: indexer entry, 2: rings and window, 3: (cos, sin) table
   if (role == 1) {
     if (a.has_idx)
       compress_one<IdxRawT, kIdxOut>(0, b, static_cast<const IdxRawT*>(a.kx),

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     uint32_t* status) {
   const int id = static_cast<int>(blockIdx.x), npro = pa.B * kPrologueRoles;
   if (id < npro) {
-    decode_prologue_block<MainT, kIdxOut>(id % kPrologueRoles, id / kPrologueRoles, pa);
+    decode_prologue_block<MainT, kIdxOut, 1>(id % kPrologueRoles, id / kPrologueRoles, pa);
   } else {
     const int sid = id - npro;
     index_stream_block<true, kEnt>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale, q_pos, 1,

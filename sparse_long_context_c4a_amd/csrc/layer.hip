@@ -77,7 +77,7 @@ __global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int
 
 template <typename MainT, int kIdxOut>
 __global__ __launch_bounds__(kCompressThreads) void k_decode_prologue(PrologueArgs a) {
-  decode_prologue_block<MainT, kIdxOut>(blockIdx.x / a.B, blockIdx.x % a.B, a);
+  decode_prologue_block<MainT, kIdxOut, kStandaloneSlices>(blockIdx.x / a.B, blockIdx.x % a.B, a);
 }
 
 // Decode-step epilogue when the window ring has no spare slot: the rotated
@@ -183,7 +183,7 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
                                   float* cs_tab, hipStream_t st) {
   const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab);
-  const dim3 grid(kPrologueRoles * a.n_seqs), block(kCompressThreads);
+  const dim3 grid(prologue_roles<kStandaloneSlices>() * a.n_seqs), block(kCompressThreads);
   if (a.dtype == DSA_F32) {
     if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_decode_prologue<float, DSA_FP8_E4M3>), grid, block, 0, st, p);

@@ -227,3 +227,52 @@ def test_layer_full_size_prefill_sampled_rows():
     rows = [0, 1, 2, 3, 4, 5, 127, 128, 1000, 2047, 3333, 4092, 4093, 4094, 4095]
     ores = _oracle(w, inp, only=rows)
     _compare(w, inp, ores, out, lse, idx, rows=rows, label=w.name)
+
+
+WRITTEN = [
+    # name, workload, overrides, RMSNorm on the compressor
+    ("c4a_L3000", configs.C4A_DECODE_64K, dict(B=3, L=3000), False),
+    ("c4a_L3000_rmsnorm", configs.C4A_DECODE_64K, dict(B=3, L=3000), True),
+    ("c128a_L5120", configs.C128A_DECODE_1M, dict(B=2, L=5120, k=64), False),
+    ("c128a_L5120_rmsnorm", configs.C128A_DECODE_1M, dict(B=2, L=5120, k=64), True),
+]
+
+
+@pytest.mark.parametrize("case", WRITTEN, ids=[c[0] for c in WRITTEN])
+def test_layer_decode_written_entry(case):
+    """The main entry a decode step completes (m + 1 a multiple of s, past
+    the first span), as stored in the cache: the decode prologue's compressor
+    (split by dims over several workgroups, or whole when the RMSNorm needs
+    the full vector) against the oracle's entry before storage rounding."""
+    name, w0, over, use_gamma = case
+    w = configs.shrink(w0, **over)
+    seed = 5600 + WRITTEN.index(case)
+    print(f"[dsa_layer written entry] {name} B={w.B} L={w.L} seed={seed}", flush=True)
+    inp = gen.layer_inputs(w, seed=seed, state="random")
+    rng = np.random.default_rng(seed)
+    gam = (1.0 + 0.5 * rng.standard_normal(w.D)).astype(np.float32) if use_gamma else None
+    gam_i = (1.0 + 0.5 * rng.standard_normal(w.Di)).astype(np.float32) \
+        if use_gamma and w.Hi else None
+    Ly = _layer()
+    st = Ly.state_from_inputs(inp, DEV)
+    ch = Ly.chunk_from_inputs(w, inp, DEV)
+    tg = torch.tensor(gam, device=DEV) if gam is not None else None
+    tgi = torch.tensor(gam_i, device=DEV) if gam_i is not None else None
+    _, _, _, status, _ = Ly.run(w, st, ch, max_pos_end=st.e_cap * w.s, rms_gamma=tg,
+                                rms_gamma_idx=tgi)
+    torch.cuda.synchronize()
+    assert status.item() == 0, f"device status {status.item()}"
+    g = geometry(w, gamma=None if gam is None else gam.astype(np.float64),
+                 gamma_idx=None if gam_i is None else gam_i.astype(np.float64))
+    res = run_layer(g, inp)
+    cache = to_np(st.main_cache)
+    n = 0
+    for b in range(w.B):
+        for j0, n_new, main_new, _ in res["states"][b].entries_written:
+            for e in range(n_new):
+                ref = main_new[e]
+                tol = np.abs(ref) * 2.0 ** -8 + 1e-5  # bf16 storage + f32 sums
+                err = np.abs(cache[b, j0 + e] - ref) - tol
+                assert np.all(err <= 0), f"{name} b={b} entry {j0 + e}: {np.max(err):.3e}"
+                n += 1
+    assert n == w.B, n

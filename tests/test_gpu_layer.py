@@ -104,6 +104,10 @@ def test_layer_fp8_out(name):
     seed = 5000 + SMALL.index(case)
     print(f"[dsa_layer fp8 out] {name} B={w.B} p0={p0} T={T} seed={seed}", flush=True)
     inp = gen.layer_inputs(w, seed=seed, p0=p0, T=T, state=state)
+    _check_fp8_layer(w, inp, name)
+
+
+def _check_fp8_layer(w, inp, name):
     Ly = _layer()
     st = Ly.state_from_inputs(inp, DEV)
     ch = Ly.chunk_from_inputs(w, inp, DEV)
@@ -217,6 +221,14 @@ def test_layer_full_size_decode(w):
     ores = _oracle(w, inp)
     swaps = _compare(w, inp, ores, out, lse, idx, label=w.name)
     assert swaps <= 2
+
+
+def test_layer_full_size_decode_fp8_out():
+    """The 1M-context c4a decode step (B = 4) with its output stored as fp8,
+    as the benchmark also times it."""
+    w = configs.C4A_DECODE_1M
+    print(f"[dsa_layer_decode fp8 out] {w.name} full size, seed={w.seed}", flush=True)
+    _check_fp8_layer(w, gen.layer_inputs(w), w.name + " fp8")
 
 
 def test_layer_full_size_prefill_sampled_rows():

@@ -28,6 +28,15 @@ METRIC = "c4a DSA decode queries/s + HBM GB/s (% peak) at L=1M k=512; prefill TF
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0
+# KV-cache sizes the pages print for whole models at 1M tokens ("DeepSeek V4
+# 稀疏注意力完全解剖", opening table: 61 layers), reported beside the
+# throughput as context only -- they are memory sizes, not kernel timings.
+PAGE_KV_CONTEXT = {
+    "source": "DeepSeek V4 稀疏注意力完全解剖, opening table (61 layers, 1M-token sequence)",
+    "kv_gib_per_seq": {"V3.2": 83.9, "V4 bf16": 9.62, "V4 fp4 indexer + fp8 attention": 4.8},
+    "kv_bytes_per_token_per_layer": {"V3.2": 1408, "V4 bf16 (average over layers)": 160,
+                                     "V4 fp4 indexer + fp8 attention (average)": 80},
+}
 
 
 # Hardware byte counters of the scoring kernel, from the committed rocprofv3
@@ -281,6 +290,14 @@ def main():
                      "traffic": measured_traffic() if w.name == "c4a_decode_B4_L1M" else None,
                      "kernel": kern, "alg_bytes_per_launch": kbytes},
     }
+    # this layer's own cache per raw token: one main entry (D dims) and one
+    # indexer key (Di fp8 codes + an f32 scale) per s tokens; the window ring
+    # is a fixed W tokens per sequence
+    el = 2 if w.main_dtype == "bf16" else 4
+    ikey = (w.Di + 4 if w.idx_dtype == "fp8" else 4 * w.Di) if w.Hi else 0
+    line["kv_context"] = dict(PAGE_KV_CONTEXT, this_layer={
+        "layer": w.name.split("_")[0], "bytes_per_token": (w.D * el + ikey) / w.s,
+        "window_bytes_per_seq": w.W * w.D * el})
     extra = {}
     if not args.no_extra and w.name == "c4a_decode_B4_L1M":
         # the same step with the output stored as fp8 (scale per row and head)

@@ -79,3 +79,19 @@ def test_window_brute_force():
         assert list(dsa.window_range(m, W)) == mask
     assert len(dsa.window_range(0, W)) == 0
     assert len(dsa.window_range(10_000, W)) == W
+
+
+def test_kv_memory_figures_are_consistent():
+    """The pages' KV-size figures agree with each other: 1M tokens x 61
+    layers x 1408 B is 83.9 GiB, and the per-sequence sizes of the V4 rows
+    divide to their per-token averages (about 160 and 80 B) and to the
+    quoted ~8.7x reduction."""
+    f = GOLD["kv_memory"]
+    per_layer_tokens = f["context"] * f["layers"]
+    assert round(per_layer_tokens * f["v32_bytes_per_token_layer"] / 2 ** 30, 1) == \
+        f["v32_gib_per_seq"]
+    b4 = f["v4_bf16_gib_per_seq"] * 2 ** 30 / per_layer_tokens
+    assert abs(b4 - f["v4_bf16_bytes_per_token_layer_about"]) / 160 < 0.02   # 161.5 B
+    b8 = f["v4_fp4_fp8_gib_per_seq_about"] * 2 ** 30 / per_layer_tokens
+    assert abs(b8 - f["v4_fp4_fp8_bytes_per_token_layer_about"]) / 80 < 0.02  # 80.6 B
+    assert round(f["v32_gib_per_seq"] / f["v4_bf16_gib_per_seq"], 1) == f["compression_factor_about"]

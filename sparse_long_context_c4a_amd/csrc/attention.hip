@@ -1096,7 +1096,8 @@ Plan plan(const dsa_attn_args& a) {
   // over four head-group workgroups per run); otherwise the 64-head
   // matrix-core kernel, which stages each vector once for all heads.
   // Measured (c4a decode, 640 slots): 4 rows 56 vs 62 us per step, 32 rows
-  // 80 vs 72 us; c128a decode (16 rows of 8320 slots) 146 vs 89 us.
+  // 78 vs 63 us (attention + combine 46 vs 31); c128a decode (16 rows of
+  // 8320 slots) 146 vs 89 us.
   const bool mfma_ok = bf16_512 && a.heads % 64 == 0;
   const bool dec_ok = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048;
   p.dec = dec_ok && (!mfma_ok || (total < 4096 && rows * (a.heads / 64) < 16));

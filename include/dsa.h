@@ -184,6 +184,13 @@ dsa_status dsa_index_topk(const dsa_index_args* a, void* ws, size_t ws_bytes, vo
  * token-wise one, [P2] 第三层): per (row, head) sigma = max_d |out_h[d]| / 448
  * (f32, into out_scale), out = e4m3fn codes of out_h / sigma rounded to
  * nearest even; sigma = 0 gives zero codes.
+ * With cache_fp8 = 1 the compressed entries are stored token-wise in fp8
+ * ([P2] 第三层: decode KV in token-wise fp8): cache holds e4m3fn codes
+ * [B, e_cap, D] (one byte per dim) and cache_scale one f32 scale per entry
+ * [B, e_cap]; entry j's vector is cache_scale[b, j] * code.  The window
+ * stays dtype.  Built for dtype BF16, D = 512, heads a multiple of 16 and
+ * B * Tq * H / 16 <= 2048 (decode shapes); other shapes return
+ * DSA_ERR_UNSUPPORTED.
  */
 typedef struct dsa_attn_args {
   int32_t n_seqs;             /* B                                           */
@@ -214,6 +221,8 @@ typedef struct dsa_attn_args {
   uint32_t* status;
   int32_t out_fp8;            /* 0: out is dtype; 1: out is fp8 codes        */
   float* out_scale;           /* [B * Tq, H] (out_fp8)                       */
+  int32_t cache_fp8;          /* 0: cache is dtype; 1: fp8 codes + scales    */
+  const float* cache_scale;   /* [B, e_cap] (cache_fp8)                      */
 } dsa_attn_args;
 
 size_t dsa_sparse_attn_workspace(const dsa_attn_args* a);

@@ -60,7 +60,8 @@ class AttnArgs(ctypes.Structure):
                 ("window", c_vp), ("w_cap", c_i32), ("window_size", c_i32),
                 ("chunk_win", c_vp), ("chunk_pos0", c_vp), ("chunk_len", c_i64),
                 ("softmax_scale", c_f32), ("max_pos_end", c_i64), ("out", c_vp),
-                ("lse", c_vp), ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp)]
+                ("lse", c_vp), ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp),
+                ("cache_fp8", c_i32), ("cache_scale", c_vp)]
 
 
 class LayerArgs(ctypes.Structure):

@@ -118,6 +118,10 @@ dsa_status validate_attn(const dsa_attn_args* a) {
   REQUIRE(a->max_pos_end >= 1, "dsa_sparse_attn: max_pos_end < 1");
   REQUIRE(a->out_fp8 == 0 || a->out_fp8 == 1, "dsa_sparse_attn: out_fp8 must be 0 or 1");
   REQUIRE(!a->out_fp8 || a->out_scale, "dsa_sparse_attn: out_fp8 needs out_scale");
+  REQUIRE(a->cache_fp8 == 0 || a->cache_fp8 == 1, "dsa_sparse_attn: cache_fp8 must be 0 or 1");
+  REQUIRE(!a->cache_fp8 || a->k == 0 || a->cache_scale, "dsa_sparse_attn: cache_fp8 needs cache_scale");
+  SUPPORT(!a->cache_fp8 || (a->dtype == DSA_BF16 && a->dim == 512),
+          "dsa_sparse_attn: an fp8 cache needs dtype BF16 and dim 512");
   return DSA_OK;
 }
 

@@ -46,6 +46,7 @@ struct AttnGeom {
   // a bf16 / f32 output); false: it leaves partials for a combine kernel
   bool direct;
   float* out_scale;  // fp8 output: one scale per (row, head), else nullptr
+  const float* cache_scale;  // fp8 cache: one scale per entry [B, e_cap], else nullptr
 };
 
 // Source of slot a of row `row`; nullptr if the slot is empty.
@@ -608,12 +609,16 @@ constexpr int kDecWaves = 4;
 
 // Source of slot a of row `row` given its cache index j (read by the caller
 // for a < k); nullptr if the slot is empty.
+template <bool kFp8>
 __device__ __forceinline__ const uint16_t* dslot_ptr(const AttnGeom& g, int b, int64_t m, int a,
                                                      int32_t j, const uint16_t* cache,
                                                      const uint16_t* window,
                                                      const uint16_t* chunk_win) {
   if (a < g.k) {
     if (j < 0 || j >= g.e_cap) return nullptr;
+    if constexpr (kFp8)  // one byte per dim
+      return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(cache) +
+                                               (static_cast<int64_t>(b) * g.e_cap + j) * kMD);
     return cache + (static_cast<int64_t>(b) * g.e_cap + j) * kMD;
   }
   const int64_t n = m - g.W + (a - g.k);
@@ -662,6 +667,58 @@ __device__ __forceinline__ void gather_store(const u32x4 (&stg)[kDStep], int lan
   for (int v = 0; v < kDStep; ++v) *reinterpret_cast<u32x4*>(wl + v * kMPitch + lane * 16) = stg[v];
 }
 
+// The same for a step of fp8 cache entries (512 bytes each): one 16-byte
+// load covers two vectors, lanes 0-31 vector 2u and lanes 32-63 vector
+// 2u + 1, lane l holding the codes of dims 16 (l % 32) .. +15 in stg[u].
+__device__ __forceinline__ uint64_t gather_load8(const uint16_t* src, const uint16_t* dummy,
+                                                 int lane, u32x4 (&stg)[kDStep]) {
+  const uint64_t vmask = __ballot(lane < kDStep && src != nullptr);
+  if (vmask == 0) return 0;
+  if (src == nullptr) src = dummy;
+  const uint64_t sp = reinterpret_cast<uint64_t>(src);
+  const uint32_t sp_lo = static_cast<uint32_t>(sp), sp_hi = static_cast<uint32_t>(sp >> 32);
+  const bool upper = lane >= 32;
+  const uint64_t off = static_cast<uint64_t>(lane & 31) * 16;
+#pragma unroll
+  for (int u = 0; u < kDStep / 2; ++u) {
+    const uint32_t lo0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_lo, 2 * u));
+    const uint32_t hi0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_hi, 2 * u));
+    const uint32_t lo1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_lo, 2 * u + 1));
+    const uint32_t hi1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(sp_hi, 2 * u + 1));
+    const uint64_t base = upper ? ((static_cast<uint64_t>(hi1) << 32) | lo1)
+                                : ((static_cast<uint64_t>(hi0) << 32) | lo0);
+    typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+    stg[u] = *reinterpret_cast<g_u32x4*>(base + off);
+  }
+  return vmask;
+}
+
+// Eight fp8 e4m3fn codes -> eight bf16 (exact: bf16 holds every e4m3 value).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+}
+
+// Stage an fp8 step: the codes widened to bf16 (the entries' scales go on
+// their logits and probabilities); an empty slot, whose stand-in bytes need
+// not be finite as fp8, is staged as zeros.
+__device__ __forceinline__ void gather_store8(const u32x4 (&stg)[kDStep], int lane, uint8_t* wl,
+                                              uint64_t vmask) {
+  const int c = lane & 31, hv = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < kDStep / 2; ++u) {
+    const int v = 2 * u + hv;
+    u32x4 lo = fp8x8_to_bf16x8(stg[u].x, stg[u].y), hi = fp8x8_to_bf16x8(stg[u].z, stg[u].w);
+    if (!((vmask >> v) & 1ull)) lo = hi = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(wl + v * kMPitch + c * 32) = lo;
+    *reinterpret_cast<u32x4*>(wl + v * kMPitch + c * 32 + 16) = hi;
+  }
+}
+
 // Normalise and apply R_m^{-1} to dims 4 d4 .. 4 d4 + 3 of one head.
 __device__ __forceinline__ void head_dims4(float4 acc, float L, int d4, int rot0, const float* cs,
                                            float (&v)[4]) {
@@ -703,7 +760,11 @@ __device__ __forceinline__ void store_head_dims4_fp8(float4 acc, float L, int d4
   if (d4 == 0) *scale = sc;
 }
 
-template <int NW>
+// kFp8: the cache holds fp8 e4m3fn codes with one scale per entry (the
+// pages' token-wise fp8 decode KV; k a multiple of 32, so a wave step is all
+// cache or all window); the window stays bf16.  An entry's scale multiplies
+// its logit and its probability in the weighted sum of code vectors.
+template <int NW, bool kFp8>
 __global__ __launch_bounds__(NW * 64) void k_attn_decode(
     AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
     const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
@@ -746,12 +807,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
   // the first step's gather goes out before the set-up below; later steps
   // load at the top of their iteration
   uint64_t vmask0 = 0;
+  float sig0 = 1.f;
   u32x4 stg0[kDStep];
+  // an fp8 cache slot's scale (1 for window slots and without kFp8)
+  auto slot_scale = [&](int a, const uint16_t* src, int32_t j) -> float {
+    if constexpr (kFp8)
+      if (src != nullptr && a < g.k) return g.cache_scale[static_cast<int64_t>(b) * g.e_cap + j];
+    return 1.f;
+  };
   if (a0 < a_end) {
     const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
-                              ? dslot_ptr(g, b, m, a0 + lane, jn, cache, window, chunk_win)
+                              ? dslot_ptr<kFp8>(g, b, m, a0 + lane, jn, cache, window, chunk_win)
                               : nullptr;
-    vmask0 = gather_load(src, dummy, lane, stg0);
+    sig0 = slot_scale(a0 + lane, src, jn);
+    vmask0 = (kFp8 && a0 < g.k) ? gather_load8(src, dummy, lane, stg0)
+                                : gather_load(src, dummy, lane, stg0);
   }
   // (after the gather: its loads wait on every load issued before them)
   if (g.cs_tab)
@@ -796,11 +866,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
   const int te = (lane & 15) >> 2, tq = lane & 3;
   // one step: the staged vectors to the wave's tile, logits, online softmax,
   // weighted sum
-  auto step = [&](const u32x4 (&stg)[kDStep], uint64_t vmask) {
+  auto step = [&](const u32x4 (&stg)[kDStep], uint64_t vmask, bool st8, float sig) {
     if (vmask != 0) {
       // each wave reads only its own tile, so no barrier: LDS operations of
       // one wave complete in order
-      gather_store(stg, lane, wl);
+      if (kFp8 && st8)
+        gather_store8(stg, lane, wl, vmask);
+      else
+        gather_store(stg, lane, wl);
       v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
@@ -814,11 +887,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
       // log2 units; the running max is raised lazily: the weights
     // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
     // so most tiles need no rescale
+      // the scale of this lane's vector i (4 gq + i, then 16 + 4 gq + i)
+      auto sgi = [&](int i) -> float {
+        if constexpr (kFp8) return __shfl(sig, (i < 4 ? 4 * gq + i : 12 + 4 * gq + i), 64);
+        return 1.f;
+      };
+      // (the lane exchanges run on every lane: outside the selects below)
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * scale2 : -INFINITY;
-        x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * scale2 : -INFINITY;
+        const float sa = sgi(i) * scale2, sb = sgi(4 + i) * scale2;
+        x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * sa : -INFINITY;
+        x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * sb : -INFINITY;
       }
       float tmax = x[0];
 #pragma unroll
@@ -842,6 +922,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       l_run += psum;
+      if constexpr (kFp8)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] *= sgi(i);  // the weighted sum of code vectors
       const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
                        static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
                        static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
@@ -859,16 +942,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
   if (a0 < a_end) {
     // next step's cache indices in flight during this step
     jn = a0 + kSlotsPerIter < a_end ? dslot_index(g, row, a0 + kSlotsPerIter + lane, a_end) : -1;
-    step(stg0, vmask0);
+    step(stg0, vmask0, a0 < g.k, sig0);
     for (a0 += kSlotsPerIter; a0 < a_end; a0 += kSlotsPerIter) {
       u32x4 stg[kDStep];
       const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
-                                ? dslot_ptr(g, b, m, a0 + lane, jn, cache, window, chunk_win)
+                                ? dslot_ptr<kFp8>(g, b, m, a0 + lane, jn, cache, window, chunk_win)
                                 : nullptr;
-      const uint64_t vmask = gather_load(src, dummy, lane, stg);
+      const float sig = slot_scale(a0 + lane, src, jn);
+      const bool st8 = kFp8 && a0 < g.k;
+      const uint64_t vmask = st8 ? gather_load8(src, dummy, lane, stg)
+                                 : gather_load(src, dummy, lane, stg);
       const int nxt = a0 + kSlotsPerIter;
       jn = nxt < a_end ? dslot_index(g, row, nxt + lane, a_end) : -1;
-      step(stg, vmask);
+      step(stg, vmask, st8, sig);
     }
   }
   // merge the NW waves (natural-log units from here on): lane holds
@@ -1100,7 +1186,8 @@ Plan plan(const dsa_attn_args& a) {
   // 8320 slots) 146 vs 89 us.
   const bool mfma_ok = bf16_512 && a.heads % 64 == 0;
   const bool dec_ok = bf16_512 && a.heads % kDH == 0 && rows * (a.heads / kDH) <= 2048;
-  p.dec = dec_ok && (!mfma_ok || (total < 4096 && rows * (a.heads / 64) < 16));
+  // (an fp8 cache is read by the decode kernel only)
+  p.dec = dec_ok && (a.cache_fp8 || !mfma_ok || (total < 4096 && rows * (a.heads / 64) < 16));
   p.mfma = !p.dec && mfma_ok;
   if (p.dec) {
     // about 1024 workgroups: runs of whole NW x 32-slot iterations
@@ -1173,6 +1260,7 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.rows = rows;
   g.direct = !p.part;
   g.out_scale = a.out_fp8 ? a.out_scale : nullptr;
+  g.cache_scale = a.cache_fp8 ? a.cache_scale : nullptr;
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
@@ -1183,8 +1271,8 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
       float* cs_ws = p.part ? reinterpret_cast<float*>(base + p.off_cs) : nullptr;
       const int64_t G = a.heads / kDH, pairs = static_cast<int64_t>(rows) * p.n_runs;
       const dim3 grid(static_cast<unsigned>(ceil_div(pairs, 8) * 8 * G));
-      launch_timed(k_attn_decode<kDecWaves>, grid, dim3(kDecWaves * 64), 0, st, ev0,
-                   p.part ? nullptr : ev1, g,
+      launch_timed(a.cache_fp8 ? k_attn_decode<kDecWaves, true> : k_attn_decode<kDecWaves, false>,
+                   grid, dim3(kDecWaves * 64), 0, st, ev0, p.part ? nullptr : ev1, g,
                    static_cast<const uint16_t*>(a.q), a.rotate_q,
                    static_cast<const uint16_t*>(a.cache), static_cast<const uint16_t*>(a.window),
                    static_cast<const uint16_t*>(a.chunk_win), static_cast<uint16_t*>(a.out), a.lse,
@@ -1245,6 +1333,9 @@ dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st, const A
   const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
   if (shm > 160 * 1024 - 8192) return fail(DSA_ERR_UNSUPPORTED, "attention dim %d too large", a.dim);
   const Plan p = plan(a);
+  if (a.cache_fp8 && (!p.dec || a.k % kDStep != 0))
+    return fail(DSA_ERR_UNSUPPORTED, "an fp8 cache needs bf16, dim 512, k a multiple of %d, heads "
+                "a multiple of %d and rows * heads / %d <= 2048", kDStep, kDH, kDH);
   return a.dtype == DSA_F32 ? launch_typed<float>(a, p, ws, st, lx)
                             : launch_typed<uint16_t>(a, p, ws, st, lx);
 }

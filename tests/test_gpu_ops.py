@@ -343,16 +343,45 @@ def test_sparse_attn_fp8_out(name):
     _attn_case(next(c for c in ATTN_CASES if c[0] == name), fp8_out=True)
 
 
-def _attn_case(case, fp8_out):
+# token-wise fp8 cache (codes + one scale per entry; the window stays bf16):
+# several runs per row, a pre-rotated query, a 40-row chunk (on the decode
+# kernel, which alone reads an fp8 cache), an empty set, no entries at all
+FP8_CACHE_CASES = ["bf16_decode_mixed", "bf16_prerotated_q", "bf16_chunk_window",
+                   "bf16_empty_set", "bf16_window_only"]
+
+
+@pytest.mark.parametrize("name", FP8_CACHE_CASES)
+def test_sparse_attn_fp8_cache(name):
+    _attn_case(next(c for c in ATTN_CASES if c[0] == name), fp8_out=False, fp8_cache=True)
+
+
+def test_sparse_attn_fp8_cache_with_fp8_out():
+    _attn_case(ATTN_CASES[0], fp8_out=True, fp8_cache=True)
+
+
+def test_sparse_attn_fp8_cache_unsupported_shape():
+    """k not a multiple of 32 (a wave step would mix fp8 and bf16 vectors):
+    refused on the host with DSA_ERR_UNSUPPORTED, nothing launched."""
+    L = _lib()
+    with pytest.raises(L.DsaError):
+        _attn_case(next(c for c in ATTN_CASES if c[0] == "bf16_decode_k8192"), fp8_out=False,
+                   fp8_cache=True)
+
+
+def _attn_case(case, fp8_out, fp8_cache=False):
     name, dt, H, D, r, k, B, Tq, positions, fill, rotq, use_chunk = case
     L = _lib()
     seed = 3000 + ATTN_CASES.index(case)
     W, w_cap = 128, 128
     rows = B * Tq
-    print(f"[dsa_sparse_attn] {name} rows={rows} k={k} seed={seed} fp8_out={fp8_out}", flush=True)
+    print(f"[dsa_sparse_attn] {name} rows={rows} k={k} seed={seed} fp8_out={fp8_out} "
+          f"fp8_cache={fp8_cache}", flush=True)
     rng = np.random.Generator(np.random.PCG64(seed))
     e_cap = max(64, -(-(max(positions) + 1) // 4))
-    cache = gen.draw(rng, (B, e_cap, D), dt)
+    if fp8_cache:
+        cache, csc = gen.draw(rng, (B, e_cap, D), "fp8")
+    else:
+        cache = gen.draw(rng, (B, e_cap, D), dt)
     win = gen.draw(rng, (B, w_cap, D), dt)
     q = gen.draw(rng, (rows, H, D), dt)
     nvis = [min(e_cap, odsa.n_vis(m, 4, 8)) for m in positions]
@@ -380,6 +409,9 @@ def _attn_case(case, fp8_out):
     a.out, a.lse = L.ptr(out), L.ptr(lse)
     if fp8_out:
         a.out_fp8, a.out_scale = 1, L.ptr(osc)
+    if fp8_cache:
+        csc_d = torch.tensor(csc, device=DEV)
+        a.cache_fp8, a.cache_scale = 1, L.ptr(csc_d)
     L.sparse_attn(a)
     torch.cuda.synchronize()
     gl = lse.cpu().numpy()
@@ -392,7 +424,7 @@ def _attn_case(case, fp8_out):
     for i in check:
         m = positions[i]
         b = i // Tq
-        ent = decode_store(cache[b], dt)
+        ent = decode_store(cache[b], "fp8", csc[b]) if fp8_cache else decode_store(cache[b], dt)
         wv = decode_store(win[b], dt)
         cv = decode_store(chunk[b], dt) if use_chunk else None
 

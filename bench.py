@@ -179,6 +179,57 @@ def cpu_baseline(w, min_seconds=10.0, max_sets=8):
                       f"{w.B}; full layer step, fp64 NumPy), {dt:.1f} s of oracle time"}
 
 
+def time_attn_cache(w, dev, fp8_cache, steps=20, warmup=5):
+    """The attention op alone (dsa_sparse_attn) at a decode workload's shapes
+    -- B rows at m = L - 1, k selected entries among the visible ones, the
+    W-token window -- over a bf16 cache or a token-wise fp8 one (codes and
+    one scale per entry, the window bf16).  Random bits drawn on the GPU."""
+    import torch
+    from sparse_long_context_c4a_amd import _lib
+    torch.manual_seed(7)
+    nv = _lib.n_complete(w.m, w.s, w.S)
+    e_cap = nv + 2
+    if fp8_cache:  # e4m3fn codes without the NaN patterns, scales in [0.5, 1.5)
+        cache = (torch.randint(0, 0x7f, (w.B, e_cap, w.D), dtype=torch.uint8, device=dev) |
+                 (torch.randint(0, 2, (w.B, e_cap, w.D), dtype=torch.uint8, device=dev) << 7))
+        csc = torch.rand((w.B, e_cap), device=dev) + 0.5
+    else:
+        cache = torch.randn((w.B, e_cap, w.D), device=dev, dtype=torch.bfloat16)
+        csc = None
+    win = torch.randn((w.B, w.W, w.D), device=dev, dtype=torch.bfloat16)
+    q = torch.randn((w.B, w.H, w.D), device=dev, dtype=torch.bfloat16)
+    idx = torch.stack([torch.randperm(nv, device=dev)[:w.k] for _ in range(w.B)]).to(torch.int32)
+    qpos = torch.full((w.B,), w.m, dtype=torch.int64, device=dev)
+    out = torch.empty((w.B, w.H, w.D), device=dev, dtype=torch.bfloat16)
+    a = _lib.AttnArgs()
+    a.n_seqs, a.queries_per_seq, a.q_pos, a.heads, a.dim = w.B, 1, _lib.ptr(qpos), w.H, w.D
+    a.rope_dim, a.rope_base, a.rope_pos_offset = w.r, w.base, 0
+    a.dtype, a.q, a.rotate_q = _lib.DSA_BF16, _lib.ptr(q), 1
+    a.cache, a.e_cap, a.idx, a.k = _lib.ptr(cache), e_cap, _lib.ptr(idx), w.k
+    a.window, a.w_cap, a.window_size = _lib.ptr(win), w.W, w.W
+    a.softmax_scale, a.max_pos_end, a.out = 0.0, w.m + 1, _lib.ptr(out)
+    if fp8_cache:
+        a.cache_fp8, a.cache_scale = 1, _lib.ptr(csc)
+    ws = _lib.sparse_attn(a)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        _lib.sparse_attn(a, ws=ws, stream=stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        _lib.sparse_attn(a, ws=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1e3
+    el = 1 if fp8_cache else 2
+    gathered = w.B * (w.k * w.D * el + w.W * w.D * 2)
+    del cache, csc
+    torch.cuda.empty_cache()
+    return {"us_per_call": us, "cache": "fp8 token-wise" if fp8_cache else "bf16",
+            "gathered_bytes": gathered, "rows": w.B, "k": w.k, "window": w.W}
+
+
 def time_prefill(dev, steps=3, warmup=1):
     """The prefill chunk workload: layer step time, indexer (+Top-k) and
     attention kernel times, and their throughput."""
@@ -324,6 +375,11 @@ def main():
             x.name: time_decode_workload(x, dev, args.steps, args.warmup, args.sets)
             for x in configs.ALL if x.mode == "decode" and x.name != w.name}
         line["workloads"].update(extra)
+        # the attention op alone over a bf16 and an fp8 cache
+        print("[bench] attention op over bf16 and fp8 caches", file=sys.stderr, flush=True)
+        line["workloads"]["attn_op_" + w.name] = {
+            "bf16_cache": time_attn_cache(w, dev, False),
+            "fp8_cache": time_attn_cache(w, dev, True)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

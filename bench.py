@@ -179,7 +179,7 @@ def cpu_baseline(w, min_seconds=10.0, max_sets=8):
                       f"{w.B}; full layer step, fp64 NumPy), {dt:.1f} s of oracle time"}
 
 
-def time_attn_cache(w, dev, fp8_cache, steps=20, warmup=5):
+def time_attn_cache(w, dev, fp8_cache, steps=200, warmup=20):
     """The attention op alone (dsa_sparse_attn) at a decode workload's shapes
     -- B rows at m = L - 1, k selected entries among the visible ones, the
     W-token window -- over a bf16 cache or a token-wise fp8 one (codes and

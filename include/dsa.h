@@ -290,6 +290,8 @@ typedef struct dsa_layer_args {
   void* ev_attn[2];           /* the scoring kernel and the attention kernels */
   int32_t out_fp8;            /* 1: out as fp8 codes + out_scale (see S5)    */
   float* out_scale;           /* [B, T, H] (out_fp8)                         */
+  int32_t main_fp8;           /* 1: main_cache holds token-wise fp8 codes    */
+  float* main_scale;          /* [B, e_cap] (main_fp8); decode only, see S5  */
 } dsa_layer_args;
 
 size_t dsa_layer_workspace(const dsa_layer_args* a);

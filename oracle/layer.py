@@ -63,6 +63,7 @@ class Geometry:
     base_idx: float = 10000.0
     pos_offset: int = 0
     main_dtype: str = "bf16"   # main cache and window
+    main_cache_dtype: str = ""  # "fp8": token-wise fp8 main cache; "": main_dtype
     idx_dtype: str = "fp8"     # indexer cache
     scale: float = None        # softmax scale; None -> 1/sqrt(D)
     gamma: np.ndarray = None   # optional RMSNorm weight of the main compressor
@@ -132,7 +133,7 @@ def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
                                          g.base_idx, off, g.gamma_idx, g.eps)
         for e in range(n_new):
             j = j0 + e
-            st.main_cache[j], _ = store(main_new[e], g.main_dtype)
+            st.main_cache[j], _ = store(main_new[e], g.main_cache_dtype or g.main_dtype)
             if idx_new is not None:
                 val, sig = store(idx_new[e], g.idx_dtype)
                 st.idx_cache[j] = val

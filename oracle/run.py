@@ -88,7 +88,9 @@ def run_layer(g: Geometry, inp, only=None, rotate_q=True):
     idxs = np.full((B, T, g.k), -1, np.int64)
     states = []
     for b in range(B):
-        main = LazyRows(inp["main_cache"][b], g.main_dtype)
+        msc = inp.get("main_scale")
+        main = LazyRows(inp["main_cache"][b], g.main_cache_dtype or g.main_dtype,
+                        None if msc is None else msc[b])
         if has_idx:
             sc = None if inp["idx_scale"] is None else inp["idx_scale"][b]
             idxc = LazyRows(inp["idx_cache"][b], g.idx_dtype, sc)

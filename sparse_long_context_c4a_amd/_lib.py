@@ -76,7 +76,7 @@ class LayerArgs(ctypes.Structure):
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
                 ("status", c_vp), ("ev_index", c_vp * 2), ("ev_attn", c_vp * 2),
-                ("out_fp8", c_i32), ("out_scale", c_vp)]
+                ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32), ("main_scale", c_vp)]
 
 
 EXPORTS = {

@@ -35,6 +35,7 @@ class Workload:
     seed: int = 0
     w_cap: int = 0       # window ring slots (0: 2 W, so a decode step can
                          # insert token m before attention reads [m-W, m-1])
+    main_cache_dtype: str = ""  # "fp8": token-wise fp8 main cache (decode); "": main_dtype
 
     @property
     def E_cap(self):

@@ -144,6 +144,10 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
   REQUIRE(a->max_pos_end >= a->chunk_len, "dsa_layer: max_pos_end < chunk_len");
   REQUIRE(a->out_fp8 == 0 || a->out_fp8 == 1, "dsa_layer: out_fp8 must be 0 or 1");
   REQUIRE(!a->out_fp8 || a->out_scale, "dsa_layer: out_fp8 needs out_scale");
+  REQUIRE(a->main_fp8 == 0 || a->main_fp8 == 1, "dsa_layer: main_fp8 must be 0 or 1");
+  REQUIRE(!a->main_fp8 || a->main_scale, "dsa_layer: main_fp8 needs main_scale");
+  SUPPORT(!a->main_fp8 || (a->dtype == DSA_BF16 && a->main.dim == 512),
+          "dsa_layer: an fp8 main cache is built for dtype BF16 and dim 512");
   if (a->idx_heads > 0) {
     REQUIRE(a->idx_dim >= 2 && a->idx_dim % 2 == 0, "dsa_layer: idx_dim must be even");
     REQUIRE(a->idx_rope_dim >= 0 && a->idx_rope_dim <= a->idx_dim && a->idx_rope_dim % 2 == 0,
@@ -230,6 +234,8 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   aa.lse = a->lse;
   aa.out_fp8 = a->out_fp8;
   aa.out_scale = a->out_scale;
+  aa.cache_fp8 = a->main_fp8;
+  aa.cache_scale = a->main_scale;
   aa.status = a->status;
   L.off_attn_ws = off;
   off = align_up(off + attn_ws_bytes(aa));
@@ -256,6 +262,8 @@ __global__ void k_row_positions(const int64_t* __restrict__ pos0, int T, int B, 
 
 dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStream_t st, bool decode) {
   dsa_status rc = validate_layer(a, decode);
+  if (rc == DSA_OK && a->main_fp8 && !decode)
+    rc = fail(DSA_ERR_UNSUPPORTED, "dsa_layer_prefill: an fp8 main cache is read by decode only");
   if (rc != DSA_OK) return rc;
   LayerWs L = layer_plan(a, nullptr);
   if (!ws || ws_bytes < L.total)

@@ -42,6 +42,7 @@ struct PrologueArgs {
   float* idx_scale;
   int64_t* qpos;
   float* cs_tab;  // role 3: (cos, sin) of R_m, r floats per sequence
+  float* main_scale;  // fp8 main cache: one scale per entry [B, e_cap], else nullptr
   uint32_t* status;
 };
 
@@ -76,6 +77,15 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
   if (kSlices == 1 ? role == 0 : static_cast<unsigned>(role) < static_cast<unsigned>(kSlices)) {
     int d0 = 0, dn = -1;  // all dims
     if constexpr (kSlices > 1) {
+      if (a.main_scale) {  // token-wise fp8: the scale needs the whole vector
+        if (role == 0)
+          compress_one<MainT, DSA_FP8_E4M3>(0, b, static_cast<const MainT*>(a.x),
+                                            static_cast<const MainT*>(a.main_ring), a.pos0,
+                                            a.logits_main, a.main_cache, a.main_scale, a.gamma,
+                                            a.eps, 1, 1, a.s, a.S, a.D, a.r, a.base, a.off,
+                                            a.e_cap, a.max_pos_end, a.status);
+        return;
+      }
       const bool split = a.gamma == nullptr && a.D % (8 * kSlices) == 0;
       if (!split && role > 0) return;
       if (split) {

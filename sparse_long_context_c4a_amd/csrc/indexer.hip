@@ -436,7 +436,7 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                                     hipStream_t st) {
   const Plan P = plan(a);
   const bool fused = P.cand && a.keys != nullptr && P.nv_cap > 0 && a.queries_per_seq == 1 &&
-                     a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16;
+                     a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16 && !la.main_fp8;
   if (!fused) {
     dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, st);
     if (rc != DSA_OK) return rc;

@@ -176,6 +176,7 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
   p.idx_scale = a.idx_scale;
   p.qpos = qpos;
   p.cs_tab = cs_tab;
+  p.main_scale = a.main_fp8 ? a.main_scale : nullptr;
   p.status = a.status;
   return p;
 }

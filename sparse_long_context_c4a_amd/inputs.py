@@ -107,11 +107,19 @@ def layer_inputs(w: Workload, seed=None, p0=None, T=None, state="random",
     out = dict(p0=p0, T=T, E_cap=E_cap, j0=j0, n_new=n_new, seed=seed)
 
     # 1. main cache, 2. indexer cache (+ scales)
-    main_cache = zeros((B, E_cap, D), w.main_dtype)
+    mcd = w.main_cache_dtype or w.main_dtype
+    main_cache = zeros((B, E_cap, D), mcd)
     if state == "random" and j0 > 0:
         for b in range(B):
-            main_cache[b, :j0] = draw(rng, (j0, D), w.main_dtype)
-    out["main_cache"] = main_cache
+            v = draw(rng, (j0, D), mcd)
+            if mcd == "fp8":
+                main_cache[0][b, :j0], main_cache[1][b, :j0] = v
+            else:
+                main_cache[b, :j0] = v
+    if mcd == "fp8":
+        out["main_cache"], out["main_scale"] = main_cache
+    else:
+        out["main_cache"], out["main_scale"] = main_cache, None
     if has_idx:
         ic = zeros((B, E_cap, Di), w.idx_dtype)
         if state == "random" and j0 > 0:

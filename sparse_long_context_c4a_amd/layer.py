@@ -64,6 +64,7 @@ class LayerState:
     idx_ring: torch.Tensor
     window: torch.Tensor
     e_cap: int
+    main_scale: torch.Tensor = None  # token-wise fp8 main cache: one scale per entry
 
 
 @dataclass
@@ -87,7 +88,8 @@ def state_from_inputs(inp, device="cuda"):
                       main_ring=to_device(inp["main_ring"], device),
                       idx_ring=to_device(inp["idx_ring"], device),
                       window=to_device(inp["win_ring"], device),
-                      e_cap=int(inp["E_cap"]))
+                      e_cap=int(inp["E_cap"]),
+                      main_scale=to_device(inp.get("main_scale"), device))
 
 
 def _pad_logits(lg, rows):
@@ -130,6 +132,8 @@ def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=No
     a.main_ring, a.idx_ring = _lib.ptr(st.main_ring), _lib.ptr(st.idx_ring)
     a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
     a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps
+    if st.main_scale is not None:  # fp8 codes in main_cache
+        a.main_fp8, a.main_scale = 1, _lib.ptr(st.main_scale)
     a.out, a.lse, a.idx_out = _lib.ptr(out), _lib.ptr(lse), _lib.ptr(idx_out)
     if out_scale is not None:  # fp8 output codes in out, one scale per (b, t, head)
         a.out_fp8, a.out_scale = 1, _lib.ptr(out_scale)

@@ -24,7 +24,8 @@ TOPK_REL = 1e-5
 
 def geometry(w, **over):
     d = dict(s=w.s, S=w.S, D=w.D, r=w.r, Di=w.Di, r_idx=w.r_idx, H=w.H, Hi=w.Hi, k=w.k, W=w.W,
-             base=w.base, base_idx=w.base, main_dtype=w.main_dtype, idx_dtype=w.idx_dtype)
+             base=w.base, base_idx=w.base, main_dtype=w.main_dtype, idx_dtype=w.idx_dtype,
+             main_cache_dtype=w.main_cache_dtype)
     d.update(over)
     return Geometry(**d)
 

@@ -288,3 +288,38 @@ def test_layer_decode_written_entry(case):
                 assert np.all(err <= 0), f"{name} b={b} entry {j0 + e}: {np.max(err):.3e}"
                 n += 1
     assert n == w.B, n
+
+
+FP8_MAIN = [
+    # name, workload, overrides: a token-wise fp8 main cache read by the
+    # decode attention and written by the decode prologue's compressor
+    ("c4a_decode_B3_L3000", configs.C4A_DECODE_64K, dict(B=3, L=3000)),
+    ("c4a_decode_L20_tiny", configs.C4A_DECODE_64K, dict(B=2, L=20)),
+    ("c128a_L5120", configs.C128A_DECODE_1M, dict(B=2, L=5120, k=64)),
+]
+
+
+@pytest.mark.parametrize("case", FP8_MAIN, ids=[c[0] for c in FP8_MAIN])
+def test_layer_decode_fp8_main_cache(case):
+    """Decode over a token-wise fp8 main cache: outputs against the oracle
+    reading the same codes and scales, and the entry the step completes
+    stored as the oracle's quantisation of it (within half a grid step)."""
+    name, w0, over = case
+    w = configs.shrink(w0, main_cache_dtype="fp8", **over)
+    seed = 5700 + FP8_MAIN.index(case)
+    print(f"[dsa_layer fp8 main cache] {name} B={w.B} L={w.L} seed={seed}", flush=True)
+    inp = gen.layer_inputs(w, seed=seed, state="random")
+    st, out, lse, idx = _run_gpu(w, inp)
+    ores = _oracle(w, inp)
+    _compare(w, inp, ores, out, lse, idx, label=name)
+    codes, sc = st.main_cache.cpu().numpy(), st.main_scale.cpu().numpy()
+    n = 0
+    for b in range(w.B):
+        for j0, n_new, main_new, _ in ores["states"][b].entries_written:
+            for e in range(n_new):
+                j = j0 + e
+                check_fp8_heads(codes[b, j][None], sc[b, j][None], main_new[e][None], 1e-4,
+                                f"{name} b={b} entry {j}")
+                n += 1
+    if (w.L - w.S) % w.s == 0 and w.L >= w.S:
+        assert n == w.B, n

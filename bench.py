@@ -357,6 +357,16 @@ def main():
         extra[w.name + "_fp8_out"] = {"queries_per_s": w.B / (ms8 / 1e3), "ms_per_step": ms8,
                                       "batch": w.B, "context": w.L, "k": w.k,
                                       "kernel_ms": {"attention": attn8}}
+        # the same step over a token-wise fp8 main cache (decode prologue
+        # unfused, the attention reading fp8 entries)
+        print("[bench] timing over an fp8 main cache", file=sys.stderr, flush=True)
+        wm = configs.shrink(w, main_cache_dtype="fp8")
+        sets_m = build_sets(wm, args.sets, dev)
+        msm, idxm, attnm = time_layer(wm, sets_m, args.steps, args.warmup, decode=True)
+        del sets_m
+        extra[w.name + "_fp8_main_cache"] = {
+            "queries_per_s": w.B / (msm / 1e3), "ms_per_step": msm, "batch": w.B,
+            "context": w.L, "k": w.k, "kernel_ms": {"indexer": idxm, "attention": attnm}}
     del sets
     torch.cuda.empty_cache()
     if args.calib_copy_mib:

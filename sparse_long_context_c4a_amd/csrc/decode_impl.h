@@ -70,22 +70,24 @@ constexpr int kStandaloneSlices = 4;
 // m-1 from the ring and m from x), and nothing here is read by the same
 // step's indexer or attention (the new entry is not visible to m), so these
 // workgroups may run beside them.
-template <typename MainT, int kIdxOut, int kSlices>
+// kMainFp8: the main entry goes out as token-wise fp8 (codes + a.main_scale),
+// whole in the first workgroup since the scale needs the vector's max.
+template <typename MainT, int kIdxOut, int kSlices, bool kMainFp8 = false>
 __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueArgs a) {
   using IdxRawT = typename std::conditional<kIdxOut == DSA_F32, float, uint16_t>::type;
   constexpr int kMainOut = std::is_same<MainT, float>::value ? DSA_F32 : DSA_BF16;
   if (kSlices == 1 ? role == 0 : static_cast<unsigned>(role) < static_cast<unsigned>(kSlices)) {
     int d0 = 0, dn = -1;  // all dims
+    if constexpr (kMainFp8) {
+      if (role == 0)
+        compress_one<MainT, DSA_FP8_E4M3>(0, b, static_cast<const MainT*>(a.x),
+                                          static_cast<const MainT*>(a.main_ring), a.pos0,
+                                          a.logits_main, a.main_cache, a.main_scale, a.gamma,
+                                          a.eps, 1, 1, a.s, a.S, a.D, a.r, a.base, a.off,
+                                          a.e_cap, a.max_pos_end, a.status);
+      return;
+    }
     if constexpr (kSlices > 1) {
-      if (a.main_scale) {  // token-wise fp8: the scale needs the whole vector
-        if (role == 0)
-          compress_one<MainT, DSA_FP8_E4M3>(0, b, static_cast<const MainT*>(a.x),
-                                            static_cast<const MainT*>(a.main_ring), a.pos0,
-                                            a.logits_main, a.main_cache, a.main_scale, a.gamma,
-                                            a.eps, 1, 1, a.s, a.S, a.D, a.r, a.base, a.off,
-                                            a.e_cap, a.max_pos_end, a.status);
-        return;
-      }
       const bool split = a.gamma == nullptr && a.D % (8 * kSlices) == 0;
       if (!split && role > 0) return;
       if (split) {

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
 // first so that they are dispatched with the first wave of workgroups, not
 // after the stream has freed compute units.  The rest stream the keys: nb
 // workgroups per row.
-template <typename MainT, int kIdxOut, int kEnt>
+template <typename MainT, int kIdxOut, int kEnt, bool kMainFp8 = false>
 __global__ __launch_bounds__(kThreads) void k_decode_index(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     uint32_t* status) {
   const int id = static_cast<int>(blockIdx.x), npro = pa.B * kPrologueRoles;
   if (id < npro) {
-    decode_prologue_block<MainT, kIdxOut, 1>(id % kPrologueRoles, id / kPrologueRoles, pa);
+    decode_prologue_block<MainT, kIdxOut, 1, kMainFp8>(id % kPrologueRoles, id / kPrologueRoles,
+                                                       pa);
   } else {
     const int sid = id - npro;
     index_stream_block<true, kEnt>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale, q_pos, 1,
@@ -436,7 +437,7 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                                     hipStream_t st) {
   const Plan P = plan(a);
   const bool fused = P.cand && a.keys != nullptr && P.nv_cap > 0 && a.queries_per_seq == 1 &&
-                     a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16 && !la.main_fp8;
+                     a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16;
   if (!fused) {
     dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, st);
     if (rc != DSA_OK) return rc;
@@ -456,7 +457,10 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                  a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,
                  pa, a.status);
   };
-  go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024>);
+  if (la.main_fp8)
+    go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024, true>);
+  else
+    go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024>);
   dsa_status rc = hip_check(hipGetLastError(), "k_decode_index launch");
   if (rc != DSA_OK) return rc;
   hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,

@@ -75,9 +75,10 @@ __global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int
   for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
 }
 
-template <typename MainT, int kIdxOut>
+template <typename MainT, int kIdxOut, bool kMainFp8 = false>
 __global__ __launch_bounds__(kCompressThreads) void k_decode_prologue(PrologueArgs a) {
-  decode_prologue_block<MainT, kIdxOut, kStandaloneSlices>(blockIdx.x / a.B, blockIdx.x % a.B, a);
+  decode_prologue_block<MainT, kIdxOut, kStandaloneSlices, kMainFp8>(blockIdx.x / a.B,
+                                                                     blockIdx.x % a.B, a);
 }
 
 // Decode-step epilogue when the window ring has no spare slot: the rotated
@@ -189,8 +190,14 @@ dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool i
     if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_decode_prologue<float, DSA_FP8_E4M3>), grid, block, 0, st, p);
   } else {
-    if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_F32>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_FP8_E4M3>), grid, block, 0, st, p);
+    if (p.main_scale) {  // token-wise fp8 main cache
+      if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_F32, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_FP8_E4M3, true>), grid, block, 0, st, p);
+    } else if (a.idx_dtype == DSA_F32) {
+      hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_F32>), grid, block, 0, st, p);
+    } else {
+      hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_FP8_E4M3>), grid, block, 0, st, p);
+    }
   }
   return hip_check(hipGetLastError(), "k_decode_prologue launch");
 }

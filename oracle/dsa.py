@@ -32,6 +32,10 @@ design notes):
 * The window [m-W, m-1] excludes m; one joint softmax runs over the selected
   entries and the window tokens.
 * Softmax scale 1/sqrt(D).
+* Token-wise fp8 (indexer keys; the optional fp8 main cache of decode; the
+  optional fp8 attention output, per query and head): one f32 scale per
+  vector, max|v| / 448, e4m3fn codes rounded to nearest even.  The pages
+  name the formats but give no scale rule for the main cache or the output.
 """
 
 import numpy as np

@@ -85,10 +85,11 @@ class SeqState:
     idx_ring: np.ndarray        # [S, Di]
     win_ring: np.ndarray        # [W_cap, D] rotated token n at slot n mod W_cap
     entries_written: list = field(default_factory=list)
+    alt_out: dict = field(default_factory=dict)
 
 
 def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
-                Q, QI, WT, rotate_q=True, only=None):
+                Q, QI, WT, rotate_q=True, only=None, alt_idx=None):
     """Run the layer over raw tokens p0 .. p0+T-1 of one sequence.
 
     X [T, D], KX [T, Di] raw (un-rotated) tokens for the main and indexer
@@ -103,6 +104,16 @@ def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
     visible entry, which needs k >= n_vis ([P2] 机制三: c128a k = 8192 over
     8K entries is full attention).  ``only``: optional iterable of chunk
     offsets whose outputs are computed (the state update is always full).
+
+    The rotated query R_m q is held in the layer's storage dtype before the
+    logits: the pages rotate and quantise the query in one fused step ahead
+    of the attention ([P2] 全景图, decode step A: "Q RoPE + quant").
+
+    ``alt_idx`` [T, k] (optional): another selection per row, already checked
+    against this one under the tie rule; where its set differs, the
+    attention is also evaluated on it (stepwise parity: the attention of a
+    row whose Top-k took an allowed tie swap is compared on the set actually
+    chosen).  Those results go to ``st.alt_out`` as {t: (out, lse)}.
 
     Returns (out [T, H, D], lse [T, H], idx [T, k]) and updates ``st`` in
     place.
@@ -170,8 +181,16 @@ def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
         idxs[t] = idx
         # S5: attention over the selected entries and the window.
         vecs = dsa.gather_set(m, idx, st.main_cache, win_vec, W)
-        q = dsa.rope_rotate(Q[t], m + off, g.r, g.base) if rotate_q else np.asarray(Q[t], np.float64)
+        if rotate_q:
+            q, _ = store(dsa.rope_rotate(Q[t], m + off, g.r, g.base), g.main_dtype)
+        else:
+            q = np.asarray(Q[t], np.float64)
         outs[t], lses[t] = dsa.sparse_attention(q, vecs, m + off, g.r, g.base, g.tau)
+        if alt_idx is not None:
+            alt = np.asarray(alt_idx[t])
+            if set(alt[alt >= 0].tolist()) != set(idx[idx >= 0].tolist()):
+                avecs = dsa.gather_set(m, alt, st.main_cache, win_vec, W)
+                st.alt_out[t] = dsa.sparse_attention(q, avecs, m + off, g.r, g.base, g.tau)
 
     # State update: compressor rings and window ring take the chunk's tokens.
     for p in range(max(p0, p0 + T - S), p0 + T):

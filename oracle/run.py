@@ -70,10 +70,12 @@ def raw_dtype_idx(idx_dtype):
     return "f32" if idx_dtype == "f32" else "bf16"
 
 
-def run_layer(g: Geometry, inp, only=None, rotate_q=True):
+def run_layer(g: Geometry, inp, only=None, rotate_q=True, alt_idx=None):
     """Run one layer step for every sequence of ``inp`` (the dict produced by
     the seeded generator).  ``only``: optional list of chunk offsets t whose
     outputs are wanted (others are skipped; the state update is complete).
+    ``alt_idx`` [B, T, k] (optional): per-row selections to also attend over
+    where they differ from the oracle's (see ``layer_chunk``).
 
     Returns dict(out [B, T, H, D], lse [B, T, H], idx [B, T, k],
     states [per-sequence SeqState]).
@@ -116,7 +118,8 @@ def run_layer(g: Geometry, inp, only=None, rotate_q=True):
         q = decode_store(inp["q"][b], g.main_dtype)
         o, l, ix = layer_chunk(g, st, p0, x, kx,
                                np.asarray(inp["logits_main"][b], np.float64), lg_idx,
-                               q, qi, wt, rotate_q=rotate_q, only=only)
+                               q, qi, wt, rotate_q=rotate_q, only=only,
+                               alt_idx=None if alt_idx is None else alt_idx[b])
         outs[b], lses[b], idxs[b] = o, l, ix
         states.append(st)
     return dict(out=outs, lse=lses, idx=idxs, states=states)

@@ -53,6 +53,30 @@ def _compile(src):
     return obj
 
 
+PROBES = os.path.join(ROOT, "tests", "hw")
+
+
+def build_probes(verbose=True):
+    """Hardware probes the tests load (tests/hw/*.hip -> tests/hw/lib*.so);
+    they are not part of libdsa.so."""
+    if not os.path.isdir(PROBES):
+        return []
+    out = []
+    for f in sorted(os.listdir(PROBES)):
+        if not f.endswith(".hip"):
+            continue
+        lib = os.path.join(PROBES, "lib" + f[:-4] + ".so")
+        cmd = [hipcc(), *FLAGS, "-shared", os.path.join(PROBES, f), "-o", lib + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {f}:\n{r.stderr}")
+        os.replace(lib + ".tmp", lib)
+        out.append(lib)
+    if verbose and out:
+        print(f"built {len(out)} test probe(s) under {PROBES}")
+    return out
+
+
 def build(verbose=True):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -66,6 +90,7 @@ def build(verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
+    build_probes(verbose)
     return LIB
 
 

@@ -148,6 +148,10 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
   REQUIRE(!a->main_fp8 || a->main_scale, "dsa_layer: main_fp8 needs main_scale");
   SUPPORT(!a->main_fp8 || (a->dtype == DSA_BF16 && a->main.dim == 512),
           "dsa_layer: an fp8 main cache is built for dtype BF16 and dim 512");
+  if (a->main_fp8) {  // refused before the step writes any state
+    rc = attn_fp8_cache_shape(a->k, a->heads, static_cast<int64_t>(a->n_seqs) * a->chunk_len);
+    if (rc != DSA_OK) return rc;
+  }
   if (a->idx_heads > 0) {
     REQUIRE(a->idx_dim >= 2 && a->idx_dim % 2 == 0, "dsa_layer: idx_dim must be even");
     REQUIRE(a->idx_rope_dim >= 0 && a->idx_rope_dim <= a->idx_dim && a->idx_rope_dim % 2 == 0,

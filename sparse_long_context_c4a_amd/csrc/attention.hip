@@ -133,6 +133,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(
         const float t0 = a0 * c - a1 * s, t1 = a0 * s + a1 * c;
         a0 = t0;
         a1 = t1;
+        if constexpr (sizeof(T) == 2) {  // the rotated query is held in bf16
+          a0 = bf16_to_f32(f32_to_bf16(a0));
+          a1 = bf16_to_f32(f32_to_bf16(a1));
+        }
       }
     }
     q_s[hh * D + 2 * pr] = a0;
@@ -1327,15 +1331,25 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
 
 size_t attn_ws_bytes(const dsa_attn_args& a) { return plan(a).total; }
 
+dsa_status attn_fp8_cache_shape(int k, int heads, int64_t rows) {
+  if (k % kDStep != 0 || heads % kDH != 0 || rows * (heads / kDH) > 2048)
+    return fail(DSA_ERR_UNSUPPORTED, "an fp8 cache needs bf16, dim 512, k a multiple of %d, heads "
+                "a multiple of %d and rows * heads / %d <= 2048 (k %d, heads %d, rows %lld)",
+                kDStep, kDH, kDH, k, heads, static_cast<long long>(rows));
+  return DSA_OK;
+}
+
 dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st, const AttnLaunch& lx) {
   if (a.dim > kMaxD || a.dim % 16 != 0)
     return fail(DSA_ERR_UNSUPPORTED, "attention dim %d must be a multiple of 16, <= %d", a.dim, kMaxD);
   const size_t shm = static_cast<size_t>(kHG + kTile) * a.dim * sizeof(float);
   if (shm > 160 * 1024 - 8192) return fail(DSA_ERR_UNSUPPORTED, "attention dim %d too large", a.dim);
   const Plan p = plan(a);
-  if (a.cache_fp8 && (!p.dec || a.k % kDStep != 0))
-    return fail(DSA_ERR_UNSUPPORTED, "an fp8 cache needs bf16, dim 512, k a multiple of %d, heads "
-                "a multiple of %d and rows * heads / %d <= 2048", kDStep, kDH, kDH);
+  if (a.cache_fp8) {
+    const dsa_status rc = attn_fp8_cache_shape(a.k, a.heads, static_cast<int64_t>(a.n_seqs) * a.queries_per_seq);
+    if (rc != DSA_OK) return rc;
+    if (!p.dec) return fail(DSA_ERR_UNSUPPORTED, "an fp8 cache is read by the decode kernel only");
+  }
   return a.dtype == DSA_F32 ? launch_typed<float>(a, p, ws, st, lx)
                             : launch_typed<uint16_t>(a, p, ws, st, lx);
 }

@@ -54,6 +54,9 @@ struct AttnLaunch {
   const float* cs_tab = nullptr;  // (cos, sin) of each row's position, rope_dim floats per row
 };
 size_t attn_ws_bytes(const dsa_attn_args& a);
+// The shapes whose attention can read a token-wise fp8 cache (the decode
+// kernel's): DSA_OK or DSA_ERR_UNSUPPORTED with the message set.
+dsa_status attn_fp8_cache_shape(int k, int heads, int64_t rows);
 dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st,
                        const AttnLaunch& lx = AttnLaunch{});
 

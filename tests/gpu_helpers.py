@@ -14,11 +14,13 @@ from oracle import dsa as odsa
 from oracle.layer import Geometry
 
 ATOL = {"f32": 1e-4, "bf16": 2e-2}
-# log-sum-exp of the logits: with bf16 storage the rotated query is rounded to
-# bf16 before the matrix-core product (relative error <= 2^-9 per element), so
-# a logit tau * q.v of N(0,1) data moves by about tau * |q| |v| 2^-9 / sqrt(3)
-# ~ 1e-3 and by at most ~4e-2; 1e-2 is taken.  f32 keeps the f32 bound.
-LSE_ATOL = {"f32": 1e-4, "bf16": 1e-2}
+# log-sum-exp of the logits.  Both sides hold the rotated query in the
+# storage dtype (the pages rotate and quantise the query in one step before
+# the attention: "DeepSeek V4 稀疏注意力完全解剖", 全景图 step A), so what is
+# left is f32 summation (~1e-6) and the rare query element whose f32 and
+# fp64 rotations round to neighbouring bf16 values: one such element moves
+# a logit by at most 2^-8 |q_d| |v_d| / sqrt(D) ~ 2e-4 for N(0,1) data.
+LSE_ATOL = {"f32": 1e-4, "bf16": 1e-3}
 TOPK_REL = 1e-5
 
 
@@ -44,7 +46,9 @@ def check_topk_row(gpu_row, scores, k, label=""):
     want = min(k, n)
     sel = gpu_row[gpu_row >= 0]
     assert len(sel) == want, f"{label}: {len(sel)} selected, expected {want}"
-    assert np.all(gpu_row[want:] == -1) or len(sel) == want, label
+    # the selection fills the first min(k, n_vis) places, then -1 padding
+    assert np.all(gpu_row[:want] >= 0), f"{label}: padding inside the selection"
+    assert np.all(gpu_row[want:] == -1), f"{label}: padding is not -1"
     assert len(np.unique(sel)) == len(sel), f"{label}: duplicate indices"
     assert np.all(sel < n), f"{label}: index beyond n_vis"
     if want == n:
@@ -61,13 +65,26 @@ def check_topk_row(gpu_row, scores, k, label=""):
     return len(diff) // 2
 
 
-def check_close(gpu, ref, atol, label=""):
+# Largest error seen per kind over the session: kind -> (err, bound, label).
+# The test session prints them at the end (tests/conftest.py).
+MAXERR = {}
+
+
+def note_err(kind, err, bound, label):
+    cur = MAXERR.get(kind)
+    if cur is None or err > cur[0]:
+        MAXERR[kind] = (float(err), float(bound), label)
+
+
+def check_close(gpu, ref, atol, label="", kind=None):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu) == np.isfinite(ref)), f"{label}: non-finite mismatch"
     fin = np.isfinite(ref)
     err = np.max(np.abs(gpu[fin] - ref[fin])) if fin.any() else 0.0
+    if kind:
+        note_err(kind, err, atol, label)
     assert err <= atol, f"{label}: max abs err {err:.3e} > {atol:.1e}"
     return err
 

@@ -200,6 +200,22 @@ def test_layer_without_indexer_needs_k_over_n_vis():
     assert _lib.layer_workspace(a) > 0
 
 
+@pytest.mark.parametrize("kw", [dict(k=100), dict(heads=40), dict(n_seqs=600)])
+def test_layer_fp8_main_cache_shapes_refused_before_launch(kw):
+    """An fp8 main cache is read by the decode attention only, which takes k
+    a multiple of 32, heads a multiple of 16 and rows * heads / 16 <= 2048;
+    other shapes are refused by the host checks (DSA_ERR_UNSUPPORTED) before
+    the step writes any state -- here with no workspace and no GPU, so a
+    launch would have failed differently."""
+    a = _layer_args(main_fp8=1, main_scale=_fake(99 * 4096), **kw)
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_layer_decode(ctypes.byref(a), None, 0, None))
+    assert e.value.code == -2, str(e.value)
+    assert "fp8" in str(e.value)
+    ok = _layer_args(main_fp8=1, main_scale=_fake(99 * 4096))
+    assert _lib.layer_workspace(ok) > 0
+
+
 def test_idx_tile_layout_roundtrip_and_offsets():
     """The key tile layout helpers: a byte permutation whose inverse restores
     the rows, and whose positions follow the documented offset formula."""

@@ -9,6 +9,7 @@ import torch
 
 from oracle import codecs as oc
 from oracle import dsa as odsa
+from oracle.layer import store as ostore
 from oracle.run import decode_store
 from sparse_long_context_c4a_amd import inputs as gen
 
@@ -434,11 +435,11 @@ def _attn_case(case, fp8_out, fp8_cache=False):
             return wv[n % w_cap]
         vecs = odsa.gather_set(m, idx[i], ent, win_vec, W)
         qq = decode_store(q[i], dt)
-        if rotq:
-            qq = odsa.rope_rotate(qq, m, r, 10000.0)
+        if rotq:  # the rotated query is held in the storage dtype
+            qq, _ = ostore(odsa.rope_rotate(qq, m, r, 10000.0), dt)
         ref, rl = odsa.sparse_attention(qq, vecs, m, r, 10000.0, 1 / np.sqrt(D))
-        check_close(gl[i], rl, LSE_ATOL[dt], f"{name} lse row {i}")
+        check_close(gl[i], rl, LSE_ATOL[dt], f"{name} lse row {i}", kind=f"attn lse {dt}")
         if fp8_out:
             check_fp8_heads(codes[i], gsc[i], ref, ATOL[dt], f"{name} fp8 row {i}")
         else:
-            check_close(got[i], ref, ATOL[dt], f"{name} row {i}")
+            check_close(got[i], ref, ATOL[dt], f"{name} row {i}", kind=f"attn out {dt}")

@@ -21,7 +21,9 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
  *    row-major in the layout given per field.  The library never allocates,
  *    frees or synchronises; scratch memory comes in through the workspace
- *    argument (size from the matching *_workspace query, alignment 256 B).
+ *    argument (size from the matching *_workspace query, alignment 256 B),
+ *    except for dsa_layer_decode_noalloc, whose scratch is a static device
+ *    array of the library.
  *  - Each call validates its arguments on the host, enqueues kernels on
  *    `stream` (a hipStream_t; NULL = the default stream) and returns.  On a
  *    validation failure nothing is launched.
@@ -49,8 +51,9 @@
  *  - RoPE acts on interleaved pairs of the last rope_dim dims of a vector,
  *    pair i rotated by angle (pos + rope_pos_offset) * rope_base^(-2i/rope_dim).
  *    rope_pos_offset shifts every rotation position and no index.
- *  - Calls hold no global mutable state; errors are returned, never printed,
- *    and dsa_last_error() gives a thread-local message for the last failure.
+ *  - Calls hold no global mutable state (dsa_layer_decode_noalloc aside: one
+ *    scratch array per GPU); errors are returned, never printed, and
+ *    dsa_last_error() gives a thread-local message for the last failure.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -297,6 +300,27 @@ typedef struct dsa_layer_args {
 size_t dsa_layer_workspace(const dsa_layer_args* a);
 dsa_status dsa_layer_decode(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream);
 dsa_status dsa_layer_prefill(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_layer_decode_noalloc: dsa_layer_decode for callers that cannot
+ * allocate memory -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same step with the same kernels and
+ * results, but its scratch memory is a static device array inside the
+ * library instead of a caller's workspace: the call allocates nothing and
+ * calls no allocating routine.  The caller still passes every input, state
+ * and output buffer in `a`.
+ *  - Capacity: dsa_layer_decode_noalloc_capacity() bytes (64 MiB), which
+ *    covers a decode step whose dsa_layer_workspace() fits in it (all of
+ *    c4a B = 4 at 1M, B = 32 at 64K, c128a B = 16 at 1M); a larger step
+ *    returns DSA_ERR_WORKSPACE before anything is launched.
+ *  - Each GPU holds its own copy of the array from the first call on it
+ *    until the process ends (its address is looked up once per device).
+ *  - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *    one GPU (other streams, other threads) race and must be ordered by the
+ *    caller.  The step writes every scratch byte it reads, so nothing needs
+ *    clearing between calls.
+ *  - Arguments, validation and errors as dsa_layer_decode. */
+dsa_status dsa_layer_decode_noalloc(const dsa_layer_args* a, void* stream);
+size_t dsa_layer_decode_noalloc_capacity(void);
 
 /* ---------------------------------------------------------------- misc */
 /* 1 if `device` is a gfx950 GPU this library was built for, else 0. */

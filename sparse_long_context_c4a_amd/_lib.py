@@ -88,6 +88,8 @@ EXPORTS = {
     "dsa_layer_workspace": (ctypes.c_size_t, [ctypes.POINTER(LayerArgs)]),
     "dsa_layer_decode": (c_i32, [ctypes.POINTER(LayerArgs), c_vp, ctypes.c_size_t, c_vp]),
     "dsa_layer_prefill": (c_i32, [ctypes.POINTER(LayerArgs), c_vp, ctypes.c_size_t, c_vp]),
+    "dsa_layer_decode_noalloc": (c_i32, [ctypes.POINTER(LayerArgs), c_vp]),
+    "dsa_layer_decode_noalloc_capacity": (ctypes.c_size_t, []),
     "dsa_device_supported": (ctypes.c_int, [ctypes.c_int]),
     "dsa_version": (ctypes.c_char_p, []),
     "dsa_last_error": (ctypes.c_char_p, []),
@@ -208,6 +210,16 @@ def layer_decode(args: LayerArgs, ws=None, stream=None, device="cuda"):
     _check(_lib.dsa_layer_decode(ctypes.byref(args), ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)))
     return ws
+
+
+def layer_decode_noalloc(args: LayerArgs, stream=None):
+    """dsa_layer_decode_noalloc: the decode step on the library's static
+    scratch (no workspace, nothing allocated)."""
+    _check(_lib.dsa_layer_decode_noalloc(ctypes.byref(args), _stream(stream)))
+
+
+def layer_decode_noalloc_capacity():
+    return int(_lib.dsa_layer_decode_noalloc_capacity())
 
 
 def layer_prefill(args: LayerArgs, ws=None, stream=None, device="cuda"):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -366,6 +367,59 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
                               a->pos0, B, a->max_pos_end, st);
 }
 
+// ------------------------------------------------ allocation-free decode
+// The scratch memory of dsa_layer_decode_noalloc: a file-scope device array
+// (each GPU holds its own copy from the library's first use on it until the
+// process ends).  In host code `scratch` only names the symbol; its device
+// address on the current GPU comes from hipGetSymbolAddress, once per GPU.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_on_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_layer_decode_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    dsa_status rc = hip_check(hipGetDevice(&cur), "hipGetDevice");
+    if (rc != DSA_OK) return rc;
+    if (cur != dev && (rc = hip_check(hipSetDevice(dev), "hipSetDevice")) != DSA_OK) return rc;
+    void* p = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (cur != dev) {
+      const dsa_status rb = hip_check(hipSetDevice(cur), "hipSetDevice");
+      if (rc == DSA_OK) rc = rb;
+    }
+    if (rc != DSA_OK) return rc;
+    if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+dsa_status layer_decode_noalloc(const dsa_layer_args* a, hipStream_t st) {
+  dsa_status rc = validate_layer(a, true);
+  if (rc != DSA_OK) return rc;
+  const size_t need = layer_plan(a, nullptr).total;
+  if (need > kScratchBytes)
+    return fail(DSA_ERR_WORKSPACE, "dsa_layer_decode_noalloc: this step needs %zu bytes of scratch, "
+                "the static scratch holds %zu (use dsa_layer_decode with a workspace)", need,
+                kScratchBytes);
+  int dev = -1;
+  rc = st ? hip_check(hipStreamGetDevice(st, &dev), "hipStreamGetDevice")
+          : hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != DSA_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_on_device(dev, &ws);
+  if (rc != DSA_OK) return rc;
+  return run_layer(a, ws, kScratchBytes, st, true);
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -415,6 +469,12 @@ size_t dsa_layer_workspace(const dsa_layer_args* a) {
 dsa_status dsa_layer_decode(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(a, ws, ws_bytes, static_cast<hipStream_t>(stream), true);
 }
+
+dsa_status dsa_layer_decode_noalloc(const dsa_layer_args* a, void* stream) {
+  return layer_decode_noalloc(a, static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_layer_decode_noalloc_capacity(void) { return kScratchBytes; }
 
 dsa_status dsa_layer_prefill(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(a, ws, ws_bytes, static_cast<hipStream_t>(stream), false);

@@ -231,3 +231,23 @@ def test_idx_tile_layout_roundtrip_and_offsets():
     for b, j, d in [(0, 0, 0), (0, 5, 17), (1, 36, 127), (1, 16, 64), (0, 31, 15)]:
         off = (b * e_pad + 16 * (j // 16)) * 128 + (d // 16) * 256 + (j % 16) * 16 + d % 16
         assert flat[off] == codes[b, j, d]
+
+
+def test_layer_decode_noalloc_refuses_steps_beyond_its_scratch():
+    """The allocation-free decode holds a fixed static scratch; a step whose
+    workspace exceeds it is refused on the host (DSA_ERR_WORKSPACE) before
+    any device call -- here without a GPU."""
+    cap = _lib._lib.dsa_layer_decode_noalloc_capacity()
+    assert cap == 64 << 20
+    big = _layer_args(main=_lib.geom(128, 128, 512, 64), idx_heads=0, k=8192, n_seqs=128,
+                      max_pos_end=1 << 20, e_cap=8192, w_cap=256)
+    need = _lib.layer_workspace(big)
+    assert need > cap
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_layer_decode_noalloc(ctypes.byref(big), None))
+    assert e.value.code == -3 and "static scratch" in str(e.value)
+    # invalid arguments are reported as by dsa_layer_decode
+    bad = _layer_args(chunk_len=2)
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_layer_decode_noalloc(ctypes.byref(bad), None))
+    assert e.value.code == -1

@@ -104,9 +104,10 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
     """Two timed passes of `steps` layer steps each, after `warmup` untimed
     ones.  The first pass gives the step time: nothing but the layer's own
     launches on the stream, bracketed by events.  The second pass hands the
-    library HIP events that it attaches to the dispatch packets of the
-    scoring kernel and of the attention kernels (hipExtLaunchKernel), which
-    gives their own durations on the stream they run on.  With out_fp8 the
+    library HIP events (dsa_set_timing_events) that it attaches to the
+    dispatch packets of the scoring kernel and of the attention kernels
+    (hipExtLaunchKernel), which gives their own durations on the stream they
+    run on.  With out_fp8 the
     layer stores its output as fp8 codes with one scale per (row, head)."""
     import torch
     from sparse_long_context_c4a_amd import _lib
@@ -135,13 +136,9 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
     ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
     ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
     for i in range(steps):
-        a = args[i % len(args)]
-        a.ev_index[0], a.ev_index[1] = ev_i[i][0].handle, ev_i[i][1].handle
-        a.ev_attn[0], a.ev_attn[1] = ev_a[i][0].handle, ev_a[i][1].handle
-        fn(a, ws=ws, stream=stream)
+        _lib.set_timing_events(index=ev_i[i], attn=ev_a[i])
+        fn(args[i % len(args)], ws=ws, stream=stream)
     torch.cuda.synchronize()
-    for a in args:
-        a.ev_index[0] = a.ev_index[1] = a.ev_attn[0] = a.ev_attn[1] = None
     st = [o[3].item() for o in outs]
     assert all(s == 0 for s in st), f"device status {st}"
     # (a workload without an indexer, k >= every n_vis, never records the

@@ -160,9 +160,6 @@ typedef struct dsa_index_args {
   int32_t* idx_out;           /* [B * Tq, k]                                 */
   float* score_out;           /* [B * Tq, k] or NULL (NaN for padding)       */
   uint32_t* status;
-  void* ev_index[2];          /* optional hipEvent_t pair recorded on the
-                                 stream right before / after the scoring
-                                 kernel (for timing it alone); NULL = none  */
 } dsa_index_args;
 
 size_t dsa_index_topk_workspace(const dsa_index_args* a);
@@ -234,7 +231,7 @@ dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* ws, size_t ws_bytes, vo
 /* ------------------------------------------------------------ layer ----
  * dsa_layer_decode / dsa_layer_prefill: one layer step over a chunk of T raw
  * tokens per sequence at positions p0 = pos0[b] .. p0 + T - 1 ([P2] 全景图,
- * decode step C-E; [P1] 6.3 flowchart).  Decode is the T = 1 case.
+ * decode step C-E; [P1] 15 flowchart).  Decode is the T = 1 case.
  *
  *  1. S1 for every entry completing in the chunk, main (dtype) and indexer
  *     (idx_dtype) caches, reading raw tokens before the chunk from the
@@ -289,8 +286,6 @@ typedef struct dsa_layer_args {
   float* lse;                 /* [B, T, H] or NULL                           */
   int32_t* idx_out;           /* [B, T, k] or NULL                           */
   uint32_t* status;
-  void* ev_index[2];          /* optional hipEvent_t pairs recorded around   */
-  void* ev_attn[2];           /* the scoring kernel and the attention kernels */
   int32_t out_fp8;            /* 1: out as fp8 codes + out_scale (see S5)    */
   float* out_scale;           /* [B, T, H] (out_fp8)                         */
   int32_t main_fp8;           /* 1: main_cache holds token-wise fp8 codes    */
@@ -322,6 +317,23 @@ dsa_status dsa_layer_prefill(const dsa_layer_args* a, void* ws, size_t ws_bytes,
 dsa_status dsa_layer_decode_noalloc(const dsa_layer_args* a, void* stream);
 size_t dsa_layer_decode_noalloc_capacity(void);
 
+/* ---------------------------------------------------------- measurement
+ * dsa_set_timing_events: HIP events (hipEvent_t, NULL = none) that the NEXT
+ * dsa_index_topk, dsa_sparse_attn or dsa_layer_* call made on this thread
+ * attaches to its own kernels' dispatch packets (hipExtLaunchKernel, so no
+ * extra packets sit between kernels): index_begin / index_end around the
+ * scoring kernel, attn_begin / attn_end around the attention kernels (the
+ * first one's start, the last one's end).  Benchmarks use it to time one
+ * kernel inside a step.  One-shot and thread-local: that call consumes it,
+ * whether it succeeds or not. */
+typedef struct dsa_timing_events {
+  void* index_begin;
+  void* index_end;
+  void* attn_begin;
+  void* attn_end;
+} dsa_timing_events;
+void dsa_set_timing_events(const dsa_timing_events* ev);
+
 /* ---------------------------------------------------------------- misc */
 /* 1 if `device` is a gfx950 GPU this library was built for, else 0. */
 int dsa_device_supported(int device);
@@ -331,7 +343,8 @@ const char* dsa_last_error(void);
  * all lie in [0, L); also the visible-entry count of a query at position L. */
 int64_t dsa_n_complete(int64_t L, int32_t stride, int32_t span);
 /* sizeof of a struct declared here ("dsa_geom", "dsa_compress_args",
- * "dsa_index_args", "dsa_attn_args", "dsa_layer_args"), 0 for other names.
+ * "dsa_index_args", "dsa_attn_args", "dsa_layer_args", "dsa_timing_events"),
+ * 0 for other names.
  * Lets a binding check its mirror of the struct layouts. */
 size_t dsa_abi_sizeof(const char* struct_name);
 

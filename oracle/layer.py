@@ -3,7 +3,7 @@
 Test infrastructure only (see the package docstring).
 
 Per-layer dataflow as the pages draw it ([P1] "DeepSeek DSA、DeepSeek V4与
-vLLM Hybrid KV Cache详解", 6.3 flowchart; [P2] "DeepSeek V4 稀疏注意力完全解剖",
+vLLM Hybrid KV Cache详解", 15 flowchart; [P2] "DeepSeek V4 稀疏注意力完全解剖",
 全景图 step C-E): the compressor turns raw tokens into compressed entries
 (main KV and the indexer's own keys), the lightning indexer scores every
 visible entry, Top-k keeps k of them, and one main attention runs over the

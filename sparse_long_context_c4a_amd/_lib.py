@@ -30,6 +30,11 @@ c_i32, c_i64, c_f32, c_f64, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
                                     ctypes.c_double, ctypes.c_void_p)
 
 
+class TimingEvents(ctypes.Structure):
+    _fields_ = [("index_begin", c_vp), ("index_end", c_vp), ("attn_begin", c_vp),
+                ("attn_end", c_vp)]
+
+
 class Geom(ctypes.Structure):
     _fields_ = [("stride", c_i32), ("span", c_i32), ("dim", c_i32), ("rope_dim", c_i32),
                 ("rope_base", c_f64), ("rope_pos_offset", c_i64)]
@@ -48,8 +53,7 @@ class IndexArgs(ctypes.Structure):
                 ("stride", c_i32), ("span", c_i32), ("heads", c_i32), ("dim", c_i32),
                 ("q", c_vp), ("q_scale", c_vp), ("w", c_vp), ("keys", c_vp), ("k_scale", c_vp),
                 ("dtype", c_i32), ("e_cap", c_i64), ("max_pos_end", c_i64), ("k", c_i32),
-                ("idx_out", c_vp), ("score_out", c_vp), ("status", c_vp),
-                ("ev_index", c_vp * 2)]
+                ("idx_out", c_vp), ("score_out", c_vp), ("status", c_vp)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -75,8 +79,7 @@ class LayerArgs(ctypes.Structure):
                 ("idx_scale", c_vp), ("e_cap", c_i64), ("main_ring", c_vp), ("idx_ring", c_vp),
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
-                ("status", c_vp), ("ev_index", c_vp * 2), ("ev_attn", c_vp * 2),
-                ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32), ("main_scale", c_vp)]
+                ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32), ("main_scale", c_vp)]
 
 
 EXPORTS = {
@@ -90,6 +93,7 @@ EXPORTS = {
     "dsa_layer_prefill": (c_i32, [ctypes.POINTER(LayerArgs), c_vp, ctypes.c_size_t, c_vp]),
     "dsa_layer_decode_noalloc": (c_i32, [ctypes.POINTER(LayerArgs), c_vp]),
     "dsa_layer_decode_noalloc_capacity": (ctypes.c_size_t, []),
+    "dsa_set_timing_events": (None, [ctypes.POINTER(TimingEvents)]),
     "dsa_device_supported": (ctypes.c_int, [ctypes.c_int]),
     "dsa_version": (ctypes.c_char_p, []),
     "dsa_last_error": (ctypes.c_char_p, []),
@@ -100,7 +104,7 @@ for _name, (_res, _args) in EXPORTS.items():
     _f = getattr(_lib, _name)
     _f.restype, _f.argtypes = _res, _args
 
-STRUCTS = {"dsa_geom": Geom, "dsa_compress_args": CompressArgs, "dsa_index_args": IndexArgs,
+STRUCTS = {"dsa_timing_events": TimingEvents, "dsa_geom": Geom, "dsa_compress_args": CompressArgs, "dsa_index_args": IndexArgs,
            "dsa_attn_args": AttnArgs, "dsa_layer_args": LayerArgs}
 for _n, _s in STRUCTS.items():
     if _lib.dsa_abi_sizeof(_n.encode()) != ctypes.sizeof(_s):
@@ -117,6 +121,13 @@ class DsaError(RuntimeError):
 def _check(rc):
     if rc != 0:
         raise DsaError(rc, _lib.dsa_last_error().decode())
+
+
+def set_timing_events(index=(None, None), attn=(None, None)):
+    """dsa_set_timing_events: HipEvent pairs (or None) for the next call made
+    on this thread."""
+    h = [None if e is None else e.handle for e in (*index, *attn)]
+    _lib.dsa_set_timing_events(ctypes.byref(TimingEvents(*h)))
 
 
 def version():
@@ -232,8 +243,8 @@ def layer_prefill(args: LayerArgs, ws=None, stream=None, device="cuda"):
 
 
 # ------------------------------------------------------------- HIP events
-# Timing events that the library records on its stream (ev_index / ev_attn
-# fields) are plain hipEvent_t handles from the HIP runtime.
+# Timing events that the library attaches to its kernels (dsa_set_timing_events)
+# are plain hipEvent_t handles from the HIP runtime.
 _hip = None
 
 

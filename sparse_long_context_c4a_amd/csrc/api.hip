@@ -15,7 +15,23 @@ namespace dsa {
 
 namespace {
 thread_local char g_err[512] = "";
-}
+thread_local dsa_timing_events g_hook = {};   // set by dsa_set_timing_events
+thread_local TimingEvents g_active = {};      // the running call's events
+
+// Moves the hook into the running call for its duration (one-shot).
+struct TimingScope {
+  TimingScope() {
+    g_active = TimingEvents{static_cast<hipEvent_t>(g_hook.index_begin),
+                            static_cast<hipEvent_t>(g_hook.index_end),
+                            static_cast<hipEvent_t>(g_hook.attn_begin),
+                            static_cast<hipEvent_t>(g_hook.attn_end)};
+    g_hook = dsa_timing_events{};
+  }
+  ~TimingScope() { g_active = TimingEvents{}; }
+};
+}  // namespace
+
+const TimingEvents& call_timing() { return g_active; }
 
 dsa_status fail(dsa_status s, const char* fmt, ...) {
   va_list ap;
@@ -201,8 +217,6 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   ia.k = a->k;
   ia.score_out = nullptr;
   ia.status = a->status;
-  ia.ev_index[0] = a->ev_index[0];
-  ia.ev_index[1] = a->ev_index[1];
   size_t off = 0;
   L.off_idx_ws = off;
   off = align_up(off + index_topk_ws_bytes(ia));
@@ -289,8 +303,8 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab, st);
     if (rc != DSA_OK) return rc;
     AttnLaunch lx;
-    lx.ev0 = a->ev_attn[0];
-    lx.ev1 = a->ev_attn[1];
+    lx.ev0 = call_timing().attn0;
+    lx.ev1 = call_timing().attn1;
     lx.cs_tab = cs_tab;
     rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
     if (rc != DSA_OK) return rc;
@@ -358,8 +372,8 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   if (rc != DSA_OK) return rc;
   // S5
   AttnLaunch lx;
-  lx.ev0 = a->ev_attn[0];
-  lx.ev1 = a->ev_attn[1];
+  lx.ev0 = call_timing().attn0;
+  lx.ev1 = call_timing().attn1;
   rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
   if (rc != DSA_OK) return rc;
   // window ring update after attention
@@ -403,6 +417,7 @@ dsa_status scratch_on_device(int dev, void** out) {
 }
 
 dsa_status layer_decode_noalloc(const dsa_layer_args* a, hipStream_t st) {
+  TimingScope ts;
   dsa_status rc = validate_layer(a, true);
   if (rc != DSA_OK) return rc;
   const size_t need = layer_plan(a, nullptr).total;
@@ -439,6 +454,7 @@ size_t dsa_index_topk_workspace(const dsa_index_args* a) {
 }
 
 dsa_status dsa_index_topk(const dsa_index_args* a, void* ws, size_t ws_bytes, void* stream) {
+  TimingScope ts;
   dsa_status rc = validate_index(a);
   if (rc != DSA_OK) return rc;
   const size_t need = index_topk_ws_bytes(*a);
@@ -453,12 +469,16 @@ size_t dsa_sparse_attn_workspace(const dsa_attn_args* a) {
 }
 
 dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+  TimingScope ts;
   dsa_status rc = validate_attn(a);
   if (rc != DSA_OK) return rc;
   const size_t need = attn_ws_bytes(*a);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn: workspace %zu < required %zu", ws_bytes, need);
-  return launch_attn(*a, ws, static_cast<hipStream_t>(stream));
+  AttnLaunch lx;
+  lx.ev0 = call_timing().attn0;
+  lx.ev1 = call_timing().attn1;
+  return launch_attn(*a, ws, static_cast<hipStream_t>(stream), lx);
 }
 
 size_t dsa_layer_workspace(const dsa_layer_args* a) {
@@ -467,6 +487,7 @@ size_t dsa_layer_workspace(const dsa_layer_args* a) {
 }
 
 dsa_status dsa_layer_decode(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
+  TimingScope ts;
   return run_layer(a, ws, ws_bytes, static_cast<hipStream_t>(stream), true);
 }
 
@@ -477,8 +498,11 @@ dsa_status dsa_layer_decode_noalloc(const dsa_layer_args* a, void* stream) {
 size_t dsa_layer_decode_noalloc_capacity(void) { return kScratchBytes; }
 
 dsa_status dsa_layer_prefill(const dsa_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
+  TimingScope ts;
   return run_layer(a, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
 }
+
+void dsa_set_timing_events(const dsa_timing_events* ev) { g_hook = ev ? *ev : dsa_timing_events{}; }
 
 int dsa_device_supported(int device) {
   hipDeviceProp_t p;
@@ -493,6 +517,7 @@ const char* dsa_last_error(void) { return g_err; }
 size_t dsa_abi_sizeof(const char* name) {
   if (!name) return 0;
   if (!std::strcmp(name, "dsa_geom")) return sizeof(dsa_geom);
+  if (!std::strcmp(name, "dsa_timing_events")) return sizeof(dsa_timing_events);
   if (!std::strcmp(name, "dsa_compress_args")) return sizeof(dsa_compress_args);
   if (!std::strcmp(name, "dsa_index_args")) return sizeof(dsa_index_args);
   if (!std::strcmp(name, "dsa_attn_args")) return sizeof(dsa_attn_args);

@@ -387,8 +387,7 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   dsa_status rc;
   if (P.pre) return launch_prefill_index_topk(a, P.nv_cap, scores, P.ld, base + P.off_pre, st);
   if (!no_keys && P.nv_cap > 0) {
-    const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
-    const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);
+    const hipEvent_t e0 = call_timing().index0, e1 = call_timing().index1;
     if (P.mfma) {
       dim3 grid(static_cast<unsigned>(P.nb), rows);
       auto go = [&](auto kern) {
@@ -451,7 +450,7 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
   const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab);
   auto go = [&](auto kern) {
     launch_timed(kern, dim3((P.nb + kPrologueRoles) * rows), dim3(kThreads), 0, st,
-                 static_cast<hipEvent_t>(a.ev_index[0]), static_cast<hipEvent_t>(a.ev_index[1]),
+                 call_timing().index0, call_timing().index1,
                  static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                  static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
                  a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,

@@ -27,6 +27,14 @@ void launch_timed(K kernel, dim3 grid, dim3 block, size_t shm, hipStream_t st, h
     hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
 }
 
+// Timing events of the entry-point call running on this thread (taken from
+// the one-shot dsa_set_timing_events hook for the call's duration; all null
+// otherwise).
+struct TimingEvents {
+  hipEvent_t index0, index1, attn0, attn1;
+};
+const TimingEvents& call_timing();
+
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -955,8 +955,7 @@ dsa_status launch_prefill_index_topk(const dsa_index_args& a, int64_t nv_cap, fl
   pa.masks = reinterpret_cast<uint16_t*>(base + P.off_masks);
   pa.keys_rm = reinterpret_cast<uint8_t*>(base + P.off_krm);
   pa.status = a.status;
-  const hipEvent_t e0 = static_cast<hipEvent_t>(a.ev_index[0]);
-  const hipEvent_t e1 = static_cast<hipEvent_t>(a.ev_index[1]);
+  const hipEvent_t e0 = call_timing().index0, e1 = call_timing().index1;
   launch_timed(k_pidx_prep, dim3(P.tiles), dim3(kThreads), 0, st, e0, nullptr, pa);
   dsa_status rc = hip_check(hipGetLastError(), "k_pidx_prep launch");
   if (rc != DSA_OK) return rc;

@@ -36,6 +36,8 @@ class Workload:
     w_cap: int = 0       # window ring slots (0: 2 W, so a decode step can
                          # insert token m before attention reads [m-W, m-1])
     main_cache_dtype: str = ""  # "fp8": token-wise fp8 main cache (decode); "": main_dtype
+    cluster: int = 0     # > 0: that many consecutive cached entries of each sequence
+                         # (seeded start) get 16x larger indexer key scales
 
     @property
     def E_cap(self):
@@ -65,6 +67,14 @@ C4A_DECODE_1M = Workload(
     name="c4a_decode_B4_L1M", mode="decode", B=4, L=1048576, D=512, r=64,
     H=64, Hi=16, Di=128, k=512, s=4, S=8, seed=20262)
 
+# The same step with the high scores clustered: the scores of 1024 consecutive
+# entries per sequence (four 256-entry waves of the indexer) are 16x larger,
+# so the positive ones among them (about a fifth) outrank the rest of the row
+# and a few waves hold far more of the Top-k than a uniform spread would.
+C4A_DECODE_1M_CLUSTERED = Workload(
+    name="c4a_decode_B4_L1M_clustered", mode="decode", B=4, L=1048576, D=512, r=64,
+    H=64, Hi=16, Di=128, k=512, s=4, S=8, seed=20265, cluster=1024)
+
 C128A_DECODE_1M = Workload(
     name="c128a_decode_B16_L1M", mode="decode", B=16, L=1048576, D=512, r=64,
     H=64, Hi=0, Di=0, k=8192, s=128, S=128, seed=20263)
@@ -75,7 +85,7 @@ C4A_PREFILL_128K = Workload(
     seed=20264)
 
 ALL = [TINY_C4A_F32, C4A_DECODE_64K, C4A_DECODE_1M, C128A_DECODE_1M,
-       C4A_PREFILL_128K]
+       C4A_PREFILL_128K, C4A_DECODE_1M_CLUSTERED]
 BY_NAME = {w.name: w for w in ALL}
 
 

@@ -300,12 +300,12 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     L.aa.chunk_win = nullptr;
     // the prologue leaves the (cos, sin) table of m for attention
     float* cs_tab = reinterpret_cast<float*>(base + L.off_cs);
-    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab, st);
-    if (rc != DSA_OK) return rc;
     AttnLaunch lx;
     lx.ev0 = call_timing().attn0;
     lx.ev1 = call_timing().attn1;
     lx.cs_tab = cs_tab;
+    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab, st);
+    if (rc != DSA_OK) return rc;
     rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
     if (rc != DSA_OK) return rc;
     return early ? DSA_OK : launch_decode_window_insert(*a, st);

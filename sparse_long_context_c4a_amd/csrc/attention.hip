@@ -768,34 +768,63 @@ __device__ __forceinline__ void store_head_dims4_fp8(float4 acc, float L, int d4
 // pages' token-wise fp8 decode KV; k a multiple of 32, so a wave step is all
 // cache or all window); the window stays bf16.  An entry's scale multiplies
 // its logit and its probability in the weighted sum of code vectors.
-template <int NW, bool kFp8>
-__global__ __launch_bounds__(NW * 64) void k_attn_decode(
-    AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
-    const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, float* __restrict__ cs_out) {
+// LDS of one run of the decode attention (NW waves).
+template <int NW>
+struct DecSmem {
+  uint8_t dsm[NW * kDWaveBytes];  // each wave's staged tile; the wave merge after
+  uint8_t q_s[kDH * kMPitch];     // rotated q, head n at row n
+  float cs_s[kMD];                // (cos, sin) of pair i at 2i, 2i+1
+  float ml_s[NW][kDH][2];
+  float hml_s[kDH][2];
+};
+
+// Slot sources of a run (slots numbered 0 .. count()-1): index(a) gives the
+// cache index of a cache slot for lane-parallel prefetch (-1 otherwise),
+// ptr<kFp8>(a, j) its vector (nullptr for an empty slot), is_cache(a)
+// whether slot a is a cache entry (else a bf16 window token).
+//
+// RunSlots: slots a_begin .. a_end-1 of the row's virtual list (k selected
+// indices, then the W window positions).
+struct RunSlots {
+  const AttnGeom* g;
+  int row, b, a_begin, a_end;
+  int64_t m;
+  const uint16_t *cache, *window, *chunk_win;
+  __device__ int count() const { return a_end - a_begin; }
+  __device__ int32_t index(int a) const { return dslot_index(*g, row, a_begin + a, a_end); }
+  template <bool kFp8>
+  __device__ const uint16_t* ptr(int a, int32_t j) const {
+    return dslot_ptr<kFp8>(*g, b, m, a_begin + a, j, cache, window, chunk_win);
+  }
+  __device__ bool is_cache(int a) const { return a_begin + a < g->k; }
+};
+
+// One run of the decode attention (NW waves of a workgroup, 16 heads hg of
+// row `row`): the run's slots in steps of NW x 32 vectors, each wave its 32,
+// then the wave merge; the run's partial (or, with g.direct, the final
+// rotated output) goes out.
+template <int NW, bool kFp8, typename Src>
+__device__ __forceinline__ void decode_attn_run(
+    const AttnGeom& g, int row, int hg, int run, const Src& src, const uint16_t* __restrict__ q,
+    int rotate_q, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_acc, float* __restrict__ part_ml, float* __restrict__ cs_out,
+    DecSmem<NW>& sm) {
   constexpr int NT = NW * 64, kSlotsPerIter = NW * kDStep;
   constexpr int kQPer = kDH * 64 / NT;  // 16-byte pieces of the query tile per thread
-  __shared__ __attribute__((aligned(16))) uint8_t dsm[NW * kDWaveBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t q_s[kDH * kMPitch];  // rotated q, head n at row n
-  __shared__ float cs_s[kMD];  // (cos, sin) of pair i at 2i, 2i+1
-  __shared__ float ml_s[NW][kDH][2];
-  __shared__ float hml_s[kDH][2];
+  uint8_t* dsm = sm.dsm;
+  uint8_t* q_s = sm.q_s;
+  float* cs_s = sm.cs_s;
+  auto& ml_s = sm.ml_s;
+  auto& hml_s = sm.hml_s;
   const int G = g.H / kDH;
-  const int id = blockIdx.x;
-  const int pair = 8 * (id / (8 * G)) + (id & 7), hg = (id >> 3) % G;
-  if (pair >= g.rows * g.n_runs) return;
-  const int row = pair / g.n_runs, run = pair % g.n_runs;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
-  const int total = g.k + g.W;
-  const int a_begin = run * g.slots_per_run;
-  const int a_end = min(total, a_begin + g.slots_per_run);
-  int a0 = a_begin + wave * kDStep;
+  const int a_end = src.count();
+  int a0 = wave * kDStep;
   // independent loads first: the first step's cache indices, the query
   // position, the 16 heads' query rows (piece c = tid + NT i: head c / 64,
   // dims 8 (c % 64) .. +7) and, when given, the R_m table
-  int32_t jn = dslot_index(g, row, a0 + lane, a_end);
+  int32_t jn = lane < kDStep ? src.index(a0 + lane) : -1;
   const int64_t m = g.q_pos[row];
   uint4 qraw[kQPer];
   {
@@ -814,18 +843,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
   float sig0 = 1.f;
   u32x4 stg0[kDStep];
   // an fp8 cache slot's scale (1 for window slots and without kFp8)
-  auto slot_scale = [&](int a, const uint16_t* src, int32_t j) -> float {
+  auto slot_scale = [&](int a, const uint16_t* sp, int32_t j) -> float {
     if constexpr (kFp8)
-      if (src != nullptr && a < g.k) return g.cache_scale[static_cast<int64_t>(b) * g.e_cap + j];
+      if (sp != nullptr && src.is_cache(a)) return g.cache_scale[static_cast<int64_t>(b) * g.e_cap + j];
     return 1.f;
   };
   if (a0 < a_end) {
-    const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
-                              ? dslot_ptr<kFp8>(g, b, m, a0 + lane, jn, cache, window, chunk_win)
-                              : nullptr;
-    sig0 = slot_scale(a0 + lane, src, jn);
-    vmask0 = (kFp8 && a0 < g.k) ? gather_load8(src, dummy, lane, stg0)
-                                : gather_load(src, dummy, lane, stg0);
+    const uint16_t* sp = (ok && a0 + lane < a_end && lane < kDStep)
+                             ? src.template ptr<kFp8>(a0 + lane, jn)
+                             : nullptr;
+    sig0 = slot_scale(a0 + lane, sp, jn);
+    vmask0 = (kFp8 && src.is_cache(a0)) ? gather_load8(sp, dummy, lane, stg0)
+                                        : gather_load(sp, dummy, lane, stg0);
   }
   // (after the gather: its loads wait on every load issued before them)
   if (g.cs_tab)
@@ -945,19 +974,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
   };
   if (a0 < a_end) {
     // next step's cache indices in flight during this step
-    jn = a0 + kSlotsPerIter < a_end ? dslot_index(g, row, a0 + kSlotsPerIter + lane, a_end) : -1;
-    step(stg0, vmask0, a0 < g.k, sig0);
+    jn = (a0 + kSlotsPerIter < a_end && lane < kDStep) ? src.index(a0 + kSlotsPerIter + lane) : -1;
+    step(stg0, vmask0, src.is_cache(a0), sig0);
     for (a0 += kSlotsPerIter; a0 < a_end; a0 += kSlotsPerIter) {
       u32x4 stg[kDStep];
-      const uint16_t* src = (ok && a0 + lane < a_end && lane < kDStep)
-                                ? dslot_ptr<kFp8>(g, b, m, a0 + lane, jn, cache, window, chunk_win)
-                                : nullptr;
-      const float sig = slot_scale(a0 + lane, src, jn);
-      const bool st8 = kFp8 && a0 < g.k;
-      const uint64_t vmask = st8 ? gather_load8(src, dummy, lane, stg)
-                                 : gather_load(src, dummy, lane, stg);
+      const uint16_t* sp = (ok && a0 + lane < a_end && lane < kDStep)
+                               ? src.template ptr<kFp8>(a0 + lane, jn)
+                               : nullptr;
+      const float sig = slot_scale(a0 + lane, sp, jn);
+      const bool st8 = kFp8 && src.is_cache(a0);
+      const uint64_t vmask = st8 ? gather_load8(sp, dummy, lane, stg)
+                                 : gather_load(sp, dummy, lane, stg);
       const int nxt = a0 + kSlotsPerIter;
-      jn = nxt < a_end ? dslot_index(g, row, nxt + lane, a_end) : -1;
+      jn = (nxt < a_end && lane < kDStep) ? src.index(nxt + lane) : -1;
       step(stg, vmask, st8, sig);
     }
   }
@@ -1023,6 +1052,25 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
       }
     }
   }
+}
+
+template <int NW, bool kFp8>
+__global__ __launch_bounds__(NW * 64) void k_attn_decode(
+    AttnGeom g, const uint16_t* __restrict__ q, int rotate_q, const uint16_t* __restrict__ cache,
+    const uint16_t* __restrict__ window, const uint16_t* __restrict__ chunk_win,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
+    float* __restrict__ part_ml, float* __restrict__ cs_out) {
+  __shared__ __attribute__((aligned(16))) DecSmem<NW> sm;
+  const int G = g.H / kDH;
+  const int id = blockIdx.x;
+  const int pair = 8 * (id / (8 * G)) + (id & 7), hg = (id >> 3) % G;
+  if (pair >= g.rows * g.n_runs) return;
+  const int row = pair / g.n_runs, run = pair % g.n_runs;
+  const int a_begin = run * g.slots_per_run;
+  const RunSlots src{&g, row, row / g.Tq, a_begin, min(g.k + g.W, a_begin + g.slots_per_run),
+                     g.q_pos[row], cache, window, chunk_win};
+  decode_attn_run<NW, kFp8>(g, row, hg, run, src, q, rotate_q, out, lse, part_acc, part_ml, cs_out,
+                            sm);
 }
 
 // Merge the runs of one (row, head) pair of heads of the decode-shaped path

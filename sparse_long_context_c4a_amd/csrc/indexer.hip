@@ -139,6 +139,10 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
 }
 
 // ------------------------------------------------------------ final passes
+// Waves of 256 entries the candidate pass scores again in full when their
+// thresholds do not certify the candidates (LDS: 2 KiB each).
+constexpr int kMaxF = 24;
+
 // Candidate path: union of the waves' candidates (empty slots are 0), the
 // certificate, and the exact top k; falls back to the full-row select when
 // the certificate does not hold.  The candidates stay in registers (8 per
@@ -152,11 +156,13 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     const float* __restrict__ q_scale, const float* __restrict__ hw,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale, int Tq, int Hi,
     int64_t e_cap) {
-  __shared__ uint64_t cand_s[kFinalCap];
+  __shared__ uint64_t cand_s[kFinalCap + 256 * kMaxF];
   __shared__ uint64_t tmp_s[kTmpCap];
   __shared__ uint32_t h_s[kBins];
   __shared__ uint32_t red[3][kSelWaves];
   __shared__ uint32_t pos_above, pos_bin, n_tmp;
+  __shared__ uint16_t f_s[kMaxF];        // waves scored again in full
+  __shared__ uint32_t fbit_s[kSel / 32];  // the same as a bit set
   const int row = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
   // the candidates and wave thresholds do not depend on the row's position:
   // their loads go out with the position's, one memory round trip for all
@@ -175,8 +181,10 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     v[2 * i] = static_cast<uint64_t>(w.x) | (static_cast<uint64_t>(w.y) << 32);
     v[2 * i + 1] = static_cast<uint64_t>(w.z) | (static_cast<uint64_t>(w.w) << 32);
   }
-  uint32_t tm = 0;
-  for (int b = t; b < nw; b += kSel) tm = max(tm, mrow[b]);
+  // wave thresholds: nw <= kSel (nw * cap <= kFinalCap with cap >= 8), one
+  // per thread
+  const uint32_t mw = t < nw ? mrow[t] : 0u;
+  uint32_t tm = mw;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
   const int64_t nv = ri.nv;
   float* srow = scores + static_cast<int64_t>(row) * ld_scores;
@@ -224,20 +232,17 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     lo = min(lo, red[1][i]);
     hi = max(hi, red[2][i]);
   }
-  // the certificate count (at least k candidates with key >= max_w t_w) and
-  // the histogram over the candidates' key range, in one pass
+  // the histogram over the candidates' key range, and their count
   const int shift = range_shift(hi - lo, 11);
-  uint32_t c_ge = 0;
+  uint32_t c_n = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (v[u] != 0) {
-      const uint32_t key = static_cast<uint32_t>(v[u] >> 32);
-      c_ge += key >= tm ? 1u : 0u;
-      atomicAdd(&h_s[(key - lo) >> shift], 1u);
+      atomicAdd(&h_s[(static_cast<uint32_t>(v[u] >> 32) - lo) >> shift], 1u);
+      ++c_n;
     }
-  const bool ok = block_reduce_u32<2>(c_ge) >= static_cast<uint32_t>(k);  // barriers
-  if (!ok) {
-    // the certificate failed: score the row exactly in full, then select
+  if (block_reduce_u32<2>(c_n) < static_cast<uint32_t>(k)) {  // barriers
+    // fewer candidates than k (ties at the wave thresholds): the whole row
     exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
     score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
     __syncthreads();
@@ -247,6 +252,77 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   const uint32_t local[2] = {h_s[2047 - 2 * t], h_s[2046 - 2 * t]};
   const Bin br = find_bin_desc<2>(local, 2047u, static_cast<uint32_t>(k));
   const uint32_t B = br.b, above = br.above, at = br.at;
+  // The certificate: the k-th candidate lies in bin B, so its key is at
+  // least kc = lo + B 2^shift.  An entry that is not a candidate has a key
+  // below its wave's threshold t_w; where every t_w <= kc no such entry can
+  // reach the k-th, and the candidates' top k is the row's.  Otherwise the
+  // waves F with t_w > kc are scored again in full: with U = (candidates
+  // of waves outside F) + (every entry of F), an entry outside U has a key
+  // below t_w <= kc <= the k-th of U, so U's top k is exact.  Each wave of F
+  // holds cap candidates above kc, so F stays small unless the scores are
+  // laid out adversarially; beyond kMaxF waves the whole row is re-scored.
+  const uint32_t kc = lo + (B << shift);
+  if (tm > kc) {
+    const bool in_f = mw > kc;
+    const uint32_t nf = block_reduce_u32<2>(in_f ? 1u : 0u);  // barriers
+    exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
+    if (nf > static_cast<uint32_t>(kMaxF)) {
+      score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+      __syncthreads();
+      row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
+      return;
+    }
+    if (t == 0) n_tmp = 0u;
+    if (t < kSel / 32) fbit_s[t] = 0u;
+    __syncthreads();
+    if (in_f) {
+      f_s[atomicAdd(&n_tmp, 1u)] = static_cast<uint16_t>(t);
+      atomicOr(&fbit_s[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    // the candidates of waves outside F, in their slots
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sl = 2 * t + 2 * kSel * i + h, wv_id = sl / cap;
+        const bool drop = sl >= slots || ((fbit_s[wv_id >> 5] >> (wv_id & 31)) & 1u);
+        cand_s[sl] = drop ? 0ull : v[2 * i + h];
+      }
+    // every entry of F, exactly, after them: tile ft = 16 entries of wave
+    // f_s[ft / 16]; each wave takes every kSelWaves-th tile, the loads of
+    // kBatch tiles in flight together
+    constexpr int kBatch = 4;
+    const int n = t & 15, g = (t & 63) >> 4, ntile = static_cast<int>(nf) * 16;
+    for (int f0 = w; f0 < ntile; f0 += kBatch * kSelWaves) {
+      uint4 blo[kBatch], bhi[kBatch];
+      float ks[kBatch];
+      int64_t jj[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int ft = f0 + u * kSelWaves;
+        jj[u] = ft < ntile ? static_cast<int64_t>(f_s[ft >> 4]) * 256 + (ft & 15) * 16 + n : nv;
+        blo[u] = bhi[u] = uint4{0u, 0u, 0u, 0u};
+        ks[u] = 0.f;
+        if (jj[u] < nv) {
+          idx_load_chunks(kb, jj[u], g, &blo[u], &bhi[u]);
+          ks[u] = ksb[jj[u]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int ft = f0 + u * kSelWaves;
+        const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
+        if (g == 0 && ft < ntile)
+          cand_s[kFinalCap + ft * 16 + n] =
+              jj[u] < nv ? composite(order_key(sc), static_cast<uint32_t>(jj[u])) : 0ull;
+      }
+    }
+    __syncthreads();
+    select_topk_composites<kSel>(cand_s, kFinalCap + static_cast<int>(nf) * 256,
+                                 static_cast<uint32_t>(k), irow, orow, tmp_s, h_s);
+    return;
+  }
   const bool fits = at <= static_cast<uint32_t>(kTmpCap);
   // places for the wave's entries above the bin and in it: the ballots of
   // all kPer values first, then one LDS counter update per kind and wave

@@ -123,17 +123,28 @@ __device__ __forceinline__ void exact_row_operands(const uint8_t* q, const float
 __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float (&wv)[4],
                                                 const uint8_t* kb, const float* ksb, int64_t nv,
                                                 float* srow, int nwaves) {
+  // four tiles' loads in flight per wave and round
+  constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
-  for (int64_t tile = wave; tile * 16 < nv; tile += nwaves) {
-    const int64_t j = tile * 16 + n;
-    uint4 blo = {0u, 0u, 0u, 0u}, bhi = {0u, 0u, 0u, 0u};
-    float ks = 0.f;
-    if (j < nv) {
-      idx_load_chunks(kb, j, g, &blo, &bhi);
-      ks = ksb[j];
+  for (int64_t t0 = wave; t0 * 16 < nv; t0 += kBatch * nwaves) {
+    uint4 blo[kBatch], bhi[kBatch];
+    float ks[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
+      blo[u] = bhi[u] = uint4{0u, 0u, 0u, 0u};
+      ks[u] = 0.f;
+      if (j < nv) {
+        idx_load_chunks(kb, j, g, &blo[u], &bhi[u]);
+        ks[u] = ksb[j];
+      }
     }
-    const float sc = exact_tile_score(aq, wv, blo, bhi) * ks;
-    if (g == 0 && j < nv) srow[j] = sc;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
+      const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
+      if (g == 0 && j < nv) srow[j] = sc;
+    }
   }
 }
 

@@ -19,6 +19,12 @@ slots j < n_complete(p0) hold random entries, the compressor rings hold the
 S raw tokens before p0 and the window ring holds W rotated tokens before
 p0 (drawn as random vectors; the layer treats them as opaque stored values).
 An "empty" state (p0 = 0) starts a sequence from nothing.
+
+Clustered scores (``Workload.cluster`` > 0, random state with an indexer):
+after every other draw, one start per sequence is drawn uniformly from
+[0, n_complete(p0) - cluster] and the indexer key scales of the cluster
+entries from there are multiplied by 16, so their scores are 16 times
+larger and the positive ones crowd the row's Top-k into a few waves.
 """
 
 import numpy as np
@@ -163,6 +169,14 @@ def layer_inputs(w: Workload, seed=None, p0=None, T=None, state="random",
         out["wt"] = _normal(rng, (B, T, Hi))
     else:
         out["qi"] = out["qi_scale"] = out["wt"] = None
+
+    # 8. clustered high scores
+    if w.cluster and has_idx and state == "random" and j0 > w.cluster and out["idx_scale"] is not None:
+        out["cluster_start"] = []
+        for b in range(B):
+            start = int(rng.integers(0, j0 - w.cluster + 1))
+            out["idx_scale"][b, start:start + w.cluster] *= np.float32(16.0)
+            out["cluster_start"].append(start)
     return out
 
 

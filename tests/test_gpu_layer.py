@@ -224,7 +224,8 @@ def test_chunked_prefill_matches_single_pass():
     check_close(got, to_np(out1), 2 * ATOL["bf16"], "chunked vs single")
 
 
-FULL = [configs.C4A_DECODE_64K, configs.C4A_DECODE_1M, configs.C128A_DECODE_1M]
+FULL = [configs.C4A_DECODE_64K, configs.C4A_DECODE_1M, configs.C128A_DECODE_1M,
+        configs.C4A_DECODE_1M_CLUSTERED]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
@@ -235,6 +236,10 @@ def test_layer_full_size_decode(w):
     ores = _oracle(w, inp, gpu_idx=idx)
     swaps = _compare(w, inp, ores, out, lse, idx, label=w.name)
     assert swaps <= 2
+    if w.cluster:  # a large share of the Top-k sits in a few waves of the cluster
+        ix = idx.cpu().numpy()
+        for b, c0 in enumerate(inp["cluster_start"]):
+            assert np.sum((ix[b, 0] >= c0) & (ix[b, 0] < c0 + w.cluster)) > 100, b
 
 
 def test_layer_full_size_decode_fp8_out():
@@ -428,3 +433,20 @@ def test_layer_rope_pos_offset_prefill_random_state():
     _, out, lse, idx = _run_gpu(w, inp, pos_offset=OFFSET)
     ores = _oracle(w, inp, gpu_idx=idx, pos_offset=OFFSET)
     _compare(w, inp, ores, out, lse, idx, label="offset prefill")
+
+
+def test_layer_decode_all_scores_tie():
+    """A decode step whose indexer query is zero, so every visible entry
+    scores 0: on the candidate path no wave threshold admits a candidate,
+    and the attention launch takes the row's cut from the whole row scored
+    exactly.  The Top-k is the k lowest indices (ties to the lower index)."""
+    w = configs.shrink(configs.C4A_DECODE_64K, B=2, L=40000)
+    inp = gen.layer_inputs(w, seed=5800, state="random")
+    inp["qi"] = np.zeros_like(inp["qi"])
+    print(f"[dsa_layer ties] zero indexer query, B={w.B} L={w.L}", flush=True)
+    _, out, lse, idx = _run_gpu(w, inp)
+    ix = idx.cpu().numpy()
+    for b in range(w.B):
+        assert sorted(ix[b, 0].tolist()) == list(range(w.k)), b
+    ores = _oracle(w, inp, gpu_idx=idx)
+    _compare(w, inp, ores, out, lse, idx, label="all scores tie")

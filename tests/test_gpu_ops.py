@@ -205,7 +205,9 @@ def test_index_topk(case):
 
 def test_index_topk_ties_go_to_lower_index():
     print("[dsa_index_topk] all-zero query: every score ties", flush=True)
-    positions = [9000, 3000]
+    # 9000 and 3000 take the per-row path; 200000 the candidate path, whose
+    # wave thresholds admit no candidate when every key ties
+    positions = [9000, 3000, 200000]
     idx, sco, *_ = _index_run("fp8", 16, 128, 512, positions, 2100, zero_q=True)
     for i, m in enumerate(positions):
         nv = odsa.n_vis(m, 4, 8)
@@ -225,6 +227,22 @@ def test_index_topk_clustered_top_entries():
         scores = odsa.indexer_scores(qd[i], wt[i], kd[i][:nv])
         assert np.sum((idx[i] >= 1024) & (idx[i] < 2048)) > 100
         check_topk_row(idx[i], scores, 512, f"clustered row {i}")
+
+
+def test_index_topk_clustered_many_waves():
+    """The Top-k spread over more waves than the candidate pass re-scores
+    one by one (40 boosted 256-entry waves of about 13 members each): the
+    whole row is scored again and selected exactly."""
+    positions = [200000]
+    print("[dsa_index_topk] Top-k crowded into 40 waves (full re-score)", flush=True)
+    idx, sco, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2301, boost=(0, 40 * 256))
+    nv = odsa.n_vis(positions[0], 4, 8)
+    scores = odsa.indexer_scores(qd[0], wt[0], kd[0][:nv])
+    oidx, _ = odsa.topk(scores, 512)
+    crowded = np.sum(np.bincount(oidx[oidx >= 0] // 256) > 11)
+    print(f"  waves holding more than 11 of the Top-k: {crowded}", flush=True)
+    assert crowded > 24
+    check_topk_row(idx[0], scores, 512, "crowded row")
 
 
 def _check_prefill_rows(idx, kd, qd, wt, positions, Tq, k, rows, label):

@@ -148,6 +148,43 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
     return ms, idx_ms, attn_ms
 
 
+def time_layer_graph(w, sets, steps, warmup):
+    """The decode step captured once per input set in a HIP graph
+    (torch.cuda.CUDAGraph over the library's launches) and replayed round
+    robin over the sets: the step time without per-launch host work.  A
+    replay repeats its set's step at the same positions, which rewrites the
+    same state values, so the replays are equivalent to the eager steps."""
+    import torch
+    from sparse_long_context_c4a_amd import _lib
+    from sparse_long_context_c4a_amd import layer as Ly
+    dev = sets[0][1].x.device
+    B = sets[0][1].x.shape[0]
+    outs = [Ly.alloc_outputs(w, B, 1, dev) for _ in sets]
+    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s)
+            for (st, ch), o in zip(sets, outs)]
+    ws = torch.empty(max(_lib.layer_workspace(a) for a in args), dtype=torch.uint8, device=dev)
+    graphs = []
+    for a in args:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            _lib.layer_decode(a, ws=ws, stream=torch.cuda.current_stream())
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    assert all(o[3].item() == 0 for o in outs)
+    del graphs
+    return t0.elapsed_time(t1) / steps
+
+
 def cpu_baseline(w, min_seconds=10.0, max_sets=8):
     """The fp64 oracle on a bounded sample of the same workload: full layer
     steps for all w.B decode queries of successive seeded input sets, until
@@ -354,6 +391,11 @@ def main():
         extra[w.name + "_fp8_out"] = {"queries_per_s": w.B / (ms8 / 1e3), "ms_per_step": ms8,
                                       "batch": w.B, "context": w.L, "k": w.k,
                                       "kernel_ms": {"attention": attn8}}
+        # the same step captured in HIP graphs and replayed
+        print("[bench] timing graph replays", file=sys.stderr, flush=True)
+        msg = time_layer_graph(w, sets, args.steps, args.warmup)
+        extra[w.name + "_graph_replay"] = {"queries_per_s": w.B / (msg / 1e3), "ms_per_step": msg,
+                                           "batch": w.B, "context": w.L, "k": w.k}
         # the same step over a token-wise fp8 main cache (decode prologue
         # unfused, the attention reading fp8 entries)
         print("[bench] timing over an fp8 main cache", file=sys.stderr, flush=True)

@@ -1,0 +1,103 @@
+"""The decode step captured once in a HIP graph and replayed, as the pages
+describe for the serving path ("DeepSeek V4 稀疏注意力完全解剖", 第六层 and
+全景图 step 3: every layer's decode step is captured and replayed, which
+removes per-launch host overhead).
+
+dsa_layer_decode takes its positions from a device array and does no host
+synchronisation, so one capture serves a whole decode loop: before each
+replay the caller copies the next token's inputs and positions into the
+captured buffers.  Five steps (positions 2999 .. 3003 of two sequences; the
+first and the last complete a compressed entry) are replayed with eager
+copies and synchronisations between the replays.  Every replay must select
+the same entries as the same step run eagerly on its own copy of the state,
+with outputs equal up to the summation order (the selected entries are
+listed in the order the Top-k pass happened to emit them), and the state
+left behind must be equal bit for bit.  The first step is also checked
+against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa as odsa
+from oracle.layer import Geometry
+from oracle.run import decode_store, run_layer
+from sparse_long_context_c4a_amd import configs, inputs as gen
+
+from gpu_helpers import ATOL, LSE_ATOL, check_close, check_topk_row, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CHUNK_FIELDS = ("pos0", "x", "kx", "logits_main", "logits_idx", "q", "qi", "qi_scale", "w")
+
+
+def _state_tensors(st):
+    return [t for t in (st.main_cache, st.idx_cache, st.idx_scale, st.main_ring, st.idx_ring,
+                        st.window) if t is not None]
+
+
+def test_decode_step_graph_replay_matches_eager():
+    from sparse_long_context_c4a_amd import _lib
+    from sparse_long_context_c4a_amd import layer as Ly
+    w = configs.shrink(configs.C4A_DECODE_64K, B=2, L=3000)
+    p_first = w.L - 1
+    inp0 = gen.layer_inputs(w, seed=7500, state="random", e_cap=(w.L + 8) // 4 + 1)
+    steps = [inp0] + [gen.layer_inputs(w, seed=7501 + i, p0=p_first + 1 + i, T=1,
+                                       state="random", e_cap=inp0["E_cap"]) for i in range(4)]
+    max_pos_end = inp0["E_cap"] * w.s
+    chunks = [Ly.chunk_from_inputs(w, s, DEV) for s in steps]
+    print(f"[graph] decode B={w.B} positions {p_first}..{p_first + 4}", flush=True)
+    # eager reference on its own state
+    st_e = Ly.state_from_inputs(inp0, DEV)
+    eager = []
+    for ch in chunks:
+        out, lse, idx, status, _ = Ly.run(w, st_e, ch, max_pos_end=max_pos_end)
+        torch.cuda.synchronize()
+        assert status.item() == 0
+        eager.append((out.clone(), lse.clone(), idx.clone()))
+    # one capture, replayed per step with the step's inputs copied in
+    st_g = Ly.state_from_inputs(inp0, DEV)
+    ch_s = Ly.chunk_from_inputs(w, inp0, DEV)
+    out, lse, idx, status = Ly.alloc_outputs(w, w.B, 1, DEV)
+    args = Ly.layer_args(w, st_g, ch_s, out, lse, idx, status, max_pos_end=max_pos_end)
+    ws = torch.empty(_lib.layer_workspace(args), dtype=torch.uint8, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _lib.layer_decode(args, ws=ws, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i, ch in enumerate(chunks):
+        for f in CHUNK_FIELDS:
+            dst, src = getattr(ch_s, f), getattr(ch, f)
+            if dst is not None:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert status.item() == 0, f"step {i}: device status {status.item()}"
+        eo, el, ei = eager[i]
+        gi, ei = idx.cpu().numpy(), ei.cpu().numpy()
+        for b in range(w.B):
+            assert set(gi[b, 0].tolist()) == set(ei[b, 0].tolist()), f"step {i} b={b}"
+        # the same set, summed in the order the Top-k pass happened to list it
+        do = check_close(to_np(out), to_np(eo), ATOL["bf16"], f"step {i} out vs eager")
+        dl = check_close(lse.cpu().numpy(), el.cpu().numpy(), LSE_ATOL["bf16"], f"step {i} lse")
+        print(f"  replay {i}: max |out - eager| {do:.2e}, |lse - eager| {dl:.2e}", flush=True)
+        if i == 0:  # the first replay against the oracle
+            g = Geometry(s=w.s, S=w.S, D=w.D, r=w.r, Di=w.Di, r_idx=w.r_idx, H=w.H, Hi=w.Hi,
+                         k=w.k, W=w.W, main_dtype=w.main_dtype, idx_dtype=w.idx_dtype)
+            ores = run_layer(g, inp0)
+            o = to_np(out)
+            for b in range(w.B):
+                nv = odsa.n_vis(p_first, w.s, w.S)
+                qi = decode_store(inp0["qi"][b], w.idx_dtype, inp0["qi_scale"][b])[0]
+                scores = odsa.indexer_scores(qi, np.asarray(inp0["wt"][b][0], np.float64),
+                                             ores["states"][b].idx_cache[:nv])
+                check_topk_row(gi[b, 0], scores, w.k, f"graph b={b}")
+                if set(gi[b, 0].tolist()) == set(ores["idx"][b, 0].tolist()):
+                    check_close(o[b, 0], ores["out"][b, 0], ATOL["bf16"], f"graph b={b}",
+                                kind="layer out bf16")
+                    check_close(lse.cpu().numpy()[b, 0], ores["lse"][b, 0], LSE_ATOL["bf16"],
+                                f"graph b={b} lse", kind="layer lse bf16")
+    for a, b in zip(_state_tensors(st_e), _state_tensors(st_g)):
+        assert torch.equal(a, b), "state after the replays differs from the eager steps"

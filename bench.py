@@ -100,7 +100,7 @@ def build_sets(w, n_sets, device):
     return sets
 
 
-def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
+def time_layer(w, sets, steps, warmup, decode, out_fp8=False, q_norm=False):
     """Two timed passes of `steps` layer steps each, after `warmup` untimed
     ones.  The first pass gives the step time: nothing but the layer's own
     launches on the stream, bracketed by events.  The second pass hands the
@@ -117,7 +117,11 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False):
     outs = [Ly.alloc_outputs(w, B, T, dev, out_fp8) for _ in sets]
     scs = [torch.empty((B, T, w.H), dtype=torch.float32, device=dev) if out_fp8 else None
            for _ in sets]
-    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s, out_scale=sc)
+    qg = None
+    if q_norm:  # a Q-norm weight around 1
+        g = torch.Generator(device="cpu").manual_seed(5)
+        qg = (1.0 + 0.5 * torch.randn(w.D, generator=g)).to(dev)
+    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s, out_scale=sc, q_norm_gamma=qg)
             for (st, ch), o, sc in zip(sets, outs, scs)]
     ws_bytes = max(_lib.layer_workspace(a) for a in args)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -391,6 +395,13 @@ def main():
         extra[w.name + "_fp8_out"] = {"queries_per_s": w.B / (ms8 / 1e3), "ms_per_step": ms8,
                                       "batch": w.B, "context": w.L, "k": w.k,
                                       "kernel_ms": {"attention": attn8}}
+        # the same step with a Q-norm of every query head, prepared in the
+        # indexer's launch
+        print("[bench] timing with a Q-norm", file=sys.stderr, flush=True)
+        msq, _, attnq = time_layer(w, sets, args.steps, args.warmup, decode=True, q_norm=True)
+        extra[w.name + "_q_norm"] = {"queries_per_s": w.B / (msq / 1e3), "ms_per_step": msq,
+                                     "batch": w.B, "context": w.L, "k": w.k,
+                                     "kernel_ms": {"attention": attnq}}
         # the same step captured in HIP graphs and replayed
         print("[bench] timing graph replays", file=sys.stderr, flush=True)
         msg = time_layer_graph(w, sets, args.steps, args.warmup)

@@ -241,7 +241,12 @@ dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* ws, size_t ws_bytes, vo
  *  3. S3/S4 for each of the T queries (entries completed earlier in the same
  *     chunk are visible to later queries); with idx_heads == 0 every visible
  *     entry is selected, which needs k >= n_vis (the c128a case);
- *  4. S5 with the window [m - W, m - 1];
+ *  4. S5 with the window [m - W, m - 1]; with q_norm_gamma each query head
+ *     is first normalised, q <- gamma * q / sqrt(mean(q^2) + rms_eps).  The
+ *     queries are normalised and rotated in one launch with the window
+ *     tokens' rotation and insert (the pages' horizontally fused
+ *     pre-attention step, [P2] 融合点 3): in decode always, riding in the
+ *     indexer's launch; in a chunk when there is a Q-norm;
  *  5. the window ring takes the chunk's rotated tokens (after attention, so
  *     slot m mod w_cap is reused only once m's own query has run).
  * Raw indexer tokens kx are F32 when idx_dtype is F32 and BF16 when it is
@@ -290,6 +295,7 @@ typedef struct dsa_layer_args {
   float* out_scale;           /* [B, T, H] (out_fp8)                         */
   int32_t main_fp8;           /* 1: main_cache holds token-wise fp8 codes    */
   float* main_scale;          /* [B, e_cap] (main_fp8); decode only, see S5  */
+  const float* q_norm_gamma;  /* [D] or NULL: Q-norm of each query head      */
 } dsa_layer_args;
 
 size_t dsa_layer_workspace(const dsa_layer_args* a);

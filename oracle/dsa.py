@@ -135,6 +135,16 @@ def compress_entry(tokens, logits, pos, r, base, gamma=None, eps=1e-6):
     return rope_rotate(c, pos, r, base)
 
 
+def rms_norm(x, gamma, eps):
+    """RMSNorm over the last axis: gamma * x / sqrt(mean(x^2) + eps).  The
+    pages name a Q-norm ahead of the attention ([P2] 融合点 3: "Q Norm", fused
+    with the window keys' RoPE and insert) without its formula; the reading
+    taken is the same RMSNorm the compressor uses ([P2] 融合点 1)."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gamma, np.float64) * x / np.sqrt(ms + eps)
+
+
 def quantize_fp8_entry(c):
     """Token-wise fp8 ([P2] 第三层: decode uses token-wise fp8): one fp32
     scale per entry, sigma = max|c| / 448, codes = RNE_e4m3fn(c / sigma).

@@ -68,6 +68,7 @@ class Geometry:
     scale: float = None        # softmax scale; None -> 1/sqrt(D)
     gamma: np.ndarray = None   # optional RMSNorm weight of the main compressor
     gamma_idx: np.ndarray = None
+    q_gamma: np.ndarray = None  # optional Q-norm weight (each query head, before rotation)
     eps: float = 1e-6
 
     @property
@@ -107,7 +108,8 @@ def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
 
     The rotated query R_m q is held in the layer's storage dtype before the
     logits: the pages rotate and quantise the query in one fused step ahead
-    of the attention ([P2] 全景图, decode step A: "Q RoPE + quant").
+    of the attention ([P2] 全景图, decode step A: "Q RoPE + quant").  With
+    ``g.q_gamma`` each head is RMS-normalised first ([P2] 融合点 3, "Q Norm").
 
     ``alt_idx`` [T, k] (optional): another selection per row, already checked
     against this one under the tie rule; where its set differs, the
@@ -182,7 +184,8 @@ def layer_chunk(g: Geometry, st: SeqState, p0, X, KX, logits_main, logits_idx,
         # S5: attention over the selected entries and the window.
         vecs = dsa.gather_set(m, idx, st.main_cache, win_vec, W)
         if rotate_q:
-            q, _ = store(dsa.rope_rotate(Q[t], m + off, g.r, g.base), g.main_dtype)
+            qt = Q[t] if g.q_gamma is None else dsa.rms_norm(Q[t], g.q_gamma, g.eps)
+            q, _ = store(dsa.rope_rotate(qt, m + off, g.r, g.base), g.main_dtype)
         else:
             q = np.asarray(Q[t], np.float64)
         outs[t], lses[t] = dsa.sparse_attention(q, vecs, m + off, g.r, g.base, g.tau)

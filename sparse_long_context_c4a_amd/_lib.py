@@ -79,7 +79,8 @@ class LayerArgs(ctypes.Structure):
                 ("idx_scale", c_vp), ("e_cap", c_i64), ("main_ring", c_vp), ("idx_ring", c_vp),
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
-                ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32), ("main_scale", c_vp)]
+                ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32),
+                ("main_scale", c_vp), ("q_norm_gamma", c_vp)]
 
 
 EXPORTS = {

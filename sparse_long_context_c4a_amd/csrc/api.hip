@@ -163,6 +163,7 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
   REQUIRE(!a->out_fp8 || a->out_scale, "dsa_layer: out_fp8 needs out_scale");
   REQUIRE(a->main_fp8 == 0 || a->main_fp8 == 1, "dsa_layer: main_fp8 must be 0 or 1");
   REQUIRE(!a->main_fp8 || a->main_scale, "dsa_layer: main_fp8 needs main_scale");
+  REQUIRE(a->q_norm_gamma == nullptr || a->rms_eps >= 0.f, "dsa_layer: rms_eps < 0");
   SUPPORT(!a->main_fp8 || (a->dtype == DSA_BF16 && a->main.dim == 512),
           "dsa_layer: an fp8 main cache is built for dtype BF16 and dim 512");
   if (a->main_fp8) {  // refused before the step writes any state
@@ -192,7 +193,7 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
 struct LayerWs {
   dsa_index_args ia;
   dsa_attn_args aa;
-  size_t off_idx_ws, off_attn_ws, off_idx, off_rot, off_cs, total;
+  size_t off_idx_ws, off_attn_ws, off_idx, off_rot, off_cs, off_qrot, total;
 };
 
 LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
@@ -227,6 +228,13 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   // decode: the (cos, sin) table of each row's position
   L.off_cs = off;
   if (a->chunk_len == 1) off = align_up(off + static_cast<size_t>(rows) * a->main.rope_dim * 4);
+  // the prepared (normalised, rotated) queries: every decode step (the
+  // prologue riding in the indexer's launch prepares them, so the attention
+  // starts from rotated queries) and chunks with a Q-norm
+  L.off_qrot = off;
+  const bool qprep = a->q_norm_gamma != nullptr || a->chunk_len == 1;
+  if (qprep)
+    off = align_up(off + static_cast<size_t>(rows) * a->heads * a->main.dim * dtype_size(a->dtype));
   // q positions (one per row)
   dsa_attn_args& aa = L.aa;
   aa.n_seqs = a->n_seqs;
@@ -267,6 +275,10 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
     ia.idx_out = idx;
     aa.idx = idx;
     aa.chunk_win = base + L.off_rot;
+    if (qprep) {  // attention reads the prepared queries
+      aa.q = base + L.off_qrot;
+      aa.rotate_q = 0;
+    }
     int64_t* qpos = reinterpret_cast<int64_t*>(base + off_pos);
     ia.q_pos = qpos;
     aa.q_pos = qpos;
@@ -304,7 +316,8 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     lx.ev0 = call_timing().attn0;
     lx.ev1 = call_timing().attn1;
     lx.cs_tab = cs_tab;
-    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab, st);
+    rc = launch_decode_index_topk(L.ia, base + L.off_idx_ws, *a, qpos, early, cs_tab,
+                                  base + L.off_qrot, st);
     if (rc != DSA_OK) return rc;
     rc = launch_attn(L.aa, base + L.off_attn_ws, st, lx);
     if (rc != DSA_OK) return rc;
@@ -365,10 +378,14 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   // S3 + S4
   rc = launch_index_topk(L.ia, base + L.off_idx_ws, st);
   if (rc != DSA_OK) return rc;
-  // rotated chunk tokens: the window of the chunk's own queries, then the ring
-  rc = launch_rotate_chunk(a->x, a->dtype, a->main.dim, T, a->main.rope_dim, a->main.rope_base,
-                           a->main.rope_pos_offset, a->pos0, B, base + L.off_rot, a->max_pos_end,
-                           st);
+  // rotated chunk tokens: the window of the chunk's own queries, then the
+  // ring; with a Q-norm, the queries prepared in the same launch
+  if (a->q_norm_gamma)
+    rc = launch_qk_prep(*a, base + L.off_qrot, base + L.off_rot, st);
+  else
+    rc = launch_rotate_chunk(a->x, a->dtype, a->main.dim, T, a->main.rope_dim, a->main.rope_base,
+                             a->main.rope_pos_offset, a->pos0, B, base + L.off_rot,
+                             a->max_pos_end, st);
   if (rc != DSA_OK) return rc;
   // S5
   AttnLaunch lx;

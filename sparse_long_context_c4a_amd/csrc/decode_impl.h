@@ -29,8 +29,51 @@ __device__ __forceinline__ void rotate_store(const T* __restrict__ x, T* __restr
   }
 }
 
+// Q-norm and rotation of one query head by one wave of 64 lanes (the pages'
+// horizontally fused pre-attention step, "DeepSeek V4 稀疏注意力完全解剖"
+// 融合点 3: each wave owns one head, no exchange between waves):
+// q <- gamma * q / sqrt(mean(q^2) + eps) when gamma is given (the RMSNorm
+// form of the compressor's), then R_pos on the tail r dims, stored in the
+// storage dtype T.
+template <typename T>
+__device__ __forceinline__ void q_prep_head(const T* __restrict__ qh, T* __restrict__ dst, int D,
+                                            int r, double base, int64_t pos,
+                                            const float* __restrict__ gamma, float eps) {
+  const int lane = threadIdx.x & 63;
+  float rs = 1.f;
+  if (gamma) {
+    float ss = 0.f;
+    for (int pr = lane; pr < D / 2; pr += 64) {
+      const float a0 = load_as_f32(qh, 2 * pr), a1 = load_as_f32(qh, 2 * pr + 1);
+      ss += a0 * a0 + a1 * a1;
+    }
+    rs = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(D) + eps);
+  }
+  const int first_rot = (D - r) / 2;
+  for (int pr = lane; pr < D / 2; pr += 64) {
+    float a0 = load_as_f32(qh, 2 * pr), a1 = load_as_f32(qh, 2 * pr + 1);
+    if (gamma) {
+      a0 *= gamma[2 * pr] * rs;
+      a1 *= gamma[2 * pr + 1] * rs;
+    }
+    if (pr >= first_rot) {
+      float c, sn;
+      rope_cs(pos, pr - first_rot, r, base, &c, &sn);
+      const float t0 = a0 * c - a1 * sn, t1 = a0 * sn + a1 * c;
+      a0 = t0;
+      a1 = t1;
+    }
+    store_from_f32(dst, 2 * pr, a0);
+    store_from_f32(dst, 2 * pr + 1, a1);
+  }
+}
+
 struct PrologueArgs {
   int B, D, Di, s, S, r, r_idx, w_cap;
+  int H, nq_roles;             // query heads; workgroups of q preparation per sequence (0: none)
+  const void* q;               // [B, H, D] queries
+  void* q_rot;                 // [B, H, D] normalised, rotated queries
+  const float* q_gamma;        // [D] Q-norm weight or nullptr
   double base, idx_base;
   int64_t off, e_cap, max_pos_end;
   float eps;
@@ -59,7 +102,8 @@ constexpr int prologue_roles() { return kSlices + 3; }
 constexpr int kPrologueRoles = prologue_roles<1>();
 constexpr int kStandaloneSlices = 4;
 
-// Decode-step prologue, one role per workgroup: roles 0 .. kSlices-1
+// Decode-step prologue, one role per workgroup (then, when the queries are
+// prepared here, a.nq_roles roles of four query heads each): roles 0 .. kSlices-1
 // write (their dims of) the main entry completing at m (if any); the next
 // role the indexer entry; the next puts token m into the compressor rings,
 // the row's query position, and -- when the window ring has a spare slot
@@ -76,6 +120,16 @@ template <typename MainT, int kIdxOut, int kSlices, bool kMainFp8 = false>
 __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueArgs a) {
   using IdxRawT = typename std::conditional<kIdxOut == DSA_F32, float, uint16_t>::type;
   constexpr int kMainOut = std::is_same<MainT, float>::value ? DSA_F32 : DSA_BF16;
+  if (role >= prologue_roles<kSlices>()) {
+    // query preparation: four heads per workgroup, one per wave
+    const int h = 4 * (role - prologue_roles<kSlices>()) + static_cast<int>(threadIdx.x >> 6);
+    const int64_t m = a.pos0[b];
+    if (h >= a.H || m < 0 || m >= a.max_pos_end) return;
+    const int64_t o = (static_cast<int64_t>(b) * a.H + h) * a.D;
+    q_prep_head(static_cast<const MainT*>(a.q) + o, static_cast<MainT*>(a.q_rot) + o, a.D, a.r,
+                a.base, m + a.off, a.q_gamma, a.eps);
+    return;
+  }
   if (kSlices == 1 ? role == 0 : static_cast<unsigned>(role) < static_cast<unsigned>(kSlices)) {
     int d0 = 0, dn = -1;  // all dims
     if constexpr (kMainFp8) {

@@ -80,10 +80,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb, PrologueArgs pa,
     uint32_t* status) {
-  const int id = static_cast<int>(blockIdx.x), npro = pa.B * kPrologueRoles;
+  const int rpr = kPrologueRoles + pa.nq_roles;  // prologue workgroups per sequence
+  const int id = static_cast<int>(blockIdx.x), npro = pa.B * rpr;
   if (id < npro) {
-    decode_prologue_block<MainT, kIdxOut, 1, kMainFp8>(id % kPrologueRoles, id / kPrologueRoles,
-                                                       pa);
+    decode_prologue_block<MainT, kIdxOut, 1, kMainFp8>(id % rpr, id / rpr, pa);
   } else {
     const int sid = id - npro;
     index_stream_block<true, kEnt>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale, q_pos, 1,
@@ -508,13 +508,13 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
 }
 
 dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
-                                    int64_t* qpos, bool insert_window, float* cs_tab,
+                                    int64_t* qpos, bool insert_window, float* cs_tab, void* q_rot,
                                     hipStream_t st) {
   const Plan P = plan(a);
   const bool fused = P.cand && a.keys != nullptr && P.nv_cap > 0 && a.queries_per_seq == 1 &&
                      a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16;
   if (!fused) {
-    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, st);
+    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, q_rot, st);
     if (rc != DSA_OK) return rc;
     return launch_index_topk(a, ws, st);
   }
@@ -523,9 +523,9 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
   float* scores = reinterpret_cast<float*>(base + P.off_scores);
   uint64_t* cand = reinterpret_cast<uint64_t*>(base + P.off_cand);
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
-  const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab);
+  const PrologueArgs pa = make_prologue_args(la, qpos, insert_window, cs_tab, q_rot);
   auto go = [&](auto kern) {
-    launch_timed(kern, dim3((P.nb + kPrologueRoles) * rows), dim3(kThreads), 0, st,
+    launch_timed(kern, dim3((P.nb + kPrologueRoles + pa.nq_roles) * rows), dim3(kThreads), 0, st,
                  call_timing().index0, call_timing().index1,
                  static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                  static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,

@@ -82,15 +82,18 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 // has no spare slot, the window insert after attention.
 struct PrologueArgs;
 PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                float* cs_tab);
+                                float* cs_tab, void* q_rot);
 // The indexer + Top-k of a decode step with the prologue's workgroups riding
 // in the indexer's launch (or launched first when the indexer takes another
 // path).
 dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
-                                    int64_t* qpos, bool insert_window, float* cs_tab,
+                                    int64_t* qpos, bool insert_window, float* cs_tab, void* q_rot,
                                     hipStream_t st);
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  float* cs_tab, hipStream_t st);
+                                  float* cs_tab, void* q_rot, hipStream_t st);
+// The chunk's pre-attention step: queries normalised and rotated into q_rot,
+// the raw tokens rotated into rot_chunk (one launch).
+dsa_status launch_qk_prep(const dsa_layer_args& a, void* q_rot, void* rot_chunk, hipStream_t st);
 dsa_status launch_decode_window_insert(const dsa_layer_args& a, hipStream_t st);
 
 inline size_t dtype_size(dsa_dtype t) {

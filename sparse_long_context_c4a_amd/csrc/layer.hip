@@ -60,6 +60,49 @@ __global__ void k_rotate_chunk(const T* __restrict__ x, int D, int64_t Tn, int r
   }
 }
 
+// The pre-attention step of a chunk, horizontally fused ("DeepSeek V4 稀疏注意力
+// 完全解剖", 融合点 3): the first B T nq workgroups prepare the queries (Q-norm
+// and rotation, four heads per workgroup, one per wave), the next B T rotate
+// the chunk's raw tokens for the window (K RoPE; the window ring takes them
+// after attention).  No workgroup waits on another.
+template <typename T>
+__global__ __launch_bounds__(256) void k_qk_prep(const T* __restrict__ q, T* __restrict__ q_rot,
+                                                 int H, int nq, const float* __restrict__ gamma,
+                                                 float eps, const T* __restrict__ x, T* __restrict__ rot,
+                                                 int D, int64_t Tn, int r, double base, int64_t off,
+                                                 const int64_t* __restrict__ pos0, int B,
+                                                 int64_t max_pos_end) {
+  const int64_t id = blockIdx.x, nqw = static_cast<int64_t>(B) * Tn * nq;
+  if (id < nqw) {
+    const int64_t row = id / nq;  // b * T + t
+    const int b = static_cast<int>(row / Tn);
+    const int64_t t = row % Tn, p0 = pos0[b];
+    const int h = 4 * static_cast<int>(id % nq) + static_cast<int>(threadIdx.x >> 6);
+    if (h >= H || p0 < 0 || p0 + Tn > max_pos_end) return;
+    const int64_t o = (row * H + h) * D;
+    q_prep_head(q + o, q_rot + o, D, r, base, p0 + t + off, gamma, eps);
+    return;
+  }
+  const int64_t tk = id - nqw;
+  const int b = static_cast<int>(tk / Tn);
+  const int64_t t = tk % Tn, p0 = pos0[b];
+  if (p0 < 0 || p0 + Tn > max_pos_end) return;
+  const int64_t o = (static_cast<int64_t>(b) * Tn + t) * D;
+  const int first_rot = (D - r) / 2;
+  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) {
+    float a0 = load_as_f32(x, o + 2 * pr), a1 = load_as_f32(x, o + 2 * pr + 1);
+    if (pr >= first_rot) {
+      float c, s;
+      rope_cs(p0 + t + off, pr - first_rot, r, base, &c, &s);
+      const float t0 = a0 * c - a1 * s, t1 = a0 * s + a1 * c;
+      a0 = t0;
+      a1 = t1;
+    }
+    store_from_f32(rot, o + 2 * pr, a0);
+    store_from_f32(rot, o + 2 * pr + 1, a1);
+  }
+}
+
 // Window ring takes the last min(T, w_cap) rotated chunk tokens.
 __global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int64_t T,
                                 uint16_t* __restrict__ win, int w_cap,
@@ -128,6 +171,26 @@ dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, in
   return hip_check(hipGetLastError(), "k_rotate_chunk launch");
 }
 
+dsa_status launch_qk_prep(const dsa_layer_args& a, void* q_rot, void* rot_chunk, hipStream_t st) {
+  const int B = a.n_seqs, H = a.heads, D = a.main.dim;
+  const int64_t T = a.chunk_len;
+  const int nq = (H + 3) / 4;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * T * (nq + 1)));
+  if (a.dtype == DSA_F32)
+    hipLaunchKernelGGL(k_qk_prep<float>, grid, dim3(256), 0, st, static_cast<const float*>(a.q),
+                       static_cast<float*>(q_rot), H, nq, a.q_norm_gamma, a.rms_eps,
+                       static_cast<const float*>(a.x), static_cast<float*>(rot_chunk), D, T,
+                       a.main.rope_dim, a.main.rope_base, a.main.rope_pos_offset, a.pos0, B,
+                       a.max_pos_end);
+  else
+    hipLaunchKernelGGL(k_qk_prep<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(q_rot), H, nq,
+                       a.q_norm_gamma, a.rms_eps, static_cast<const uint16_t*>(a.x),
+                       static_cast<uint16_t*>(rot_chunk), D, T, a.main.rope_dim, a.main.rope_base,
+                       a.main.rope_pos_offset, a.pos0, B, a.max_pos_end);
+  return hip_check(hipGetLastError(), "k_qk_prep launch");
+}
+
 dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
                                 int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
                                 hipStream_t st) {
@@ -144,8 +207,13 @@ dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int6
 namespace dsa {
 
 PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                float* cs_tab) {
+                                float* cs_tab, void* q_rot) {
   PrologueArgs p{};
+  p.H = a.heads;
+  p.nq_roles = q_rot ? (a.heads + 3) / 4 : 0;
+  p.q = a.q;
+  p.q_rot = q_rot;
+  p.q_gamma = a.q_norm_gamma;
   p.B = a.n_seqs;
   p.D = a.main.dim;
   p.Di = a.idx_dim;
@@ -183,9 +251,10 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
 }
 
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  float* cs_tab, hipStream_t st) {
-  const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab);
-  const dim3 grid(prologue_roles<kStandaloneSlices>() * a.n_seqs), block(kCompressThreads);
+                                  float* cs_tab, void* q_rot, hipStream_t st) {
+  const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab, q_rot);
+  const dim3 grid((prologue_roles<kStandaloneSlices>() + p.nq_roles) * a.n_seqs),
+      block(kCompressThreads);
   if (a.dtype == DSA_F32) {
     if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((k_decode_prologue<float, DSA_FP8_E4M3>), grid, block, 0, st, p);

@@ -114,7 +114,8 @@ def chunk_from_inputs(w: Workload, inp, device="cuda"):
 
 def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=None,
                status=None, max_pos_end=None, pos_offset=0, rms_gamma=None,
-               rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0, out_scale=None):
+               rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0, out_scale=None,
+               q_norm_gamma=None):
     a = _lib.LayerArgs()
     a.main = _lib.geom(w.s, w.S, w.D, w.r, w.base, pos_offset)
     a.heads, a.idx_heads, a.idx_dim = w.H, w.Hi, w.Di
@@ -132,6 +133,7 @@ def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=No
     a.main_ring, a.idx_ring = _lib.ptr(st.main_ring), _lib.ptr(st.idx_ring)
     a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
     a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps
+    a.q_norm_gamma = _lib.ptr(q_norm_gamma)
     if st.main_scale is not None:  # fp8 codes in main_cache
         a.main_fp8, a.main_scale = 1, _lib.ptr(st.main_scale)
     a.out, a.lse, a.idx_out = _lib.ptr(out), _lib.ptr(lse), _lib.ptr(idx_out)

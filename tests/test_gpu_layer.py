@@ -450,3 +450,35 @@ def test_layer_decode_all_scores_tie():
         assert sorted(ix[b, 0].tolist()) == list(range(w.k)), b
     ores = _oracle(w, inp, gpu_idx=idx)
     _compare(w, inp, ores, out, lse, idx, label="all scores tie")
+
+
+QNORM = [
+    # name, workload, overrides, p0, T, state: the Q-norm in the decode
+    # prologue riding in the indexer's launch (L = 40000: the candidate
+    # path), in the stand-alone prologue (L = 3000, c128a), and in the
+    # prefill chunk's pre-attention launch (matrix-core and f32 attention)
+    ("c4a_decode_B2_L40000_fused", configs.C4A_DECODE_64K, dict(B=2, L=40000), None, None,
+     "random"),
+    ("c4a_decode_B3_L3000", configs.C4A_DECODE_64K, dict(B=3, L=3000), None, None, "random"),
+    ("c128a_decode_B2_L5000", configs.C128A_DECODE_1M, dict(B=2, L=5000, k=64), None, None,
+     "random"),
+    ("c4a_prefill_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077), 2000, 77, "random"),
+    ("f32_prefill_fresh_T200", configs.TINY_C4A_F32, dict(L=200, mode="prefill"), 0, 200,
+     "empty"),
+]
+
+
+@pytest.mark.parametrize("case", QNORM, ids=[c[0] for c in QNORM])
+def test_layer_q_norm(case):
+    """Each query head RMS-normalised (gamma per dim) before its rotation,
+    prepared in the same launch as the window tokens' rotation ("DeepSeek V4
+    稀疏注意力完全解剖", 融合点 3): against the oracle with the same Q-norm."""
+    name, w0, over, p0, T, state = case
+    w = configs.shrink(w0, **over)
+    seed = 5900 + QNORM.index(case)
+    print(f"[dsa_layer q-norm] {name} B={w.B} p0={p0} T={T} seed={seed}", flush=True)
+    inp = gen.layer_inputs(w, seed=seed, p0=p0, T=T, state=state)
+    gam = (1.0 + 0.5 * np.random.default_rng(seed).standard_normal(w.D)).astype(np.float32)
+    _, out, lse, idx = _run_gpu(w, inp, q_norm_gamma=torch.tensor(gam, device=DEV))
+    ores = _oracle(w, inp, gpu_idx=idx, q_gamma=gam.astype(np.float64))
+    _compare(w, inp, ores, out, lse, idx, label=name + " q-norm")

@@ -191,3 +191,20 @@ def test_fp8_output_is_nearest_code_per_head():
         # the largest magnitude maps to the top of the grid
         assert np.abs(codecs.fp8_decode(codes[h])).max() == 448.0
     assert sig[3] == 0.0 and not codes[3].any()
+
+
+def test_q_norm_is_rms_norm():
+    """The Q-norm reading (RMSNorm of each head over its D dims) against
+    torch's rms_norm in float64, and its closed form with gamma = 1."""
+    import torch
+    from oracle import dsa
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((5, 64, 32)) * 3.0
+    gamma = 1.0 + 0.5 * rng.standard_normal(32)
+    eps = 1e-6
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(q), (32,), torch.from_numpy(gamma),
+                                       eps=eps).numpy()
+    assert np.allclose(dsa.rms_norm(q, gamma, eps), ref, rtol=1e-13, atol=1e-13)
+    one = dsa.rms_norm(q, np.ones(32), eps)
+    ms = np.mean(q * q, axis=-1)
+    assert np.allclose(np.mean(one * one, axis=-1), ms / (ms + eps), rtol=1e-13)

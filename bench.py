@@ -74,14 +74,20 @@ def measured_traffic():
         return None
 
 
+def index_key_bytes(w):
+    """Bytes of one stored indexer key with its scales."""
+    if not w.Hi:
+        return 0
+    return {"fp8": w.Di + 4, "fp4": w.Di // 2 + w.Di // 32, "f32": 4 * w.Di}[w.idx_dtype]
+
+
 def decode_bytes_per_query(w, nv):
     """Algorithmic HBM bytes of one decode query: the visible indexer keys
-    (Di fp8 bytes + a 4-byte scale each), the k + W gathered latent vectors,
-    q and out, and the k selected indices."""
+    (fp8: Di bytes + a 4-byte scale each; MXFP4: Di / 2 bytes + Di / 32
+    scale bytes), the k + W gathered latent vectors, q and out, and the k
+    selected indices."""
     el = 2 if w.main_dtype == "bf16" else 4
-    idx_b = nv * (w.Di + (4 if w.idx_dtype == "fp8" else 0)) if w.Hi else 0
-    if w.idx_dtype == "f32":
-        idx_b = nv * w.Di * 4
+    idx_b = nv * index_key_bytes(w)
     sel = min(w.k, nv)
     attn = (sel + min(w.W, w.m)) * w.D * el
     return idx_b + attn + 2 * w.H * w.D * el + w.k * 4
@@ -304,10 +310,14 @@ def time_decode_workload(w, dev, steps, warmup, n_sets):
     nv = _lib.n_complete(w.m, w.s, w.S)
     step_bytes = w.B * decode_bytes_per_query(w, nv)
     gbps = step_bytes / (ms / 1e3) / 1e9
-    return {"queries_per_s": w.B / (ms / 1e3), "ms_per_step": ms, "batch": w.B, "context": w.L,
-            "k": w.k, "n_vis": nv, "alg_bytes_per_step": step_bytes, "hbm_gbps": gbps,
-            "hbm_frac": gbps / PEAK_HBM_GBPS,
-            "kernel_ms": {"indexer": idx_ms, "attention": attn_ms}}
+    r = {"queries_per_s": w.B / (ms / 1e3), "ms_per_step": ms, "batch": w.B, "context": w.L,
+         "k": w.k, "n_vis": nv, "alg_bytes_per_step": step_bytes, "hbm_gbps": gbps,
+         "hbm_frac": gbps / PEAK_HBM_GBPS,
+         "kernel_ms": {"indexer": idx_ms, "attention": attn_ms}}
+    if w.Hi and idx_ms:  # the key stream's own rate (keys and their scales)
+        r["indexer_key_bytes"] = index_key_bytes(w)
+        r["indexer_gbps"] = w.B * nv * index_key_bytes(w) / (idx_ms / 1e3) / 1e9
+    return r
 
 
 def main():
@@ -355,7 +365,7 @@ def main():
     gbps = step_bytes / (ms / 1e3) / 1e9
     if w.Hi:
         # the dominant kernel: the indexer's stream over the visible keys
-        kern, kbytes, kms = "k_decode_index", w.B * nv * (w.Di + 4), idx_ms
+        kern, kbytes, kms = "k_decode_index", w.B * nv * index_key_bytes(w), idx_ms
     else:
         # no indexer (the selection is every visible entry): the attention
         # kernels' gather of the n_vis + W vectors, q and out
@@ -380,10 +390,10 @@ def main():
                      "kernel": kern, "alg_bytes_per_launch": kbytes},
     }
     # this layer's own cache per raw token: one main entry (D dims) and one
-    # indexer key (Di fp8 codes + an f32 scale) per s tokens; the window ring
+    # indexer key (with its scales) per s tokens; the window ring
     # is a fixed W tokens per sequence
     el = 2 if w.main_dtype == "bf16" else 4
-    ikey = (w.Di + 4 if w.idx_dtype == "fp8" else 4 * w.Di) if w.Hi else 0
+    ikey = index_key_bytes(w)
     line["kv_context"] = dict(PAGE_KV_CONTEXT, this_layer={
         "layer": w.name.split("_")[0], "bytes_per_token": (w.D * el + ikey) / w.s,
         "window_bytes_per_seq": w.W * w.D * el})

@@ -37,7 +37,13 @@
  *    memory accesses stay in bounds.
  *  - Storage formats: DSA_F32 IEEE binary32; DSA_BF16 bfloat16;
  *    DSA_FP8_E4M3 OCP fp8 e4m3fn (bias 7, max 448, no infinities) with one
- *    fp32 scale per row (value = scale * code).
+ *    fp32 scale per row (value = scale * code); DSA_FP4_E2M1 OCP MX FP4
+ *    (indexer keys only): E2M1 codes (sign, 2 exponent bits with bias 1, one
+ *    mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with
+ *    the lower nibble first, and one E8M0 scale byte e per 32 consecutive
+ *    dims (value = 2^(e - 127) * code), the scales in their own row-major
+ *    array [B, e_cap, dim / 32].  The pages store the indexer in fp4 ([P2]
+ *    第三层, 机制三) without a format; MX FP4 is the reading taken.
  *  - Key tile layout: an FP8 cache of dim 128 (the indexer keys) is not
  *    row-major.  Each sequence holds e_pad = ceil(e_cap / 16) * 16 entries
  *    (allocate B * e_pad * 128 bytes) in tiles of 16 entries; tile t is 2048
@@ -47,7 +53,11 @@
  *    This is the order in which the matrix-core operands are read, so each
  *    load instruction of the indexer streams 1 KiB of contiguous bytes.  The
  *    scales stay row-major [B, e_cap].  FP8 caches of other dims are
- *    row-major.
+ *    row-major.  An FP4 cache of dim 128 uses the same 16-entry tiles at 64
+ *    bytes per entry (allocate B * e_pad * 64 bytes): tile t is 1024 bytes,
+ *    4 chunks of 32 dims (16 bytes), chunk c holding the 16 entries' bytes;
+ *    the byte of dim d of entry j of sequence b (nibble d % 2) sits at
+ *      ((b * e_pad + 16 * (j / 16)) * 64) + (d / 32) * 256 + (j % 16) * 16 + (d % 32) / 2.
  *  - RoPE acts on interleaved pairs of the last rope_dim dims of a vector,
  *    pair i rotated by angle (pos + rope_pos_offset) * rope_base^(-2i/rope_dim).
  *    rope_pos_offset shifts every rotation position and no index.
@@ -73,7 +83,7 @@ typedef enum dsa_status {
   DSA_ERR_HIP = -4          /* a HIP runtime call failed                     */
 } dsa_status;
 
-typedef enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
+typedef enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2, DSA_FP4_E2M1 = 3 } dsa_dtype;
 
 /* Bits OR-ed into the optional device status word by kernels. */
 #define DSA_DEVERR_POSITION 1u  /* a position outside [0, max_pos_end)        */
@@ -104,6 +114,9 @@ typedef struct dsa_geom {
  * raw token shared across D.  Optional RMSNorm (gamma != NULL):
  * c <- gamma * c / sqrt(mean(c^2) + eps).  Then RoPE at position s j.
  * FP8 output: scale = max|c| / 448 (fp32), codes round to nearest even.
+ * FP4 output (MXFP4): per 32-dim block e = floor(log2(max|c|)) - 2 (clamped
+ * to [-127, 127]; -127 for an all-zero block), codes = E2M1 of c / 2^e
+ * rounded to nearest even and saturating at 6 (the OCP MX conversion).
  */
 typedef struct dsa_compress_args {
   dsa_geom geom;
@@ -125,6 +138,8 @@ typedef struct dsa_compress_args {
   int64_t e_cap;              /* cache slots per sequence                    */
   int64_t max_pos_end;        /* host bound: raw_pos0[b] + raw_len <= this   */
   uint32_t* status;           /* optional device status word                 */
+  uint8_t* out_mx_scale;      /* [B, e_cap, D / 32] E8M0 block scales for FP4
+                                 output (D a multiple of 32), else ignored   */
 } dsa_compress_args;
 
 dsa_status dsa_compress(const dsa_compress_args* a, void* stream);
@@ -153,13 +168,16 @@ typedef struct dsa_index_args {
   const float* w;             /* [B * Tq, Hi] head weights                   */
   const void* keys;           /* [B, e_cap, Di]; FP8 Di = 128: tile layout   */
   const float* k_scale;       /* [B, e_cap] (FP8)                            */
-  dsa_dtype dtype;            /* q and keys: DSA_F32 or DSA_FP8_E4M3         */
+  dsa_dtype dtype;            /* q and keys: DSA_F32 or DSA_FP8_E4M3; or
+                                 DSA_FP4_E2M1: keys MXFP4 (Di == 128, tile
+                                 layout, k_mx_scale), q fp8 with q_scale     */
   int64_t e_cap;
   int64_t max_pos_end;        /* host bound: q_pos[i] < max_pos_end          */
   int32_t k;                  /* >= 1                                        */
   int32_t* idx_out;           /* [B * Tq, k]                                 */
   float* score_out;           /* [B * Tq, k] or NULL (NaN for padding)       */
   uint32_t* status;
+  const uint8_t* k_mx_scale;  /* [B, e_cap, Di / 32] E8M0 scales (FP4 keys)  */
 } dsa_index_args;
 
 size_t dsa_index_topk_workspace(const dsa_index_args* a);
@@ -267,7 +285,8 @@ typedef struct dsa_layer_args {
   const int64_t* pos0;        /* device [B]                                  */
   int64_t max_pos_end;        /* host bound: pos0[b] + T <= max_pos_end      */
   dsa_dtype dtype;            /* DSA_F32 or DSA_BF16                         */
-  dsa_dtype idx_dtype;        /* DSA_F32 or DSA_FP8_E4M3                     */
+  dsa_dtype idx_dtype;        /* DSA_F32, DSA_FP8_E4M3 or DSA_FP4_E2M1 (keys
+                                 MXFP4 with Di == 128, queries qi fp8)       */
   const void* x;              /* [B, T, D] raw tokens                        */
   const void* kx;             /* [B, T, Di] raw indexer tokens               */
   const float* logits_main;   /* [B, ceil(T/s), S]                           */
@@ -296,6 +315,7 @@ typedef struct dsa_layer_args {
   int32_t main_fp8;           /* 1: main_cache holds token-wise fp8 codes    */
   float* main_scale;          /* [B, e_cap] (main_fp8); decode only, see S5  */
   const float* q_norm_gamma;  /* [D] or NULL: Q-norm of each query head      */
+  uint8_t* idx_mx_scale;      /* [B, e_cap, Di / 32] (idx_dtype FP4)         */
 } dsa_layer_args;
 
 size_t dsa_layer_workspace(const dsa_layer_args* a);

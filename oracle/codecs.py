@@ -15,16 +15,29 @@ definitions:
   bits with bias 7, 3 fraction bits, no infinities, the single NaN pattern
   S.1111.111 per sign, largest finite magnitude 448, smallest subnormal 2^-9.
   Encoding rounds to nearest, ties to even, and saturates to +-448.
+* fp4 e2m1 (OCP Microscaling Formats (MX) specification, FP4 element type):
+  1 sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1,
+  1.5, 2, 3, 4, 6; no infinities or NaN.  Encoding rounds to nearest, ties to
+  the even code, and saturates to +-6; a negative value that rounds to zero
+  keeps its sign (code 8).  The MX block scale (E8M0, 2^(e-127)) is in
+  ``oracle.dsa.quantize_mxfp4``.
 
 Pins (tests/test_oracle_codecs.py): every one of the 256 fp8 codes against
 torch's float8_e4m3fn decode, the format's landmark values (448, 2^-6, 2^-9,
 1.0), exhaustive round-trip of all finite codes, midpoint ties, and bf16
-against torch's bfloat16 conversion on random and edge values.
+against torch's bfloat16 conversion on random and edge values; the 16 fp4
+codes against the E2M1 magnitudes written out, every midpoint tie and the
+saturation by hand, fp4 encoding against brute-force nearest search, and the
+MX block-scale rule on hand-computed blocks.
 """
 
 import numpy as np
 
 FP8_MAX = 448.0
+FP4_MAX = 6.0
+# E2M1 magnitudes of codes 0..7 (OCP MX FP4: 1 sign, 2 exponent bits with
+# bias 1, 1 mantissa bit; no infinities or NaN)
+FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
 def bf16_decode(bits):
@@ -100,3 +113,24 @@ def fp8_encode(x):
     code = np.where(normal, code_n, code_s)
     code = np.where(nan, 0x7F, sign | code)
     return code.astype(np.uint8)
+
+
+def fp4_decode(codes):
+    """E2M1 codes (uint8, values 0..15; bit 3 the sign) -> float64 values."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c & 8, -1.0, 1.0) * FP4_GRID[c & 7]
+
+
+def fp4_encode(x):
+    """float64 values -> E2M1 codes (uint8 0..15): the nearest magnitude of
+    the grid, a tie to the even code (the grid's codes alternate mantissa
+    bits 0, 1), saturating at 6; the sign bit is set for negative inputs."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP4_MAX)
+    d = np.abs(a[..., None] - FP4_GRID)          # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    tie = d == best
+    # among equally near magnitudes take the even code
+    even = tie & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tie, axis=-1))
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.uint8)

@@ -158,6 +158,36 @@ def quantize_fp8_entry(c):
     return codecs.fp8_encode(c / sigma), sigma
 
 
+MX_BLOCK = 32  # elements sharing one E8M0 scale (OCP MX)
+
+
+def quantize_mxfp4(c):
+    """MXFP4 ([P2] 第三层 "indexer 用 fp4"; [P2] 机制三: the indexer is light
+    because it is stored in fp4).  The pages name the precision only; the
+    reading taken is the OCP Microscaling (MX) FP4 format: blocks of 32
+    consecutive elements share an E8M0 scale X = 2^e, with the spec's
+    conversion e = floor(log2(max|block|)) - 2 (2 = the largest E2M1
+    exponent), clamped to [-127, 127], e = -127 for an all-zero block; each
+    element is the E2M1 code of v / X (nearest, ties to even, saturating at
+    6).  c: [..., D] with D a multiple of 32.  Returns (codes uint8 [..., D],
+    scale bytes uint8 [..., D / 32] = e + 127)."""
+    c = np.asarray(c, dtype=np.float64)
+    blk = c.reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = f 2^ex, f in [0.5, 1)
+    e = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), -127)
+    codes = codecs.fp4_encode(blk / np.ldexp(1.0, e)[..., None])
+    return codes.reshape(c.shape), (e + 127).astype(np.uint8)
+
+
+def mxfp4_decode(codes, scales):
+    """MXFP4 codes [..., D] and scale bytes [..., D / 32] -> float64."""
+    v = codecs.fp4_decode(codes)
+    blk = v.reshape(v.shape[:-1] + (v.shape[-1] // MX_BLOCK, MX_BLOCK))
+    x = np.ldexp(1.0, np.asarray(scales).astype(np.int64) - 127)
+    return (blk * x[..., None]).reshape(v.shape)
+
+
 def compress_range(token_at, logits, j0, n, s, S, r, base, pos_offset=0,
                    gamma=None, eps=1e-6):
     """Entries j0 .. j0+n-1.  ``token_at(p)`` returns raw token p (float64

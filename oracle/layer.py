@@ -44,6 +44,9 @@ def store(v, dtype):
     if dtype == "fp8":
         codes, sigma = dsa.quantize_fp8_entry(v)
         return sigma * codecs.fp8_decode(codes), sigma
+    if dtype == "fp4":  # MXFP4: the block scales are part of the value
+        codes, sc = dsa.quantize_mxfp4(v)
+        return dsa.mxfp4_decode(codes, sc), None
     raise ValueError(dtype)
 
 

@@ -9,6 +9,7 @@ context does not need a float64 copy of the whole main cache.
 import numpy as np
 
 from . import codecs
+from . import dsa
 from .layer import Geometry, SeqState, layer_chunk
 
 
@@ -25,6 +26,8 @@ def decode_store(a, dtype, scale=None):
     if dtype == "fp8":
         v = codecs.fp8_decode(a)
         return v * np.asarray(scale, np.float64)[..., None]
+    if dtype == "fp4":  # MXFP4 codes with their E8M0 block scales
+        return dsa.mxfp4_decode(a, scale)
     raise ValueError(dtype)
 
 
@@ -70,6 +73,11 @@ def raw_dtype_idx(idx_dtype):
     return "f32" if idx_dtype == "f32" else "bf16"
 
 
+def q_dtype_idx(idx_dtype):
+    """The indexer queries' storage: fp8 beside fp4 keys, else the keys'."""
+    return "fp8" if idx_dtype == "fp4" else idx_dtype
+
+
 def run_layer(g: Geometry, inp, only=None, rotate_q=True, alt_idx=None):
     """Run one layer step for every sequence of ``inp`` (the dict produced by
     the seeded generator).  ``only``: optional list of chunk offsets t whose
@@ -94,11 +102,14 @@ def run_layer(g: Geometry, inp, only=None, rotate_q=True, alt_idx=None):
         main = LazyRows(inp["main_cache"][b], g.main_cache_dtype or g.main_dtype,
                         None if msc is None else msc[b])
         if has_idx:
-            sc = None if inp["idx_scale"] is None else inp["idx_scale"][b]
+            if g.idx_dtype == "fp4":
+                sc = inp["idx_mx"][b]
+            else:
+                sc = None if inp["idx_scale"] is None else inp["idx_scale"][b]
             idxc = LazyRows(inp["idx_cache"][b], g.idx_dtype, sc)
             idx_ring = decode_store(inp["idx_ring"][b], rdt)
             kx = decode_store(inp["kx"][b], rdt)
-            qi = decode_store(inp["qi"][b], g.idx_dtype,
+            qi = decode_store(inp["qi"][b], q_dtype_idx(g.idx_dtype),
                               None if inp["qi_scale"] is None else inp["qi_scale"][b])
             wt = np.asarray(inp["wt"][b], np.float64)
             lg_idx = np.asarray(inp["logits_idx"][b], np.float64)

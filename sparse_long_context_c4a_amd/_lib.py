@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # DSA_LIB_PATH selects another build of the same library (same ABI)
 LIB_PATH = os.environ.get("DSA_LIB_PATH") or os.path.join(_HERE, "libdsa.so")
 
-DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_FP4_E2M1 = 0, 1, 2, 3
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED",
           -3: "DSA_ERR_WORKSPACE", -4: "DSA_ERR_HIP"}
 DEVERR_POSITION, DEVERR_CAPACITY, DEVERR_NO_INDEX = 1, 2, 4
@@ -45,7 +45,7 @@ class CompressArgs(ctypes.Structure):
                 ("raw_len", c_i64), ("ring", c_vp), ("raw_pos0", c_vp), ("logits", c_vp),
                 ("logits_rows", c_i32), ("rms_gamma", c_vp), ("rms_eps", c_f32), ("out", c_vp),
                 ("out_dtype", c_i32), ("out_scale", c_vp), ("e_cap", c_i64),
-                ("max_pos_end", c_i64), ("status", c_vp)]
+                ("max_pos_end", c_i64), ("status", c_vp), ("out_mx_scale", c_vp)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -53,7 +53,8 @@ class IndexArgs(ctypes.Structure):
                 ("stride", c_i32), ("span", c_i32), ("heads", c_i32), ("dim", c_i32),
                 ("q", c_vp), ("q_scale", c_vp), ("w", c_vp), ("keys", c_vp), ("k_scale", c_vp),
                 ("dtype", c_i32), ("e_cap", c_i64), ("max_pos_end", c_i64), ("k", c_i32),
-                ("idx_out", c_vp), ("score_out", c_vp), ("status", c_vp)]
+                ("idx_out", c_vp), ("score_out", c_vp), ("status", c_vp),
+                ("k_mx_scale", c_vp)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -80,7 +81,7 @@ class LayerArgs(ctypes.Structure):
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
                 ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32),
-                ("main_scale", c_vp), ("q_norm_gamma", c_vp)]
+                ("main_scale", c_vp), ("q_norm_gamma", c_vp), ("idx_mx_scale", c_vp)]
 
 
 EXPORTS = {

@@ -29,7 +29,8 @@ class Workload:
     r_idx: int = 0       # rotary dims of the indexer keys
     base: float = 10000.0
     main_dtype: str = "bf16"   # main cache, window, q, out, raw tokens
-    idx_dtype: str = "fp8"     # indexer cache and indexer query
+    idx_dtype: str = "fp8"     # indexer cache and indexer query ("fp4": MXFP4
+                               # cache, fp8 query)
     p0: int = 0          # prefill: first position of the chunk
     T: int = 1           # prefill: chunk length
     seed: int = 0
@@ -84,8 +85,15 @@ C4A_PREFILL_128K = Workload(
     r=64, H=64, Hi=16, Di=128, k=512, s=4, S=8, p0=126976, T=4096,
     seed=20264)
 
+# The same step with the indexer cache stored in MXFP4 (64 bytes of E2M1 codes
+# and 4 E8M0 block scales per entry instead of 128 fp8 bytes and an f32 scale):
+# the pages keep the indexer in fp4 so that scanning the whole history is cheap.
+C4A_DECODE_1M_FP4 = Workload(
+    name="c4a_decode_B4_L1M_fp4idx", mode="decode", B=4, L=1048576, D=512, r=64,
+    H=64, Hi=16, Di=128, k=512, s=4, S=8, seed=20266, idx_dtype="fp4")
+
 ALL = [TINY_C4A_F32, C4A_DECODE_64K, C4A_DECODE_1M, C128A_DECODE_1M,
-       C4A_PREFILL_128K, C4A_DECODE_1M_CLUSTERED]
+       C4A_PREFILL_128K, C4A_DECODE_1M_CLUSTERED, C4A_DECODE_1M_FP4]
 BY_NAME = {w.name: w for w in ALL}
 
 

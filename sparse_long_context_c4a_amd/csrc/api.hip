@@ -79,9 +79,13 @@ dsa_status validate_compress(const dsa_compress_args* a) {
           "dsa_compress: raw, ring, raw_pos0, logits and out must be non-null");
   REQUIRE(a->raw_dtype == DSA_F32 || a->raw_dtype == DSA_BF16,
           "dsa_compress: raw_dtype must be F32 or BF16");
-  REQUIRE(is_dtype(a->out_dtype), "dsa_compress: bad out_dtype %d", a->out_dtype);
+  REQUIRE(is_dtype(a->out_dtype) || a->out_dtype == DSA_FP4_E2M1, "dsa_compress: bad out_dtype %d",
+          a->out_dtype);
   REQUIRE(a->out_dtype != DSA_FP8_E4M3 || a->out_scale,
           "dsa_compress: FP8 output needs out_scale");
+  REQUIRE(a->out_dtype != DSA_FP4_E2M1 || (a->out_mx_scale && a->geom.dim % 32 == 0),
+          "dsa_compress: FP4 output needs out_mx_scale and dim a multiple of 32 (got %d)",
+          a->geom.dim);
   REQUIRE(a->logits_rows >= ceil_div(a->raw_len, a->geom.stride),
           "dsa_compress: logits_rows %d < ceil(raw_len / stride) = %lld", a->logits_rows,
           (long long)ceil_div(a->raw_len, a->geom.stride));
@@ -107,9 +111,15 @@ dsa_status validate_index(const dsa_index_args* a) {
   }
   REQUIRE(a->q && a->w, "dsa_index_topk: q and w must be non-null");
   REQUIRE(a->heads >= 1 && a->dim >= 1, "dsa_index_topk: heads and dim must be >= 1");
-  REQUIRE(a->dtype == DSA_F32 || a->dtype == DSA_FP8_E4M3,
-          "dsa_index_topk: dtype must be F32 or FP8_E4M3");
+  REQUIRE(a->dtype == DSA_F32 || a->dtype == DSA_FP8_E4M3 || a->dtype == DSA_FP4_E2M1,
+          "dsa_index_topk: dtype must be F32, FP8_E4M3 or FP4_E2M1");
   if (a->dtype == DSA_FP8_E4M3) REQUIRE(a->k_scale, "dsa_index_topk: FP8 keys need k_scale");
+  if (a->dtype == DSA_FP4_E2M1) {
+    REQUIRE(a->k_mx_scale, "dsa_index_topk: FP4 keys need k_mx_scale");
+    SUPPORT(a->dim == 128 && a->heads <= 16,
+            "dsa_index_topk: FP4 keys are built for dim 128 and at most 16 heads (got %d, %d)",
+            a->dim, a->heads);
+  }
   SUPPORT(a->heads * a->dim <= 16384, "dsa_index_topk: heads * dim %d too large", a->heads * a->dim);
   return DSA_OK;
 }
@@ -174,12 +184,17 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
     REQUIRE(a->idx_dim >= 2 && a->idx_dim % 2 == 0, "dsa_layer: idx_dim must be even");
     REQUIRE(a->idx_rope_dim >= 0 && a->idx_rope_dim <= a->idx_dim && a->idx_rope_dim % 2 == 0,
             "dsa_layer: bad idx_rope_dim");
-    REQUIRE(a->idx_dtype == DSA_F32 || a->idx_dtype == DSA_FP8_E4M3,
-            "dsa_layer: idx_dtype must be F32 or FP8_E4M3");
+    REQUIRE(a->idx_dtype == DSA_F32 || a->idx_dtype == DSA_FP8_E4M3 ||
+                a->idx_dtype == DSA_FP4_E2M1,
+            "dsa_layer: idx_dtype must be F32, FP8_E4M3 or FP4_E2M1");
     REQUIRE(a->kx && a->logits_idx && a->qi && a->w && a->idx_cache && a->idx_ring,
             "dsa_layer: the indexer needs kx, logits_idx, qi, w, idx_cache and idx_ring");
     REQUIRE(a->idx_dtype != DSA_FP8_E4M3 || a->idx_scale,
             "dsa_layer: FP8 indexer cache needs idx_scale");
+    REQUIRE(a->idx_dtype != DSA_FP4_E2M1 || a->idx_mx_scale,
+            "dsa_layer: FP4 indexer cache needs idx_mx_scale");
+    SUPPORT(a->idx_dtype != DSA_FP4_E2M1 || (a->idx_dim == 128 && a->idx_heads <= 16),
+            "dsa_layer: an FP4 indexer cache is built for idx_dim 128 and at most 16 heads");
   } else {
     const int64_t nv_max = n_complete(a->max_pos_end - 1, a->main.stride, a->main.span);
     REQUIRE(nv_max <= a->k, "dsa_layer: without an indexer k (%d) must cover every visible entry "
@@ -208,10 +223,11 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   ia.heads = a->idx_heads;
   ia.dim = a->idx_dim;
   ia.q = a->qi;
-  ia.q_scale = a->idx_dtype == DSA_FP8_E4M3 ? a->qi_scale : nullptr;
+  ia.q_scale = a->idx_dtype != DSA_F32 ? a->qi_scale : nullptr;  // fp8 queries
   ia.w = a->w;
   ia.keys = a->idx_heads > 0 ? a->idx_cache : nullptr;
-  ia.k_scale = a->idx_scale;
+  ia.k_scale = a->idx_dtype == DSA_FP8_E4M3 ? a->idx_scale : nullptr;
+  ia.k_mx_scale = a->idx_dtype == DSA_FP4_E2M1 ? a->idx_mx_scale : nullptr;
   ia.dtype = a->idx_dtype;
   ia.e_cap = a->e_cap;
   ia.max_pos_end = a->max_pos_end;
@@ -363,6 +379,7 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     ci.out = a->idx_cache;
     ci.out_dtype = a->idx_dtype;
     ci.out_scale = a->idx_scale;
+    ci.out_mx_scale = a->idx_mx_scale;
     rc = launch_compress(ci, st);
     if (rc != DSA_OK) return rc;
   }

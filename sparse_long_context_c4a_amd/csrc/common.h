@@ -54,6 +54,23 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
   return sign | (ef << 3) | m;
 }
 
+// float -> OCP MX FP4 (E2M1) code: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// with ties to the even code (mantissa bit 0), saturating at 6; the sign
+// bit (8) is set for negative inputs.
+__device__ __forceinline__ uint32_t f32_to_fp4(float x) {
+  const float a = fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0u;
+  else if (a < 0.75f) c = 1u;
+  else if (a <= 1.25f) c = 2u;
+  else if (a < 1.75f) c = 3u;
+  else if (a <= 2.5f) c = 4u;
+  else if (a < 3.5f) c = 5u;
+  else if (a <= 5.0f) c = 6u;
+  else c = 7u;
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
 template <>
@@ -108,6 +125,19 @@ __device__ __forceinline__ void idx_load_chunks(const uint8_t* seq_keys, int64_t
   const int n = static_cast<int>(j & 15);
   *lo = t[g * 16 + n];
   *hi = t[(4 + g) * 16 + n];
+}
+
+// fp4 (MXFP4) caches of dim 128 use the same 16-entry tiles at 64 bytes per
+// entry: tile t holds 4 chunks of 16 bytes (32 dims each, two codes per byte,
+// the lower nibble first), chunk-major, each chunk the 16 entries' bytes in
+// entry order.  Lane (g, n) reads chunk g of entry n, 1 KiB per wave load.
+// Byte of dim d (its nibble: d % 2) of entry j of sequence b:
+__host__ __device__ __forceinline__ int64_t idx4_tile_off(int64_t b, int64_t e_pad, int64_t j, int d) {
+  return (b * e_pad + (j & ~int64_t{15})) * 64 + (d >> 5) * 256 + (j & 15) * 16 + ((d & 31) >> 1);
+}
+__device__ __forceinline__ uint4 idx4_load_chunk(const uint8_t* seq_keys, int64_t j, int g) {
+  const uint4* t = reinterpret_cast<const uint4*>(seq_keys + (j & ~int64_t{15}) * 64);
+  return t[g * 16 + static_cast<int>(j & 15)];
 }
 
 // ------------------------------------------------------- counts / keys

@@ -11,10 +11,12 @@ template <typename RawT, int kOut>
 __global__ __launch_bounds__(kCompressThreads) void k_compress(
     const RawT* __restrict__ raw, const RawT* __restrict__ ring, const int64_t* __restrict__ pos0v,
     const float* __restrict__ logits, void* __restrict__ out, float* __restrict__ out_scale,
-    const float* __restrict__ gamma, float eps, int64_t T, int logits_rows, int s, int S, int D,
-    int r, double base, int64_t off, int64_t e_cap, int64_t max_pos_end, uint32_t* status) {
+    uint8_t* __restrict__ out_mx, const float* __restrict__ gamma, float eps, int64_t T,
+    int logits_rows, int s, int S, int D, int r, double base, int64_t off, int64_t e_cap,
+    int64_t max_pos_end, uint32_t* status) {
   compress_one<RawT, kOut>(blockIdx.x, blockIdx.y, raw, ring, pos0v, logits, out, out_scale, gamma,
-                           eps, T, logits_rows, s, S, D, r, base, off, e_cap, max_pos_end, status);
+                           eps, T, logits_rows, s, S, D, r, base, off, e_cap, max_pos_end, status,
+                           0, -1, out_mx);
 }
 
 template <typename RawT>
@@ -25,12 +27,14 @@ dsa_status launch_typed(const dsa_compress_args& a, hipStream_t st) {
   const dsa_geom& g = a.geom;
 #define DSA_COMPRESS_LAUNCH(OUT)                                                                  \
   hipLaunchKernelGGL((k_compress<RawT, OUT>), grid, dim3(kCompressThreads), 0, st, raw, ring, a.raw_pos0, \
-                     a.logits, a.out, a.out_scale, a.rms_gamma, a.rms_eps, a.raw_len,            \
+                     a.logits, a.out, a.out_scale, a.out_mx_scale, a.rms_gamma, a.rms_eps,       \
+                     a.raw_len,                                                                  \
                      a.logits_rows, g.stride, g.span, g.dim, g.rope_dim, g.rope_base,            \
                      g.rope_pos_offset, a.e_cap, a.max_pos_end, a.status)
   switch (a.out_dtype) {
     case DSA_F32: DSA_COMPRESS_LAUNCH(DSA_F32); break;
     case DSA_BF16: DSA_COMPRESS_LAUNCH(DSA_BF16); break;
+    case DSA_FP4_E2M1: DSA_COMPRESS_LAUNCH(DSA_FP4_E2M1); break;
     default: DSA_COMPRESS_LAUNCH(DSA_FP8_E4M3); break;
   }
 #undef DSA_COMPRESS_LAUNCH

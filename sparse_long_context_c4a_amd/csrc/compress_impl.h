@@ -59,7 +59,7 @@ __device__ __forceinline__ void compress_one(
     const int64_t* __restrict__ pos0v, const float* __restrict__ logits, void* __restrict__ out,
     float* __restrict__ out_scale, const float* __restrict__ gamma, float eps, int64_t T,
     int logits_rows, int s, int S, int D, int r, double base, int64_t off, int64_t e_cap,
-    int64_t max_pos_end, uint32_t* status, int d0 = 0, int dn = -1) {
+    int64_t max_pos_end, uint32_t* status, int d0 = 0, int dn = -1, uint8_t* out_mx = nullptr) {
   // dims d0 .. d0 + dn - 1 only (dn = -1: all D); a slice is a multiple of 8
   // dims and needs neither gamma nor fp8 output, which take the whole vector
   if (dn < 0) dn = D;
@@ -209,6 +209,36 @@ __device__ __forceinline__ void compress_one(
       if (pr < npairs) {
         store_from_f32(op, d0 + 2 * pr, acc[k][0]);
         store_from_f32(op, d0 + 2 * pr + 1, acc[k][1]);
+      }
+    }
+  } else if constexpr (kOut == DSA_FP4_E2M1) {
+    // MXFP4: 32 dims (16 consecutive threads' pairs) share an E8M0 scale
+    // 2^e, e = floor(log2(block max)) - 2, the elements the E2M1 codes of
+    // c / 2^e (OCP MX conversion); dim 128 in the fp4 tile layout
+    const bool tiled = D == 128;
+    uint8_t* op = static_cast<uint8_t*>(out);
+    const int64_t e_pad = idx_e_pad(e_cap);
+    const int64_t ro = static_cast<int64_t>(b) * e_cap + j;
+#pragma unroll
+    for (int k = 0; k < kCompressPairs; ++k) {
+      const int pr = tid + k * kCompressThreads;
+      const bool in = pr < npairs;
+      float am = in ? fmaxf(fabsf(acc[k][0]), fabsf(acc[k][1])) : 0.f;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
+      int e = -127;
+      if (am > 0.f) {
+        int ex;
+        frexpf(am, &ex);  // am = f 2^ex, f in [0.5, 1)
+        e = min(127, max(-127, ex - 3));
+      }
+      const float inv = ldexpf(1.0f, -e);  // exact: a power of two
+      if (in) {
+        const uint32_t c0 = f32_to_fp4(acc[k][0] * inv), c1 = f32_to_fp4(acc[k][1] * inv);
+        const int d = d0 + 2 * pr;
+        const int64_t at = tiled ? idx4_tile_off(b, e_pad, j, d) : ro * (D / 2) + d / 2;
+        op[at] = static_cast<uint8_t>(c0 | (c1 << 4));
+        if ((d & 31) == 0) out_mx[ro * (D / 32) + d / 32] = static_cast<uint8_t>(e + 127);
       }
     }
   } else {  // fp8 e4m3fn, token-wise scale = amax / 448

@@ -83,6 +83,7 @@ struct PrologueArgs {
   const float *logits_main, *logits_idx, *gamma, *gamma_idx;
   void *main_cache, *idx_cache, *main_ring, *idx_ring, *window;
   float* idx_scale;
+  uint8_t* idx_mx;  // fp4 indexer cache: E8M0 block scales [B, e_cap, Di / 32]
   int64_t* qpos;
   float* cs_tab;  // role 3: (cos, sin) of R_m, r floats per sequence
   float* main_scale;  // fp8 main cache: one scale per entry [B, e_cap], else nullptr
@@ -162,7 +163,7 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
                                      static_cast<const IdxRawT*>(a.idx_ring), a.pos0, a.logits_idx,
                                      a.idx_cache, a.idx_scale, a.gamma_idx, a.eps, 1, 1, a.s, a.S,
                                      a.Di, a.r_idx, a.idx_base, a.off, a.e_cap, a.max_pos_end,
-                                     a.status);
+                                     a.status, 0, -1, a.idx_mx);
     return;
   }
   if (role == 3) {

@@ -52,16 +52,17 @@ namespace {
 // sum every one of the 128 products exactly once.  With the keys' tile
 // layout each of the two 16-byte loads of a wave reads 1 KiB of contiguous
 // bytes.
-template <bool kCand, int kEnt>
+template <bool kCand, int kEnt, int kFmt>
 __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
-    const int64_t* __restrict__ q_pos, int Tq, int Hi, int s, int S, int64_t e_cap,
-    int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, uint32_t* status) {
-  index_stream_block<kCand, kEnt>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys, k_scale, q_pos,
-                            Tq, Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand,
-                            meta, cap, status);
+    const uint8_t* __restrict__ k_mx, const int64_t* __restrict__ q_pos, int Tq, int Hi, int s,
+    int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
+    int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap,
+    uint32_t* status) {
+  index_stream_block<kCand, kEnt, kFmt>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys,
+                                        k_scale, k_mx, q_pos, Tq, Hi, s, S, e_cap, nv_cap,
+                                        max_pos_end, scores, ld_scores, cand, meta, cap, status);
 }
 
 // A decode step's indexer with the step's state updates riding along: the
@@ -76,19 +77,19 @@ template <typename MainT, int kIdxOut, int kEnt, bool kMainFp8 = false>
 __global__ __launch_bounds__(kThreads) void k_decode_index(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
-    const int64_t* __restrict__ q_pos, int Hi, int s, int S, int64_t e_cap, int64_t nv_cap,
-    int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb, PrologueArgs pa,
-    uint32_t* status) {
+    const uint8_t* __restrict__ k_mx, const int64_t* __restrict__ q_pos, int Hi, int s, int S,
+    int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
+    int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb,
+    PrologueArgs pa, uint32_t* status) {
   const int rpr = kPrologueRoles + pa.nq_roles;  // prologue workgroups per sequence
   const int id = static_cast<int>(blockIdx.x), npro = pa.B * rpr;
   if (id < npro) {
     decode_prologue_block<MainT, kIdxOut, 1, kMainFp8>(id % rpr, id / rpr, pa);
   } else {
     const int sid = id - npro;
-    index_stream_block<true, kEnt>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale, q_pos, 1,
-                                   Hi, s, S, e_cap, nv_cap, max_pos_end, scores, ld_scores, cand,
-                                   meta, cap, status);
+    index_stream_block<true, kEnt, kIdxOut>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale,
+                                            k_mx, q_pos, 1, Hi, s, S, e_cap, nv_cap, max_pos_end,
+                                            scores, ld_scores, cand, meta, cap, status);
   }
 }
 
@@ -148,14 +149,15 @@ constexpr int kMaxF = 24;
 // the certificate does not hold.  The candidates stay in registers (8 per
 // thread) through one combined reduction pass, one histogram pass and the
 // emit pass.
+template <int kFmt>
 __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     float* __restrict__ scores, int64_t ld_scores, const int64_t* __restrict__ q_pos,
     int s, int S, int64_t nv_cap, int64_t max_pos_end, const uint64_t* __restrict__ cand,
     const uint32_t* __restrict__ meta, int nw, int cap, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out, int k, const uint8_t* __restrict__ q,
     const float* __restrict__ q_scale, const float* __restrict__ hw,
-    const uint8_t* __restrict__ keys, const float* __restrict__ k_scale, int Tq, int Hi,
-    int64_t e_cap) {
+    const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
+    const uint8_t* __restrict__ k_mx, int Tq, int Hi, int64_t e_cap) {
   __shared__ uint64_t cand_s[kFinalCap + 256 * kMaxF];
   __shared__ uint64_t tmp_s[kTmpCap];
   __shared__ uint32_t h_s[kBins];
@@ -191,14 +193,15 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
   float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
   const int b = row / Tq;
-  const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * 128;
-  const float* ksb = k_scale + static_cast<int64_t>(b) * e_cap;
+  const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * KeyOps<kFmt>::kBytes;
+  const float* ksb = k_scale ? k_scale + static_cast<int64_t>(b) * e_cap : nullptr;
+  const uint8_t* msb = k_mx ? k_mx + static_cast<int64_t>(b) * e_cap * 4 : nullptr;
   v8bf aq[4];
   float wv[4];
   if (nv <= k) {
     if (orow) {  // the visible entries' scores (the stream kept them in registers)
-      exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
-      score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+      exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
+      score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
       __syncthreads();
     }
     emit_all_visible(srow, nv, k, irow, orow);
@@ -243,8 +246,8 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     }
   if (block_reduce_u32<2>(c_n) < static_cast<uint32_t>(k)) {  // barriers
     // fewer candidates than k (ties at the wave thresholds): the whole row
-    exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
-    score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+    exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
+    score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
     __syncthreads();
     row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
     return;
@@ -265,9 +268,9 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   if (tm > kc) {
     const bool in_f = mw > kc;
     const uint32_t nf = block_reduce_u32<2>(in_f ? 1u : 0u);  // barriers
-    exact_row_operands(q, q_scale, hw, row, Hi, aq, wv);
+    exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
     if (nf > static_cast<uint32_t>(kMaxF)) {
-      score_row_exact(aq, wv, kb, ksb, nv, srow, kSelWaves);
+      score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
       __syncthreads();
       row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
       return;
@@ -295,27 +298,20 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     constexpr int kBatch = 4;
     const int n = t & 15, g = (t & 63) >> 4, ntile = static_cast<int>(nf) * 16;
     for (int f0 = w; f0 < ntile; f0 += kBatch * kSelWaves) {
-      uint4 blo[kBatch], bhi[kBatch];
-      float ks[kBatch];
       int64_t jj[kBatch];
+      float sc[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int ft = f0 + u * kSelWaves;
         jj[u] = ft < ntile ? static_cast<int64_t>(f_s[ft >> 4]) * 256 + (ft & 15) * 16 + n : nv;
-        blo[u] = bhi[u] = uint4{0u, 0u, 0u, 0u};
-        ks[u] = 0.f;
-        if (jj[u] < nv) {
-          idx_load_chunks(kb, jj[u], g, &blo[u], &bhi[u]);
-          ks[u] = ksb[jj[u]];
-        }
       }
+      exact_scores<kFmt, kBatch>(aq, wv, kb, ksb, msb, jj, nv, sc);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int ft = f0 + u * kSelWaves;
-        const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
         if (g == 0 && ft < ntile)
           cand_s[kFinalCap + ft * 16 + n] =
-              jj[u] < nv ? composite(order_key(sc), static_cast<uint32_t>(jj[u])) : 0ull;
+              jj[u] < nv ? composite(order_key(sc[u]), static_cast<uint32_t>(jj[u])) : 0ull;
       }
     }
     __syncthreads();
@@ -418,7 +414,8 @@ Plan plan(const dsa_index_args& a) {
   p.nv_cap = std::min<int64_t>(a.e_cap, n_complete(a.max_pos_end - 1, a.stride, a.span));
   if (p.nv_cap < 0) p.nv_cap = 0;
   p.ld = (p.nv_cap + 63) / 64 * 64;
-  p.mfma = a.keys != nullptr && a.dtype == DSA_FP8_E4M3 && a.dim == 128 && a.heads <= 16;
+  p.mfma = a.keys != nullptr && (a.dtype == DSA_FP8_E4M3 || a.dtype == DSA_FP4_E2M1) &&
+           a.dim == 128 && a.heads <= 16;
   // entries per stream workgroup (1024: at 1M context 1024 workgroups of 4
   // waves keep every SIMD busy; 2048 halves the waves and loses more to
   // latency than it saves in candidate extraction)
@@ -448,6 +445,19 @@ Plan plan(const dsa_index_args& a) {
   return p;
 }
 
+void launch_cand_final(const dsa_index_args& a, const Plan& P, float* scores, uint64_t* cand,
+                       uint32_t* meta, int rows, int Tq, hipStream_t st) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos, a.stride,
+                       a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap, a.idx_out,
+                       a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
+                       static_cast<const uint8_t*>(a.keys), a.k_scale, a.k_mx_scale, Tq, a.heads,
+                       a.e_cap);
+  };
+  if (a.dtype == DSA_FP4_E2M1) go(k_topk_cand_final<DSA_FP4_E2M1>);
+  else go(k_topk_cand_final<DSA_FP8_E4M3>);
+}
+
 }  // namespace
 
 size_t index_topk_ws_bytes(const dsa_index_args& a) { return plan(a).total; }
@@ -468,12 +478,18 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
       dim3 grid(static_cast<unsigned>(P.nb), rows);
       auto go = [&](auto kern) {
         launch_timed(kern, grid, dim3(kThreads), 0, st, e0, e1, static_cast<const uint8_t*>(a.q),
-                     a.q_scale, a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
-                     a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
+                     a.q_scale, a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.k_mx_scale,
+                     a.q_pos, a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
                      a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
       };
-      if (P.cand) go(k_index_fp8_stream<true, 1024>);
-      else go(k_index_fp8_stream<false, 1024>);
+      const bool fp4 = a.dtype == DSA_FP4_E2M1;
+      if (P.cand) {
+        if (fp4) go(k_index_fp8_stream<true, 1024, DSA_FP4_E2M1>);
+        else go(k_index_fp8_stream<true, 1024, DSA_FP8_E4M3>);
+      } else {
+        if (fp4) go(k_index_fp8_stream<false, 1024, DSA_FP4_E2M1>);
+        else go(k_index_fp8_stream<false, 1024, DSA_FP8_E4M3>);
+      }
     } else {
       dim3 grid(static_cast<unsigned>(ceil_div(P.nv_cap, kThreads)), rows);
       const size_t shm = (static_cast<size_t>(a.heads) * a.dim + a.heads) * sizeof(float);
@@ -494,11 +510,7 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
     if (rc != DSA_OK) return rc;
   }
   if (P.cand && !no_keys) {
-    hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
-                       a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
-                       a.idx_out, a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale,
-                       a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.queries_per_seq,
-                       a.heads, a.e_cap);
+    launch_cand_final(a, P, scores, cand, meta, rows, a.queries_per_seq, st);
   } else {
     hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kSel), 0, st, no_keys ? nullptr : scores,
                        P.ld, a.q_pos, a.stride, a.span, P.nv_cap, a.max_pos_end, a.idx_out,
@@ -512,7 +524,8 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                                     hipStream_t st) {
   const Plan P = plan(a);
   const bool fused = P.cand && a.keys != nullptr && P.nv_cap > 0 && a.queries_per_seq == 1 &&
-                     a.dtype == DSA_FP8_E4M3 && la.dtype == DSA_BF16;
+                     (a.dtype == DSA_FP8_E4M3 || a.dtype == DSA_FP4_E2M1) &&
+                     la.dtype == DSA_BF16;
   if (!fused) {
     dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, q_rot, st);
     if (rc != DSA_OK) return rc;
@@ -528,20 +541,21 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
     launch_timed(kern, dim3((P.nb + kPrologueRoles + pa.nq_roles) * rows), dim3(kThreads), 0, st,
                  call_timing().index0, call_timing().index1,
                  static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-                 static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos, a.heads, a.stride,
-                 a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta, P.cap, P.nb,
-                 pa, a.status);
+                 static_cast<const uint8_t*>(a.keys), a.k_scale, a.k_mx_scale, a.q_pos, a.heads,
+                 a.stride, a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta,
+                 P.cap, P.nb, pa, a.status);
   };
-  if (la.main_fp8)
+  if (a.dtype == DSA_FP4_E2M1) {
+    if (la.main_fp8) go(k_decode_index<uint16_t, DSA_FP4_E2M1, 1024, true>);
+    else go(k_decode_index<uint16_t, DSA_FP4_E2M1, 1024>);
+  } else if (la.main_fp8) {
     go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024, true>);
-  else
+  } else {
     go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024>);
+  }
   dsa_status rc = hip_check(hipGetLastError(), "k_decode_index launch");
   if (rc != DSA_OK) return rc;
-  hipLaunchKernelGGL(k_topk_cand_final, dim3(rows), dim3(kSel), 0, st, scores, P.ld, a.q_pos,
-                     a.stride, a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap,
-                     a.idx_out, a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale,
-                     a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, 1, a.heads, a.e_cap);
+  launch_cand_final(a, P, scores, cand, meta, rows, 1, st);
   return hip_check(hipGetLastError(), "top-k launch");
 }
 

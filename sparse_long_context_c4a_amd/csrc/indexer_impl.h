@@ -22,6 +22,101 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Eight fp4 (E2M1) codes per dword, times the block scale -> eight bf16
+// values (exact: a code has two significant bits, the scale is a power of two).
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t w, float sc) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E8M0 scale byte -> 2^(e - 127) as f32 (e = 0: the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// The key formats of the matrix-core indexer (dim 128, 16-entry tiles).
+// Per lane (g, n) of a tile: its raw bytes of entry n, the four bf16 B
+// operands widened from them exactly, and the entry's scale factor (fp8:
+// the per-entry f32 scale; fp4: 1, the block scale is applied in the
+// widening).  The query's A operands take the same dims: fp8 keys give lane
+// g the 32 bytes 16g.. and 64 + 16g.. (two 16-byte chunks); fp4 keys give it
+// dims 32g .. 32g + 31 (one chunk, one E8M0 scale).  Either way the four
+// MFMAs of a tile sum each of the 128 products exactly once.
+template <int kFmt>
+struct KeyOps;
+
+template <>
+struct KeyOps<DSA_FP8_E4M3> {
+  static constexpr int kBytes = 128;  // per entry
+  struct Raw {
+    uint4 lo, hi;
+    float ks;
+  };
+  // kb: the sequence's keys; ksb: its per-entry scales; (msb unused)
+  __device__ static Raw load(const uint8_t* kb, const float* ksb, const uint8_t*, int64_t j, int g) {
+    Raw r;
+    idx_load_chunks(kb, j, g, &r.lo, &r.hi);
+    r.ks = ksb[j];
+    return r;
+  }
+  __device__ static Raw zero() { return Raw{{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, 0.f}; }
+  __device__ static void operands(const Raw& r, v8bf (&bo)[4]) {
+    bo[0] = fp8x8_to_bf16(r.lo.x, r.lo.y);
+    bo[1] = fp8x8_to_bf16(r.lo.z, r.lo.w);
+    bo[2] = fp8x8_to_bf16(r.hi.x, r.hi.y);
+    bo[3] = fp8x8_to_bf16(r.hi.z, r.hi.w);
+  }
+  __device__ static float scale(const Raw& r) { return r.ks; }
+  // head n's fp8 query row (128 bytes) -> A operands for lane group g
+  __device__ static void q_operands(const uint8_t* qrow, int g, v8bf (&a)[4]) {
+    uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (qrow) {
+      lo = reinterpret_cast<const uint4*>(qrow)[g];
+      hi = reinterpret_cast<const uint4*>(qrow)[4 + g];
+    }
+    a[0] = fp8x8_to_bf16(lo.x, lo.y);
+    a[1] = fp8x8_to_bf16(lo.z, lo.w);
+    a[2] = fp8x8_to_bf16(hi.x, hi.y);
+    a[3] = fp8x8_to_bf16(hi.z, hi.w);
+  }
+};
+
+template <>
+struct KeyOps<DSA_FP4_E2M1> {
+  static constexpr int kBytes = 64;
+  struct Raw {
+    uint4 c;     // dims 32g .. 32g + 31 of the entry
+    uint32_t e;  // their E8M0 scale byte
+  };
+  // kb: the sequence's keys; msb: its scale bytes [e_cap, 4]
+  __device__ static Raw load(const uint8_t* kb, const float*, const uint8_t* msb, int64_t j, int g) {
+    return Raw{idx4_load_chunk(kb, j, g), msb[j * 4 + g]};
+  }
+  __device__ static Raw zero() { return Raw{{0u, 0u, 0u, 0u}, 0u}; }
+  __device__ static void operands(const Raw& r, v8bf (&bo)[4]) {
+    const float sc = e8m0_to_f32(r.e);
+    bo[0] = fp4x8_to_bf16(r.c.x, sc);
+    bo[1] = fp4x8_to_bf16(r.c.y, sc);
+    bo[2] = fp4x8_to_bf16(r.c.z, sc);
+    bo[3] = fp4x8_to_bf16(r.c.w, sc);
+  }
+  __device__ static float scale(const Raw&) { return 1.f; }
+  __device__ static void q_operands(const uint8_t* qrow, int g, v8bf (&a)[4]) {
+    uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (qrow) {
+      lo = reinterpret_cast<const uint4*>(qrow)[2 * g];
+      hi = reinterpret_cast<const uint4*>(qrow)[2 * g + 1];
+    }
+    a[0] = fp8x8_to_bf16(lo.x, lo.y);
+    a[1] = fp8x8_to_bf16(lo.z, lo.w);
+    a[2] = fp8x8_to_bf16(hi.x, hi.y);
+    a[3] = fp8x8_to_bf16(hi.z, hi.w);
+  }
+};
+
 struct RowInfo {
   int64_t nv;
   bool ok;
@@ -75,15 +170,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Exact score (before the key scale) of entry column n for one row: A = the
 // row's 16 heads widened to bf16 (aq), f32 head weights wv for heads
-// 4g .. 4g+3; B = the entry's operand chunks.  Every lane of column n gets
-// the sum over heads.
+// 4g .. 4g+3; B = the entry's operands.  Every lane of column n gets the sum
+// over heads.
 __device__ __forceinline__ float exact_tile_score(const v8bf (&aq)[4], const float (&wv)[4],
-                                                  uint4 blo, uint4 bhi) {
+                                                  const v8bf (&bo)[4]) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[0], fp8x8_to_bf16(blo.x, blo.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[1], fp8x8_to_bf16(blo.z, blo.w), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[2], fp8x8_to_bf16(bhi.x, bhi.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[3], fp8x8_to_bf16(bhi.z, bhi.w), acc, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[c], bo[c], acc, 0, 0, 0);
   float v = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
             wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
   v += __shfl_xor(v, 16, 64);
@@ -91,22 +184,14 @@ __device__ __forceinline__ float exact_tile_score(const v8bf (&aq)[4], const flo
   return v;
 }
 
-// A row's exact operands: its heads (lane = head n, chunks g and 4 + g)
-// widened to bf16, and w * q_scale for heads 4g .. 4g+3.
+// A row's exact operands: its heads (lane = head n) widened to bf16 in the
+// key format's dim assignment, and w * q_scale for heads 4g .. 4g+3.
+template <int kFmt>
 __device__ __forceinline__ void exact_row_operands(const uint8_t* q, const float* q_scale,
                                                    const float* w, int64_t row, int Hi,
                                                    v8bf (&aq)[4], float (&wv)[4]) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  uint4 qlo = {0u, 0u, 0u, 0u}, qhi = {0u, 0u, 0u, 0u};
-  if (n < Hi) {
-    const uint4* qp = reinterpret_cast<const uint4*>(q + (row * Hi + n) * 128);
-    qlo = qp[g];
-    qhi = qp[4 + g];
-  }
-  aq[0] = fp8x8_to_bf16(qlo.x, qlo.y);
-  aq[1] = fp8x8_to_bf16(qlo.z, qlo.w);
-  aq[2] = fp8x8_to_bf16(qhi.x, qhi.y);
-  aq[3] = fp8x8_to_bf16(qhi.z, qhi.w);
+  KeyOps<kFmt>::q_operands(n < Hi ? q + (row * Hi + n) * 128 : nullptr, g, aq);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * g + i;
@@ -118,33 +203,45 @@ __device__ __forceinline__ void exact_row_operands(const uint8_t* q, const float
   }
 }
 
+// The exact score of entry j (j < nv, else 0) for lane (g, n) of a tile:
+// kBatch entries' loads go out before the first product.
+template <int kFmt, int kBatch>
+__device__ __forceinline__ void exact_scores(const v8bf (&aq)[4], const float (&wv)[4],
+                                             const uint8_t* kb, const float* ksb,
+                                             const uint8_t* msb, const int64_t (&j)[kBatch],
+                                             int64_t nv, float (&sc)[kBatch]) {
+  using K = KeyOps<kFmt>;
+  const int g = (threadIdx.x & 63) >> 4;
+  typename K::Raw r[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) r[u] = j[u] < nv ? K::load(kb, ksb, msb, j[u], g) : K::zero();
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    v8bf bo[4];
+    K::operands(r[u], bo);
+    sc[u] = exact_tile_score(aq, wv, bo) * K::scale(r[u]);
+  }
+}
+
 // Exact scores of a row's first nv entries into srow (every wave of the
 // workgroup takes every nwaves-th tile of 16 entries).
+template <int kFmt>
 __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float (&wv)[4],
-                                                const uint8_t* kb, const float* ksb, int64_t nv,
-                                                float* srow, int nwaves) {
+                                                const uint8_t* kb, const float* ksb,
+                                                const uint8_t* msb, int64_t nv, float* srow,
+                                                int nwaves) {
   // four tiles' loads in flight per wave and round
   constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
   for (int64_t t0 = wave; t0 * 16 < nv; t0 += kBatch * nwaves) {
-    uint4 blo[kBatch], bhi[kBatch];
-    float ks[kBatch];
+    int64_t j[kBatch];
+    float sc[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t j = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
-      blo[u] = bhi[u] = uint4{0u, 0u, 0u, 0u};
-      ks[u] = 0.f;
-      if (j < nv) {
-        idx_load_chunks(kb, j, g, &blo[u], &bhi[u]);
-        ks[u] = ksb[j];
-      }
-    }
+    for (int u = 0; u < kBatch; ++u) j[u] = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
+    exact_scores<kFmt, kBatch>(aq, wv, kb, ksb, msb, j, nv, sc);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t j = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
-      const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
-      if (g == 0 && j < nv) srow[j] = sc;
-    }
+    for (int u = 0; u < kBatch; ++u)
+      if (g == 0 && j[u] < nv) srow[j[u]] = sc[u];
   }
 }
 
@@ -152,13 +249,15 @@ __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float
 // stay in registers (candidates and wave thresholds go out; a row whose
 // certificate fails is re-scored by the final pass); without, every score
 // is written to its row.
-template <bool kCand, int kEnt>
+template <bool kCand, int kEnt, int kFmt = DSA_FP8_E4M3>
 __device__ __forceinline__ void index_stream_block(
     int bx, int nbx, int row, const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
-    const int64_t* __restrict__ q_pos, int Tq, int Hi, int s, int S, int64_t e_cap,
-    int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores, int64_t ld_scores,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, uint32_t* status) {
+    const uint8_t* __restrict__ k_mx, const int64_t* __restrict__ q_pos, int Tq, int Hi, int s,
+    int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
+    int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap,
+    uint32_t* status) {
+  using K = KeyOps<kFmt>;
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -172,31 +271,24 @@ __device__ __forceinline__ void index_stream_block(
   // each lane keeps the keys of groups 4i + 2 (g & 1) + (g >> 1), i < kKeep
   uint32_t kk[kKeep] = {};
   if (wbase < nv) {
-    const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * 128;
-    const float* ksb = k_scale + static_cast<int64_t>(b) * e_cap;
+    const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * K::kBytes;
+    const float* ksb = k_scale ? k_scale + static_cast<int64_t>(b) * e_cap : nullptr;
+    const uint8_t* msb = k_mx ? k_mx + static_cast<int64_t>(b) * e_cap * 4 : nullptr;
     // key loads: a ring of two slots of two groups; unconditional (clamped
     // to a visible entry, masked later) so the compiler can count them, and
     // the first slot issued before the query set-up
     const int64_t jmax = nv - 1;
-    uint4 blo[2][2], bhi[2][2];
-    float ks[2][2];
+    typename K::Raw kr[2][2];
     auto load = [&](int slot, int gr) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int64_t ent = min<int64_t>(wbase + (gr + u) * 16 + n, jmax);
-        idx_load_chunks(kb, ent, g, &blo[slot][u], &bhi[slot][u]);
-        ks[slot][u] = ksb[ent];
+        kr[slot][u] = K::load(kb, ksb, msb, ent, g);
       }
     };
     load(0, 0);
-    uint4 qlo = {0u, 0u, 0u, 0u}, qhi = {0u, 0u, 0u, 0u};
-    if (n < Hi) {
-      const uint4* qp = reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(row) * Hi + n) * 128);
-      qlo = qp[g];
-      qhi = qp[4 + g];
-    }
-    const v8bf a0 = fp8x8_to_bf16(qlo.x, qlo.y), a1 = fp8x8_to_bf16(qlo.z, qlo.w);
-    const v8bf a2 = fp8x8_to_bf16(qhi.x, qhi.y), a3 = fp8x8_to_bf16(qhi.z, qhi.w);
+    v8bf aq[4];
+    K::q_operands(n < Hi ? q + (static_cast<int64_t>(row) * Hi + n) * 128 : nullptr, g, aq);
     float wv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -215,11 +307,12 @@ __device__ __forceinline__ void index_stream_block(
       float part[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        v8bf bo[4];
+        K::operands(kr[sl][u], bo);
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp8x8_to_bf16(blo[sl][u].x, blo[sl][u].y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp8x8_to_bf16(blo[sl][u].z, blo[sl][u].w), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, fp8x8_to_bf16(bhi[sl][u].x, bhi[sl][u].y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, fp8x8_to_bf16(bhi[sl][u].z, bhi[sl][u].w), acc, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[c], bo[c], acc, 0, 0, 0);
         // lane holds rows (heads) 4g..4g+3 of column (entry) n
         part[u] = wv[0] * fmaxf(acc[0], 0.f) + wv[1] * fmaxf(acc[1], 0.f) +
                   wv[2] * fmaxf(acc[2], 0.f) + wv[3] * fmaxf(acc[3], 0.f);
@@ -233,7 +326,7 @@ __device__ __forceinline__ void index_stream_block(
       const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
       const float v = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
       const int u = g >> 1;
-      const float sc = v * ks[sl][u];
+      const float sc = v * K::scale(kr[sl][u]);
       const int64_t ent = wbase + (2 * st + u) * 16 + n;
       const bool vis = ent < nv;
       if constexpr (!kCand)

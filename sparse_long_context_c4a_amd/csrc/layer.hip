@@ -243,6 +243,7 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
   p.idx_ring = a.idx_ring;
   p.window = a.window;
   p.idx_scale = a.idx_scale;
+  p.idx_mx = a.idx_dtype == DSA_FP4_E2M1 ? a.idx_mx_scale : nullptr;
   p.qpos = qpos;
   p.cs_tab = cs_tab;
   p.main_scale = a.main_fp8 ? a.main_scale : nullptr;
@@ -255,19 +256,22 @@ dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool i
   const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab, q_rot);
   const dim3 grid((prologue_roles<kStandaloneSlices>() + p.nq_roles) * a.n_seqs),
       block(kCompressThreads);
-  if (a.dtype == DSA_F32) {
-    if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<float, DSA_F32>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_decode_prologue<float, DSA_FP8_E4M3>), grid, block, 0, st, p);
-  } else {
-    if (p.main_scale) {  // token-wise fp8 main cache
-      if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_F32, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_FP8_E4M3, true>), grid, block, 0, st, p);
-    } else if (a.idx_dtype == DSA_F32) {
-      hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_F32>), grid, block, 0, st, p);
-    } else {
-      hipLaunchKernelGGL((k_decode_prologue<uint16_t, DSA_FP8_E4M3>), grid, block, 0, st, p);
-    }
-  }
+  // the indexer entry's output format picks the instantiation
+  auto by_idx = [&](auto f32, auto fp8, auto fp4) {
+    if (a.idx_dtype == DSA_F32) hipLaunchKernelGGL(f32, grid, block, 0, st, p);
+    else if (a.idx_dtype == DSA_FP4_E2M1) hipLaunchKernelGGL(fp4, grid, block, 0, st, p);
+    else hipLaunchKernelGGL(fp8, grid, block, 0, st, p);
+  };
+  if (a.dtype == DSA_F32)
+    by_idx(k_decode_prologue<float, DSA_F32>, k_decode_prologue<float, DSA_FP8_E4M3>,
+           k_decode_prologue<float, DSA_FP4_E2M1>);
+  else if (p.main_scale)  // token-wise fp8 main cache
+    by_idx(k_decode_prologue<uint16_t, DSA_F32, true>,
+           k_decode_prologue<uint16_t, DSA_FP8_E4M3, true>,
+           k_decode_prologue<uint16_t, DSA_FP4_E2M1, true>);
+  else
+    by_idx(k_decode_prologue<uint16_t, DSA_F32>, k_decode_prologue<uint16_t, DSA_FP8_E4M3>,
+           k_decode_prologue<uint16_t, DSA_FP4_E2M1>);
   return hip_check(hipGetLastError(), "k_decode_prologue launch");
 }
 

@@ -817,7 +817,7 @@ __global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) 
   cnt = cnt_s;
   v8bf aq[4];
   float wv[4];
-  exact_row_operands(a.q, a.q_scale, a.w, row, a.Hi, aq, wv);
+  exact_row_operands<DSA_FP8_E4M3>(a.q, a.q_scale, a.w, row, a.Hi, aq, wv);
   const uint8_t* kb = a.keys + static_cast<int64_t>(b) * idx_e_pad(a.e_cap) * 128;
   const uint8_t* krm = a.keys_rm + static_cast<int64_t>(b) * a.nv_cap * 128;
   const float* ksb = a.k_scale + static_cast<int64_t>(b) * a.e_cap;
@@ -849,7 +849,9 @@ __global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) 
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = (t0 + u * kW) * 16 + n;
-        const float sc = exact_tile_score(aq, wv, blo[u], bhi[u]) * ks[u];
+        v8bf bo[4];
+        KeyOps<DSA_FP8_E4M3>::operands(KeyOps<DSA_FP8_E4M3>::Raw{blo[u], bhi[u], ks[u]}, bo);
+        const float sc = exact_tile_score(aq, wv, bo) * ks[u];
         if (g == 0 && i < ct * 16) {
           cand_s[i] = j[u] >= 0 ? composite(order_key(sc), static_cast<uint32_t>(j[u])) : 0ull;
           c_ge += (j[u] >= 0 && sc >= theta) ? 1u : 0u;
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) 
   }
   // fallback: score the whole row exactly, then select from the scores
   float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-  score_row_exact(aq, wv, kb, ksb, nv, srow, kW);
+  score_row_exact<DSA_FP8_E4M3>(aq, wv, kb, ksb, nullptr, nv, srow, kW);
   __syncthreads();
   row_select_from_scores<kPCandCap, kPSelT, 11>(srow, nv, a.k, irow, nullptr, cand_s, h_s);
 }

@@ -12,7 +12,13 @@ the fixed order listed in ``layer_inputs``):
   standard normal (float32 draws), stored as f32 or rounded to bf16;
 * fp8 tensors (indexer keys, indexer queries): codes = e4m3fn(clip(64 g,
   +-448)) for g standard normal, with one positive f32 scale per row drawn
-  as (1 + U[0, 0.25)) / 64, so the dequantised values are about N(0, 1).
+  as (1 + U[0, 0.25)) / 64, so the dequantised values are about N(0, 1);
+* fp4 tensors (MXFP4 indexer keys; their queries are fp8): each E2M1 code
+  drawn directly, magnitude code 0..7 with probabilities FP4_MAG_P and a
+  fair sign bit, and one E8M0 scale byte per 32 elements uniform in
+  {126, 127, 128} (block scales 1/2, 1, 2), so the dequantised values are of
+  unit order.  The codes come from no quantisation: a stored MXFP4 cache is
+  any codes and scale bytes.
 
 A "random" state stands for a context that was processed earlier: cache
 slots j < n_complete(p0) hold random entries, the compressor rings hold the
@@ -33,6 +39,9 @@ import torch
 from .configs import Workload
 
 FP8_CODE_GAIN = 64.0
+# magnitude codes 0..7 of the drawn fp4 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6)
+FP4_MAG_P = np.array([0.10, 0.20, 0.18, 0.15, 0.13, 0.12, 0.08, 0.04])
+MX_BLOCK = 32
 
 
 def _rng(seed):
@@ -66,6 +75,11 @@ def draw(rng, shape, dtype):
         scales = ((1.0 + 0.25 * rng.random(shape[:-1], dtype=np.float32))
                   / np.float32(FP8_CODE_GAIN)).astype(np.float32)
         return codes, scales
+    if dtype == "fp4":  # (codes uint8 0..15 [..., n], scale bytes [..., n / 32])
+        mag = rng.choice(8, size=shape, p=FP4_MAG_P)
+        sign = rng.integers(0, 2, size=shape) * 8
+        scales = rng.integers(126, 129, size=shape[:-1] + (shape[-1] // MX_BLOCK,))
+        return (mag | sign).astype(np.uint8), scales.astype(np.uint8)
     raise ValueError(dtype)
 
 
@@ -76,6 +90,8 @@ def zeros(shape, dtype):
         return np.zeros(shape, np.uint16)
     if dtype == "fp8":
         return np.zeros(shape, np.uint8), np.zeros(shape[:-1], np.float32)
+    if dtype == "fp4":
+        return np.zeros(shape, np.uint8), np.zeros(shape[:-1] + (shape[-1] // MX_BLOCK,), np.uint8)
     raise ValueError(dtype)
 
 
@@ -84,8 +100,13 @@ def _complete(L, s, S):
 
 
 def raw_idx_dtype(w: Workload):
-    """Raw indexer tokens are bf16 when the indexer cache is fp8."""
+    """Raw indexer tokens are bf16 when the indexer cache is fp8 or fp4."""
     return "f32" if w.idx_dtype == "f32" else "bf16"
+
+
+def q_idx_dtype(w: Workload):
+    """Indexer queries: fp8 beside fp4 keys, else the keys' storage."""
+    return "fp8" if w.idx_dtype == "fp4" else w.idx_dtype
 
 
 def layer_inputs(w: Workload, seed=None, p0=None, T=None, state="random",
@@ -126,17 +147,20 @@ def layer_inputs(w: Workload, seed=None, p0=None, T=None, state="random",
         out["main_cache"], out["main_scale"] = main_cache
     else:
         out["main_cache"], out["main_scale"] = main_cache, None
+    out["idx_mx"] = None
     if has_idx:
         ic = zeros((B, E_cap, Di), w.idx_dtype)
         if state == "random" and j0 > 0:
             for b in range(B):
                 v = draw(rng, (j0, Di), w.idx_dtype)
-                if w.idx_dtype == "fp8":
+                if w.idx_dtype in ("fp8", "fp4"):
                     ic[0][b, :j0], ic[1][b, :j0] = v
                 else:
                     ic[b, :j0] = v
         if w.idx_dtype == "fp8":
             out["idx_cache"], out["idx_scale"] = ic
+        elif w.idx_dtype == "fp4":
+            (out["idx_cache"], out["idx_mx"]), out["idx_scale"] = ic, None
         else:
             out["idx_cache"], out["idx_scale"] = ic, None
     else:
@@ -161,8 +185,9 @@ def layer_inputs(w: Workload, seed=None, p0=None, T=None, state="random",
     # 7. queries, indexer queries (+ scales), head weights
     out["q"] = draw(rng, (B, T, H, D), w.main_dtype)
     if has_idx:
-        v = draw(rng, (B, T, Hi, Di), w.idx_dtype)
-        if w.idx_dtype == "fp8":
+        qdt = q_idx_dtype(w)
+        v = draw(rng, (B, T, Hi, Di), qdt)
+        if qdt == "fp8":
             out["qi"], out["qi_scale"] = v
         else:
             out["qi"], out["qi_scale"] = v, None

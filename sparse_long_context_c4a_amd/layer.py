@@ -45,13 +45,40 @@ def idx_rows(tiles, E):
     return t.reshape(B, Ep, D)[:, :E]
 
 
-def idx_to_device(codes, device="cuda"):
-    """Indexer keys to the device: fp8 codes of dim 128 in the tile layout,
-    anything else (f32, other dims) unchanged."""
+def idx4_tiles(codes):
+    """fp4 key codes [B, E, 128] (one E2M1 code 0..15 per byte) -> the
+    library's fp4 tile layout [B, E_pad, 64]: two codes per byte (the even
+    dim in the lower nibble), each 16-entry tile stored chunk-major (4 chunks
+    of 32 dims = 16 bytes, each the 16 entries' bytes of that chunk)."""
+    t = codes if isinstance(codes, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(codes))
+    B, E, D = t.shape
+    assert D == 128
+    packed = (t[..., 0::2] & 15) | ((t[..., 1::2] & 15) << 4)
+    Ep = -(-E // 16) * 16
+    if Ep != E:
+        packed = torch.cat([packed, torch.zeros((B, Ep - E, 64), dtype=packed.dtype,
+                                                device=packed.device)], dim=1)
+    return packed.reshape(B, Ep // 16, 16, 4, 16).permute(0, 1, 3, 2, 4).contiguous().reshape(B, Ep, 64)
+
+
+def idx4_rows(tiles, E):
+    """Inverse of idx4_tiles: [B, E_pad, 64] fp4 tiles -> codes [B, E, 128]."""
+    B, Ep, _ = tiles.shape
+    t = tiles.reshape(B, Ep // 16, 4, 16, 16).permute(0, 1, 3, 2, 4).contiguous()
+    t = t.reshape(B, Ep, 64)[:, :E]
+    out = torch.empty((B, E, 128), dtype=t.dtype, device=t.device)
+    out[..., 0::2] = t & 15
+    out[..., 1::2] = t >> 4
+    return out
+
+
+def idx_to_device(codes, device="cuda", fp4=False):
+    """Indexer keys to the device: fp8 (or, with fp4, E2M1) codes of dim 128
+    in the tile layout, anything else (f32, other dims) unchanged."""
     if codes is None:
         return None
     if codes.dtype == np.uint8 and codes.ndim == 3 and codes.shape[-1] == 128:
-        return idx_tiles(codes).to(device)
+        return (idx4_tiles(codes) if fp4 else idx_tiles(codes)).to(device)
     return to_device(codes, device)
 
 
@@ -65,6 +92,7 @@ class LayerState:
     window: torch.Tensor
     e_cap: int
     main_scale: torch.Tensor = None  # token-wise fp8 main cache: one scale per entry
+    idx_mx: torch.Tensor = None      # fp4 indexer cache: E8M0 scale bytes [B, e_cap, Di / 32]
 
 
 @dataclass
@@ -82,14 +110,16 @@ class Chunk:
 
 
 def state_from_inputs(inp, device="cuda"):
+    mx = inp.get("idx_mx")
     return LayerState(main_cache=to_device(inp["main_cache"], device),
-                      idx_cache=idx_to_device(inp["idx_cache"], device),
+                      idx_cache=idx_to_device(inp["idx_cache"], device, fp4=mx is not None),
                       idx_scale=to_device(inp["idx_scale"], device),
                       main_ring=to_device(inp["main_ring"], device),
                       idx_ring=to_device(inp["idx_ring"], device),
                       window=to_device(inp["win_ring"], device),
                       e_cap=int(inp["E_cap"]),
-                      main_scale=to_device(inp.get("main_scale"), device))
+                      main_scale=to_device(inp.get("main_scale"), device),
+                      idx_mx=to_device(mx, device))
 
 
 def _pad_logits(lg, rows):
@@ -125,11 +155,13 @@ def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=No
     a.pos0 = _lib.ptr(ch.pos0)
     a.max_pos_end = max_pos_end if max_pos_end is not None else st.e_cap * w.s
     a.dtype = _lib.DSA_F32 if w.main_dtype == "f32" else _lib.DSA_BF16
-    a.idx_dtype = _lib.DSA_F32 if w.idx_dtype == "f32" else _lib.DSA_FP8_E4M3
+    a.idx_dtype = {"f32": _lib.DSA_F32, "fp8": _lib.DSA_FP8_E4M3,
+                   "fp4": _lib.DSA_FP4_E2M1}[w.idx_dtype]
     for name in ("x", "kx", "logits_main", "logits_idx", "q", "qi", "qi_scale", "w"):
         setattr(a, name, _lib.ptr(getattr(ch, name)))
     a.main_cache, a.idx_cache = _lib.ptr(st.main_cache), _lib.ptr(st.idx_cache)
     a.idx_scale, a.e_cap = _lib.ptr(st.idx_scale), st.e_cap
+    a.idx_mx_scale = _lib.ptr(st.idx_mx)
     a.main_ring, a.idx_ring = _lib.ptr(st.main_ring), _lib.ptr(st.idx_ring)
     a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
     a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps

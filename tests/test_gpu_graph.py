@@ -22,7 +22,7 @@ import torch
 
 from oracle import dsa as odsa
 from oracle.layer import Geometry
-from oracle.run import decode_store, run_layer
+from oracle.run import decode_store, q_dtype_idx, run_layer
 from sparse_long_context_c4a_amd import configs, inputs as gen
 
 from gpu_helpers import ATOL, LSE_ATOL, check_close, check_topk_row, to_np
@@ -90,7 +90,7 @@ def test_decode_step_graph_replay_matches_eager():
             o = to_np(out)
             for b in range(w.B):
                 nv = odsa.n_vis(p_first, w.s, w.S)
-                qi = decode_store(inp0["qi"][b], w.idx_dtype, inp0["qi_scale"][b])[0]
+                qi = decode_store(inp0["qi"][b], q_dtype_idx(w.idx_dtype), inp0["qi_scale"][b])[0]
                 scores = odsa.indexer_scores(qi, np.asarray(inp0["wt"][b][0], np.float64),
                                              ores["states"][b].idx_cache[:nv])
                 check_topk_row(gi[b, 0], scores, w.k, f"graph b={b}")

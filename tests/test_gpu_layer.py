@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import dsa as odsa
-from oracle.run import decode_store, run_layer
+from oracle.run import decode_store, q_dtype_idx, run_layer
 from sparse_long_context_c4a_amd import configs, inputs as gen
 
 from gpu_helpers import (ATOL, LSE_ATOL, check_close, check_fp8_heads, check_topk_row,
@@ -70,7 +70,7 @@ def _oracle(w, inp, only=None, gpu_idx=None, **geo):
     alt = None if gpu_idx is None else np.asarray(gpu_idx.cpu().numpy(), np.int64)
     res = run_layer(g, inp, only=only, alt_idx=alt)
     if w.Hi > 0:
-        res["qi_dec"] = [decode_store(inp["qi"][b], w.idx_dtype,
+        res["qi_dec"] = [decode_store(inp["qi"][b], q_dtype_idx(w.idx_dtype),
                                       None if inp["qi_scale"] is None else inp["qi_scale"][b])
                          for b in range(inp["x"].shape[0])]
     return res
@@ -98,6 +98,15 @@ SMALL = [
     ("c4a_prefill_fresh_T300", configs.C4A_PREFILL_128K, dict(L=300), 0, 300, "empty"),
     ("f32_prefill_fresh_T200", configs.TINY_C4A_F32, dict(L=200, mode="prefill"), 0, 200,
      "empty"),
+    # MXFP4 indexer cache: a decode step completing an entry (stand-alone
+    # prologue), the same with the prologue in the indexer's launch, and a
+    # ragged prefill chunk
+    ("c4a_decode_fp4_B3_L3000", configs.C4A_DECODE_1M_FP4, dict(B=3, L=3000), None, None,
+     "random"),
+    ("c4a_decode_fp4_B2_L40000_fused", configs.C4A_DECODE_1M_FP4, dict(B=2, L=40000), None,
+     None, "random"),
+    ("c4a_prefill_fp4_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077, idx_dtype="fp4"),
+     2000, 77, "random"),
 ]
 
 
@@ -159,6 +168,40 @@ def test_layer_small(case):
         check_close(ring, ores["states"][b].main_ring, 0.0, f"{name} main ring")
         win = to_np(st.window[b])
         check_close(win, ores["states"][b].win_ring, ATOL[w.main_dtype] / 4, f"{name} window")
+    if w.idx_dtype == "fp4":
+        assert _check_fp4_entries(w, st, ores, name) == inp["n_new"] * w.B
+
+
+def _check_fp4_entries(w, st, ores, name):
+    """The indexer entries a step wrote in MXFP4 (codes in the tile layout
+    and E8M0 block scales) against the oracle's quantisation of its f64
+    entries: scale bytes equal unless a block maximum lies within f32
+    rounding of a power of two, each element within its rounding step, and
+    the codes equal but for rounding-boundary cases.  Returns the count."""
+    Ly = _layer()
+    codes = Ly.idx4_rows(st.idx_cache, st.idx_cache.shape[1]).cpu().numpy()
+    mx = st.idx_mx.cpu().numpy()
+    n = same = tot = 0
+    for b in range(w.B):
+        for j0, n_new, _, idx_new in ores["states"][b].entries_written:
+            for e in range(n_new):
+                j, ref = j0 + e, idx_new[e]
+                oc, osc = odsa.quantize_mxfp4(ref)
+                amax = np.abs(ref).reshape(-1, 32).max(axis=-1)
+                lg = np.log2(np.maximum(amax, 1e-300))
+                near = np.abs(lg - np.round(lg)) < 1e-5
+                assert np.all((mx[b, j] == osc) | near), f"{name} b={b} entry {j} scales"
+                x = 2.0 ** (np.repeat(mx[b, j].astype(np.float64), 32) - 127.0)
+                am = np.abs(ref) / x
+                bound = np.where(am < 2, 0.25, np.where(am < 4, 0.5,
+                                                        np.where(am < 6, 1.0, am - 6.0)))
+                err = np.abs(odsa.mxfp4_decode(codes[b, j], mx[b, j]) - ref)
+                assert np.all(err <= (bound * (1 + 1e-5) + 1e-6) * x), f"{name} b={b} entry {j}"
+                same += int(np.sum(codes[b, j] == oc))
+                tot += oc.size
+                n += 1
+    assert tot == 0 or same >= 0.99 * tot, (same, tot)
+    return n
 
 
 def test_tiny_f32_workload_prefill_then_decode():
@@ -225,17 +268,19 @@ def test_chunked_prefill_matches_single_pass():
 
 
 FULL = [configs.C4A_DECODE_64K, configs.C4A_DECODE_1M, configs.C128A_DECODE_1M,
-        configs.C4A_DECODE_1M_CLUSTERED]
+        configs.C4A_DECODE_1M_CLUSTERED, configs.C4A_DECODE_1M_FP4]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
 def test_layer_full_size_decode(w):
     print(f"[dsa_layer_decode] {w.name} full size, seed={w.seed}", flush=True)
     inp = gen.layer_inputs(w)
-    _, out, lse, idx = _run_gpu(w, inp)
+    st, out, lse, idx = _run_gpu(w, inp)
     ores = _oracle(w, inp, gpu_idx=idx)
     swaps = _compare(w, inp, ores, out, lse, idx, label=w.name)
     assert swaps <= 2
+    if w.idx_dtype == "fp4":
+        assert _check_fp4_entries(w, st, ores, w.name) == w.B
     if w.cluster:  # a large share of the Top-k sits in a few waves of the cluster
         ix = idx.cpu().numpy()
         for b, c0 in enumerate(inp["cluster_start"]):
@@ -400,7 +445,7 @@ def test_layer_rope_pos_offset_fresh_sequence():
     g = geometry(w, pos_offset=OFFSET)
     ores = run_layer(g, inp, alt_idx=np.concatenate(
         [i1.cpu().numpy(), i2.cpu().numpy()], axis=1).astype(np.int64))
-    ores["qi_dec"] = [decode_store(inp["qi"][b], w.idx_dtype, inp["qi_scale"][b])
+    ores["qi_dec"] = [decode_store(inp["qi"][b], q_dtype_idx(w.idx_dtype), inp["qi_scale"][b])
                       for b in range(w.B)]
     out = torch.cat([o1, o2], dim=1)
     lse = torch.cat([l1, l2], dim=1)
@@ -465,6 +510,15 @@ QNORM = [
     ("c4a_prefill_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077), 2000, 77, "random"),
     ("f32_prefill_fresh_T200", configs.TINY_C4A_F32, dict(L=200, mode="prefill"), 0, 200,
      "empty"),
+    # MXFP4 indexer cache: a decode step completing an entry (stand-alone
+    # prologue), the same with the prologue in the indexer's launch, and a
+    # ragged prefill chunk
+    ("c4a_decode_fp4_B3_L3000", configs.C4A_DECODE_1M_FP4, dict(B=3, L=3000), None, None,
+     "random"),
+    ("c4a_decode_fp4_B2_L40000_fused", configs.C4A_DECODE_1M_FP4, dict(B=2, L=40000), None,
+     None, "random"),
+    ("c4a_prefill_fp4_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077, idx_dtype="fp4"),
+     2000, 77, "random"),
 ]
 
 

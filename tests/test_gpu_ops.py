@@ -43,6 +43,11 @@ COMPRESS_CASES = [
     # whose first entry mixes ring and new raw tokens
     ("c4a_wide_d1024", 4, 8, 1024, 64, "bf16", "bf16", 1, 40, 1002, False),
     ("c128a_chunk_ring_and_raw", 128, 128, 512, 64, "bf16", "bf16", 1, 300, 1000, False),
+    # MXFP4 indexer keys: the tile layout at dim 128 (a decode step and a
+    # ragged chunk with an RMSNorm), row-major at another dim
+    ("c4a_idx_decode_fp4", 4, 8, 128, 0, "bf16", "fp4", 3, 1, 70003, False),
+    ("c4a_idx_ragged_fp4_rmsnorm", 4, 8, 128, 16, "bf16", "fp4", 2, 77, 4094, True),
+    ("fp4_rowmajor_d64", 4, 8, 64, 16, "bf16", "fp4", 1, 40, 1002, False),
 ]
 
 
@@ -59,11 +64,13 @@ def test_compress(case):
     logits = rng.standard_normal((B, rows, S), dtype=np.float32)
     gamma = (1.0 + 0.5 * rng.standard_normal(D)).astype(np.float32) if use_gamma else None
     e_cap = -(-(p0 + T) // s)
-    out_t = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[odt]
-    tiled = odt == "fp8" and D == 128  # indexer keys: 16-entry tile layout
+    out_t = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+             "fp4": torch.uint8}[odt]
+    tiled = odt in ("fp8", "fp4") and D == 128  # indexer keys: 16-entry tile layout
     e_rows = -(-e_cap // 16) * 16 if tiled else e_cap
-    out = torch.zeros((B, e_rows, D), dtype=out_t, device=DEV)
+    out = torch.zeros((B, e_rows, D // 2 if odt == "fp4" else D), dtype=out_t, device=DEV)
     scale = torch.zeros((B, e_cap), dtype=torch.float32, device=DEV)
+    mx = torch.zeros((B, e_cap, D // 32), dtype=torch.uint8, device=DEV)
     a = L.CompressArgs()
     a.geom = L.geom(s, S, D, r, 10000.0, 0)
     raw_d, ring_d = _tensor(raw), _tensor(ring)
@@ -74,16 +81,21 @@ def test_compress(case):
     g_d = _tensor(gamma) if gamma is not None else None
     a.raw_pos0, a.logits, a.logits_rows = L.ptr(pos0), L.ptr(lg), rows
     a.rms_gamma, a.rms_eps = L.ptr(g_d), 1e-6
-    a.out, a.out_dtype = L.ptr(out), {"f32": 0, "bf16": 1, "fp8": 2}[odt]
+    a.out, a.out_dtype = L.ptr(out), {"f32": 0, "bf16": 1, "fp8": 2, "fp4": 3}[odt]
     a.out_scale, a.e_cap, a.max_pos_end = L.ptr(scale), e_cap, p0 + T
+    a.out_mx_scale = L.ptr(mx)
     L.compress(a)
     torch.cuda.synchronize()
     j0, j1 = odsa.n_complete(p0, s, S), odsa.n_complete(p0 + T, s, S)
     if tiled:
-        from sparse_long_context_c4a_amd.layer import idx_rows
-        rows_all = idx_rows(out, out.shape[1])
+        from sparse_long_context_c4a_amd.layer import idx4_rows, idx_rows
+        rows_all = idx4_rows(out, out.shape[1]) if odt == "fp4" else idx_rows(out, out.shape[1])
         assert not rows_all[:, e_cap:].any().item()  # padding entries untouched
         got = rows_all[:, :e_cap].cpu()
+    elif odt == "fp4":  # row-major, two codes per byte (even dim low)
+        pk = out.cpu()
+        got = torch.empty((B, e_cap, D), dtype=torch.uint8)
+        got[..., 0::2], got[..., 1::2] = pk & 15, pk >> 4
     else:
         got = out.cpu()
     sc = scale.cpu().numpy()
@@ -113,6 +125,26 @@ def test_compress(case):
             assert np.all(np.abs(deq - ref) <= (0.5 + 1e-3) * step * gs[:, None] + 1e-12)
             ocodes = np.stack([odsa.quantize_fp8_entry(v)[0] for v in ref])
             assert np.mean(codes == ocodes) > 0.999
+        elif odt == "fp4":
+            codes = got[b, j0:j1].numpy()
+            gm = mx.cpu().numpy()[b, j0:j1]
+            ocodes, osc = odsa.quantize_mxfp4(ref)
+            # the block scale byte: equal, except where the block's largest
+            # magnitude sits within f32 rounding of a power of two
+            amax = np.abs(ref).reshape(j1 - j0, D // 32, 32).max(axis=-1)
+            lg = np.log2(np.maximum(amax, 1e-300))
+            near = np.abs(lg - np.round(lg)) < 1e-5
+            assert np.all((gm == osc) | near), np.argwhere((gm != osc) & ~near)[:5]
+            # every element within its rounding step of the f64 entry (a
+            # step of 2 at 6 and saturation above), at the kernel's scale
+            x = 2.0 ** (np.repeat(gm.astype(np.float64), 32, axis=-1) - 127.0)
+            deq = odsa.mxfp4_decode(codes, gm)
+            am = np.abs(ref) / x
+            bound = np.where(am < 2, 0.25, np.where(am < 4, 0.5, np.where(am < 6, 1.0, am - 6.0)))
+            assert np.all(np.abs(deq - ref) <= (bound * (1 + 1e-5) + 1e-6) * x)
+            assert np.mean(codes == ocodes) > 0.999
+            # slots outside [j0, j1) keep zero scale bytes
+            assert not mx.cpu().numpy()[b, untouched].any()
         else:
             g = to_np(got[b, j0:j1])
             tol = np.abs(ref) * (2.0 ** -7 if odt == "bf16" else 2e-6) + 1e-5
@@ -128,6 +160,11 @@ INDEX_CASES = [
     ("decode_fp8_generic_heads", "fp8", 20, 96, 100, [5000, 300]),
     ("rows_fp8_prefill", "fp8", 16, 128, 512, ("rows", 20000, 300)),
     ("rows_f32", "f32", 4, 64, 32, ("rows", 1500, 260)),
+    # MXFP4 keys (fp8 queries): the stream path with candidates, fewer heads
+    # than the tile's 16, and many rows per sequence (scores to memory)
+    ("decode_fp4_mixed_nvis", "fp4", 16, 128, 512, [20000, 4097, 37, 2100]),
+    ("decode_fp4_9_heads_small_k", "fp4", 9, 128, 64, [70001, 9000]),
+    ("rows_fp4_prefill", "fp4", 16, 128, 512, ("rows", 20000, 300)),
 ]
 
 
@@ -140,16 +177,23 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
     e_cap = -(-max_pos // 4)
     rng = np.random.Generator(np.random.PCG64(seed))
     keys = gen.draw(rng, (B, e_cap, Di), dtype)
-    q = gen.draw(rng, (rows, Hi, Di), dtype)
+    q = gen.draw(rng, (rows, Hi, Di), "fp8" if dtype == "fp4" else dtype)
     wt = rng.standard_normal((rows, Hi), dtype=np.float32)
+    kmx = None
     if dtype == "fp8":
         kc, ks = keys
+        qc, qs = q
+    elif dtype == "fp4":  # codes and E8M0 block scale bytes; fp8 queries
+        (kc, kmx), ks = keys, None
         qc, qs = q
     else:
         kc, ks, qc, qs = keys, None, q, None
     if zero_q:
         qc = np.zeros_like(qc)
-    if boost is not None:  # entries j0..j1 get 16x larger key scales (scores 16x)
+    if boost is not None and dtype == "fp4":  # scale bytes + 4: 16x the scores
+        kmx = kmx.copy()
+        kmx[:, boost[0]:boost[1]] += np.uint8(4)
+    elif boost is not None:  # entries j0..j1 get 16x larger key scales (scores 16x)
         ks = ks.copy()
         ks[:, boost[0]:boost[1]] *= boost_scale
     if boost_mod is not None:  # entries j = 0 mod boost_mod get 16x larger key scales
@@ -161,7 +205,8 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
     a = L.IndexArgs()
     qpos = torch.tensor(np.asarray(positions, np.int64), device=DEV)
     from sparse_long_context_c4a_amd.layer import idx_to_device
-    t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt), k=idx_to_device(kc, DEV), ks=_tensor(ks))
+    t = dict(q=_tensor(qc), qs=_tensor(qs), w=_tensor(wt),
+             k=idx_to_device(kc, DEV, fp4=dtype == "fp4"), ks=_tensor(ks), mx=_tensor(kmx))
     idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
     sco = torch.zeros((rows, k), dtype=torch.float32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -169,14 +214,15 @@ def _index_run(dtype, Hi, Di, k, positions, seed, B=None, Tq=1, zero_q=False, bo
     a.stride, a.span, a.heads, a.dim = 4, 8, Hi, Di
     a.q, a.q_scale, a.w, a.keys, a.k_scale = (L.ptr(t["q"]), L.ptr(t["qs"]), L.ptr(t["w"]),
                                               L.ptr(t["k"]), L.ptr(t["ks"]))
-    a.dtype = L.DSA_F32 if dtype == "f32" else L.DSA_FP8_E4M3
+    a.dtype = {"f32": L.DSA_F32, "fp8": L.DSA_FP8_E4M3, "fp4": L.DSA_FP4_E2M1}[dtype]
+    a.k_mx_scale = L.ptr(t["mx"])
     a.e_cap, a.max_pos_end, a.k = e_cap, max_pos, k
     a.idx_out, a.score_out, a.status = L.ptr(idx), L.ptr(sco) if want_scores else None, L.ptr(status)
     L.index_topk(a)
     torch.cuda.synchronize()
     assert status.item() == 0
-    kd = decode_store(kc, dtype, ks)
-    qd = decode_store(qc, dtype, qs)
+    kd = decode_store(kc, dtype, kmx if dtype == "fp4" else ks)
+    qd = decode_store(qc, "fp8" if dtype == "fp4" else dtype, qs)
     return idx.cpu().numpy(), sco.cpu().numpy(), kd, qd, wt.astype(np.float64)
 
 
@@ -203,25 +249,28 @@ def test_index_topk(case):
     assert swaps <= max(1, len(positions) // 50)
 
 
-def test_index_topk_ties_go_to_lower_index():
-    print("[dsa_index_topk] all-zero query: every score ties", flush=True)
+@pytest.mark.parametrize("dtype", ["fp8", "fp4"])
+def test_index_topk_ties_go_to_lower_index(dtype):
+    print(f"[dsa_index_topk] {dtype} keys, all-zero query: every score ties", flush=True)
     # 9000 and 3000 take the per-row path; 200000 the candidate path, whose
     # wave thresholds admit no candidate when every key ties
     positions = [9000, 3000, 200000]
-    idx, sco, *_ = _index_run("fp8", 16, 128, 512, positions, 2100, zero_q=True)
+    idx, sco, *_ = _index_run(dtype, 16, 128, 512, positions, 2100, zero_q=True)
     for i, m in enumerate(positions):
         nv = odsa.n_vis(m, 4, 8)
         assert sorted(idx[i][idx[i] >= 0].tolist()) == list(range(min(512, nv)))
         assert np.all(sco[i][idx[i] >= 0] == 0.0)
 
 
-def test_index_topk_clustered_top_entries():
+@pytest.mark.parametrize("dtype", ["fp8", "fp4"])
+def test_index_topk_clustered_top_entries(dtype):
     """Adversarial layout: most of the row's top-512 sit in one workgroup's
     1024 entries, so the per-workgroup candidate certificate cannot hold and
     the exact full-row selection must take over."""
     positions = [200000, 150001]
-    print("[dsa_index_topk] clustered top entries (certificate fallback)", flush=True)
-    idx, sco, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2300, boost=(1024, 2048))
+    print(f"[dsa_index_topk] {dtype} keys, clustered top entries (certificate fallback)",
+          flush=True)
+    idx, sco, kd, qd, wt = _index_run(dtype, 16, 128, 512, positions, 2300, boost=(1024, 2048))
     for i, m in enumerate(positions):
         nv = odsa.n_vis(m, 4, 8)
         scores = odsa.indexer_scores(qd[i], wt[i], kd[i][:nv])
@@ -229,13 +278,17 @@ def test_index_topk_clustered_top_entries():
         check_topk_row(idx[i], scores, 512, f"clustered row {i}")
 
 
-def test_index_topk_clustered_many_waves():
+@pytest.mark.parametrize("dtype,n_waves", [("fp8", 40), ("fp4", 32)])
+def test_index_topk_clustered_many_waves(dtype, n_waves):
     """The Top-k spread over more waves than the candidate pass re-scores
-    one by one (40 boosted 256-entry waves of about 13 members each): the
-    whole row is scored again and selected exactly."""
+    one by one (40 boosted 256-entry waves of about 13 members each, or 32
+    of about 16 with the coarser fp4 values): the whole row is scored again
+    and selected exactly."""
     positions = [200000]
-    print("[dsa_index_topk] Top-k crowded into 40 waves (full re-score)", flush=True)
-    idx, sco, kd, qd, wt = _index_run("fp8", 16, 128, 512, positions, 2301, boost=(0, 40 * 256))
+    print(f"[dsa_index_topk] {dtype} keys, Top-k crowded into {n_waves} waves (full re-score)",
+          flush=True)
+    idx, sco, kd, qd, wt = _index_run(dtype, 16, 128, 512, positions, 2301,
+                                      boost=(0, n_waves * 256))
     nv = odsa.n_vis(positions[0], 4, 8)
     scores = odsa.indexer_scores(qd[0], wt[0], kd[0][:nv])
     oidx, _ = odsa.topk(scores, 512)

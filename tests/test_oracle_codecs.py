@@ -90,3 +90,63 @@ def test_bf16_single_rounding_from_fp64():
     assert codecs.bf16_decode(codecs.bf16_encode(np.array([v])))[0] == 4.53125
     assert codecs.bf16_decode(codecs.bf16_encode(np.array([4.515625])))[0] == 4.5
     assert np.isinf(codecs.bf16_decode(codecs.bf16_encode(np.array([3.5e38])))[0])
+
+
+# ------------------------------------------------------------ fp4 / MXFP4
+def test_fp4_every_code():
+    """The 16 E2M1 codes (OCP MX FP4: sign, 2 exponent bits with bias 1, one
+    mantissa bit), written out: 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = codecs.fp4_decode(np.arange(16, dtype=np.uint8))
+    assert np.array_equal(got[:8], want)
+    assert np.array_equal(got[8:], [-v for v in want])
+    assert np.signbit(got[8])  # code 8 is -0
+    assert np.array_equal(codecs.fp4_encode(np.array(want + [-v for v in want])),
+                          np.arange(16, dtype=np.uint8))
+
+
+def test_fp4_rounding_ties_and_saturation():
+    x = np.array([0.25, 0.26, 0.74, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.01, 6.0, 7.0, 1e9,
+                  -0.1, -0.25, -0.75, -2.5, -7.0])
+    # midpoints go to the code with mantissa bit 0; beyond 6 saturates
+    want = [0, 1, 1, 2, 2, 4, 4, 6, 6, 7, 7, 7, 7, 8, 8, 10, 12, 15]
+    assert codecs.fp4_encode(x).tolist() == want
+
+
+def test_fp4_nearest_by_brute_force():
+    x = np.random.default_rng(5).uniform(-8, 8, 20000)
+    c = codecs.fp4_encode(x)
+    err = np.abs(codecs.fp4_decode(c) - np.clip(x, -6, 6))
+    grid = np.concatenate([-codecs.FP4_GRID, codecs.FP4_GRID])
+    best = np.min(np.abs(np.clip(x, -6, 6)[:, None] - grid[None, :]), axis=1)
+    assert np.allclose(err, best, atol=0, rtol=0)
+
+
+def test_mxfp4_block_scale_rule():
+    """OCP MX conversion: e = floor(log2(max|block|)) - 2 for E2M1, elements
+    v / 2^e rounded to E2M1 (saturating); an all-zero block gets e = -127."""
+    from oracle import dsa
+    blocks = np.zeros((6, 32))
+    blocks[0, 3] = 6.0             # amax 6: e = 0, exact
+    blocks[1, 0] = 7.0             # amax 7: e = 0, saturates to 6
+    blocks[2, 5] = 8.0             # amax 8: e = 1, 8 = 4 * 2
+    blocks[3, :] = 0.3             # amax 0.3: e = -4, 0.3 * 16 = 4.8 -> 4, value 0.25
+    blocks[4, :4] = [-3.0, 1.5, 0.75, 0.0]  # amax 3: e = -1; -6, 3, 1.5, 0
+    codes, sc = dsa.quantize_mxfp4(blocks.reshape(1, -1)[:, :32 * 6].reshape(6, 32))
+    assert sc[:, 0].tolist() == [127, 127, 128, 123, 126, 0]
+    dec = dsa.mxfp4_decode(codes, sc)
+    assert dec[0, 3] == 6.0 and dec[1, 0] == 6.0 and dec[2, 5] == 8.0
+    assert np.all(dec[3] == 0.25)
+    assert dec[4, :4].tolist() == [-3.0, 1.5, 0.75, 0.0]
+    assert np.all(dec[5] == 0.0) and np.all(codes[5] == 0)
+    # a 128-dim vector holds 4 independent blocks
+    v = np.random.default_rng(3).standard_normal(128) * np.repeat([1e-3, 1.0, 50.0, 3e4], 32)
+    c4, s4 = dsa.quantize_mxfp4(v)
+    assert s4.shape == (4,)
+    d4 = dsa.mxfp4_decode(c4, s4)
+    for i in range(4):
+        blk = v[32 * i:32 * i + 32]
+        x = np.ldexp(1.0, int(s4[i]) - 127)
+        # at most half of the widest step (2 X) below 6 X, and up to 2 X where
+        # the largest element (< 8 X) saturates to 6 X
+        assert np.max(np.abs(d4[32 * i:32 * i + 32] - blk)) <= 2.0 * x

@@ -15,7 +15,10 @@ into binary32, fp8 codes through the e4m3fn codec times their scales), on:
   which exercises the slice reads of rows written by the step;
 * a decode step over a token-wise fp8 main cache (codes times one scale per
   entry);
-* a c128a decode step, which has no indexer.
+* a c128a decode step, which has no indexer;
+* a decode step over an MXFP4 indexer cache (E2M1 codes from a magnitude
+  table written here, times 2^(scale byte - 127) per 32 dims), with fp8
+  indexer queries.
 
 The outputs, selections and final states must be equal element by element:
 both sides run the same float64 arithmetic on the same values, so any
@@ -43,6 +46,14 @@ def _full(bits, dtype, scale=None):
         return np.asarray(bits, np.float32).astype(np.float64)
     if dtype == "bf16":
         return _bf16(bits)
+    if dtype == "fp4":
+        # E2M1 magnitudes by code (OCP MX FP4), bit 3 the sign; one E8M0
+        # scale byte per 32 dims
+        mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        c = np.asarray(bits, np.int64)
+        v = mag[c & 7] * (1.0 - 2.0 * ((c >> 3) & 1))
+        x = 2.0 ** (np.asarray(scale, np.float64) - 127.0)
+        return v * np.repeat(x, 32, axis=-1)
     assert dtype == "fp8"
     return codecs.fp8_decode(bits) * np.asarray(scale, np.float64)[..., None]
 
@@ -65,12 +76,15 @@ def _reference(w, inp):
         msc = None if inp["main_scale"] is None else inp["main_scale"][b]
         main = _full(inp["main_cache"][b], mcd, msc)
         if w.Hi:
-            isc = None if inp["idx_scale"] is None else inp["idx_scale"][b]
+            if w.idx_dtype == "fp4":
+                isc = inp["idx_mx"][b]
+            else:
+                isc = None if inp["idx_scale"] is None else inp["idx_scale"][b]
             idxc = _full(inp["idx_cache"][b], w.idx_dtype, isc)
             iring = _full(inp["idx_ring"][b], rdt)
             kx = _full(inp["kx"][b], rdt)
             qsc = None if inp["qi_scale"] is None else inp["qi_scale"][b]
-            qi = _full(inp["qi"][b], w.idx_dtype, qsc)
+            qi = _full(inp["qi"][b], "fp8" if w.idx_dtype == "fp4" else w.idx_dtype, qsc)
             wt = np.asarray(inp["wt"][b], np.float64)
             lgi = np.asarray(inp["logits_idx"][b], np.float64)
         else:
@@ -118,6 +132,7 @@ CASES = [
      dict(B=2, L=2000, H=8, main_cache_dtype="fp8"), None, None),
     ("c128a_decode_no_indexer", configs.C128A_DECODE_1M, dict(B=2, L=5120, k=64, H=8), None,
      None),
+    ("c4a_decode_fp4_index", configs.C4A_DECODE_1M_FP4, dict(B=2, L=3000, H=8), None, None),
 ]
 
 

@@ -89,6 +89,53 @@ typedef enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2, DSA_FP4_E2
 #define DSA_DEVERR_POSITION 1u  /* a position outside [0, max_pos_end)        */
 #define DSA_DEVERR_CAPACITY 2u  /* an entry slot or n_vis beyond e_cap        */
 #define DSA_DEVERR_NO_INDEX 4u  /* no indexer but n_vis(m) > k                */
+#define DSA_DEVERR_BLOCK 8u     /* a block table entry outside its pool       */
+
+/* ------------------------------------------------------------ paging ----
+ * Paged caches ([P2] 第三层 设计 1 and 设计 2; [P1] 6.1 and 6.2).  A logical
+ * block is DSA_BLOCK_TOKENS = 256 raw token positions of a sequence, whatever
+ * the layer's compression, so every cache is addressed through the same
+ * logical block numbers; each cache type decides how many of its own rows a
+ * physical block holds.  A zeroed dsa_paging (every pointer NULL) keeps the
+ * dense per-sequence layouts described with each field.
+ *
+ *  - block_table [B, blocks_per_seq]: the compressed caches (main_cache /
+ *    cache, main_scale / cache_scale, idx_cache / keys, idx_scale / k_scale,
+ *    idx_mx_scale / k_mx_scale / out_mx_scale) become pools of physical
+ *    blocks of entries_per_block = 256 / stride entries (c4a 64, c128a 2).
+ *    Entry j of sequence b is row  block_table[b, j / E] * E + j % E  (E =
+ *    entries_per_block) of the pool, the pool laid out as the dense cache
+ *    with (sequence, entry) replaced by that row: main [n_blocks * E, D],
+ *    scales [n_blocks * E] and [n_blocks * E, Di / 32]; FP8 / FP4 keys of dim
+ *    128 keep their 16-entry tiles (E a multiple of 16; rows n_blocks * E).
+ *    e_cap stays the entries a sequence may hold (<= blocks_per_seq * E).
+ *  - swa_block_table [B, blocks_per_seq]: the window.  Raw token n of
+ *    sequence b is stored (rotated) in slot n % 256 of block
+ *    swa_block_table[b, n / 256] of a pool [n_swa_blocks, 256, D]; w_cap is
+ *    then not used, and blocks wholly before the window may be released
+ *    (their entries are not read).
+ *  - state_block [B]: the compressor states (rings of the last S raw tokens,
+ *    [P2] 设计 2 treats them as sliding-window state): sequence b's rings are
+ *    block state_block[b] of pools [n_state_blocks, S, D] and
+ *    [n_state_blocks, S, Di].
+ *
+ * A block id outside [0, pool size) sets DSA_DEVERR_BLOCK in the status word;
+ * reads through it then take block 0 and writes are dropped, so memory
+ * accesses stay inside the pools.  Only entries a call reads or writes need
+ * a valid block.
+ */
+#define DSA_BLOCK_TOKENS 256
+
+typedef struct dsa_paging {
+  const int32_t* block_table;      /* device [B, blocks_per_seq] or NULL      */
+  const int32_t* swa_block_table;  /* device [B, blocks_per_seq] or NULL      */
+  const int32_t* state_block;      /* device [B] or NULL                      */
+  int32_t blocks_per_seq;          /* row stride of the two tables            */
+  int32_t entries_per_block;       /* 256 / stride, a power of two            */
+  int32_t n_blocks;                /* physical blocks of the entry pools      */
+  int32_t n_swa_blocks;            /* physical blocks of the window pool      */
+  int32_t n_state_blocks;          /* physical blocks of the ring pools       */
+} dsa_paging;
 
 /* Compressor / attention geometry. */
 typedef struct dsa_geom {
@@ -140,6 +187,7 @@ typedef struct dsa_compress_args {
   uint32_t* status;           /* optional device status word                 */
   uint8_t* out_mx_scale;      /* [B, e_cap, D / 32] E8M0 block scales for FP4
                                  output (D a multiple of 32), else ignored   */
+  dsa_paging paging;          /* zeroed: dense caches (see paging above)  */
 } dsa_compress_args;
 
 dsa_status dsa_compress(const dsa_compress_args* a, void* stream);
@@ -178,6 +226,7 @@ typedef struct dsa_index_args {
   float* score_out;           /* [B * Tq, k] or NULL (NaN for padding)       */
   uint32_t* status;
   const uint8_t* k_mx_scale;  /* [B, e_cap, Di / 32] E8M0 scales (FP4 keys)  */
+  dsa_paging paging;          /* zeroed: dense caches (see paging above)  */
 } dsa_index_args;
 
 size_t dsa_index_topk_workspace(const dsa_index_args* a);
@@ -241,6 +290,7 @@ typedef struct dsa_attn_args {
   float* out_scale;           /* [B * Tq, H] (out_fp8)                       */
   int32_t cache_fp8;          /* 0: cache is dtype; 1: fp8 codes + scales    */
   const float* cache_scale;   /* [B, e_cap] (cache_fp8)                      */
+  dsa_paging paging;          /* zeroed: dense caches (see paging above)  */
 } dsa_attn_args;
 
 size_t dsa_sparse_attn_workspace(const dsa_attn_args* a);
@@ -316,6 +366,7 @@ typedef struct dsa_layer_args {
   float* main_scale;          /* [B, e_cap] (main_fp8); decode only, see S5  */
   const float* q_norm_gamma;  /* [D] or NULL: Q-norm of each query head      */
   uint8_t* idx_mx_scale;      /* [B, e_cap, Di / 32] (idx_dtype FP4)         */
+  dsa_paging paging;          /* zeroed: dense caches (see paging above)  */
 } dsa_layer_args;
 
 size_t dsa_layer_workspace(const dsa_layer_args* a);

@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("DSA_LIB_PATH") or os.path.join(_HERE, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_FP4_E2M1 = 0, 1, 2, 3
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED",
           -3: "DSA_ERR_WORKSPACE", -4: "DSA_ERR_HIP"}
-DEVERR_POSITION, DEVERR_CAPACITY, DEVERR_NO_INDEX = 1, 2, 4
+DEVERR_POSITION, DEVERR_CAPACITY, DEVERR_NO_INDEX, DEVERR_BLOCK = 1, 2, 4, 8
+BLOCK_TOKENS = 256  # raw positions per logical block of the paged caches
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -40,12 +41,19 @@ class Geom(ctypes.Structure):
                 ("rope_base", c_f64), ("rope_pos_offset", c_i64)]
 
 
+class Paging(ctypes.Structure):
+    _fields_ = [("block_table", c_vp), ("swa_block_table", c_vp), ("state_block", c_vp),
+                ("blocks_per_seq", c_i32), ("entries_per_block", c_i32), ("n_blocks", c_i32),
+                ("n_swa_blocks", c_i32), ("n_state_blocks", c_i32)]
+
+
 class CompressArgs(ctypes.Structure):
     _fields_ = [("geom", Geom), ("batch", c_i32), ("raw", c_vp), ("raw_dtype", c_i32),
                 ("raw_len", c_i64), ("ring", c_vp), ("raw_pos0", c_vp), ("logits", c_vp),
                 ("logits_rows", c_i32), ("rms_gamma", c_vp), ("rms_eps", c_f32), ("out", c_vp),
                 ("out_dtype", c_i32), ("out_scale", c_vp), ("e_cap", c_i64),
-                ("max_pos_end", c_i64), ("status", c_vp), ("out_mx_scale", c_vp)]
+                ("max_pos_end", c_i64), ("status", c_vp), ("out_mx_scale", c_vp),
+                ("paging", Paging)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -54,7 +62,7 @@ class IndexArgs(ctypes.Structure):
                 ("q", c_vp), ("q_scale", c_vp), ("w", c_vp), ("keys", c_vp), ("k_scale", c_vp),
                 ("dtype", c_i32), ("e_cap", c_i64), ("max_pos_end", c_i64), ("k", c_i32),
                 ("idx_out", c_vp), ("score_out", c_vp), ("status", c_vp),
-                ("k_mx_scale", c_vp)]
+                ("k_mx_scale", c_vp), ("paging", Paging)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -66,7 +74,7 @@ class AttnArgs(ctypes.Structure):
                 ("chunk_win", c_vp), ("chunk_pos0", c_vp), ("chunk_len", c_i64),
                 ("softmax_scale", c_f32), ("max_pos_end", c_i64), ("out", c_vp),
                 ("lse", c_vp), ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp),
-                ("cache_fp8", c_i32), ("cache_scale", c_vp)]
+                ("cache_fp8", c_i32), ("cache_scale", c_vp), ("paging", Paging)]
 
 
 class LayerArgs(ctypes.Structure):
@@ -81,7 +89,8 @@ class LayerArgs(ctypes.Structure):
                 ("window", c_vp), ("w_cap", c_i32), ("rms_gamma", c_vp), ("rms_gamma_idx", c_vp),
                 ("rms_eps", c_f32), ("out", c_vp), ("lse", c_vp), ("idx_out", c_vp),
                 ("status", c_vp), ("out_fp8", c_i32), ("out_scale", c_vp), ("main_fp8", c_i32),
-                ("main_scale", c_vp), ("q_norm_gamma", c_vp), ("idx_mx_scale", c_vp)]
+                ("main_scale", c_vp), ("q_norm_gamma", c_vp), ("idx_mx_scale", c_vp),
+                ("paging", Paging)]
 
 
 EXPORTS = {
@@ -106,7 +115,7 @@ for _name, (_res, _args) in EXPORTS.items():
     _f = getattr(_lib, _name)
     _f.restype, _f.argtypes = _res, _args
 
-STRUCTS = {"dsa_timing_events": TimingEvents, "dsa_geom": Geom, "dsa_compress_args": CompressArgs, "dsa_index_args": IndexArgs,
+STRUCTS = {"dsa_timing_events": TimingEvents, "dsa_geom": Geom, "dsa_paging": Paging, "dsa_compress_args": CompressArgs, "dsa_index_args": IndexArgs,
            "dsa_attn_args": AttnArgs, "dsa_layer_args": LayerArgs}
 for _n, _s in STRUCTS.items():
     if _lib.dsa_abi_sizeof(_n.encode()) != ctypes.sizeof(_s):

@@ -69,6 +69,36 @@ dsa_status check_geom(const dsa_geom& g, const char* who) {
 
 bool is_dtype(int t) { return t == DSA_F32 || t == DSA_BF16 || t == DSA_FP8_E4M3; }
 
+// The paging of a call: stride > 0 ties entries_per_block to the logical
+// block (256 / stride); tiled: the compressed caches include 16-entry key
+// tiles; max_pos_end bounds the positions the window table must cover.
+dsa_status check_paging(const dsa_paging& p, int stride, int64_t e_cap, int64_t max_pos_end,
+                        bool tiled, const char* who) {
+  const bool any = p.block_table || p.swa_block_table;
+  if (any) REQUIRE(p.blocks_per_seq >= 1, "%s: paging needs blocks_per_seq >= 1", who);
+  if (p.block_table) {
+    const int e = p.entries_per_block;
+    REQUIRE(e >= 1 && (e & (e - 1)) == 0, "%s: entries_per_block %d must be a power of two", who, e);
+    REQUIRE(stride <= 0 || static_cast<int64_t>(e) * stride == DSA_BLOCK_TOKENS,
+            "%s: entries_per_block %d * stride %d must be %d raw positions", who, e, stride,
+            DSA_BLOCK_TOKENS);
+    REQUIRE(p.n_blocks >= 1, "%s: n_blocks < 1", who);
+    REQUIRE(e_cap <= static_cast<int64_t>(p.blocks_per_seq) * e,
+            "%s: e_cap %lld > blocks_per_seq * entries_per_block = %lld", who, (long long)e_cap,
+            (long long)p.blocks_per_seq * e);
+    SUPPORT(!tiled || e % 16 == 0, "%s: paged key tiles need entries_per_block a multiple of 16 "
+            "(got %d)", who, e);
+  }
+  if (p.swa_block_table) {
+    REQUIRE(p.n_swa_blocks >= 1, "%s: n_swa_blocks < 1", who);
+    REQUIRE(static_cast<int64_t>(p.blocks_per_seq) * DSA_BLOCK_TOKENS >= max_pos_end,
+            "%s: the window table covers %lld positions < max_pos_end %lld", who,
+            (long long)p.blocks_per_seq * DSA_BLOCK_TOKENS, (long long)max_pos_end);
+  }
+  if (p.state_block) REQUIRE(p.n_state_blocks >= 1, "%s: n_state_blocks < 1", who);
+  return DSA_OK;
+}
+
 dsa_status validate_compress(const dsa_compress_args* a) {
   REQUIRE(a, "dsa_compress: null args");
   dsa_status rc = check_geom(a->geom, "dsa_compress");
@@ -92,7 +122,9 @@ dsa_status validate_compress(const dsa_compress_args* a) {
   REQUIRE(a->e_cap >= 1, "dsa_compress: e_cap < 1");
   REQUIRE(a->max_pos_end >= a->raw_len, "dsa_compress: max_pos_end < raw_len");
   REQUIRE(a->rms_gamma == nullptr || a->rms_eps >= 0.f, "dsa_compress: rms_eps < 0");
-  return DSA_OK;
+  const bool tiled = (a->out_dtype == DSA_FP8_E4M3 || a->out_dtype == DSA_FP4_E2M1) &&
+                     a->geom.dim == 128;
+  return check_paging(a->paging, a->geom.stride, a->e_cap, a->max_pos_end, tiled, "dsa_compress");
 }
 
 dsa_status validate_index(const dsa_index_args* a) {
@@ -121,7 +153,8 @@ dsa_status validate_index(const dsa_index_args* a) {
             a->dim, a->heads);
   }
   SUPPORT(a->heads * a->dim <= 16384, "dsa_index_topk: heads * dim %d too large", a->heads * a->dim);
-  return DSA_OK;
+  const bool tiled = (a->dtype == DSA_FP8_E4M3 || a->dtype == DSA_FP4_E2M1) && a->dim == 128;
+  return check_paging(a->paging, a->stride, a->e_cap, a->max_pos_end, tiled, "dsa_index_topk");
 }
 
 dsa_status validate_attn(const dsa_attn_args* a) {
@@ -137,8 +170,9 @@ dsa_status validate_attn(const dsa_attn_args* a) {
   REQUIRE(a->k >= 0 && a->window_size >= 0, "dsa_sparse_attn: k and window_size must be >= 0");
   REQUIRE(a->k == 0 || (a->idx && a->cache && a->e_cap >= 1),
           "dsa_sparse_attn: k > 0 needs idx, cache and e_cap >= 1");
-  REQUIRE(a->window_size == 0 || (a->window && a->w_cap >= a->window_size),
-          "dsa_sparse_attn: the window needs a ring with w_cap >= window_size");
+  REQUIRE(a->window_size == 0 ||
+              (a->window && (a->paging.swa_block_table || a->w_cap >= a->window_size)),
+          "dsa_sparse_attn: the window needs a ring with w_cap >= window_size (or a window table)");
   REQUIRE(a->chunk_win == nullptr || (a->chunk_pos0 && a->chunk_len >= 1),
           "dsa_sparse_attn: chunk_win needs chunk_pos0 and chunk_len >= 1");
   REQUIRE(a->k + a->window_size >= 1, "dsa_sparse_attn: empty attention set");
@@ -149,7 +183,7 @@ dsa_status validate_attn(const dsa_attn_args* a) {
   REQUIRE(!a->cache_fp8 || a->k == 0 || a->cache_scale, "dsa_sparse_attn: cache_fp8 needs cache_scale");
   SUPPORT(!a->cache_fp8 || (a->dtype == DSA_BF16 && a->dim == 512),
           "dsa_sparse_attn: an fp8 cache needs dtype BF16 and dim 512");
-  return DSA_OK;
+  return check_paging(a->paging, 0, a->e_cap, a->max_pos_end, false, "dsa_sparse_attn");
 }
 
 dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
@@ -167,7 +201,8 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
   REQUIRE(a->e_cap >= ceil_div(a->max_pos_end, a->main.stride),
           "dsa_layer: e_cap %lld < ceil(max_pos_end / stride) = %lld", (long long)a->e_cap,
           (long long)ceil_div(a->max_pos_end, a->main.stride));
-  REQUIRE(a->w_cap >= a->window_size && a->w_cap >= 1, "dsa_layer: w_cap < window_size");
+  REQUIRE(a->paging.swa_block_table || (a->w_cap >= a->window_size && a->w_cap >= 1),
+          "dsa_layer: w_cap < window_size");
   REQUIRE(a->max_pos_end >= a->chunk_len, "dsa_layer: max_pos_end < chunk_len");
   REQUIRE(a->out_fp8 == 0 || a->out_fp8 == 1, "dsa_layer: out_fp8 must be 0 or 1");
   REQUIRE(!a->out_fp8 || a->out_scale, "dsa_layer: out_fp8 needs out_scale");
@@ -200,7 +235,9 @@ dsa_status validate_layer(const dsa_layer_args* a, bool decode) {
     REQUIRE(nv_max <= a->k, "dsa_layer: without an indexer k (%d) must cover every visible entry "
             "(up to %lld)", a->k, (long long)nv_max);
   }
-  return DSA_OK;
+  const bool tiled = a->idx_heads > 0 && a->idx_dim == 128 &&
+                     (a->idx_dtype == DSA_FP8_E4M3 || a->idx_dtype == DSA_FP4_E2M1);
+  return check_paging(a->paging, a->main.stride, a->e_cap, a->max_pos_end, tiled, "dsa_layer");
 }
 
 // Workspace plan of a layer step: index/top-k scratch, attention scratch,
@@ -234,6 +271,7 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   ia.k = a->k;
   ia.score_out = nullptr;
   ia.status = a->status;
+  ia.paging = a->paging;
   size_t off = 0;
   L.off_idx_ws = off;
   off = align_up(off + index_topk_ws_bytes(ia));
@@ -280,6 +318,7 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   aa.cache_fp8 = a->main_fp8;
   aa.cache_scale = a->main_scale;
   aa.status = a->status;
+  aa.paging = a->paging;
   L.off_attn_ws = off;
   off = align_up(off + attn_ws_bytes(aa));
   // per-row positions
@@ -321,7 +360,9 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   if (T == 1) {
     // one token per sequence: fused prologue, indexer + Top-k, attention over
     // the selected entries and the window ring, window insert
-    const bool early = a->w_cap > a->window_size;  // slot m mod w_cap is outside m's window
+    // slot m mod w_cap (a ring with a spare slot) or m's slot of its window
+    // block (paged) is outside m's window
+    const bool early = a->w_cap > a->window_size || a->paging.swa_block_table != nullptr;
     int64_t* qpos = const_cast<int64_t*>(L.ia.q_pos);
     L.ia.q_pos = a->pos0;  // one query per sequence, at pos0
     L.aa.q_pos = a->pos0;
@@ -363,6 +404,7 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   c.e_cap = a->e_cap;
   c.max_pos_end = a->max_pos_end;
   c.status = a->status;
+  c.paging = a->paging;
   rc = launch_compress(c, st);
   if (rc != DSA_OK) return rc;
   const dsa_dtype raw_idx_dt = a->idx_dtype == DSA_F32 ? DSA_F32 : DSA_BF16;
@@ -385,11 +427,11 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   }
   // rings take the chunk's raw tokens
   rc = launch_ring_update(a->x, a->dtype, a->main.dim, T, a->main_ring, a->main.span, a->pos0, B,
-                          a->max_pos_end, st);
+                          a->max_pos_end, a->paging, a->status, st);
   if (rc != DSA_OK) return rc;
   if (a->idx_heads > 0) {
     rc = launch_ring_update(a->kx, raw_idx_dt, a->idx_dim, T, a->idx_ring, a->main.span, a->pos0,
-                            B, a->max_pos_end, st);
+                            B, a->max_pos_end, a->paging, a->status, st);
     if (rc != DSA_OK) return rc;
   }
   // S3 + S4
@@ -412,7 +454,8 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   if (rc != DSA_OK) return rc;
   // window ring update after attention
   return launch_window_update(base + L.off_rot, a->dtype, a->main.dim, T, a->window, a->w_cap,
-                              a->pos0, B, a->max_pos_end, st);
+                              a->window_size, a->pos0, B, a->max_pos_end, a->paging, a->status,
+                              st);
 }
 
 // ------------------------------------------------ allocation-free decode
@@ -552,6 +595,7 @@ size_t dsa_abi_sizeof(const char* name) {
   if (!name) return 0;
   if (!std::strcmp(name, "dsa_geom")) return sizeof(dsa_geom);
   if (!std::strcmp(name, "dsa_timing_events")) return sizeof(dsa_timing_events);
+  if (!std::strcmp(name, "dsa_paging")) return sizeof(dsa_paging);
   if (!std::strcmp(name, "dsa_compress_args")) return sizeof(dsa_compress_args);
   if (!std::strcmp(name, "dsa_index_args")) return sizeof(dsa_index_args);
   if (!std::strcmp(name, "dsa_attn_args")) return sizeof(dsa_attn_args);

@@ -47,7 +47,16 @@ struct AttnGeom {
   bool direct;
   float* out_scale;  // fp8 output: one scale per (row, head), else nullptr
   const float* cache_scale;  // fp8 cache: one scale per entry [B, e_cap], else nullptr
+  PageMap ent, swa;          // paged cache entries and window tokens (tables nullptr: dense)
 };
+
+// Row of cache entry j (0 <= j < e_cap) of sequence b, and of window token n.
+__device__ __forceinline__ int64_t cache_row(const AttnGeom& g, int b, int64_t j) {
+  return entry_row(g.ent, b, j, g.e_cap, g.status);
+}
+__device__ __forceinline__ int64_t win_row(const AttnGeom& g, int b, int64_t n) {
+  return window_row(g.swa, b, n, g.w_cap, g.status);
+}
 
 // Source of slot a of row `row`; nullptr if the slot is empty.
 template <typename T>
@@ -57,7 +66,7 @@ __device__ __forceinline__ const T* slot_ptr(const AttnGeom& g, int row, int b, 
   if (a < g.k) {
     const int32_t j = g.idx[static_cast<int64_t>(row) * g.k + a];
     if (j < 0 || j >= g.e_cap) return nullptr;
-    return cache + (static_cast<int64_t>(b) * g.e_cap + j) * g.D;
+    return cache + cache_row(g, b, j) * g.D;
   }
   const int64_t n = m - g.W + (a - g.k);
   if (n < 0 || n >= m) return nullptr;
@@ -66,7 +75,7 @@ __device__ __forceinline__ const T* slot_ptr(const AttnGeom& g, int row, int b, 
     if (n >= c0 && n - c0 < g.chunk_len)
       return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (n - c0)) * g.D;
   }
-  return window + (static_cast<int64_t>(b) * g.w_cap + (n % g.w_cap)) * g.D;
+  return window + win_row(g, b, n) * g.D;
 }
 
 // Largest value of x over the workgroup's NT threads (every thread calls it
@@ -439,13 +448,13 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
     if (a < g.k) {
       const int32_t j = idx_s[a - a_begin];
       if (j < 0 || j >= g.e_cap) return nullptr;
-      return cache + (static_cast<int64_t>(b) * g.e_cap + j) * kMD;
+      return cache + cache_row(g, b, j) * kMD;
     }
     const int64_t nn = m - g.W + (a - g.k);
     if (nn < 0 || nn >= m) return nullptr;
     if (chunk_win && nn >= c0 && nn - c0 < g.chunk_len)
       return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (nn - c0)) * kMD;
-    return window + (static_cast<int64_t>(b) * g.w_cap + (nn % g.w_cap)) * kMD;
+    return window + win_row(g, b, nn) * kMD;
   };
   v4f o[16];
 #pragma unroll
@@ -622,8 +631,8 @@ __device__ __forceinline__ const uint16_t* dslot_ptr(const AttnGeom& g, int b, i
     if (j < 0 || j >= g.e_cap) return nullptr;
     if constexpr (kFp8)  // one byte per dim
       return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(cache) +
-                                               (static_cast<int64_t>(b) * g.e_cap + j) * kMD);
-    return cache + (static_cast<int64_t>(b) * g.e_cap + j) * kMD;
+                                               cache_row(g, b, j) * kMD);
+    return cache + cache_row(g, b, j) * kMD;
   }
   const int64_t n = m - g.W + (a - g.k);
   if (n < 0 || n >= m) return nullptr;
@@ -632,7 +641,7 @@ __device__ __forceinline__ const uint16_t* dslot_ptr(const AttnGeom& g, int b, i
     if (n >= c0 && n - c0 < g.chunk_len)
       return chunk_win + (static_cast<int64_t>(b) * g.chunk_len + (n - c0)) * kMD;
   }
-  return window + (static_cast<int64_t>(b) * g.w_cap + (n % g.w_cap)) * kMD;
+  return window + win_row(g, b, n) * kMD;
 }
 
 // Cache index of slot a for lane-parallel prefetch (only slots a < k have one).
@@ -845,7 +854,7 @@ __device__ __forceinline__ void decode_attn_run(
   // an fp8 cache slot's scale (1 for window slots and without kFp8)
   auto slot_scale = [&](int a, const uint16_t* sp, int32_t j) -> float {
     if constexpr (kFp8)
-      if (sp != nullptr && src.is_cache(a)) return g.cache_scale[static_cast<int64_t>(b) * g.e_cap + j];
+      if (sp != nullptr && src.is_cache(a)) return g.cache_scale[cache_row(g, b, j)];
     return 1.f;
   };
   if (a0 < a_end) {
@@ -1313,6 +1322,9 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.direct = !p.part;
   g.out_scale = a.out_fp8 ? a.out_scale : nullptr;
   g.cache_scale = a.cache_fp8 ? a.cache_scale : nullptr;
+  const Paging pg = make_paging(a.paging);
+  g.ent = pg.ent;
+  g.swa = pg.swa;
   char* base = static_cast<char*>(ws);
   float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
   float* part_ml = reinterpret_cast<float*>(base + p.off_ml);

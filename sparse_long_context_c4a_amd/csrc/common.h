@@ -117,6 +117,11 @@ __host__ __device__ __forceinline__ int64_t idx_e_pad(int64_t e_cap) { return (e
 __host__ __device__ __forceinline__ int64_t idx_tile_off(int64_t b, int64_t e_pad, int64_t j, int d) {
   return (b * e_pad + (j & ~int64_t{15})) * 128 + (d >> 4) * 256 + (j & 15) * 16 + (d & 15);
 }
+// The same by tile row R (dense: b * e_pad + j; paged: the entry's pool row,
+// blocks being whole tiles).
+__host__ __device__ __forceinline__ int64_t idx_tile_off_row(int64_t R, int d) {
+  return (R & ~int64_t{15}) * 128 + (d >> 4) * 256 + (R & 15) * 16 + (d & 15);
+}
 // The two 16-byte operand chunks of lane (g, n) for entry j (n = j mod 16
 // in the operand layout): chunks g and 4 + g.
 __device__ __forceinline__ void idx_load_chunks(const uint8_t* seq_keys, int64_t j, int g, uint4* lo,
@@ -134,6 +139,9 @@ __device__ __forceinline__ void idx_load_chunks(const uint8_t* seq_keys, int64_t
 // Byte of dim d (its nibble: d % 2) of entry j of sequence b:
 __host__ __device__ __forceinline__ int64_t idx4_tile_off(int64_t b, int64_t e_pad, int64_t j, int d) {
   return (b * e_pad + (j & ~int64_t{15})) * 64 + (d >> 5) * 256 + (j & 15) * 16 + ((d & 31) >> 1);
+}
+__host__ __device__ __forceinline__ int64_t idx4_tile_off_row(int64_t R, int d) {
+  return (R & ~int64_t{15}) * 64 + (d >> 5) * 256 + (R & 15) * 16 + ((d & 31) >> 1);
 }
 __device__ __forceinline__ uint4 idx4_load_chunk(const uint8_t* seq_keys, int64_t j, int g) {
   const uint4* t = reinterpret_cast<const uint4*>(seq_keys + (j & ~int64_t{15}) * 64);
@@ -158,6 +166,76 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 
 __device__ __forceinline__ void set_status(uint32_t* st, uint32_t bits) {
   if (st) atomicOr(st, bits);
+}
+
+// ------------------------------------------------------ paged caches
+// A logical block is 256 raw token positions; a cache type holds 2^shift of
+// its rows per physical block (compressed entries: 256 / stride; window:
+// 256 tokens).  With a table, row j of sequence b is
+//   table[b, j >> shift] << shift | (j mod 2^shift);
+// a block id outside [0, n_blocks) sets DSA_DEVERR_BLOCK and maps to block 0
+// (ok = false: the caller drops a write).
+struct PageMap {
+  const int32_t* table;  // [B, stride] or nullptr (dense)
+  int64_t stride;
+  int shift;
+  int32_t n_blocks;
+};
+
+__device__ __forceinline__ int64_t paged_row(const PageMap& p, int b, int64_t j, uint32_t* status,
+                                             bool* ok = nullptr) {
+  int32_t blk = p.table[b * p.stride + (j >> p.shift)];
+  if (static_cast<uint32_t>(blk) >= static_cast<uint32_t>(p.n_blocks)) {
+    set_status(status, DSA_DEVERR_BLOCK);
+    blk = 0;
+    if (ok) *ok = false;
+  }
+  return (static_cast<int64_t>(blk) << p.shift) | (j & ((int64_t{1} << p.shift) - 1));
+}
+
+// Row of entry j of sequence b: dense b * dense_rows + j, or its pool row.
+__device__ __forceinline__ int64_t entry_row(const PageMap& p, int b, int64_t j, int64_t dense_rows,
+                                             uint32_t* status, bool* ok = nullptr) {
+  return p.table ? paged_row(p, b, j, status, ok) : b * dense_rows + j;
+}
+
+// The paging of a call: compressed caches, window, compressor rings.
+struct Paging {
+  PageMap ent;
+  PageMap swa;
+  const int32_t* state;  // [B] ring block of each sequence or nullptr
+  int32_t n_state;
+};
+
+inline Paging make_paging(const dsa_paging& p) {
+  Paging g{};
+  int sh = 0;
+  while (sh < 30 && (1 << sh) < p.entries_per_block) ++sh;
+  g.ent = PageMap{p.block_table, p.blocks_per_seq, sh, p.n_blocks};
+  g.swa = PageMap{p.swa_block_table, p.blocks_per_seq, 8, p.n_swa_blocks};  // 256 tokens
+  g.state = p.state_block;
+  g.n_state = p.n_state_blocks;
+  return g;
+}
+
+// Row of window token n of sequence b: slot n mod w_cap of the sequence's
+// ring, or slot n mod 256 of its window block.
+__device__ __forceinline__ int64_t window_row(const PageMap& w, int b, int64_t n, int w_cap,
+                                              uint32_t* status, bool* ok = nullptr) {
+  return w.table ? paged_row(w, b, n, status, ok) : static_cast<int64_t>(b) * w_cap + n % w_cap;
+}
+
+// The compressor rings' block of sequence b (b itself when dense).
+__device__ __forceinline__ int64_t state_seq(const Paging& pg, int b, uint32_t* status,
+                                             bool* ok = nullptr) {
+  if (!pg.state) return b;
+  const int32_t s = pg.state[b];
+  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(pg.n_state)) {
+    set_status(status, DSA_DEVERR_BLOCK);
+    if (ok) *ok = false;
+    return 0;
+  }
+  return s;
 }
 
 // ------------------------------------------------------ reductions

@@ -13,10 +13,10 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(
     const float* __restrict__ logits, void* __restrict__ out, float* __restrict__ out_scale,
     uint8_t* __restrict__ out_mx, const float* __restrict__ gamma, float eps, int64_t T,
     int logits_rows, int s, int S, int D, int r, double base, int64_t off, int64_t e_cap,
-    int64_t max_pos_end, uint32_t* status) {
+    int64_t max_pos_end, uint32_t* status, Paging pg) {
   compress_one<RawT, kOut>(blockIdx.x, blockIdx.y, raw, ring, pos0v, logits, out, out_scale, gamma,
                            eps, T, logits_rows, s, S, D, r, base, off, e_cap, max_pos_end, status,
-                           0, -1, out_mx);
+                           0, -1, out_mx, pg);
 }
 
 template <typename RawT>
@@ -25,12 +25,13 @@ dsa_status launch_typed(const dsa_compress_args& a, hipStream_t st) {
   const RawT* raw = static_cast<const RawT*>(a.raw);
   const RawT* ring = static_cast<const RawT*>(a.ring);
   const dsa_geom& g = a.geom;
+  const Paging pg = make_paging(a.paging);
 #define DSA_COMPRESS_LAUNCH(OUT)                                                                  \
   hipLaunchKernelGGL((k_compress<RawT, OUT>), grid, dim3(kCompressThreads), 0, st, raw, ring, a.raw_pos0, \
                      a.logits, a.out, a.out_scale, a.out_mx_scale, a.rms_gamma, a.rms_eps,       \
                      a.raw_len,                                                                  \
                      a.logits_rows, g.stride, g.span, g.dim, g.rope_dim, g.rope_base,            \
-                     g.rope_pos_offset, a.e_cap, a.max_pos_end, a.status)
+                     g.rope_pos_offset, a.e_cap, a.max_pos_end, a.status, pg)
   switch (a.out_dtype) {
     case DSA_F32: DSA_COMPRESS_LAUNCH(DSA_F32); break;
     case DSA_BF16: DSA_COMPRESS_LAUNCH(DSA_BF16); break;

@@ -59,7 +59,8 @@ __device__ __forceinline__ void compress_one(
     const int64_t* __restrict__ pos0v, const float* __restrict__ logits, void* __restrict__ out,
     float* __restrict__ out_scale, const float* __restrict__ gamma, float eps, int64_t T,
     int logits_rows, int s, int S, int D, int r, double base, int64_t off, int64_t e_cap,
-    int64_t max_pos_end, uint32_t* status, int d0 = 0, int dn = -1, uint8_t* out_mx = nullptr) {
+    int64_t max_pos_end, uint32_t* status, int d0 = 0, int dn = -1, uint8_t* out_mx = nullptr,
+    Paging pg = Paging{}) {
   // dims d0 .. d0 + dn - 1 only (dn = -1: all D); a slice is a multiple of 8
   // dims and needs neither gamma nor fp8 output, which take the whole vector
   if (dn < 0) dn = D;
@@ -79,6 +80,13 @@ __device__ __forceinline__ void compress_one(
     if (tid == 0) set_status(status, DSA_DEVERR_CAPACITY);
     return;
   }
+  // the entry's row: b * e_cap + j, or its row in the paged pool (a block
+  // outside the pool drops the entry; uniform across the block)
+  bool ok = true;
+  const int64_t erow = entry_row(pg.ent, b, j, e_cap, tid == 0 ? status : nullptr, &ok);
+  if (!ok) return;
+  // tile row of the key layouts: b * e_pad + j dense, the pool row paged
+  const int64_t trow = pg.ent.table ? erow : static_cast<int64_t>(b) * idx_e_pad(e_cap) + j;
 
   // softmax weights of this entry
   const float* lg = logits + (static_cast<int64_t>(b) * logits_rows + e) * S;
@@ -100,7 +108,7 @@ __device__ __forceinline__ void compress_one(
 #pragma unroll
   for (int k = 0; k < kCompressPairs; ++k) acc[k][0] = acc[k][1] = 0.f;
   const RawT* rawb = raw + static_cast<int64_t>(b) * T * D;
-  const RawT* ringb = ring + static_cast<int64_t>(b) * S * D;
+  const RawT* ringb = ring + state_seq(pg, b, tid == 0 ? status : nullptr) * S * D;
   if (dn % 8 == 0 && d0 % 8 == 0 && dn / 8 <= kCompressThreads) {
     // 16-byte loads: thread (group gr, column c) sums dims 8c .. 8c+7 over
     // the tokens i = gr (mod ngrp) -- a token row is D/8 threads wide, and
@@ -199,7 +207,7 @@ __device__ __forceinline__ void compress_one(
     }
   }
 
-  const int64_t o = (static_cast<int64_t>(b) * e_cap + j) * D;
+  const int64_t o = erow * D;
   if constexpr (kOut == DSA_F32 || kOut == DSA_BF16) {
     using OT = typename std::conditional<kOut == DSA_F32, float, uint16_t>::type;
     OT* op = static_cast<OT*>(out) + o;
@@ -217,28 +225,27 @@ __device__ __forceinline__ void compress_one(
     // c / 2^e (OCP MX conversion); dim 128 in the fp4 tile layout
     const bool tiled = D == 128;
     uint8_t* op = static_cast<uint8_t*>(out);
-    const int64_t e_pad = idx_e_pad(e_cap);
-    const int64_t ro = static_cast<int64_t>(b) * e_cap + j;
+    const int64_t ro = erow;
 #pragma unroll
     for (int k = 0; k < kCompressPairs; ++k) {
       const int pr = tid + k * kCompressThreads;
       const bool in = pr < npairs;
       float am = in ? fmaxf(fabsf(acc[k][0]), fabsf(acc[k][1])) : 0.f;
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
-      int e = -127;
+      for (int sh = 8; sh > 0; sh >>= 1) am = fmaxf(am, __shfl_xor(am, sh, 16));
+      int se = -127;  // the block's scale exponent
       if (am > 0.f) {
         int ex;
         frexpf(am, &ex);  // am = f 2^ex, f in [0.5, 1)
-        e = min(127, max(-127, ex - 3));
+        se = min(127, max(-127, ex - 3));
       }
-      const float inv = ldexpf(1.0f, -e);  // exact: a power of two
+      const float rsc = ldexpf(1.0f, -se);  // exact: a power of two
       if (in) {
-        const uint32_t c0 = f32_to_fp4(acc[k][0] * inv), c1 = f32_to_fp4(acc[k][1] * inv);
+        const uint32_t c0 = f32_to_fp4(acc[k][0] * rsc), c1 = f32_to_fp4(acc[k][1] * rsc);
         const int d = d0 + 2 * pr;
-        const int64_t at = tiled ? idx4_tile_off(b, e_pad, j, d) : ro * (D / 2) + d / 2;
+        const int64_t at = tiled ? idx4_tile_off_row(trow, d) : ro * (D / 2) + d / 2;
         op[at] = static_cast<uint8_t>(c0 | (c1 << 4));
-        if ((d & 31) == 0) out_mx[ro * (D / 32) + d / 32] = static_cast<uint8_t>(e + 127);
+        if ((d & 31) == 0) out_mx[ro * (D / 32) + d / 32] = static_cast<uint8_t>(se + 127);
       }
     }
   } else {  // fp8 e4m3fn, token-wise scale = amax / 448
@@ -251,18 +258,17 @@ __device__ __forceinline__ void compress_one(
     // dim 128: the 16-entry tile layout of the indexer keys; else row-major
     const bool tiled = D == 128;
     uint8_t* op = static_cast<uint8_t*>(out) + (tiled ? 0 : o);
-    const int64_t e_pad = idx_e_pad(e_cap);
 #pragma unroll
     for (int k = 0; k < kCompressPairs; ++k) {
       const int pr = tid + k * kCompressThreads;
       if (pr < npairs) {
         const uint32_t c0 = sc > 0.f ? f32_to_fp8(acc[k][0] / sc) : 0u;
         const uint32_t c1 = sc > 0.f ? f32_to_fp8(acc[k][1] / sc) : 0u;
-        const int64_t at = tiled ? idx_tile_off(b, e_pad, j, d0 + 2 * pr) : d0 + 2 * pr;
+        const int64_t at = tiled ? idx_tile_off_row(trow, d0 + 2 * pr) : d0 + 2 * pr;
         *reinterpret_cast<uint16_t*>(op + at) = static_cast<uint16_t>(c0 | (c1 << 8));
       }
     }
-    if (tid == 0) out_scale[static_cast<int64_t>(b) * e_cap + j] = sc;
+    if (tid == 0) out_scale[erow] = sc;
   }
 }
 

@@ -88,6 +88,7 @@ struct PrologueArgs {
   float* cs_tab;  // role 3: (cos, sin) of R_m, r floats per sequence
   float* main_scale;  // fp8 main cache: one scale per entry [B, e_cap], else nullptr
   uint32_t* status;
+  Paging pg;          // paged caches, window and rings (tables nullptr: dense)
 };
 
 // Workgroups of the prologue: kSlices for the main entry, then three.
@@ -139,7 +140,8 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
                                           static_cast<const MainT*>(a.main_ring), a.pos0,
                                           a.logits_main, a.main_cache, a.main_scale, a.gamma,
                                           a.eps, 1, 1, a.s, a.S, a.D, a.r, a.base, a.off,
-                                          a.e_cap, a.max_pos_end, a.status);
+                                          a.e_cap, a.max_pos_end, a.status, 0, -1, nullptr,
+                                          a.pg);
       return;
     }
     if constexpr (kSlices > 1) {
@@ -153,7 +155,8 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
     compress_one<MainT, kMainOut>(0, b, static_cast<const MainT*>(a.x),
                                   static_cast<const MainT*>(a.main_ring), a.pos0, a.logits_main,
                                   a.main_cache, nullptr, a.gamma, a.eps, 1, 1, a.s, a.S, a.D, a.r,
-                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status, d0, dn);
+                                  a.base, a.off, a.e_cap, a.max_pos_end, a.status, d0, dn, nullptr,
+                                  a.pg);
     return;
   }
   role -= kSlices - 1;  // 1: indexer entry, 2: rings and window, 3: (cos, sin) table
@@ -163,7 +166,7 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
                                      static_cast<const IdxRawT*>(a.idx_ring), a.pos0, a.logits_idx,
                                      a.idx_cache, a.idx_scale, a.gamma_idx, a.eps, 1, 1, a.s, a.S,
                                      a.Di, a.r_idx, a.idx_base, a.off, a.e_cap, a.max_pos_end,
-                                     a.status, 0, -1, a.idx_mx);
+                                     a.status, 0, -1, a.idx_mx, a.pg);
     return;
   }
   if (role == 3) {
@@ -182,16 +185,24 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
   if (threadIdx.x == 0) a.qpos[b] = m;
   if (m < 0 || m >= a.max_pos_end) return;
   const MainT* xb = static_cast<const MainT*>(a.x) + static_cast<int64_t>(b) * a.D;
-  MainT* rb = static_cast<MainT*>(a.main_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.D;
-  for (int i = threadIdx.x; i < a.D; i += blockDim.x) rb[i] = xb[i];
-  if (a.has_idx) {
-    const IdxRawT* kb = static_cast<const IdxRawT*>(a.kx) + static_cast<int64_t>(b) * a.Di;
-    IdxRawT* ib = static_cast<IdxRawT*>(a.idx_ring) + (static_cast<int64_t>(b) * a.S + m % a.S) * a.Di;
-    for (int i = threadIdx.x; i < a.Di; i += blockDim.x) ib[i] = kb[i];
+  uint32_t* st0 = threadIdx.x == 0 ? a.status : nullptr;
+  bool ring_ok = true;
+  const int64_t sq = state_seq(a.pg, b, st0, &ring_ok);  // the rings' block
+  if (ring_ok) {
+    MainT* rb = static_cast<MainT*>(a.main_ring) + (sq * a.S + m % a.S) * a.D;
+    for (int i = threadIdx.x; i < a.D; i += blockDim.x) rb[i] = xb[i];
+    if (a.has_idx) {
+      const IdxRawT* kb = static_cast<const IdxRawT*>(a.kx) + static_cast<int64_t>(b) * a.Di;
+      IdxRawT* ib = static_cast<IdxRawT*>(a.idx_ring) + (sq * a.S + m % a.S) * a.Di;
+      for (int i = threadIdx.x; i < a.Di; i += blockDim.x) ib[i] = kb[i];
+    }
   }
-  if (a.insert_window)
-    rotate_store(xb, static_cast<MainT*>(a.window) + (static_cast<int64_t>(b) * a.w_cap + m % a.w_cap) * a.D,
-                 a.D, a.r, a.base, m + a.off);
+  if (a.insert_window) {
+    bool ok = true;
+    const int64_t wr = window_row(a.pg.swa, b, m, a.w_cap, st0, &ok);
+    if (ok)
+      rotate_store(xb, static_cast<MainT*>(a.window) + wr * a.D, a.D, a.r, a.base, m + a.off);
+  }
 }
 
 

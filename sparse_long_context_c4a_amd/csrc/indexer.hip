@@ -35,6 +35,8 @@
 //
 // Many rows per sequence (a prefill chunk) take the matrix-core contraction
 // of prefill_index.hip.
+#include <type_traits>
+
 #include "common.h"
 #include "decode_impl.h"
 #include "indexer_impl.h"
@@ -52,17 +54,18 @@ namespace {
 // sum every one of the 128 products exactly once.  With the keys' tile
 // layout each of the two 16-byte loads of a wave reads 1 KiB of contiguous
 // bytes.
-template <bool kCand, int kEnt, int kFmt>
+template <bool kCand, int kEnt, int kFmt, bool kPaged>
 __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ k_mx, const int64_t* __restrict__ q_pos, int Tq, int Hi, int s,
     int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
     int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap,
-    uint32_t* status) {
-  index_stream_block<kCand, kEnt, kFmt>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys,
+    uint32_t* status, PageMap pm) {
+  index_stream_block<kCand, kEnt, kFmt, kPaged>(blockIdx.x, gridDim.x, blockIdx.y, q, q_scale, w, keys,
                                         k_scale, k_mx, q_pos, Tq, Hi, s, S, e_cap, nv_cap,
-                                        max_pos_end, scores, ld_scores, cand, meta, cap, status);
+                                        max_pos_end, scores, ld_scores, cand, meta, cap, status,
+                                        pm);
 }
 
 // A decode step's indexer with the step's state updates riding along: the
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void k_index_fp8_stream(
 // first so that they are dispatched with the first wave of workgroups, not
 // after the stream has freed compute units.  The rest stream the keys: nb
 // workgroups per row.
-template <typename MainT, int kIdxOut, int kEnt, bool kMainFp8 = false>
+template <typename MainT, int kIdxOut, int kEnt, bool kMainFp8, bool kPaged>
 __global__ __launch_bounds__(kThreads) void k_decode_index(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
@@ -81,15 +84,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
     int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb,
     PrologueArgs pa, uint32_t* status) {
+  // the keys' paging is the layer's (the prologue's)
   const int rpr = kPrologueRoles + pa.nq_roles;  // prologue workgroups per sequence
   const int id = static_cast<int>(blockIdx.x), npro = pa.B * rpr;
   if (id < npro) {
     decode_prologue_block<MainT, kIdxOut, 1, kMainFp8>(id % rpr, id / rpr, pa);
   } else {
     const int sid = id - npro;
-    index_stream_block<true, kEnt, kIdxOut>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale,
+    index_stream_block<true, kEnt, kIdxOut, kPaged>(sid % nb, nb, sid / nb, q, q_scale, w, keys, k_scale,
                                             k_mx, q_pos, 1, Hi, s, S, e_cap, nv_cap, max_pos_end,
-                                            scores, ld_scores, cand, meta, cap, status);
+                                            scores, ld_scores, cand, meta, cap, status, pa.pg.ent);
   }
 }
 
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
     const T* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const T* __restrict__ keys, const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
     int Tq, int Hi, int Di, int s, int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end,
-    float* __restrict__ scores, int64_t ld_scores, uint32_t* status) {
+    float* __restrict__ scores, int64_t ld_scores, uint32_t* status, PageMap pm) {
   extern __shared__ float q_s[];  // [Hi * Di] then [Hi] weights
   const int row = blockIdx.y, b = row / Tq, tid = threadIdx.x;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, blockIdx.x == 0 && tid == 0);
@@ -118,23 +122,26 @@ __global__ __launch_bounds__(kThreads) void k_index_generic(
   __syncthreads();
   const int64_t ent = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid;
   if (ent < nv) {
-    // fp8 keys of dim 128 use the tile layout, everything else is row-major
+    // fp8 keys of dim 128 use the tile layout, everything else is row-major;
+    // row: the entry's row (b * e_cap + ent dense, its pool row paged), trow
+    // its tile row
     const bool tiled = sizeof(T) == 1 && Di == 128;
-    const T* kr = keys + (tiled ? 0 : (static_cast<int64_t>(b) * e_cap + ent) * Di);
-    const int64_t e_pad = idx_e_pad(e_cap);
+    const int64_t erow = entry_row(pm, b, ent, e_cap, status);
+    const int64_t trow = pm.table ? erow : static_cast<int64_t>(b) * idx_e_pad(e_cap) + ent;
+    const T* kr = keys + (tiled ? 0 : erow * Di);
     float tot = 0.f;
     for (int h = 0; h < Hi; ++h) {
       float d = 0.f;
       for (int i = 0; i < Di; ++i) {
         float kv;
         if constexpr (sizeof(T) == 1)
-          kv = fp8_to_f32(tiled ? kr[idx_tile_off(b, e_pad, ent, i)] : kr[i]);
+          kv = fp8_to_f32(tiled ? kr[idx_tile_off_row(trow, i)] : kr[i]);
         else kv = kr[i];
         d = fmaf(q_s[h * Di + i], kv, d);
       }
       tot += w_s[h] * fmaxf(d, 0.f);
     }
-    if constexpr (sizeof(T) == 1) tot *= k_scale[static_cast<int64_t>(b) * e_cap + ent];
+    if constexpr (sizeof(T) == 1) tot *= k_scale[erow];
     scores[static_cast<int64_t>(row) * ld_scores + ent] = tot;
   }
 }
@@ -157,7 +164,8 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     float* __restrict__ score_out, int k, const uint8_t* __restrict__ q,
     const float* __restrict__ q_scale, const float* __restrict__ hw,
     const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
-    const uint8_t* __restrict__ k_mx, int Tq, int Hi, int64_t e_cap) {
+    const uint8_t* __restrict__ k_mx, int Tq, int Hi, int64_t e_cap, PageMap kpm,
+    uint32_t* status) {
   __shared__ uint64_t cand_s[kFinalCap + 256 * kMaxF];
   __shared__ uint64_t tmp_s[kTmpCap];
   __shared__ uint32_t h_s[kBins];
@@ -193,15 +201,13 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   int32_t* irow = idx_out + static_cast<int64_t>(row) * k;
   float* orow = score_out ? score_out + static_cast<int64_t>(row) * k : nullptr;
   const int b = row / Tq;
-  const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * KeyOps<kFmt>::kBytes;
-  const float* ksb = k_scale ? k_scale + static_cast<int64_t>(b) * e_cap : nullptr;
-  const uint8_t* msb = k_mx ? k_mx + static_cast<int64_t>(b) * e_cap * 4 : nullptr;
+  const KeySrc src = key_src<kFmt>(keys, k_scale, k_mx, kpm, b, e_cap, status);
   v8bf aq[4];
   float wv[4];
   if (nv <= k) {
     if (orow) {  // the visible entries' scores (the stream kept them in registers)
       exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
-      score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
+      score_row_exact<kFmt>(aq, wv, src, nv, srow, kSelWaves);
       __syncthreads();
     }
     emit_all_visible(srow, nv, k, irow, orow);
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   if (block_reduce_u32<2>(c_n) < static_cast<uint32_t>(k)) {  // barriers
     // fewer candidates than k (ties at the wave thresholds): the whole row
     exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
-    score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
+    score_row_exact<kFmt>(aq, wv, src, nv, srow, kSelWaves);
     __syncthreads();
     row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
     return;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     const uint32_t nf = block_reduce_u32<2>(in_f ? 1u : 0u);  // barriers
     exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
     if (nf > static_cast<uint32_t>(kMaxF)) {
-      score_row_exact<kFmt>(aq, wv, kb, ksb, msb, nv, srow, kSelWaves);
+      score_row_exact<kFmt>(aq, wv, src, nv, srow, kSelWaves);
       __syncthreads();
       row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
       return;
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
         const int ft = f0 + u * kSelWaves;
         jj[u] = ft < ntile ? static_cast<int64_t>(f_s[ft >> 4]) * 256 + (ft & 15) * 16 + n : nv;
       }
-      exact_scores<kFmt, kBatch>(aq, wv, kb, ksb, msb, jj, nv, sc);
+      exact_scores<kFmt, kBatch>(aq, wv, src, jj, nv, sc);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int ft = f0 + u * kSelWaves;
@@ -401,11 +407,32 @@ __global__ __launch_bounds__(kSel) void k_topk_rows(
   row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
 }
 
+// Paged fp8 keys for the many-rows contraction: the visible tiles of each
+// sequence (16 entries: 2 KiB of keys, contiguous in a block) and their
+// scales copied to a dense per-sequence layout in the workspace, which the
+// contraction's 16 KiB stages then stream as usual.  One workgroup per
+// (tile, sequence).
+__global__ __launch_bounds__(256) void k_densify_keys(const uint8_t* __restrict__ pool,
+                                                      const float* __restrict__ ks_pool,
+                                                      PageMap pm, int64_t e_cap,
+                                                      uint8_t* __restrict__ keys,
+                                                      float* __restrict__ ks,
+                                                      uint32_t* status) {
+  const int b = blockIdx.y, t = threadIdx.x;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t R = paged_row(pm, b, j0, t == 0 ? status : nullptr);
+  const int64_t d0 = static_cast<int64_t>(b) * idx_e_pad(e_cap) + j0;
+  if (t < 128)
+    reinterpret_cast<uint4*>(keys + d0 * 128)[t] = reinterpret_cast<const uint4*>(pool + R * 128)[t];
+  else if (t < 144 && j0 + (t - 128) < e_cap)
+    ks[static_cast<int64_t>(b) * e_cap + j0 + (t - 128)] = ks_pool[R + (t - 128)];
+}
+
 struct Plan {
   int64_t nv_cap, ld;
-  bool mfma, cand, pre;
+  bool mfma, cand, pre, dense_copy;
   int ent, nb, nw, cap;
-  size_t off_scores, off_cand, off_meta, off_pre, total;
+  size_t off_scores, off_cand, off_meta, off_pre, off_dkeys, off_dks, total;
 };
 
 Plan plan(const dsa_index_args& a) {
@@ -441,6 +468,12 @@ Plan plan(const dsa_index_args& a) {
   if (p.cand) off = align_up(off + static_cast<size_t>(rows) * p.nw * sizeof(uint32_t));
   p.off_pre = off;
   if (p.pre) off = align_up(off + prefill_index_ws_bytes(a, p.nv_cap));
+  // paged keys for the contraction: a dense copy of the visible tiles
+  p.dense_copy = p.pre && a.paging.block_table != nullptr;
+  p.off_dkeys = off;
+  if (p.dense_copy) off = align_up(off + static_cast<size_t>(a.n_seqs) * idx_e_pad(a.e_cap) * 128);
+  p.off_dks = off;
+  if (p.dense_copy) off = align_up(off + static_cast<size_t>(a.n_seqs) * a.e_cap * sizeof(float));
   p.total = off;
   return p;
 }
@@ -452,7 +485,7 @@ void launch_cand_final(const dsa_index_args& a, const Plan& P, float* scores, ui
                        a.span, P.nv_cap, a.max_pos_end, cand, meta, P.nw, P.cap, a.idx_out,
                        a.score_out, a.k, static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                        static_cast<const uint8_t*>(a.keys), a.k_scale, a.k_mx_scale, Tq, a.heads,
-                       a.e_cap);
+                       a.e_cap, make_paging(a.paging).ent, a.status);
   };
   if (a.dtype == DSA_FP4_E2M1) go(k_topk_cand_final<DSA_FP4_E2M1>);
   else go(k_topk_cand_final<DSA_FP8_E4M3>);
@@ -471,6 +504,21 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
   uint32_t* meta = reinterpret_cast<uint32_t*>(base + P.off_meta);
   const bool no_keys = a.keys == nullptr;  // only allowed when k >= every n_vis
   dsa_status rc;
+  if (P.pre && P.dense_copy) {
+    dsa_index_args d = a;
+    d.keys = base + P.off_dkeys;
+    d.k_scale = reinterpret_cast<float*>(base + P.off_dks);
+    d.paging = dsa_paging{};
+    if (P.nv_cap > 0) {
+      hipLaunchKernelGGL(k_densify_keys, dim3(static_cast<unsigned>(ceil_div(P.nv_cap, 16)), a.n_seqs),
+                         dim3(256), 0, st, static_cast<const uint8_t*>(a.keys), a.k_scale,
+                         make_paging(a.paging).ent, a.e_cap, reinterpret_cast<uint8_t*>(base + P.off_dkeys),
+                         reinterpret_cast<float*>(base + P.off_dks), a.status);
+      rc = hip_check(hipGetLastError(), "k_densify_keys launch");
+      if (rc != DSA_OK) return rc;
+    }
+    return launch_prefill_index_topk(d, P.nv_cap, scores, P.ld, base + P.off_pre, st);
+  }
   if (P.pre) return launch_prefill_index_topk(a, P.nv_cap, scores, P.ld, base + P.off_pre, st);
   if (!no_keys && P.nv_cap > 0) {
     const hipEvent_t e0 = call_timing().index0, e1 = call_timing().index1;
@@ -480,16 +528,23 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
         launch_timed(kern, grid, dim3(kThreads), 0, st, e0, e1, static_cast<const uint8_t*>(a.q),
                      a.q_scale, a.w, static_cast<const uint8_t*>(a.keys), a.k_scale, a.k_mx_scale,
                      a.q_pos, a.queries_per_seq, a.heads, a.stride, a.span, a.e_cap, P.nv_cap,
-                     a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status);
+                     a.max_pos_end, scores, P.ld, cand, meta, P.cap, a.status,
+                     make_paging(a.paging).ent);
       };
-      const bool fp4 = a.dtype == DSA_FP4_E2M1;
-      if (P.cand) {
-        if (fp4) go(k_index_fp8_stream<true, 1024, DSA_FP4_E2M1>);
-        else go(k_index_fp8_stream<true, 1024, DSA_FP8_E4M3>);
-      } else {
-        if (fp4) go(k_index_fp8_stream<false, 1024, DSA_FP4_E2M1>);
-        else go(k_index_fp8_stream<false, 1024, DSA_FP8_E4M3>);
-      }
+      const bool fp4 = a.dtype == DSA_FP4_E2M1, paged = a.paging.block_table != nullptr;
+      auto by_fmt = [&](auto tag_cand) {
+        constexpr bool kC = decltype(tag_cand)::value;
+        if (fp4) {
+          if (paged) go(k_index_fp8_stream<kC, 1024, DSA_FP4_E2M1, true>);
+          else go(k_index_fp8_stream<kC, 1024, DSA_FP4_E2M1, false>);
+        } else if (paged) {
+          go(k_index_fp8_stream<kC, 1024, DSA_FP8_E4M3, true>);
+        } else {
+          go(k_index_fp8_stream<kC, 1024, DSA_FP8_E4M3, false>);
+        }
+      };
+      if (P.cand) by_fmt(std::true_type{});
+      else by_fmt(std::false_type{});
     } else {
       dim3 grid(static_cast<unsigned>(ceil_div(P.nv_cap, kThreads)), rows);
       const size_t shm = (static_cast<size_t>(a.heads) * a.dim + a.heads) * sizeof(float);
@@ -498,13 +553,13 @@ dsa_status launch_index_topk(const dsa_index_args& a, void* ws, hipStream_t st) 
                            static_cast<const float*>(a.q), a.q_scale, a.w,
                            static_cast<const float*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
-                           a.max_pos_end, scores, P.ld, a.status);
+                           a.max_pos_end, scores, P.ld, a.status, make_paging(a.paging).ent);
       else
         launch_timed(k_index_generic<uint8_t>, grid, dim3(kThreads), shm, st, e0, e1,
                            static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                            static_cast<const uint8_t*>(a.keys), a.k_scale, a.q_pos,
                            a.queries_per_seq, a.heads, a.dim, a.stride, a.span, a.e_cap, P.nv_cap,
-                           a.max_pos_end, scores, P.ld, a.status);
+                           a.max_pos_end, scores, P.ld, a.status, make_paging(a.paging).ent);
     }
     rc = hip_check(hipGetLastError(), "indexer launch");
     if (rc != DSA_OK) return rc;
@@ -545,13 +600,22 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                  a.stride, a.span, a.e_cap, P.nv_cap, a.max_pos_end, scores, P.ld, cand, meta,
                  P.cap, P.nb, pa, a.status);
   };
+  auto by_main = [&](auto tag_fmt, auto tag_paged) {
+    constexpr int kF = decltype(tag_fmt)::value;
+    constexpr bool kP = decltype(tag_paged)::value;
+    if (la.main_fp8) go(k_decode_index<uint16_t, kF, 1024, true, kP>);
+    else go(k_decode_index<uint16_t, kF, 1024, false, kP>);
+  };
+  const bool paged = a.paging.block_table != nullptr;
+  using Fp4 = std::integral_constant<int, DSA_FP4_E2M1>;
+  using Fp8 = std::integral_constant<int, DSA_FP8_E4M3>;
   if (a.dtype == DSA_FP4_E2M1) {
-    if (la.main_fp8) go(k_decode_index<uint16_t, DSA_FP4_E2M1, 1024, true>);
-    else go(k_decode_index<uint16_t, DSA_FP4_E2M1, 1024>);
-  } else if (la.main_fp8) {
-    go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024, true>);
+    if (paged) by_main(Fp4{}, std::true_type{});
+    else by_main(Fp4{}, std::false_type{});
+  } else if (paged) {
+    by_main(Fp8{}, std::true_type{});
   } else {
-    go(k_decode_index<uint16_t, DSA_FP8_E4M3, 1024>);
+    by_main(Fp8{}, std::false_type{});
   }
   dsa_status rc = hip_check(hipGetLastError(), "k_decode_index launch");
   if (rc != DSA_OK) return rc;

@@ -117,6 +117,29 @@ struct KeyOps<DSA_FP4_E2M1> {
   }
 };
 
+// Where a sequence's keys are: dense, its own tiles (kb), scales (ksb) and
+// MX scale bytes (msb), entry j at row j; paged, the pools, entry j at its
+// pool row.
+struct KeySrc {
+  const uint8_t* kb;
+  const float* ksb;
+  const uint8_t* msb;
+  PageMap pm;
+  int b;
+  uint32_t* status;
+  __device__ int64_t row(int64_t j) const { return pm.table ? paged_row(pm, b, j, status) : j; }
+};
+
+template <int kFmt>
+__device__ __forceinline__ KeySrc key_src(const uint8_t* keys, const float* k_scale,
+                                          const uint8_t* k_mx, const PageMap& pm, int b,
+                                          int64_t e_cap, uint32_t* status) {
+  if (pm.table) return KeySrc{keys, k_scale, k_mx, pm, b, status};
+  return KeySrc{keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * KeyOps<kFmt>::kBytes,
+                k_scale ? k_scale + static_cast<int64_t>(b) * e_cap : nullptr,
+                k_mx ? k_mx + static_cast<int64_t>(b) * e_cap * 4 : nullptr, pm, b, status};
+}
+
 struct RowInfo {
   int64_t nv;
   bool ok;
@@ -207,14 +230,14 @@ __device__ __forceinline__ void exact_row_operands(const uint8_t* q, const float
 // kBatch entries' loads go out before the first product.
 template <int kFmt, int kBatch>
 __device__ __forceinline__ void exact_scores(const v8bf (&aq)[4], const float (&wv)[4],
-                                             const uint8_t* kb, const float* ksb,
-                                             const uint8_t* msb, const int64_t (&j)[kBatch],
+                                             const KeySrc& src, const int64_t (&j)[kBatch],
                                              int64_t nv, float (&sc)[kBatch]) {
   using K = KeyOps<kFmt>;
   const int g = (threadIdx.x & 63) >> 4;
   typename K::Raw r[kBatch];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) r[u] = j[u] < nv ? K::load(kb, ksb, msb, j[u], g) : K::zero();
+  for (int u = 0; u < kBatch; ++u)
+    r[u] = j[u] < nv ? K::load(src.kb, src.ksb, src.msb, src.row(j[u]), g) : K::zero();
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
     v8bf bo[4];
@@ -227,8 +250,7 @@ __device__ __forceinline__ void exact_scores(const v8bf (&aq)[4], const float (&
 // workgroup takes every nwaves-th tile of 16 entries).
 template <int kFmt>
 __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float (&wv)[4],
-                                                const uint8_t* kb, const float* ksb,
-                                                const uint8_t* msb, int64_t nv, float* srow,
+                                                const KeySrc& src, int64_t nv, float* srow,
                                                 int nwaves) {
   // four tiles' loads in flight per wave and round
   constexpr int kBatch = 4;
@@ -238,7 +260,7 @@ __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float
     float sc[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) j[u] = (t0 + static_cast<int64_t>(u) * nwaves) * 16 + n;
-    exact_scores<kFmt, kBatch>(aq, wv, kb, ksb, msb, j, nv, sc);
+    exact_scores<kFmt, kBatch>(aq, wv, src, j, nv, sc);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
       if (g == 0 && j[u] < nv) srow[j[u]] = sc[u];
@@ -249,14 +271,14 @@ __device__ __forceinline__ void score_row_exact(const v8bf (&aq)[4], const float
 // stay in registers (candidates and wave thresholds go out; a row whose
 // certificate fails is re-scored by the final pass); without, every score
 // is written to its row.
-template <bool kCand, int kEnt, int kFmt = DSA_FP8_E4M3>
+template <bool kCand, int kEnt, int kFmt = DSA_FP8_E4M3, bool kPaged = false>
 __device__ __forceinline__ void index_stream_block(
     int bx, int nbx, int row, const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ keys, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ k_mx, const int64_t* __restrict__ q_pos, int Tq, int Hi, int s,
     int S, int64_t e_cap, int64_t nv_cap, int64_t max_pos_end, float* __restrict__ scores,
     int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap,
-    uint32_t* status) {
+    uint32_t* status, PageMap pm) {
   using K = KeyOps<kFmt>;
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -271,19 +293,29 @@ __device__ __forceinline__ void index_stream_block(
   // each lane keeps the keys of groups 4i + 2 (g & 1) + (g >> 1), i < kKeep
   uint32_t kk[kKeep] = {};
   if (wbase < nv) {
-    const uint8_t* kb = keys + static_cast<int64_t>(b) * idx_e_pad(e_cap) * K::kBytes;
-    const float* ksb = k_scale ? k_scale + static_cast<int64_t>(b) * e_cap : nullptr;
-    const uint8_t* msb = k_mx ? k_mx + static_cast<int64_t>(b) * e_cap * 4 : nullptr;
+    const KeySrc src = key_src<kFmt>(keys, k_scale, k_mx, pm, b, e_cap, status);
     // key loads: a ring of two slots of two groups; unconditional (clamped
     // to a visible entry, masked later) so the compiler can count them, and
     // the first slot issued before the query set-up
     const int64_t jmax = nv - 1;
+    // paged: lane l < kGroups holds the block of the wave's group l (16
+    // entries never straddle a block), read once per wave; each load takes
+    // its group's block id from that lane
+    int32_t gblk = 0;
+    if constexpr (kPaged)
+      if (lane < kGroups)
+        gblk = static_cast<int32_t>(
+            paged_row(pm, b, min<int64_t>(wbase + lane * 16, jmax), status) >> pm.shift);
     typename K::Raw kr[2][2];
     auto load = [&](int slot, int gr) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int64_t ent = min<int64_t>(wbase + (gr + u) * 16 + n, jmax);
-        kr[slot][u] = K::load(kb, ksb, msb, ent, g);
+        int64_t rw = ent;
+        if constexpr (kPaged)
+          rw = (static_cast<int64_t>(__builtin_amdgcn_readlane(gblk, gr + u)) << pm.shift) |
+               (ent & ((int64_t{1} << pm.shift) - 1));
+        kr[slot][u] = K::load(src.kb, src.ksb, src.msb, rw, g);
       }
     };
     load(0, 0);
@@ -326,7 +358,9 @@ __device__ __forceinline__ void index_stream_block(
       const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
       const float v = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
       const int u = g >> 1;
-      const float sc = v * K::scale(kr[sl][u]);
+      // (a select, not an index by u: a lane-dependent index into kr would
+      // put the whole ring in scratch memory)
+      const float sc = v * (u ? K::scale(kr[sl][1]) : K::scale(kr[sl][0]));
       const int64_t ent = wbase + (2 * st + u) * 16 + n;
       const bool vis = ent < nv;
       if constexpr (!kCand)

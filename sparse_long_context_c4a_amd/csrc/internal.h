@@ -70,12 +70,14 @@ dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st,
 
 // Layer helpers: ring and window maintenance, chunk rotation.
 dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
-                              const int64_t* pos0, int B, int64_t max_pos_end, hipStream_t st);
+                              const int64_t* pos0, int B, int64_t max_pos_end,
+                              const dsa_paging& pg, uint32_t* status, hipStream_t st);
 dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, int r, double base,
                                int64_t off, const int64_t* pos0, int B, void* out,
                                int64_t max_pos_end, hipStream_t st);
 dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
-                                int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
+                                int w_cap, int window_size, const int64_t* pos0, int B,
+                                int64_t max_pos_end, const dsa_paging& pg, uint32_t* status,
                                 hipStream_t st);
 
 // Decode (one token per sequence): fused prologue and, when the window ring

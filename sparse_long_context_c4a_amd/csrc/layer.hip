@@ -4,7 +4,10 @@
 // The compressor state is the last S raw tokens of each compressor (c4a 8,
 // c128a 128: "DeepSeek V4 稀疏注意力完全解剖", 设计 2), raw position p at slot
 // p mod S.  The window keeps the rotated raw tokens R_n x_n of the last w_cap
-// positions (same page, 机制四), position n at slot n mod w_cap.
+// positions (same page, 机制四), position n at slot n mod w_cap.  Paged
+// (same page, 第三层 设计 1 and 2), a sequence's rings are one block of the
+// ring pools and window token n sits in slot n mod 256 of its logical block's
+// window block.
 #include "common.h"
 #include "compress_impl.h"
 #include "decode_impl.h"
@@ -23,15 +26,18 @@ __global__ void k_zero(uint32_t* p, size_t n) {
 // (min(T, S), B); element size in 2-byte units.
 __global__ void k_ring_update(const uint16_t* __restrict__ raw, int units, int64_t T,
                               uint16_t* __restrict__ ring, int S, const int64_t* __restrict__ pos0,
-                              int64_t max_pos_end) {
+                              int64_t max_pos_end, Paging pg, uint32_t* status) {
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
   if (p0 < 0 || p0 + T > max_pos_end) return;
+  bool ok = true;
+  const int64_t sq = state_seq(pg, b, threadIdx.x == 0 ? status : nullptr, &ok);
+  if (!ok) return;
   const int64_t keep = T < S ? T : S;
   const int64_t t = T - keep + blockIdx.x;  // chunk offset of the token
   const int64_t p = p0 + t;
   const uint16_t* src = raw + (static_cast<int64_t>(b) * T + t) * units;
-  uint16_t* dst = ring + (static_cast<int64_t>(b) * S + (p % S)) * units;
+  uint16_t* dst = ring + (sq * S + (p % S)) * units;
   for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
 }
 
@@ -103,18 +109,23 @@ __global__ __launch_bounds__(256) void k_qk_prep(const T* __restrict__ q, T* __r
   }
 }
 
-// Window ring takes the last min(T, w_cap) rotated chunk tokens.
+// The window takes the last min(T, keep_cap) rotated chunk tokens (ring:
+// keep_cap = w_cap; paged: the window size, the tokens later steps read).
 __global__ void k_window_update(const uint16_t* __restrict__ rot, int units, int64_t T,
-                                uint16_t* __restrict__ win, int w_cap,
-                                const int64_t* __restrict__ pos0, int64_t max_pos_end) {
+                                uint16_t* __restrict__ win, int w_cap, int keep_cap,
+                                const int64_t* __restrict__ pos0, int64_t max_pos_end,
+                                PageMap swa, uint32_t* status) {
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
   if (p0 < 0 || p0 + T > max_pos_end) return;
-  const int64_t keep = T < w_cap ? T : w_cap;
+  const int64_t keep = T < keep_cap ? T : keep_cap;
   const int64_t t = T - keep + blockIdx.x;
   const int64_t n = p0 + t;
+  bool ok = true;
+  const int64_t wr = window_row(swa, b, n, w_cap, threadIdx.x == 0 ? status : nullptr, &ok);
+  if (!ok) return;
   const uint16_t* src = rot + (static_cast<int64_t>(b) * T + t) * units;
-  uint16_t* dst = win + (static_cast<int64_t>(b) * w_cap + (n % w_cap)) * units;
+  uint16_t* dst = win + wr * units;
   for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
 }
 
@@ -129,12 +140,14 @@ __global__ __launch_bounds__(kCompressThreads) void k_decode_prologue(PrologueAr
 template <typename MainT>
 __global__ void k_decode_window_insert(const MainT* __restrict__ x, MainT* __restrict__ win, int D,
                                        int w_cap, int r, double base, int64_t off,
-                                       const int64_t* __restrict__ pos0, int64_t max_pos_end) {
+                                       const int64_t* __restrict__ pos0, int64_t max_pos_end,
+                                       PageMap swa, uint32_t* status) {
   const int b = blockIdx.x;
   const int64_t m = pos0[b];
   if (m < 0 || m >= max_pos_end) return;
-  rotate_store(x + static_cast<int64_t>(b) * D, win + (static_cast<int64_t>(b) * w_cap + m % w_cap) * D,
-               D, r, base, m + off);
+  bool ok = true;
+  const int64_t wr = window_row(swa, b, m, w_cap, threadIdx.x == 0 ? status : nullptr, &ok);
+  if (ok) rotate_store(x + static_cast<int64_t>(b) * D, win + wr * D, D, r, base, m + off);
 }
 
 }  // namespace
@@ -148,12 +161,13 @@ dsa_status launch_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
-                              const int64_t* pos0, int B, int64_t max_pos_end, hipStream_t st) {
+                              const int64_t* pos0, int B, int64_t max_pos_end,
+                              const dsa_paging& pg, uint32_t* status, hipStream_t st) {
   const int units = static_cast<int>(D * dtype_size(dt) / 2);
   const int64_t keep = T < S ? T : S;
   hipLaunchKernelGGL(k_ring_update, dim3(static_cast<unsigned>(keep), B), dim3(256), 0, st,
                      static_cast<const uint16_t*>(raw), units, T, static_cast<uint16_t*>(ring), S,
-                     pos0, max_pos_end);
+                     pos0, max_pos_end, make_paging(pg), status);
   return hip_check(hipGetLastError(), "k_ring_update launch");
 }
 
@@ -192,13 +206,18 @@ dsa_status launch_qk_prep(const dsa_layer_args& a, void* q_rot, void* rot_chunk,
 }
 
 dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
-                                int w_cap, const int64_t* pos0, int B, int64_t max_pos_end,
+                                int w_cap, int window_size, const int64_t* pos0, int B,
+                                int64_t max_pos_end, const dsa_paging& pg, uint32_t* status,
                                 hipStream_t st) {
   const int units = static_cast<int>(D * dtype_size(dt) / 2);
-  const int64_t keep = T < w_cap ? T : w_cap;
+  const Paging P = make_paging(pg);
+  const int keep_cap = P.swa.table ? window_size : w_cap;
+  const int64_t keep = T < keep_cap ? T : keep_cap;
+  if (keep <= 0) return DSA_OK;
   hipLaunchKernelGGL(k_window_update, dim3(static_cast<unsigned>(keep), B), dim3(256), 0, st,
                      static_cast<const uint16_t*>(rot_chunk), units, T,
-                     static_cast<uint16_t*>(win), w_cap, pos0, max_pos_end);
+                     static_cast<uint16_t*>(win), w_cap, keep_cap, pos0, max_pos_end, P.swa,
+                     status);
   return hip_check(hipGetLastError(), "k_window_update launch");
 }
 
@@ -248,6 +267,7 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
   p.cs_tab = cs_tab;
   p.main_scale = a.main_fp8 ? a.main_scale : nullptr;
   p.status = a.status;
+  p.pg = make_paging(a.paging);
   return p;
 }
 
@@ -280,12 +300,13 @@ dsa_status launch_decode_window_insert(const dsa_layer_args& a, hipStream_t st) 
     hipLaunchKernelGGL(k_decode_window_insert<float>, dim3(a.n_seqs), dim3(256), 0, st,
                        static_cast<const float*>(a.x), static_cast<float*>(a.window), a.main.dim,
                        a.w_cap, a.main.rope_dim, a.main.rope_base, a.main.rope_pos_offset, a.pos0,
-                       a.max_pos_end);
+                       a.max_pos_end, make_paging(a.paging).swa, a.status);
   else
     hipLaunchKernelGGL(k_decode_window_insert<uint16_t>, dim3(a.n_seqs), dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.x), static_cast<uint16_t*>(a.window),
                        a.main.dim, a.w_cap, a.main.rope_dim, a.main.rope_base,
-                       a.main.rope_pos_offset, a.pos0, a.max_pos_end);
+                       a.main.rope_pos_offset, a.pos0, a.max_pos_end, make_paging(a.paging).swa,
+                       a.status);
   return hip_check(hipGetLastError(), "k_decode_window_insert launch");
 }
 

@@ -867,7 +867,8 @@ __global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) 
   }
   // fallback: score the whole row exactly, then select from the scores
   float* srow = scores + static_cast<int64_t>(row) * ld_scores;
-  score_row_exact<DSA_FP8_E4M3>(aq, wv, kb, ksb, nullptr, nv, srow, kW);
+  score_row_exact<DSA_FP8_E4M3>(aq, wv, KeySrc{kb, ksb, nullptr, PageMap{}, b, nullptr}, nv, srow,
+                                kW);
   __syncthreads();
   row_select_from_scores<kPCandCap, kPSelT, 11>(srow, nv, a.k, irow, nullptr, cand_s, h_s);
 }

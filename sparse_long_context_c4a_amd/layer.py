@@ -145,7 +145,7 @@ def chunk_from_inputs(w: Workload, inp, device="cuda"):
 def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=None,
                status=None, max_pos_end=None, pos_offset=0, rms_gamma=None,
                rms_gamma_idx=None, rms_eps=1e-6, softmax_scale=0.0, out_scale=None,
-               q_norm_gamma=None):
+               q_norm_gamma=None, pages=None):
     a = _lib.LayerArgs()
     a.main = _lib.geom(w.s, w.S, w.D, w.r, w.base, pos_offset)
     a.heads, a.idx_heads, a.idx_dim = w.H, w.Hi, w.Di
@@ -164,6 +164,9 @@ def layer_args(w: Workload, st: LayerState, ch: Chunk, out, lse=None, idx_out=No
     a.idx_mx_scale = _lib.ptr(st.idx_mx)
     a.main_ring, a.idx_ring = _lib.ptr(st.main_ring), _lib.ptr(st.idx_ring)
     a.window, a.w_cap = _lib.ptr(st.window), st.window.shape[1]
+    if pages is not None:  # block tables; the state's tensors are the pools
+        a.paging = pages.args()
+        a.w_cap = 0
     a.rms_gamma, a.rms_gamma_idx, a.rms_eps = _lib.ptr(rms_gamma), _lib.ptr(rms_gamma_idx), rms_eps
     a.q_norm_gamma = _lib.ptr(q_norm_gamma)
     if st.main_scale is not None:  # fp8 codes in main_cache
@@ -198,3 +201,148 @@ def run(w: Workload, st: LayerState, ch: Chunk, decode=None, ws=None, out_fp8=Fa
     fn = _lib.layer_decode if decode else _lib.layer_prefill
     ws = fn(a, ws=ws, device=ch.x.device)
     return (out, osc) if out_fp8 else out, lse, idx, status, ws
+
+
+# ------------------------------------------------------------ paged state
+@dataclass
+class Pages:
+    """Block tables of a paged layer state (logical block = 256 raw
+    positions): entry pools hold epb = 256 / s entries per block, the window
+    pool 256 tokens per block, the ring pools one sequence's rings per block."""
+    table: torch.Tensor      # [B, blocks_per_seq] int32
+    swa_table: torch.Tensor  # [B, blocks_per_seq] int32
+    state: torch.Tensor      # [B] int32
+    epb: int
+    n_blocks: int
+    n_swa: int
+    n_state: int
+
+    def args(self):
+        p = _lib.Paging()
+        p.block_table, p.swa_block_table = _lib.ptr(self.table), _lib.ptr(self.swa_table)
+        p.state_block = _lib.ptr(self.state)
+        p.blocks_per_seq, p.entries_per_block = self.table.shape[1], self.epb
+        p.n_blocks, p.n_swa_blocks, p.n_state_blocks = self.n_blocks, self.n_swa, self.n_state
+        return p
+
+
+def _perm_table(gen, B, nb, n_pool):
+    """Distinct physical blocks for every (sequence, logical block), drawn
+    as a random permutation of a pool with spare blocks."""
+    perm = torch.randperm(n_pool, generator=gen)[:B * nb]
+    return perm.reshape(B, nb).to(torch.int32)
+
+
+def page_state(w: Workload, st: LayerState, p0, seed=0, spare=3):
+    """A paged copy of a dense state (same values, scattered over block
+    pools in a seeded random order) and its block tables.  Only the window
+    tokens before p0 that the ring holds are carried over."""
+    dev = st.main_cache.device
+    gen = torch.Generator().manual_seed(seed)
+    B = st.main_cache.shape[0]
+    epb = 256 // w.s
+    nb = -(-st.e_cap // epb)
+    nb_w = -(-(st.e_cap * w.s) // 256)
+    nbps = max(nb, nb_w)
+    n_blocks, n_swa, n_state = B * nbps + spare, B * nbps + spare, B + spare
+    table = _perm_table(gen, B, nbps, n_blocks)
+    swa = _perm_table(gen, B, nbps, n_swa)
+    state = torch.randperm(n_state, generator=gen)[:B].to(torch.int32)
+    rows = table.long()[:, :, None] * epb + torch.arange(epb)[None, None, :]  # [B, nbps, epb]
+    rows = rows.reshape(B, nbps * epb)[:, :st.e_cap].to(dev)                 # pool row of (b, j)
+
+    def scatter_rows(dense, per_row_shape, dtype):
+        pool = torch.zeros((n_blocks * epb,) + per_row_shape, dtype=dtype, device=dev)
+        if dense is not None:
+            pool[rows.reshape(-1)] = dense[:, :st.e_cap].reshape((-1,) + per_row_shape)
+        return pool
+
+    def scatter_tiles(tiles, bpe):
+        # dense tile layout [B, E_pad, bpe]: a block of epb entries is a
+        # contiguous run of epb * bpe bytes in both layouts
+        Ep = tiles.shape[1]
+        pad = nbps * epb - Ep
+        t = torch.cat([tiles, torch.zeros((B, pad, bpe), dtype=tiles.dtype, device=dev)], 1) \
+            if pad > 0 else tiles[:, :nbps * epb]
+        pool = torch.zeros((n_blocks, epb, bpe), dtype=tiles.dtype, device=dev)
+        pool[table.long().reshape(-1).to(dev)] = t.reshape(B * nbps, epb, bpe)
+        return pool.reshape(n_blocks * epb, bpe)
+
+    D = st.main_cache.shape[-1]
+    main = scatter_rows(st.main_cache, (D,), st.main_cache.dtype)
+    main_scale = scatter_rows(st.main_scale, (), torch.float32) if st.main_scale is not None else None
+    idx_cache = idx_scale = idx_mx = None
+    if st.idx_cache is not None:
+        if st.idx_cache.dtype == torch.uint8 and st.idx_cache.shape[-1] in (64, 128) and \
+                w.Di == 128:
+            idx_cache = scatter_tiles(st.idx_cache, st.idx_cache.shape[-1])
+        else:
+            idx_cache = scatter_rows(st.idx_cache, tuple(st.idx_cache.shape[2:]), st.idx_cache.dtype)
+        if st.idx_scale is not None:
+            idx_scale = scatter_rows(st.idx_scale, (), torch.float32)
+        if st.idx_mx is not None:
+            idx_mx = scatter_rows(st.idx_mx, (st.idx_mx.shape[-1],), torch.uint8)
+    # window: tokens n in [max(0, p0 - w_cap), p0) from ring slot n mod w_cap
+    w_cap = st.window.shape[1]
+    win = torch.zeros((n_swa * 256, D), dtype=st.window.dtype, device=dev)
+    n = torch.arange(max(0, p0 - w_cap), p0)
+    if len(n):
+        srow = swa.long()[:, n // 256] * 256 + (n % 256)[None, :]            # [B, len]
+        win[srow.reshape(-1).to(dev)] = st.window[:, n % w_cap].reshape(-1, D)
+    # rings: one block per sequence
+    def scatter_state(ring):
+        if ring is None:
+            return None
+        pool = torch.zeros((n_state,) + tuple(ring.shape[1:]), dtype=ring.dtype, device=dev)
+        pool[state.long().to(dev)] = ring
+        return pool
+    pst = LayerState(main_cache=main, idx_cache=idx_cache, idx_scale=idx_scale,
+                     main_ring=scatter_state(st.main_ring), idx_ring=scatter_state(st.idx_ring),
+                     window=win.reshape(n_swa, 256, D), e_cap=st.e_cap, main_scale=main_scale,
+                     idx_mx=idx_mx)
+    pages = Pages(table=table.to(dev), swa_table=swa.to(dev), state=state.to(dev), epb=epb,
+                  n_blocks=n_blocks, n_swa=n_swa, n_state=n_state)
+    return pst, pages
+
+
+def unpage_state(w: Workload, pst: LayerState, pages: Pages, like: LayerState):
+    """The dense view of a paged state (caches and rings; the window as the
+    tokens of positions [lo, hi) is separate: unpage_window)."""
+    B = like.main_cache.shape[0]
+    epb, e_cap = pages.epb, like.e_cap
+    nbps = pages.table.shape[1]
+    rows = (pages.table.long()[:, :, None] * epb +
+            torch.arange(epb, device=pages.table.device)[None, None, :]).reshape(B, -1)[:, :e_cap]
+    out = {}
+    out["main_cache"] = pst.main_cache[rows]
+    if pst.main_scale is not None:
+        out["main_scale"] = pst.main_scale[rows]
+    if pst.idx_cache is not None:
+        if like.idx_cache.dtype == torch.uint8 and w.Di == 128:
+            bpe = pst.idx_cache.shape[-1]
+            blocks = pst.idx_cache.reshape(pages.n_blocks, epb, bpe)[pages.table.long()]
+            Ep = like.idx_cache.shape[1]
+            out["idx_cache"] = blocks.reshape(B, nbps * epb, bpe)[:, :Ep]
+        else:
+            out["idx_cache"] = pst.idx_cache[rows]
+        if pst.idx_scale is not None:
+            out["idx_scale"] = pst.idx_scale[rows]
+        if pst.idx_mx is not None:
+            out["idx_mx"] = pst.idx_mx[rows]
+    out["main_ring"] = pst.main_ring[pages.state.long()]
+    if pst.idx_ring is not None:
+        out["idx_ring"] = pst.idx_ring[pages.state.long()]
+    return out
+
+
+def unpage_window(pst: LayerState, pages: Pages, lo, hi):
+    """Window tokens of positions lo .. hi-1 of every sequence [B, hi-lo, D]."""
+    n = torch.arange(lo, hi, device=pages.swa_table.device)
+    r = pages.swa_table.long()[:, n // 256] * 256 + (n % 256)[None, :]
+    D = pst.window.shape[-1]
+    return pst.window.reshape(-1, D)[r]
+
+
+def dense_window(st: LayerState, lo, hi):
+    n = torch.arange(lo, hi, device=st.window.device)
+    return st.window[:, n % st.window.shape[1]]

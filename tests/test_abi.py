@@ -251,3 +251,62 @@ def test_layer_decode_noalloc_refuses_steps_beyond_its_scratch():
     with pytest.raises(_lib.DsaError) as e:
         _lib._check(_lib._lib.dsa_layer_decode_noalloc(ctypes.byref(bad), None))
     assert e.value.code == -1
+
+
+def _paging(**kw):
+    p = _lib.Paging()
+    p.block_table, p.swa_block_table, p.state_block = _fake(1 << 20), _fake(2 << 20), _fake(3 << 20)
+    p.blocks_per_seq, p.entries_per_block = 16, 64
+    p.n_blocks, p.n_swa_blocks, p.n_state_blocks = 40, 40, 3
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), -3),                                   # valid: only the workspace is missing
+    (dict(entries_per_block=48), -1),               # not a power of two
+    (dict(entries_per_block=32), -1),               # 32 * stride 4 != 256 positions
+    (dict(blocks_per_seq=15), -1),                  # 15 * 64 < e_cap 1024; window < 4096
+    (dict(n_blocks=0), -1),
+    (dict(n_swa_blocks=0), -1),
+    (dict(n_state_blocks=0), -1),
+    (dict(blocks_per_seq=0), -1),
+])
+def test_layer_paging_validation(kw, code):
+    """dsa_paging: entries_per_block a power of two equal to 256 / stride,
+    the tables long enough for e_cap entries and max_pos_end positions, and
+    non-empty pools; a valid paging passes (the call then asks for its
+    workspace)."""
+    a = _layer_args(paging=_paging(**kw), w_cap=0)
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_layer_decode(ctypes.byref(a), None, 0, None))
+    assert e.value.code == code, str(e.value)
+
+
+def test_paging_key_tiles_need_whole_tiles_per_block():
+    """Indexer keys in 16-entry tiles cannot be paged in blocks of fewer than
+    16 entries (stride 32 -> 8 entries per block): unsupported."""
+    a = _index_args(stride=32, span=32, max_pos_end=4096, e_cap=128,
+                    paging=_paging(entries_per_block=8, blocks_per_seq=16))
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_index_topk(ctypes.byref(a), None, 0, None))
+    assert e.value.code == -2, str(e.value)
+    # the same keys in f32 rows page fine (validation passes)
+    a = _index_args(stride=32, span=32, max_pos_end=4096, e_cap=128, dtype=_lib.DSA_F32,
+                    k_scale=None, paging=_paging(entries_per_block=8, blocks_per_seq=16))
+    assert _lib.index_topk_workspace(a) > 0
+
+
+def test_attention_window_table_replaces_w_cap():
+    """A window table stands in for the ring (w_cap unused): without one,
+    w_cap = 0 is refused."""
+    a = _attn_args(w_cap=0, n_seqs=16, k=512)
+    assert _lib.sparse_attn_workspace(a) == 0
+    p = _paging(block_table=None, state_block=None)
+    a = _attn_args(w_cap=0, n_seqs=16, k=512, paging=p)
+    need = _lib.sparse_attn_workspace(a)
+    assert need > 0
+    with pytest.raises(_lib.DsaError) as e:
+        _lib._check(_lib._lib.dsa_sparse_attn(ctypes.byref(a), None, 0, None))
+    assert e.value.code == -3

@@ -127,8 +127,10 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False, q_norm=False):
     if q_norm:  # a Q-norm weight around 1
         g = torch.Generator(device="cpu").manual_seed(5)
         qg = (1.0 + 0.5 * torch.randn(w.D, generator=g)).to(dev)
-    args = [Ly.layer_args(w, st, ch, *o, max_pos_end=st.e_cap * w.s, out_scale=sc, q_norm_gamma=qg)
-            for (st, ch), o, sc in zip(sets, outs, scs)]
+    # a set is (state, chunk) or, paged, (pool state, chunk, block tables)
+    args = [Ly.layer_args(w, s[0], s[1], *o, max_pos_end=s[0].e_cap * w.s, out_scale=sc,
+                          q_norm_gamma=qg, pages=s[2] if len(s) > 2 else None)
+            for s, o, sc in zip(sets, outs, scs)]
     ws_bytes = max(_lib.layer_workspace(a) for a in args)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     fn = _lib.layer_decode if decode else _lib.layer_prefill
@@ -417,6 +419,21 @@ def main():
         msg = time_layer_graph(w, sets, args.steps, args.warmup)
         extra[w.name + "_graph_replay"] = {"queries_per_s": w.B / (msg / 1e3), "ms_per_step": msg,
                                            "batch": w.B, "context": w.L, "k": w.k}
+        # the same step over paged caches (256-position logical blocks, the
+        # blocks scattered over the pools in a seeded random order)
+        print("[bench] timing over paged caches", file=sys.stderr, flush=True)
+        from sparse_long_context_c4a_amd import layer as Ly
+        sets_p = []
+        for i, (st, ch) in enumerate(sets):
+            pst, pages = Ly.page_state(w, st, w.m, seed=i)
+            sets_p.append((pst, ch, pages))
+        msp, idxp, attnp = time_layer(w, sets_p, args.steps, args.warmup, decode=True)
+        del sets_p
+        torch.cuda.empty_cache()
+        extra[w.name + "_paged"] = {
+            "queries_per_s": w.B / (msp / 1e3), "ms_per_step": msp, "batch": w.B,
+            "context": w.L, "k": w.k, "entries_per_block": 256 // w.s,
+            "kernel_ms": {"indexer": idxp, "attention": attnp}}
         # the same step over a token-wise fp8 main cache (decode prologue
         # unfused, the attention reading fp8 entries)
         print("[bench] timing over an fp8 main cache", file=sys.stderr, flush=True)

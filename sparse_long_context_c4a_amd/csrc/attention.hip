@@ -78,6 +78,23 @@ __device__ __forceinline__ const T* slot_ptr(const AttnGeom& g, int row, int b, 
   return window + win_row(g, b, n) * g.D;
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes n, n + 16, n + 32,
+// n + 48, every lane getting the result) with the gfx950 lane swaps:
+// permlane16_swap(x, x) gives rows (r0, r0, r2, r2) and (r1, r1, r3, r3),
+// permlane32_swap(x, x) the two halves; no LDS round trip.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Largest value of x over the workgroup's NT threads (every thread calls it
 // once; red holds one float per wave).
 template <int NT>
@@ -519,8 +536,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
     float tmax = x[0];
 #pragma unroll
     for (int i = 1; i < 4 * kNB; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = rows_max(tmax);
     if (__any(tmax > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, tmax);
       const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -535,8 +551,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
       p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
       psum += p[i];
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = rows_sum(psum);
     l_run += psum;
     // O^T += V^T P^T over this wave's dims, 32 vectors per product: P of
     // blocks 2 u and 2 u + 1 is the B operand
@@ -945,8 +960,7 @@ __device__ __forceinline__ void decode_attn_run(
       float tmax = x[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = rows_max(tmax);
       if (__any(tmax > m_run + kLazy)) {
         const float m_new = fmaxf(m_run, tmax);
         const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -961,8 +975,7 @@ __device__ __forceinline__ void decode_attn_run(
         p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
         psum += p[i];
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = rows_sum(psum);
       l_run += psum;
       if constexpr (kFp8)
 #pragma unroll

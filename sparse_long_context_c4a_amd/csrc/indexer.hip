@@ -365,12 +365,14 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     keep_largest_small(tmp_s, static_cast<int>(at), need, out_bin);
   } else if (fits) {
     const uint64_t cut = kth_largest_composite(tmp_s, static_cast<int>(at), need,
-                                               [](uint64_t) { return true; });
+                                               [](uint64_t) { return true; }, lo + (B << shift),
+                                               shift);
     for (int i = t; i < static_cast<int>(at); i += kSel)
       if (tmp_s[i] >= cut) out_bin(tmp_s[i]);
   } else {
     const uint64_t cut = kth_largest_composite(cand_s, kFinalCap, need,
-                                               [](uint64_t x) { return x != 0; });
+                                               [](uint64_t x) { return x != 0; },
+                                               lo + (B << shift), shift);
     for (int i = t; i < kFinalCap; i += kSel)
       if (cand_s[i] != 0 && cand_s[i] >= cut) out_bin(cand_s[i]);
   }

@@ -131,20 +131,33 @@ __device__ void keep_largest_small(const uint64_t* v, int n, uint32_t need, F f)
 
 // Exact selection of the `need` largest of n distinct composites c[] (LDS)
 // by radix passes of 8 bits, for the rare large tie groups; returns the
-// smallest kept composite.  pred() filters which elements take part.
+// smallest kept composite.  pred() filters which elements take part.  When
+// every taking part has its key in [base_key, base_key + 2^key_bits) (one
+// histogram bin), the passes run over the key's offset from base_key and
+// then the index, so that no pass is spent on key bits the bin already
+// fixes.
 template <int NT = kSel, typename P>
-__device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t need, P pred) {
+__device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t need, P pred,
+                                          uint32_t base_key = 0u, int key_bits = 32) {
   static_assert(NT >= 256, "one thread per digit");
   __shared__ uint32_t cnt[256];
   __shared__ uint32_t res[3];
   const int t = threadIdx.x;
+  // offset form: (key - base_key) above the 32 index bits (order-preserving
+  // within the bin)
+  auto off = [=](uint64_t v) {
+    return (static_cast<uint64_t>(static_cast<uint32_t>(v >> 32) - base_key) << 32) |
+           (v & 0xffffffffull);
+  };
   uint64_t prefix = 0, mask = 0;
-  for (int sh = 56; sh >= 0; sh -= 8) {
+  for (int sh = ((key_bits + 32 + 7) / 8 - 1) * 8; sh >= 0; sh -= 8) {
     if (t < 256) cnt[t] = 0;
     __syncthreads();
     for (int i = t; i < n; i += NT) {
       const uint64_t v = c[i];
-      if (pred(v) && (v & mask) == prefix) atomicAdd(&cnt[(v >> sh) & 255u], 1u);
+      if (!pred(v)) continue;
+      const uint64_t o = off(v);
+      if ((o & mask) == prefix) atomicAdd(&cnt[(o >> sh) & 255u], 1u);
     }
     __syncthreads();
     // digit d: count(digits > d) < need <= count(digits >= d); thread t < 256
@@ -165,7 +178,8 @@ __device__ uint64_t kth_largest_composite(const uint64_t* c, int n, uint32_t nee
     need -= above;
     if (at == need) break;  // every composite with this prefix is kept
   }
-  return prefix;
+  return (static_cast<uint64_t>(static_cast<uint32_t>(prefix >> 32) + base_key) << 32) |
+         (prefix & 0xffffffffull);
 }
 
 // Rows with n_vis <= k: every visible entry, in index order, then padding.
@@ -261,7 +275,8 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
     keep_largest_small(tmp, static_cast<int>(at), need, out_bin);
   } else if (fits) {
     const uint64_t cut = kth_largest_composite<NT>(tmp, static_cast<int>(at), need,
-                                                   [](uint64_t) { return true; });
+                                                   [](uint64_t) { return true; },
+                                                   lo + (B << shift), shift);
     for (int i = t; i < static_cast<int>(at); i += NT)
       if (tmp[i] >= cut) out_bin(tmp[i]);
   } else {
@@ -272,7 +287,7 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
     auto in_bin = [=](uint64_t v) {
       return v != 0 && v >= bin_lo && (v < bin_hi || bin_hi == ~0ull);
     };
-    const uint64_t cut = kth_largest_composite<NT>(c, n, need, in_bin);
+    const uint64_t cut = kth_largest_composite<NT>(c, n, need, in_bin, lo + (B << shift), shift);
     for (int i = t; i < n; i += NT)
       if (in_bin(c[i]) && c[i] >= cut) out_bin(c[i]);
   }
@@ -365,7 +380,8 @@ __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_
       keep_largest_small(cand_s, static_cast<int>(at), need, out_bin);
     } else {
       const uint64_t cut = kth_largest_composite<NT>(cand_s, static_cast<int>(at), need,
-                                                     [](uint64_t) { return true; });
+                                                     [](uint64_t) { return true; },
+                                                     lo + (thr << shift), shift);
       for (int i = t; i < static_cast<int>(at); i += NT)
         if (cand_s[i] >= cut) out_bin(cand_s[i]);
     }

@@ -50,6 +50,17 @@ struct AttnGeom {
   PageMap ent, swa;          // paged cache entries and window tokens (tables nullptr: dense)
 };
 
+// Holds each value in scalar registers at this point, so that the loads of
+// kernel arguments feeding them are issued together.
+template <typename T>
+__device__ __forceinline__ void pin_scalar(const T& v) {
+  asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void pin_scalars(const T&... v) {
+  (pin_scalar(v), ...);
+}
+
 // Row of cache entry j (0 <= j < e_cap) of sequence b, and of window token n.
 __device__ __forceinline__ int64_t cache_row(const AttnGeom& g, int b, int64_t j) {
   return entry_row(g.ent, b, j, g.e_cap, g.status);
@@ -413,6 +424,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
   __shared__ int valid_s[kT8];
   __shared__ int32_t idx_s[kMRunSlots];
   __shared__ v4f spart[8][kT8 / 16][64];  // each wave's partial logits
+  pin_scalars(g.q_pos, g.Tq, g.H, g.r, g.off, g.idx, g.k, g.e_cap, g.W, g.chunk_pos0, g.chunk_len,
+              g.scale, g.max_pos_end, g.slots_per_run, g.n_runs, g.ent.table, g.swa.table, q,
+              cache, window, chunk_win);
   const int row = blockIdx.y, hq = blockIdx.x, run = blockIdx.z;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4, hgw = wave & 3, dh = wave >> 2;
@@ -499,19 +513,20 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
       *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 8 + sc) * 16) = pre[j];
     if (sc == 0) valid_s[se] = valid_next;
     __syncthreads();
-    if (a0 + kT8 < a_end) {  // prefetch the next tile while this one computes
-      const uint16_t* src = src_of(a0 + kT8 + se);
-      valid_next = src != nullptr;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        pre[j] = src ? reinterpret_cast<const uint4*>(src)[j * 8 + sc] : uint4{0u, 0u, 0u, 0u};
-    }
+    // the next tile's gather goes out while this one computes, one load per
+    // step of the logits products: issued together, the eight waves' loads
+    // queue at the texture unit (64 bytes a cycle) and hold up the products
+    const bool pf = a0 + kT8 < a_end;
+    const uint16_t* nsrc = pf ? src_of(a0 + kT8 + se) : nullptr;
+    if (pf) valid_next = nsrc != nullptr;
     // partial S^T over this wave's dims: block i holds vectors 16 i .. +15
     v4f sv[kNB];
 #pragma unroll
     for (int i = 0; i < kNB; ++i) sv[i] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
+      if (pf)
+        pre[cc] = nsrc ? reinterpret_cast<const uint4*>(nsrc)[cc * 8 + sc] : uint4{0u, 0u, 0u, 0u};
       const int off = (32 * (8 * dh + cc) + 8 * gq) * 2;
 #pragma unroll
       for (int i = 0; i < kNB; ++i) {
@@ -1083,6 +1098,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_decode(
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_acc,
     float* __restrict__ part_ml, float* __restrict__ cs_out) {
   __shared__ __attribute__((aligned(16))) DecSmem<NW> sm;
+  // the fields the set-up reads, loaded in one batch: left to itself the
+  // compiler spreads these kernel-argument loads over a chain of dependent
+  // waits ahead of the first index load
+  pin_scalars(g.q_pos, g.Tq, g.H, g.r, g.off, g.idx, g.k, g.e_cap, g.w_cap, g.W, g.chunk_pos0,
+              g.chunk_len, g.scale, g.max_pos_end, g.slots_per_run, g.n_runs, g.cs_tab, g.rows,
+              g.ent.table, g.swa.table, g.cache_scale, q, cache, window, chunk_win);
   const int G = g.H / kDH;
   const int id = blockIdx.x;
   const int pair = 8 * (id / (8 * G)) + (id & 7), hg = (id >> 3) % G;

@@ -450,9 +450,10 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
   // query head h as the B operand, this wave's dim half: chunks c = 8 dh +
   // cc, dims 32 c + 8 gq + (0..7)
   const int h = hq * 64 + hgw * 16 + n;
+  const uint16_t* qrow0 = q + (static_cast<int64_t>(row) * g.H + h) * kMD;
   v8bf qb[8];
   {
-    const uint16_t* qrow = q + (static_cast<int64_t>(row) * g.H + h) * kMD;
+    const uint16_t* qrow = qrow0;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const int d0 = 32 * (8 * dh + cc) + 8 * gq;
@@ -512,27 +513,45 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4*>(v_lds + se * kMPitch + (j * 8 + sc) * 16) = pre[j];
     if (sc == 0) valid_s[se] = valid_next;
-    __syncthreads();
     // the next tile's gather goes out while this one computes, one load per
     // step of the logits products: issued together, the eight waves' loads
-    // queue at the texture unit (64 bytes a cycle) and hold up the products
+    // queue at the texture unit (64 bytes a cycle) and hold up the products.
+    // Its sources are found while the barrier waits (idx_s is not written
+    // again).
+    // (after the last tile the loads read the query row and are dropped)
     const bool pf = a0 + kT8 < a_end;
     const uint16_t* nsrc = pf ? src_of(a0 + kT8 + se) : nullptr;
     if (pf) valid_next = nsrc != nullptr;
+    const uint4* lsrc = reinterpret_cast<const uint4*>(nsrc ? nsrc : qrow0);
+    __syncthreads();
     // partial S^T over this wave's dims: block i holds vectors 16 i .. +15
     v4f sv[kNB];
 #pragma unroll
     for (int i = 0; i < kNB; ++i) sv[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    v8bf kv[8][kNB];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      if (pf)
-        pre[cc] = nsrc ? reinterpret_cast<const uint4*>(nsrc)[cc * 8 + sc] : uint4{0u, 0u, 0u, 0u};
       const int off = (32 * (8 * dh + cc) + 8 * gq) * 2;
 #pragma unroll
-      for (int i = 0; i < kNB; ++i) {
-        const v8bf kv = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 * i + n) * kMPitch + off));
-        sv[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[cc], sv[i], 0, 0, 0);
-      }
+      for (int i = 0; i < kNB; ++i)
+        kv[cc][i] = as_v8bf(*reinterpret_cast<const uint4*>(v_lds + (16 * i + n) * kMPitch + off));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const uint4 t = lsrc[cc * 8 + sc];
+      pre[cc] = nsrc ? t : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        sv[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[cc][i], qb[cc], sv[i], 0, 0, 0);
+    }
+    // issue order: the K fragments two steps ahead of their products, one
+    // gather load per step
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNB, 0);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+      if (cc < 6) __builtin_amdgcn_sched_group_barrier(0x100, kNB, 0);
     }
 #pragma unroll
     for (int i = 0; i < kNB; ++i) spart[wave][i][lane] = sv[i];
@@ -579,12 +598,23 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
       lds_u8* lds_base = (lds_u8*)v_lds;
       lds_u8* r_lo = lds_base + (32 * u + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
       lds_u8* r_hi = lds_base + (32 * u + 16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
+      v4s lo[16], hi[16];
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
-        const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
+        hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
+      }
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+      }
+      // issue order: the V^T fragments four products ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (db < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
   }

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     uint32_t* status) {
   __shared__ uint64_t cand_s[kFinalCap + 256 * kMaxF];
   __shared__ uint64_t tmp_s[kTmpCap];
-  __shared__ uint32_t h_s[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h_s[kBins];
   __shared__ uint32_t red[3][kSelWaves];
   __shared__ uint32_t pos_above, pos_bin, n_tmp;
   __shared__ uint16_t f_s[kMaxF];        // waves scored again in full
@@ -221,12 +221,9 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
       hi = max(hi, static_cast<uint32_t>(v[u] >> 32));
     }
   // one combined block reduction: max t_w, min and max candidate key
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    tm = max(tm, shfl_xor_u32(tm, o));
-    lo = min(lo, shfl_xor_u32(lo, o));
-    hi = max(hi, shfl_xor_u32(hi, o));
-  }
+  tm = wave_reduce_u32<0>(tm);
+  lo = wave_reduce_u32<1>(lo);
+  hi = wave_reduce_u32<0>(hi);
   if (l == 0) {
     red[0][w] = tm;
     red[1][w] = lo;
@@ -241,16 +238,16 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     lo = min(lo, red[1][i]);
     hi = max(hi, red[2][i]);
   }
-  // the histogram over the candidates' key range, and their count
+  // the histogram over the candidates' key range; its total is the number
+  // of candidates
   const int shift = range_shift(hi - lo, 11);
-  uint32_t c_n = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
-    if (v[u] != 0) {
-      atomicAdd(&h_s[(static_cast<uint32_t>(v[u] >> 32) - lo) >> shift], 1u);
-      ++c_n;
-    }
-  if (block_reduce_u32<2>(c_n) < static_cast<uint32_t>(k)) {  // barriers
+    if (v[u] != 0) atomicAdd(&h_s[(static_cast<uint32_t>(v[u] >> 32) - lo) >> shift], 1u);
+  __syncthreads();
+  uint32_t c_tot;
+  const Bin br = find_bin_wave<2048>(h_s, static_cast<uint32_t>(k), &c_tot);  // barrier
+  if (c_tot < static_cast<uint32_t>(k)) {
     // fewer candidates than k (ties at the wave thresholds): the whole row
     exact_row_operands<kFmt>(q, q_scale, hw, row, Hi, aq, wv);
     score_row_exact<kFmt>(aq, wv, src, nv, srow, kSelWaves);
@@ -258,8 +255,6 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     row_select_from_scores(srow, nv, k, irow, orow, cand_s, h_s);
     return;
   }
-  const uint32_t local[2] = {h_s[2047 - 2 * t], h_s[2046 - 2 * t]};
-  const Bin br = find_bin_desc<2>(local, 2047u, static_cast<uint32_t>(k));
   const uint32_t B = br.b, above = br.above, at = br.at;
   // The certificate: the k-th candidate lies in bin B, so its key is at
   // least kc = lo + B 2^shift.  An entry that is not a candidate has a key
@@ -343,8 +338,8 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     if (nu) pu = atomicAdd(&pos_above, nu);
     if (nm) pm = atomicAdd(&n_tmp, nm);
   }
-  pu = static_cast<uint32_t>(__shfl(static_cast<int>(pu), 0, 64));
-  pm = static_cast<uint32_t>(__shfl(static_cast<int>(pm), 0, 64));
+  pu = __builtin_amdgcn_readlane(pu, 0);
+  pm = __builtin_amdgcn_readlane(pm, 0);
   const uint64_t below = (1ull << l) - 1ull;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {

@@ -19,8 +19,46 @@ constexpr int kFinalCap = 8192;       // candidates resolved in LDS
 constexpr int kSel = 1024;
 constexpr int kSelWaves = kSel / 64;
 
-__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int o) {
-  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
+// Lane exchanges within a wave without an LDS round trip: DPP moves inside
+// each 16-lane row, the gfx950 row swaps across rows.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, kRowMask, 0xf, false));
+}
+
+template <int kOp>  // 0 max, 1 min, 2 sum
+__device__ __forceinline__ uint32_t op_u32(uint32_t a, uint32_t b) {
+  return kOp == 0 ? max(a, b) : kOp == 1 ? min(a, b) : a + b;
+}
+
+// Max / min / sum over the wave, every lane getting the result: partners
+// within quads (lane ^ 1, lane ^ 2), then the mirrored half-row and row
+// (which pair each quad, then each half, with the other), then the row
+// swaps.
+template <int kOp>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  v = op_u32<kOp>(v, dpp_u32<0xb1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op_u32<kOp>(v, dpp_u32<0x4e>(v));   // quad_perm [2, 3, 0, 1]
+  v = op_u32<kOp>(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = op_u32<kOp>(v, dpp_u32<0x140>(v));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op_u32<kOp>(a[0], a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op_u32<kOp>(c[0], c[1]);
+}
+
+// Inclusive prefix sum over the wave's lanes (in lane order): shifts by 1,
+// 2, 4 and 8 within each row, then the last lane of row 0 added to row 1
+// and of row 2 to row 3, then lane 31 added to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111>(x);  // row_shr:1 (lanes shifted in from outside the row read 0)
+  x += dpp_u32<0x112>(x);
+  x += dpp_u32<0x114>(x);
+  x += dpp_u32<0x118>(x);
+  x += dpp_u32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_u32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 // Block-wide max / min / sum over NT threads; every thread gets the result.
@@ -28,11 +66,7 @@ template <int kOp, int NT = kSel>  // 0 max, 1 min, 2 sum
 __device__ __forceinline__ uint32_t block_reduce_u32(uint32_t v) {
   __shared__ uint32_t wv[NT / 64];
   const int t = threadIdx.x;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t y = shfl_xor_u32(v, o);
-    v = kOp == 0 ? max(v, y) : kOp == 1 ? min(v, y) : v + y;
-  }
+  v = wave_reduce_u32<kOp>(v);
   if ((t & 63) == 0) wv[t >> 6] = v;
   __syncthreads();
   uint32_t r = wv[0];
@@ -47,12 +81,7 @@ template <int NT = kSel>
 __device__ __forceinline__ uint32_t block_prefix_excl(uint32_t v, uint32_t* total) {
   __shared__ uint32_t wsum[NT / 64];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(x), o, 64));
-    if (l >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (l == 63) wsum[w] = x;
   __syncthreads();
   uint32_t add = 0, tot = 0;
@@ -73,7 +102,7 @@ __device__ __forceinline__ uint32_t wave_alloc(bool cond, uint32_t* ctr) {
   const int l = threadIdx.x & 63;
   uint32_t base = 0;
   if (l == 0 && m) base = atomicAdd(ctr, static_cast<uint32_t>(__popcll(m)));
-  base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0, 64));
+  base = __builtin_amdgcn_readlane(base, 0);
   return base + static_cast<uint32_t>(__popcll(m & ((1ull << l) - 1ull)));
 }
 
@@ -113,6 +142,54 @@ __device__ __forceinline__ Bin find_bin_desc(const uint32_t (&local)[per], uint3
   const Bin r = res;
   __syncthreads();
   return r;
+}
+
+// The same search over NB bins held in LDS (bin i at h[i], searched from the
+// highest), done by the first wave alone: one barrier instead of the four of
+// a block-wide scan.  Also gives the total count; the result is meaningful
+// only when total >= need.  Every thread of the block must call it, once per
+// kernel (its result slot is not guarded against a second call).
+template <int NB>
+__device__ __forceinline__ Bin find_bin_wave(const uint32_t* h, uint32_t need, uint32_t* total) {
+  static_assert(NB % 256 == 0, "whole 16-byte reads per lane");
+  constexpr int kL = NB / 64;  // bins per lane
+  __shared__ Bin res;
+  __shared__ uint32_t tot;
+  const int t = threadIdx.x;
+  if (t < 64) {
+    // lane l: bins NB-1 - kL l down to NB - kL (l + 1), read upwards
+    uint32_t up[kL];
+    const uint4* src = reinterpret_cast<const uint4*>(h + (NB - kL * (t + 1)));
+#pragma unroll
+    for (int i = 0; i < kL / 4; ++i) {
+      const uint4 v = src[i];
+      up[4 * i] = v.x;
+      up[4 * i + 1] = v.y;
+      up[4 * i + 2] = v.z;
+      up[4 * i + 3] = v.w;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kL; ++i) sum += up[i];
+    const uint32_t x = wave_incl_scan(sum);
+    const uint32_t before = x - sum;
+    if (t == 63) tot = x;
+    // the lane whose range holds the bin, then the bin within it: lane i
+    // takes that range's i-th bin from the top, a second wave scan
+    const uint64_t hit = __ballot(before < need && x >= need);
+    if (hit != 0) {
+      const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      const uint32_t bL = __builtin_amdgcn_readlane(before, L);
+      const int bin = NB - 1 - (kL * L + (t < kL ? t : 0));
+      const uint32_t c = t < kL ? h[bin] : 0u;
+      const uint32_t y = wave_incl_scan(c);
+      if (t < kL && bL + y - c < need && bL + y >= need)
+        res = Bin{static_cast<uint32_t>(bin), bL + y - c, c};
+    }
+  }
+  __syncthreads();
+  *total = tot;
+  return res;
 }
 
 // Keep the `need` largest of the n distinct composites in v[] (LDS): each
@@ -255,8 +332,8 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
     if (nu) pu = atomicAdd(&pos_above, nu);
     if (nm) pm = atomicAdd(&n_tmp, nm);
   }
-  pu = static_cast<uint32_t>(__shfl(static_cast<int>(pu), 0, 64));
-  pm = static_cast<uint32_t>(__shfl(static_cast<int>(pm), 0, 64));
+  pu = __builtin_amdgcn_readlane(pu, 0);
+  pm = __builtin_amdgcn_readlane(pm, 0);
   for (int i0 = 0; i0 < n; i0 += NT) {
     bool up, mid;
     const uint64_t v = classify(i0 + t, &up, &mid);

@@ -50,17 +50,6 @@ struct AttnGeom {
   PageMap ent, swa;          // paged cache entries and window tokens (tables nullptr: dense)
 };
 
-// Holds each value in scalar registers at this point, so that the loads of
-// kernel arguments feeding them are issued together.
-template <typename T>
-__device__ __forceinline__ void pin_scalar(const T& v) {
-  asm volatile("" ::"s"(v));
-}
-template <typename... T>
-__device__ __forceinline__ void pin_scalars(const T&... v) {
-  (pin_scalar(v), ...);
-}
-
 // Row of cache entry j (0 <= j < e_cap) of sequence b, and of window token n.
 __device__ __forceinline__ int64_t cache_row(const AttnGeom& g, int b, int64_t j) {
   return entry_row(g.ent, b, j, g.e_cap, g.status);

@@ -273,4 +273,16 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return t;
 }
 
+// Holds each value in scalar registers at this point, so that the loads of
+// kernel arguments feeding them are issued together (left to itself the
+// compiler spreads them over a chain of dependent waits).
+template <typename T>
+__device__ __forceinline__ void pin_scalar(const T& v) {
+  asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void pin_scalars(const T&... v) {
+  (pin_scalar(v), ...);
+}
+
 }  // namespace dsa

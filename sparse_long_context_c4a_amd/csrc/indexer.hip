@@ -85,6 +85,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_index(
     int64_t ld_scores, uint64_t* __restrict__ cand, uint32_t* __restrict__ meta, int cap, int nb,
     PrologueArgs pa, uint32_t* status) {
   // the keys' paging is the layer's (the prologue's)
+  pin_scalars(q, q_scale, w, keys, k_scale, k_mx, q_pos, Hi, s, S, e_cap, nv_cap, max_pos_end,
+              scores, ld_scores, cand, meta, cap, nb, status, pa.B, pa.nq_roles, pa.pg.ent.table);
   const int rpr = kPrologueRoles + pa.nq_roles;  // prologue workgroups per sequence
   const int id = static_cast<int>(blockIdx.x), npro = pa.B * rpr;
   if (id < npro) {

@@ -283,42 +283,48 @@ __device__ __forceinline__ void index_stream_block(
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, bx == 0 && tid == 0);
-  const int64_t nv = ri.nv;
   const int64_t e_begin = static_cast<int64_t>(bx) * kEnt;
   constexpr int kGroups = kEnt / 4 / 16;            // 16-entry groups per wave
   constexpr int kSteps = kGroups / 2;               // two groups per step
   constexpr int kKeep = kGroups / 4;                // keys kept per lane
   const int64_t wbase = e_begin + wave * (kEnt / 4);
+  const KeySrc src = key_src<kFmt>(keys, k_scale, k_mx, pm, b, e_cap, status);
+  // key loads: a ring of two slots of two groups; unconditional (clamped to
+  // an entry that exists, masked later) so the compiler can count them.
+  // Dense keys: the first slot goes out before the row's visible count is
+  // known (clamped to the cache's capacity), so its latency overlaps that
+  // of the position load
+  typename K::Raw kr[2][2];
+  int64_t jmax = e_cap - 1;
+  int32_t gblk = 0;
+  auto load = [&](int slot, int gr) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t ent = min<int64_t>(wbase + (gr + u) * 16 + n, jmax);
+      int64_t rw = ent;
+      if constexpr (kPaged)
+        rw = (static_cast<int64_t>(__builtin_amdgcn_readlane(gblk, gr + u)) << pm.shift) |
+             (ent & ((int64_t{1} << pm.shift) - 1));
+      kr[slot][u] = K::load(src.kb, src.ksb, src.msb, rw, g);
+    }
+  };
+  const bool early = !kPaged && e_cap > 0;
+  if (early) load(0, 0);
+  const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, bx == 0 && tid == 0);
+  const int64_t nv = ri.nv;
   // each lane keeps the keys of groups 4i + 2 (g & 1) + (g >> 1), i < kKeep
   uint32_t kk[kKeep] = {};
   if (wbase < nv) {
-    const KeySrc src = key_src<kFmt>(keys, k_scale, k_mx, pm, b, e_cap, status);
-    // key loads: a ring of two slots of two groups; unconditional (clamped
-    // to a visible entry, masked later) so the compiler can count them, and
-    // the first slot issued before the query set-up
-    const int64_t jmax = nv - 1;
+    jmax = nv - 1;
     // paged: lane l < kGroups holds the block of the wave's group l (16
     // entries never straddle a block), read once per wave; each load takes
-    // its group's block id from that lane
-    int32_t gblk = 0;
+    // its group's block id from that lane (the table is read only for
+    // visible entries)
     if constexpr (kPaged)
       if (lane < kGroups)
         gblk = static_cast<int32_t>(
             paged_row(pm, b, min<int64_t>(wbase + lane * 16, jmax), status) >> pm.shift);
-    typename K::Raw kr[2][2];
-    auto load = [&](int slot, int gr) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t ent = min<int64_t>(wbase + (gr + u) * 16 + n, jmax);
-        int64_t rw = ent;
-        if constexpr (kPaged)
-          rw = (static_cast<int64_t>(__builtin_amdgcn_readlane(gblk, gr + u)) << pm.shift) |
-               (ent & ((int64_t{1} << pm.shift) - 1));
-        kr[slot][u] = K::load(src.kb, src.ksb, src.msb, rw, g);
-      }
-    };
-    load(0, 0);
+    if (!early) load(0, 0);
     v8bf aq[4];
     K::q_operands(n < Hi ? q + (static_cast<int64_t>(row) * Hi + n) * 128 : nullptr, g, aq);
     float wv[4];

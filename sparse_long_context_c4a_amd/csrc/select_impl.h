@@ -196,7 +196,7 @@ __device__ __forceinline__ Bin find_bin_wave(const uint32_t* h, uint32_t need, u
 // is kept iff fewer than `need` others exceed it.  For small n (one wave
 // compares every pair through LDS broadcasts); calls f(v) for the kept.
 template <typename F>
-__device__ void keep_largest_small(const uint64_t* v, int n, uint32_t need, F f) {
+__device__ __forceinline__ void keep_largest_small(const uint64_t* v, int n, uint32_t need, F f) {
   const int t = threadIdx.x;
   if (t < n) {
     const uint64_t x = v[t];

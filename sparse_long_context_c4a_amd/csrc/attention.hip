@@ -663,7 +663,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
 constexpr int kDH = 16;                       // heads per workgroup
 constexpr int kDStep = 32;                    // vectors per wave step
 constexpr int kDWaveBytes = kDStep * kMPitch; // 33,792 B of LDS per wave
-constexpr int kDOPitch = kMD + 4;             // floats per head row when merging waves
 // waves (32-slot steps) per workgroup: measured at the c4a decode B=4
 // workload, 4 (80 workgroups) beat 2 (160) and 1 (320, whose partials make
 // the combine four times longer)
@@ -829,11 +828,13 @@ __device__ __forceinline__ void store_head_dims4_fp8(float4 acc, float L, int d4
 // LDS of one run of the decode attention (NW waves).
 template <int NW>
 struct DecSmem {
-  uint8_t dsm[NW * kDWaveBytes];  // each wave's staged tile; the wave merge after
+  uint8_t dsm[NW * kDWaveBytes];  // each wave's staged tile of 32 vectors
   uint8_t q_s[kDH * kMPitch];     // rotated q, head n at row n
   float cs_s[kMD];                // (cos, sin) of pair i at 2i, 2i+1
-  float ml_s[NW][kDH][2];
-  float hml_s[kDH][2];
+  v8bf p_s[NW][64];               // each wave's probabilities, as the PV B operand
+  float mx_s[NW][kDH];            // each wave's step max per head (log2 units)
+  float ps_s[NW][kDH];            // each wave's step sum per head
+  int vm_s[NW];                   // whether the wave staged a vector this step
 };
 
 // Slot sources of a run (slots numbered 0 .. count()-1): index(a) gives the
@@ -858,22 +859,24 @@ struct RunSlots {
 };
 
 // One run of the decode attention (NW waves of a workgroup, 16 heads hg of
-// row `row`): the run's slots in steps of NW x 32 vectors, each wave its 32,
-// then the wave merge; the run's partial (or, with g.direct, the final
-// rotated output) goes out.
+// row `row`): the run's slots in steps of NW x 32 vectors.  In a step wave w
+// stages and scores its own 32 vectors; the waves agree on each head's
+// running max and share their probabilities through LDS; then wave w
+// accumulates dims 128 w .. +127 over all the step's vectors, so the run
+// ends with no merge of the waves.  The run's partial (or, with g.direct,
+// the final rotated output) goes out from registers.
 template <int NW, bool kFp8, typename Src>
 __device__ __forceinline__ void decode_attn_run(
     const AttnGeom& g, int row, int hg, int run, const Src& src, const uint16_t* __restrict__ q,
     int rotate_q, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_acc, float* __restrict__ part_ml, float* __restrict__ cs_out,
     DecSmem<NW>& sm) {
+  static_assert(NW * 128 == kMD, "each wave accumulates a quarter of the dims");
   constexpr int NT = NW * 64, kSlotsPerIter = NW * kDStep;
   constexpr int kQPer = kDH * 64 / NT;  // 16-byte pieces of the query tile per thread
   uint8_t* dsm = sm.dsm;
   uint8_t* q_s = sm.q_s;
   float* cs_s = sm.cs_s;
-  auto& ml_s = sm.ml_s;
-  auto& hml_s = sm.hml_s;
   const int G = g.H / kDH;
   const int b = row / g.Tq, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
@@ -948,19 +951,29 @@ __device__ __forceinline__ void decode_attn_run(
     *reinterpret_cast<uint4*>(q_s + (c >> 6) * kMPitch + 2 * d0) = raw;
   }
   __syncthreads();
-  v4f o[32];
+  v4f o[8];  // O^T[dims 128 wave + 16 db + 4 gq + i][head n]
 #pragma unroll
-  for (int db = 0; db < 32; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 8; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float scale2 = g.scale * kLog2e;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const int te = (lane & 15) >> 2, tq = lane & 3;
-  // one step: the staged vectors to the wave's tile, logits, online softmax,
-  // weighted sum
+  // one step (every wave of the workgroup, barriers inside): the wave's
+  // staged vectors to its tile and their logits; the step's max per head
+  // agreed through LDS (raised lazily: the weights exp2(x - m_run) may reach
+  // 2^kLazy before the accumulators are rescaled); the probabilities shared
+  // through LDS; then this wave's dims over every tile of the step
   auto step = [&](const u32x4 (&stg)[kDStep], uint64_t vmask, bool st8, float sig) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = -INFINITY;
+    // the scale of this lane's vector i (4 gq + i, then 16 + 4 gq + i)
+    auto sgi = [&](int i) -> float {
+      if constexpr (kFp8) return __shfl(sig, (i < 4 ? 4 * gq + i : 12 + 4 * gq + i), 64);
+      return 1.f;
+    };
     if (vmask != 0) {
-      // each wave reads only its own tile, so no barrier: LDS operations of
-      // one wave complete in order
+      // (a tile's empty slots hold the stand-in vector: finite, weight 0)
       if (kFp8 && st8)
         gather_store8(stg, lane, wl, vmask);
       else
@@ -975,52 +988,62 @@ __device__ __forceinline__ void decode_attn_run(
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb, s1, 0, 0, 0);
       }
-      // log2 units; the running max is raised lazily: the weights
-    // exp2(x - m_run) may reach 2^kLazy before the accumulators are rescaled,
-    // so most tiles need no rescale
-      // the scale of this lane's vector i (4 gq + i, then 16 + 4 gq + i)
-      auto sgi = [&](int i) -> float {
-        if constexpr (kFp8) return __shfl(sig, (i < 4 ? 4 * gq + i : 12 + 4 * gq + i), 64);
-        return 1.f;
-      };
-      // (the lane exchanges run on every lane: outside the selects below)
-      float x[8];
+      // log2 units (the lane exchanges run on every lane: outside the
+      // selects below)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float sa = sgi(i) * scale2, sb = sgi(4 + i) * scale2;
         x[i] = ((vmask >> (4 * gq + i)) & 1) ? s0[i] * sa : -INFINITY;
         x[4 + i] = ((vmask >> (16 + 4 * gq + i)) & 1) ? s1[i] * sb : -INFINITY;
       }
-      float tmax = x[0];
+    }
+    float tmax = x[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-      tmax = rows_max(tmax);
-      if (__any(tmax > m_run + kLazy)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= corr;
-        m_run = m_new;
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = rows_max(tmax);
+    if (gq == 0) sm.mx_s[wave][n] = tmax;
+    if (lane == 0) sm.vm_s[wave] = vmask != 0;
+    __syncthreads();  // tiles staged, maxima out
+    float ms = sm.mx_s[0][n];
 #pragma unroll
-        for (int db = 0; db < 32; ++db) o[db] *= corr;
-      }
-      float p[8], psum = 0.f;
+    for (int w = 1; w < NW; ++w) ms = fmaxf(ms, sm.mx_s[w][n]);
+    // (the same values in every wave, so the same decision)
+    if (ms > m_run + kLazy) {
+      const float m_new = fmaxf(m_run, ms);
+      const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+      m_run = m_new;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
-        psum += p[i];
-      }
-      psum = rows_sum(psum);
-      l_run += psum;
-      if constexpr (kFp8)
+      for (int db = 0; db < 8; ++db) o[db] *= corr;
+    }
+    float p[8], psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] *= sgi(i);  // the weighted sum of code vectors
-      const v8bf pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
-                       static_cast<__bf16>(p[3]), static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
-                       static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
-      lds_u8* r_lo = (lds_u8*)wl + (4 * gq + te) * kMPitch + tq * 8;
-      lds_u8* r_hi = (lds_u8*)wl + (16 + 4 * gq + te) * kMPitch + tq * 8;
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_run);
+      psum += p[i];
+    }
+    psum = rows_sum(psum);
+    if (gq == 0) sm.ps_s[wave][n] = psum;
+    if constexpr (kFp8)
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
+      for (int i = 0; i < 8; ++i) p[i] *= sgi(i);  // the weighted sum of code vectors
+    sm.p_s[wave][lane] = v8bf{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                              static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3]),
+                              static_cast<__bf16>(p[4]), static_cast<__bf16>(p[5]),
+                              static_cast<__bf16>(p[6]), static_cast<__bf16>(p[7])};
+    __syncthreads();  // probabilities and sums out
+#pragma unroll
+    for (int w = 0; w < NW; ++w) l_run += sm.ps_s[w][n];
+    // O^T += V^T P^T over this wave's dims, one 32-vector product per tile
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (!sm.vm_s[w]) continue;  // (uniform)
+      const v8bf pb = sm.p_s[w][lane];
+      lds_u8* tile = (lds_u8*)(dsm + w * kDWaveBytes) + wave * 256;
+      lds_u8* r_lo = tile + (4 * gq + te) * kMPitch + tq * 8;
+      lds_u8* r_hi = tile + (16 + 4 * gq + te) * kMPitch + tq * 8;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
         const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1028,11 +1051,15 @@ __device__ __forceinline__ void decode_attn_run(
       }
     }
   };
-  if (a0 < a_end) {
+  // the same number of steps in every wave (a wave past the run's end
+  // stages nothing)
+  const int nsteps = (a_end + kSlotsPerIter - 1) / kSlotsPerIter;
+  if (nsteps > 0) {
     // next step's cache indices in flight during this step
     jn = (a0 + kSlotsPerIter < a_end && lane < kDStep) ? src.index(a0 + kSlotsPerIter + lane) : -1;
     step(stg0, vmask0, src.is_cache(a0), sig0);
-    for (a0 += kSlotsPerIter; a0 < a_end; a0 += kSlotsPerIter) {
+    for (int st = 1; st < nsteps; ++st) {
+      a0 += kSlotsPerIter;
       u32x4 stg[kDStep];
       const uint16_t* sp = (ok && a0 + lane < a_end && lane < kDStep)
                                ? src.template ptr<kFp8>(a0 + lane, jn)
@@ -1043,69 +1070,31 @@ __device__ __forceinline__ void decode_attn_run(
                                  : gather_load(sp, dummy, lane, stg);
       const int nxt = a0 + kSlotsPerIter;
       jn = (nxt < a_end && lane < kDStep) ? src.index(nxt + lane) : -1;
+      __syncthreads();  // every wave done with the previous step's tiles
       step(stg, vmask, st8, sig);
     }
   }
-  // merge the NW waves (natural-log units from here on): lane holds
-  // O^T[dims 16 db + 4 gq + i][head n]
-  m_run *= kLn2;
-  if (gq == 0) {
-    ml_s[wave][n][0] = m_run;
-    ml_s[wave][n][1] = l_run;
-  }
-  __syncthreads();
-  if (tid < kDH) {  // per head: the block's max and sum over its waves
-    float M = -INFINITY, L = 0.f;
+  // lane holds O^T[dims 128 wave + 16 db + 4 gq + i][head n]; m_run (log2
+  // units) and l_run are the run's max and sum for head n
+  const float M = m_run * kLn2, L = l_run;
+  const int hh = hg * kDH + n;
+  if (g.direct) {
+    uint16_t* orow = out + (static_cast<int64_t>(row) * g.H + hh) * kMD;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_s[w][tid][0]);
+    for (int db = 0; db < 8; ++db)
+      store_head_dims4(float4{o[db][0], o[db][1], o[db][2], o[db][3]}, L, 32 * wave + 4 * db + gq,
+                       rot0, cs_s, orow);
+    if (lse && wave == 0 && gq == 0)
+      lse[static_cast<int64_t>(row) * g.H + hh] = L > 0.f ? M + logf(L) : -INFINITY;
+  } else {
+    const int64_t pi = ((static_cast<int64_t>(row) * G + hg) * g.n_runs + run) * kDH + n;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = ml_s[w][tid][0];
-      if (mw != -INFINITY) L += ml_s[w][tid][1] * expf(mw - M);
-    }
-    hml_s[tid][0] = M;
-    hml_s[tid][1] = L;
-  }
-  {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_s[w][n][0]);
-    const float cw = (m_run == -INFINITY) ? 0.f : expf(m_run - M);
-    float* ow = reinterpret_cast<float*>(wl);
-#pragma unroll
-    for (int db = 0; db < 32; ++db)
-      *reinterpret_cast<float4*>(ow + n * kDOPitch + 16 * db + 4 * gq) =
-          float4{o[db][0] * cw, o[db][1] * cw, o[db][2] * cw, o[db][3] * cw};
-  }
-  __syncthreads();
-  // thread -> dims 4 d4 .. +3 of heads ch = (tid + NT i) / 128
-  const int64_t pbase = (static_cast<int64_t>(row) * G + hg) * g.n_runs + run;
-#pragma unroll 2
-  for (int it = tid; it < 128 * kDH; it += NT) {
-    const int d4 = it & 127, ch = it >> 7;
-    const float M = hml_s[ch][0], L = hml_s[ch][1];
-    float4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float4 u = *reinterpret_cast<const float4*>(
-          reinterpret_cast<const float*>(dsm + w * kDWaveBytes) + ch * kDOPitch + 4 * d4);
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-    }
-    const int hh = hg * kDH + ch;
-    if (g.direct) {
-      store_head_dims4(t, L, d4, rot0, cs_s, out + (static_cast<int64_t>(row) * g.H + hh) * kMD);
-      if (lse && d4 == 0)
-        lse[static_cast<int64_t>(row) * g.H + hh] = L > 0.f ? M + logf(L) : -INFINITY;
-    } else {
-      const int64_t pi = pbase * kDH + ch;
-      reinterpret_cast<float4*>(part_acc + pi * kMD)[d4] = t;
-      if (d4 == 0) {
-        part_ml[2 * pi] = M;
-        part_ml[2 * pi + 1] = L;
-      }
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<float4*>(part_acc + pi * kMD + 128 * wave + 16 * db + 4 * gq) =
+          float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+    if (wave == 0 && gq == 0) {
+      part_ml[2 * pi] = M;
+      part_ml[2 * pi + 1] = L;
     }
   }
 }

@@ -664,8 +664,10 @@ constexpr int kDH = 16;                       // heads per workgroup
 constexpr int kDStep = 32;                    // vectors per wave step
 constexpr int kDWaveBytes = kDStep * kMPitch; // 33,792 B of LDS per wave
 // waves (32-slot steps) per workgroup: measured at the c4a decode B=4
-// workload, 4 (80 workgroups) beat 2 (160) and 1 (320, whose partials make
-// the combine four times longer)
+// workload, 4 (80 workgroups, each wave 128 of the dims) and 2 (160, 256
+// dims each) give the same step time; longer runs (fewer workgroups) are
+// slower: 5 runs of 128 slots 51.8 us per step, 3 of 256 54.8, 2 59.3, 1
+// 64.8
 constexpr int kDecWaves = 4;
 
 // Source of slot a of row `row` given its cache index j (read by the caller
@@ -862,8 +864,8 @@ struct RunSlots {
 // row `row`): the run's slots in steps of NW x 32 vectors.  In a step wave w
 // stages and scores its own 32 vectors; the waves agree on each head's
 // running max and share their probabilities through LDS; then wave w
-// accumulates dims 128 w .. +127 over all the step's vectors, so the run
-// ends with no merge of the waves.  The run's partial (or, with g.direct,
+// accumulates dims kWD w .. +kWD-1 (kWD = 512 / NW) over all the step's
+// vectors, so the run ends with no merge of the waves.  The run's partial (or, with g.direct,
 // the final rotated output) goes out from registers.
 template <int NW, bool kFp8, typename Src>
 __device__ __forceinline__ void decode_attn_run(
@@ -871,7 +873,8 @@ __device__ __forceinline__ void decode_attn_run(
     int rotate_q, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_acc, float* __restrict__ part_ml, float* __restrict__ cs_out,
     DecSmem<NW>& sm) {
-  static_assert(NW * 128 == kMD, "each wave accumulates a quarter of the dims");
+  constexpr int kWD = kMD / NW;  // dims each wave accumulates
+  static_assert(kWD % 16 == 0, "whole 16-dim blocks per wave");
   constexpr int NT = NW * 64, kSlotsPerIter = NW * kDStep;
   constexpr int kQPer = kDH * 64 / NT;  // 16-byte pieces of the query tile per thread
   uint8_t* dsm = sm.dsm;
@@ -951,9 +954,9 @@ __device__ __forceinline__ void decode_attn_run(
     *reinterpret_cast<uint4*>(q_s + (c >> 6) * kMPitch + 2 * d0) = raw;
   }
   __syncthreads();
-  v4f o[8];  // O^T[dims 128 wave + 16 db + 4 gq + i][head n]
+  v4f o[kWD / 16];  // O^T[dims kWD wave + 16 db + 4 gq + i][head n]
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < kWD / 16; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float scale2 = g.scale * kLog2e;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -1014,7 +1017,7 @@ __device__ __forceinline__ void decode_attn_run(
       l_run *= corr;
       m_run = m_new;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] *= corr;
+      for (int db = 0; db < kWD / 16; ++db) o[db] *= corr;
     }
     float p[8], psum = 0.f;
 #pragma unroll
@@ -1039,11 +1042,11 @@ __device__ __forceinline__ void decode_attn_run(
     for (int w = 0; w < NW; ++w) {
       if (!sm.vm_s[w]) continue;  // (uniform)
       const v8bf pb = sm.p_s[w][lane];
-      lds_u8* tile = (lds_u8*)(dsm + w * kDWaveBytes) + wave * 256;
+      lds_u8* tile = (lds_u8*)(dsm + w * kDWaveBytes) + wave * kWD * 2;
       lds_u8* r_lo = tile + (4 * gq + te) * kMPitch + tq * 8;
       lds_u8* r_hi = tile + (16 + 4 * gq + te) * kMPitch + tq * 8;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < kWD / 16; ++db) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_lo + db * 32));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(r_hi + db * 32));
         const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1074,23 +1077,23 @@ __device__ __forceinline__ void decode_attn_run(
       step(stg, vmask, st8, sig);
     }
   }
-  // lane holds O^T[dims 128 wave + 16 db + 4 gq + i][head n]; m_run (log2
+  // lane holds O^T[dims kWD wave + 16 db + 4 gq + i][head n]; m_run (log2
   // units) and l_run are the run's max and sum for head n
   const float M = m_run * kLn2, L = l_run;
   const int hh = hg * kDH + n;
   if (g.direct) {
     uint16_t* orow = out + (static_cast<int64_t>(row) * g.H + hh) * kMD;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      store_head_dims4(float4{o[db][0], o[db][1], o[db][2], o[db][3]}, L, 32 * wave + 4 * db + gq,
-                       rot0, cs_s, orow);
+    for (int db = 0; db < kWD / 16; ++db)
+      store_head_dims4(float4{o[db][0], o[db][1], o[db][2], o[db][3]}, L,
+                       kWD / 4 * wave + 4 * db + gq, rot0, cs_s, orow);
     if (lse && wave == 0 && gq == 0)
       lse[static_cast<int64_t>(row) * g.H + hh] = L > 0.f ? M + logf(L) : -INFINITY;
   } else {
     const int64_t pi = ((static_cast<int64_t>(row) * G + hg) * g.n_runs + run) * kDH + n;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<float4*>(part_acc + pi * kMD + 128 * wave + 16 * db + 4 * gq) =
+    for (int db = 0; db < kWD / 16; ++db)
+      *reinterpret_cast<float4*>(part_acc + pi * kMD + kWD * wave + 16 * db + 4 * gq) =
           float4{o[db][0], o[db][1], o[db][2], o[db][3]};
     if (wave == 0 && gq == 0) {
       part_ml[2 * pi] = M;

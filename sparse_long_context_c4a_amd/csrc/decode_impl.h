@@ -89,6 +89,11 @@ struct PrologueArgs {
   float* main_scale;  // fp8 main cache: one scale per entry [B, e_cap], else nullptr
   uint32_t* status;
   Paging pg;          // paged caches, window and rings (tables nullptr: dense)
+  // the selection when it is every visible entry (no indexer, k >= every
+  // visible count): [B, all_k] indices written by role 3, nullptr: none
+  int32_t* all_idx;
+  int all_k;
+  int64_t all_nv_cap;
 };
 
 // Workgroups of the prologue: kSlices for the main entry, then three.
@@ -179,6 +184,23 @@ __device__ __forceinline__ void decode_prologue_block(int role, int b, PrologueA
         a.cs_tab[static_cast<int64_t>(b) * a.r + 2 * i] = c;
         a.cs_tab[static_cast<int64_t>(b) * a.r + 2 * i + 1] = s;
       }
+    if (a.all_idx) {
+      // entries 0 .. nv-1 in index order, then -1 (the status bits of the
+      // selection pass it replaces)
+      int64_t nv = 0;
+      if (!ok) {
+        if (threadIdx.x == 0) set_status(a.status, DSA_DEVERR_POSITION);
+      } else {
+        nv = n_complete(m, a.s, a.S);
+        if (nv > a.all_nv_cap) {
+          if (threadIdx.x == 0) set_status(a.status, DSA_DEVERR_CAPACITY);
+          nv = a.all_nv_cap;
+        }
+      }
+      if (nv > a.all_k && threadIdx.x == 0) set_status(a.status, DSA_DEVERR_NO_INDEX);
+      int32_t* irow = a.all_idx + static_cast<int64_t>(b) * a.all_k;
+      for (int i = threadIdx.x; i < a.all_k; i += blockDim.x) irow[i] = i < nv ? i : -1;
+    }
     return;
   }
   const int64_t m = a.pos0[b];

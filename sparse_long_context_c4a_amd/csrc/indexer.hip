@@ -581,8 +581,12 @@ dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa
                      (a.dtype == DSA_FP8_E4M3 || a.dtype == DSA_FP4_E2M1) &&
                      la.dtype == DSA_BF16;
   if (!fused) {
-    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, q_rot, st);
-    if (rc != DSA_OK) return rc;
+    // no indexer keys (k >= every visible count): the selection is every
+    // visible entry, written by the prologue (one launch fewer)
+    const bool all_vis = a.keys == nullptr && a.score_out == nullptr && a.queries_per_seq == 1;
+    dsa_status rc = launch_decode_prologue(la, qpos, insert_window, cs_tab, q_rot, st,
+                                           all_vis ? a.idx_out : nullptr, a.k, P.nv_cap);
+    if (rc != DSA_OK || all_vis) return rc;
     return launch_index_topk(a, ws, st);
   }
   const int rows = a.n_seqs;

@@ -91,8 +91,12 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
 dsa_status launch_decode_index_topk(const dsa_index_args& a, void* ws, const dsa_layer_args& la,
                                     int64_t* qpos, bool insert_window, float* cs_tab, void* q_rot,
                                     hipStream_t st);
+// all_idx (may be nullptr): the step's selection when it is every visible
+// entry (no indexer keys), [B, all_k], written by the prologue itself.
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  float* cs_tab, void* q_rot, hipStream_t st);
+                                  float* cs_tab, void* q_rot, hipStream_t st,
+                                  int32_t* all_idx = nullptr, int all_k = 0,
+                                  int64_t all_nv_cap = 0);
 // The chunk's pre-attention step: queries normalised and rotated into q_rot,
 // the raw tokens rotated into rot_chunk (one launch).
 dsa_status launch_qk_prep(const dsa_layer_args& a, void* q_rot, void* rot_chunk, hipStream_t st);

@@ -272,8 +272,12 @@ PrologueArgs make_prologue_args(const dsa_layer_args& a, int64_t* qpos, bool ins
 }
 
 dsa_status launch_decode_prologue(const dsa_layer_args& a, int64_t* qpos, bool insert_window,
-                                  float* cs_tab, void* q_rot, hipStream_t st) {
-  const PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab, q_rot);
+                                  float* cs_tab, void* q_rot, hipStream_t st, int32_t* all_idx,
+                                  int all_k, int64_t all_nv_cap) {
+  PrologueArgs p = make_prologue_args(a, qpos, insert_window, cs_tab, q_rot);
+  p.all_idx = all_idx;
+  p.all_k = all_k;
+  p.all_nv_cap = all_nv_cap;
   const dim3 grid((prologue_roles<kStandaloneSlices>() + p.nq_roles) * a.n_seqs),
       block(kCompressThreads);
   // the indexer entry's output format picks the instantiation

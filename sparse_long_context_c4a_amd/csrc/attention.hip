@@ -1146,25 +1146,36 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
   const int h = blockIdx.x, d4 = tid;
   const int hg = h / kDH, ch = h % kDH, G = g.H / kDH;
   const float* cs_src = g.cs_tab ? g.cs_tab : cs_in;
-  for (int i = tid; i < g.r; i += 128) cs_s[i] = cs_src[static_cast<int64_t>(row) * g.r + i];
+  // the R_m table into registers now, into LDS after the partials' loads
+  // are out (a store to LDS here would wait for it first)
+  float csv[kMD / 128];
+#pragma unroll
+  for (int i = 0; i < kMD / 128; ++i)
+    csv[i] = tid + 128 * i < g.r ? cs_src[static_cast<int64_t>(row) * g.r + tid + 128 * i] : 0.f;
   const int64_t p0 = (static_cast<int64_t>(row) * G + hg) * g.n_runs;
   float M = -INFINITY, L = 0.f;
   float4 t = {0.f, 0.f, 0.f, 0.f};
   for (int r0 = 0; r0 < g.n_runs; r0 += kCombR) {
+    const int nr = min(kCombR, g.n_runs - r0);
+    // the runs' (max, sum) in one vector load, lane q holding run r0 + q's
+    // (loaded per run as scalars, each waited on before the next is issued)
+    const int ql = (tid & 63) < nr ? (tid & 63) : 0;
+    const float2 mlv = reinterpret_cast<const float2*>(part_ml)[(p0 + r0 + ql) * kDH + ch];
+    // an empty run left max -inf, sum 0 and acc 0; runs past the end are
+    // empty.  Every partial's load goes out before any result is used.
     float mr[kCombR], lr[kCombR];
     float4 u[kCombR];
 #pragma unroll
     for (int q = 0; q < kCombR; ++q) {
-      // an empty run left max -inf, sum 0 and acc 0; runs past the end are empty
-      mr[q] = -INFINITY;
-      lr[q] = 0.f;
       u[q] = float4{0.f, 0.f, 0.f, 0.f};
-      if (r0 + q < g.n_runs) {
-        const int64_t pi = (p0 + r0 + q) * kDH + ch;
-        mr[q] = part_ml[2 * pi];
-        lr[q] = part_ml[2 * pi + 1];
-        u[q] = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
-      }
+      if (q < nr) u[q] = reinterpret_cast<const float4*>(part_acc + ((p0 + r0 + q) * kDH + ch) * kMD)[d4];
+    }
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      const float mq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mlv.x), q));
+      const float lq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mlv.y), q));
+      mr[q] = q < nr ? mq : -INFINITY;
+      lr[q] = q < nr ? lq : 0.f;
     }
     float Mn = M;
 #pragma unroll
@@ -1187,6 +1198,9 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
     }
     M = Mn;
   }
+#pragma unroll
+  for (int i = 0; i < kMD / 128; ++i)
+    if (tid + 128 * i < g.r) cs_s[tid + 128 * i] = csv[i];
   __syncthreads();
   const int64_t oh = static_cast<int64_t>(row) * g.H + h;
   if (g.out_scale)
@@ -1209,37 +1223,44 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
   __shared__ float cs_s[kMD];
   __shared__ float red[2];
   const int row = blockIdx.y, h = blockIdx.x, tid = threadIdx.x, d4 = tid;
-  const int64_t m = g.q_pos[row];
-  const bool ok = m >= 0 && m < g.max_pos_end;
-  for (int i = tid; i < g.r / 2; i += 128) {
-    float c = 1.f, sn = 0.f;
-    if (g.cs_tab) {
-      c = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * i];
-      sn = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * i + 1];
-    } else if (ok) {
-      rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+  // the (cos, sin) pairs i = tid + 128 j this thread stages: the step's
+  // table loaded now (into LDS after the partials' loads are out), or
+  // computed after the merge
+  float cv[kMD / 256], sv[kMD / 256];
+#pragma unroll
+  for (int j = 0; j < kMD / 256; ++j) {
+    const int i = tid + 128 * j;
+    cv[j] = 1.f;
+    sv[j] = 0.f;
+    if (g.cs_tab && g.r >= 2) {  // (uniform; pairs past r / 2 read the last one, unused)
+      const int ii = min(i, g.r / 2 - 1);
+      cv[j] = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * ii];
+      sv[j] = g.cs_tab[static_cast<int64_t>(row) * g.r + 2 * ii + 1];
     }
-    cs_s[2 * i] = c;
-    cs_s[2 * i + 1] = sn;
   }
   const int64_t p0 = static_cast<int64_t>(row) * g.n_runs;
   float M = -INFINITY, L = 0.f;
   float4 t = {0.f, 0.f, 0.f, 0.f};
   for (int r0 = 0; r0 < g.n_runs; r0 += kCombR) {
+    const int nr = min(kCombR, g.n_runs - r0);
+    // the runs' (max, sum) in one vector load, lane q holding run r0 + q's
+    const int ql = (tid & 63) < nr ? (tid & 63) : 0;
+    const float2 mlv = reinterpret_cast<const float2*>(part_ml)[(p0 + r0 + ql) * g.H + h];
+    // an empty run left max -inf, sum 0 and acc 0; runs past the end are
+    // empty.  Every partial's load goes out before any result is used.
     float mr[kCombR], lr[kCombR];
     float4 u[kCombR];
 #pragma unroll
     for (int q = 0; q < kCombR; ++q) {
-      // an empty run left max -inf, sum 0 and acc 0; runs past the end are empty
-      mr[q] = -INFINITY;
-      lr[q] = 0.f;
       u[q] = float4{0.f, 0.f, 0.f, 0.f};
-      if (r0 + q < g.n_runs) {
-        const int64_t pi = (p0 + r0 + q) * g.H + h;
-        mr[q] = part_ml[2 * pi];
-        lr[q] = part_ml[2 * pi + 1];
-        u[q] = reinterpret_cast<const float4*>(part_acc + pi * kMD)[d4];
-      }
+      if (q < nr) u[q] = reinterpret_cast<const float4*>(part_acc + ((p0 + r0 + q) * g.H + h) * kMD)[d4];
+    }
+#pragma unroll
+    for (int q = 0; q < kCombR; ++q) {
+      const float mq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mlv.x), q));
+      const float lq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mlv.y), q));
+      mr[q] = q < nr ? mq : -INFINITY;
+      lr[q] = q < nr ? lq : 0.f;
     }
     float Mn = M;
 #pragma unroll
@@ -1261,6 +1282,19 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
       t.w = fmaf(wgt, u[q].w, t.w);
     }
     M = Mn;
+  }
+  {
+    const int64_t m = g.q_pos[row];
+    const bool ok = m >= 0 && m < g.max_pos_end;
+#pragma unroll
+    for (int jj = 0; jj < kMD / 256; ++jj) {
+      const int i = tid + 128 * jj;
+      if (i < g.r / 2) {
+        if (!g.cs_tab && ok) rope_cs(m + g.off, i, g.r, g.base, &cv[jj], &sv[jj]);
+        cs_s[2 * i] = cv[jj];
+        cs_s[2 * i + 1] = sv[jj];
+      }
+    }
   }
   __syncthreads();
   const int64_t oh = static_cast<int64_t>(row) * g.H + h;

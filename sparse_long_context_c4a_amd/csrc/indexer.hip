@@ -359,7 +359,9 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     if (p < need) emit(irow, orow, above + p, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
   };
   if (fits && at <= 64) {
-    keep_largest_small(tmp_s, static_cast<int>(at), need, out_bin);
+    keep_largest_small(tmp_s, static_cast<int>(at), need, [&](uint64_t x, uint32_t slot) {
+      emit(irow, orow, above + slot, comp_index(x), key_to_float(static_cast<uint32_t>(x >> 32)));
+    });
   } else if (fits) {
     const uint64_t cut = kth_largest_composite(tmp_s, static_cast<int>(at), need,
                                                [](uint64_t) { return true; }, lo + (B << shift),

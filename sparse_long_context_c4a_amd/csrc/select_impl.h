@@ -192,17 +192,27 @@ __device__ __forceinline__ Bin find_bin_wave(const uint32_t* h, uint32_t need, u
   return res;
 }
 
-// Keep the `need` largest of the n distinct composites in v[] (LDS): each
-// is kept iff fewer than `need` others exceed it.  For small n (one wave
-// compares every pair through LDS broadcasts); calls f(v) for the kept.
+// Keep the `need` largest of the n <= 64 distinct composites in v[] (LDS):
+// each is kept iff fewer than `need` others exceed it.  The first wave holds
+// one per lane and compares it with every other by lane broadcasts; calls
+// f(v, slot) for the kept, slot = 0 .. kept-1 in lane order (no atomics).
 template <typename F>
 __device__ __forceinline__ void keep_largest_small(const uint64_t* v, int n, uint32_t need, F f) {
   const int t = threadIdx.x;
-  if (t < n) {
-    const uint64_t x = v[t];
+  if (t < 64) {
+    const uint64_t x = t < n ? v[t] : 0ull;
+    const uint32_t xlo = static_cast<uint32_t>(x), xhi = static_cast<uint32_t>(x >> 32);
     uint32_t rank = 0;
-    for (int i = 0; i < n; ++i) rank += v[i] > x ? 1u : 0u;
-    if (rank < need) f(x);
+    for (int i = 0; i < n; ++i) {  // (n is uniform)
+      // (readlane returns int: through uint32_t, no sign extension)
+      const uint32_t yhi = static_cast<uint32_t>(__builtin_amdgcn_readlane(xhi, i));
+      const uint32_t ylo = static_cast<uint32_t>(__builtin_amdgcn_readlane(xlo, i));
+      const uint64_t y = (static_cast<uint64_t>(yhi) << 32) | ylo;
+      rank += y > x ? 1u : 0u;
+    }
+    const bool keep = t < n && rank < need;
+    const uint64_t km = __ballot(keep);
+    if (keep) f(x, static_cast<uint32_t>(__popcll(km & ((1ull << t) - 1ull))));
   }
 }
 
@@ -349,7 +359,9 @@ __device__ __forceinline__ void select_topk_composites(const uint64_t* c, int n,
     if (p < need) emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
   };
   if (fits && at <= 64) {
-    keep_largest_small(tmp, static_cast<int>(at), need, out_bin);
+    keep_largest_small(tmp, static_cast<int>(at), need, [&](uint64_t v, uint32_t slot) {
+      emit(irow, orow, above + slot, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+    });
   } else if (fits) {
     const uint64_t cut = kth_largest_composite<NT>(tmp, static_cast<int>(at), need,
                                                    [](uint64_t) { return true; },
@@ -454,7 +466,9 @@ __device__ __forceinline__ void row_select_from_scores(const float* srow, int64_
         emit(irow, orow, above + p, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
     };
     if (at <= 64) {
-      keep_largest_small(cand_s, static_cast<int>(at), need, out_bin);
+      keep_largest_small(cand_s, static_cast<int>(at), need, [&](uint64_t v, uint32_t slot) {
+        emit(irow, orow, above + slot, comp_index(v), key_to_float(static_cast<uint32_t>(v >> 32)));
+      });
     } else {
       const uint64_t cut = kth_largest_composite<NT>(cand_s, static_cast<int>(at), need,
                                                      [](uint64_t) { return true; },

@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   __shared__ uint64_t tmp_s[kTmpCap];
   __shared__ __attribute__((aligned(16))) uint32_t h_s[kBins];
   __shared__ uint32_t red[3][kSelWaves];
-  __shared__ uint32_t pos_above, pos_bin, n_tmp;
+  __shared__ uint32_t pos_bin, n_tmp;
+  __shared__ uint32_t nu_s[kSelWaves];  // each wave's entries above the k-th bin
   __shared__ uint16_t f_s[kMaxF];        // waves scored again in full
   __shared__ uint32_t fbit_s[kSel / 32];  // the same as a bit set
   const int row = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     red[2][w] = hi;
   }
   for (int i = t; i < 2048; i += kSel) h_s[i] = 0u;
-  if (t == 0) pos_above = pos_bin = n_tmp = 0u;
+  if (t == 0) pos_bin = n_tmp = 0u;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
@@ -324,7 +325,10 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   }
   const bool fits = at <= static_cast<uint32_t>(kTmpCap);
   // places for the wave's entries above the bin and in it: the ballots of
-  // all kPer values first, then one LDS counter update per kind and wave
+  // all kPer values first; the bin's few members take places by an LDS
+  // counter, the entries above it by the waves' counts (an exclusive sum
+  // over the waves after the barrier below: no atomics on one address from
+  // every wave)
   uint64_t bu[kPer], bm[kPer];
   uint32_t nu = 0, nm = 0;
 #pragma unroll
@@ -335,12 +339,11 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     nu += static_cast<uint32_t>(__popcll(bu[u]));
     nm += static_cast<uint32_t>(__popcll(bm[u]));
   }
-  uint32_t pu = 0, pm = 0;
+  uint32_t pm = 0;
   if (l == 0) {
-    if (nu) pu = atomicAdd(&pos_above, nu);
+    nu_s[w] = nu;
     if (nm) pm = atomicAdd(&n_tmp, nm);
   }
-  pu = __builtin_amdgcn_readlane(pu, 0);
   pm = __builtin_amdgcn_readlane(pm, 0);
   const uint64_t below = (1ull << l) - 1ull;
 #pragma unroll
@@ -353,6 +356,9 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     pm += static_cast<uint32_t>(__popcll(bm[u]));
   }
   __syncthreads();
+  uint32_t pu = 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) pu += i < w ? nu_s[i] : 0u;
   const uint32_t need = static_cast<uint32_t>(k) - above;
   auto out_bin = [&](uint64_t x) {
     const uint32_t p = atomicAdd(&pos_bin, 1u);

@@ -29,6 +29,7 @@ struct AttnGeom {
   const int64_t* q_pos;
   int Tq, H, D, r;
   double base;
+  double theta1;  // base^(-2 / r): the rotation's frequencies are its powers
   int64_t off;
   const int32_t* idx;
   int k;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(
   const int D = g.D, half = g.r / 2, first_rot = (D - g.r) / 2;
   for (int i = tid; i < half; i += kThreads) {
     float c = 1.f, s = 0.f;
-    if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &s);
+    if (ok) rope_cs1(m + g.off, i, g.theta1, &c, &s);
     cs_s[i][0] = c;
     cs_s[i][1] = s;
   }
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnGeom g, const float* _
     float a0 = acc[k][0] * inv, a1 = acc[k][1] * inv;
     if (pr >= first_rot && ok) {
       float c, sn;
-      rope_cs(m + g.off, pr - first_rot, g.r, g.base, &c, &sn);
+      rope_cs1(m + g.off, pr - first_rot, g.theta1, &c, &sn);
       const float t0 = a0 * c + a1 * sn, t1 = -a0 * sn + a1 * c;
       a0 = t0;
       a1 = t1;
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
   const int64_t c0 = chunk_win ? g.chunk_pos0[b] : 0;
   for (int i = tid; i < half; i += 512) {
     float c = 1.f, sn = 0.f;
-    if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+    if (ok) rope_cs1(m + g.off, i, g.theta1, &c, &sn);
     cs_s[i][0] = c;
     cs_s[i][1] = sn;
   }
@@ -926,7 +927,7 @@ __device__ __forceinline__ void decode_attn_run(
   if (!g.cs_tab)
     for (int i = tid; i < half; i += NT) {
       float c = 1.f, sn = 0.f;
-      if (ok) rope_cs(m + g.off, i, g.r, g.base, &c, &sn);
+      if (ok) rope_cs1(m + g.off, i, g.theta1, &c, &sn);
       cs_s[2 * i] = c;
       cs_s[2 * i + 1] = sn;
     }
@@ -1290,7 +1291,7 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
     for (int jj = 0; jj < kMD / 256; ++jj) {
       const int i = tid + 128 * jj;
       if (i < g.r / 2) {
-        if (!g.cs_tab && ok) rope_cs(m + g.off, i, g.r, g.base, &cv[jj], &sv[jj]);
+        if (!g.cs_tab && ok) rope_cs1(m + g.off, i, g.theta1, &cv[jj], &sv[jj]);
         cs_s[2 * i] = cv[jj];
         cs_s[2 * i + 1] = sv[jj];
       }
@@ -1382,6 +1383,7 @@ dsa_status launch_typed(const dsa_attn_args& a, const Plan& p, void* ws, hipStre
   g.D = a.dim;
   g.r = a.rope_dim;
   g.base = a.rope_base;
+  g.theta1 = a.rope_dim > 0 ? std::pow(a.rope_base, -2.0 / a.rope_dim) : 1.0;
   g.off = a.rope_pos_offset;
   g.idx = a.idx;
   g.k = a.k;

@@ -104,6 +104,24 @@ __device__ __forceinline__ void rope_cs(int64_t pos, int i, int r, double base, 
   sincosf(static_cast<float>(red), s, c);
 }
 
+// The same from theta1 = base^(-2/r) computed once on the host: theta_i =
+// theta1^i by repeated squaring (at most 2 log2(i) double products, relative
+// error ~1e-15 against base^(-2i/r): an angle error of ~1e-8 rad at position
+// 2^21, far below the single-precision sin/cos), instead of a double pow
+// per pair on the kernel's critical path.
+__device__ __forceinline__ void rope_cs1(int64_t pos, int i, double theta1, float* c, float* s) {
+  double theta = 1.0, b = theta1;
+  for (int e = i; e != 0; e >>= 1) {
+    if (e & 1) theta *= b;
+    b *= b;
+  }
+  const double ang = static_cast<double>(pos) * theta;
+  const double kq = rint(ang * 0.15915494309189533577);             // 1 / (2 pi)
+  double red = fma(-kq, 6.28318530717958623200, ang);                // 2 pi, high part
+  red = fma(-kq, 2.44929359829470635445e-16, red);                   // 2 pi, low part
+  sincosf(static_cast<float>(red), s, c);
+}
+
 // ------------------------------------------------ indexer key tile layout
 // fp8 caches of dim 128 (the indexer keys) are stored in tiles of 16
 // entries: tile t of sequence b holds entries 16t .. 16t+15 as 8 chunks of

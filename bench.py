@@ -276,6 +276,48 @@ def time_attn_cache(w, dev, fp8_cache, steps=200, warmup=20):
             "gathered_bytes": gathered, "rows": w.B, "k": w.k, "window": w.W}
 
 
+READ_PROBE = os.path.join(ROOT, "tests", "hw", "libhbm_read_probe.so")
+
+
+def time_plain_read(dev, total_bytes, n_wg, steps=20, warmup=5):
+    """A plain streaming read of about `total_bytes` (rounded up to 16-byte
+    pieces per workgroup) over n_wg workgroups of 256 threads, timed like
+    the indexer (events on its own dispatch packets), as the practical
+    read rate of one launch of that size.  The source is 1 GiB read in
+    rotating spans so that no launch finds its span in the Infinity Cache.
+    None when the probe library is not built."""
+    import ctypes
+    import torch
+    from sparse_long_context_c4a_amd import _lib
+    if not os.path.exists(READ_PROBE):
+        return None
+    lib = ctypes.CDLL(READ_PROBE)
+    lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    per = -(-total_bytes // (16 * n_wg)) * 16
+    src_bytes = 1 << 30
+    spans = src_bytes // (per * n_wg)
+    assert spans >= 4, "span too large for the rotation"
+    src = torch.ones(src_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(n_wg, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
+    for i in range(warmup + steps):
+        e0, e1 = evs[i - warmup] if i >= warmup else (None, None)
+        off = (i % spans) * per * n_wg
+        rc = lib.hbm_read_probe(src.data_ptr() + off, src_bytes - off, per, n_wg,
+                                sink.data_ptr(), stream, e0.handle if e0 else None,
+                                e1.handle if e1 else None)
+        assert rc == 0, f"hbm_read_probe returned {rc}"
+    torch.cuda.synchronize()
+    us = sum(e[0].elapsed_ms(e[1]) for e in evs) / steps * 1e3
+    del src, sink
+    return {"kernel": "plain streaming read (tests/hw/hbm_read_probe.hip)", "bytes": per * n_wg,
+            "workgroups": n_wg, "us": us, "gbps": per * n_wg / (us * 1e-6) / 1e9}
+
+
 def time_prefill(dev, steps=3, warmup=1):
     """The prefill chunk workload: layer step time, indexer (+Top-k) and
     attention kernel times, and their throughput."""
@@ -446,6 +488,15 @@ def main():
             "context": w.L, "k": w.k, "kernel_ms": {"indexer": idxm, "attention": attnm}}
     del sets
     torch.cuda.empty_cache()
+    if w.Hi and kgbps and not args.no_extra:
+        # what a launch that only reads the indexer's bytes, over its grid of
+        # stream workgroups (1024 entries each), reaches on this GPU
+        print("[bench] plain read of the indexer's bytes", file=sys.stderr, flush=True)
+        rd = time_plain_read(dev, kbytes, w.B * (-(-nv // 1024)))
+        if rd:
+            rd["frac_of_peak"] = rd["gbps"] / PEAK_HBM_GBPS
+            rd["indexer_vs_plain_read"] = kgbps / rd["gbps"]
+        line["roofline"]["plain_read"] = rd
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

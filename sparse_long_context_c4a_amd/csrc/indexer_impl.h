@@ -291,9 +291,9 @@ __device__ __forceinline__ void index_stream_block(
   const KeySrc src = key_src<kFmt>(keys, k_scale, k_mx, pm, b, e_cap, status);
   // key loads: a ring of two slots of two groups; unconditional (clamped to
   // an entry that exists, masked later) so the compiler can count them.
-  // Dense keys: the first slot goes out before the row's visible count is
-  // known (clamped to the cache's capacity), so its latency overlaps that
-  // of the position load
+  // Dense keys: both slots go out before the row's visible count is known
+  // (clamped to the cache's capacity), and so do the query and weight loads,
+  // so their latency overlaps that of the position load
   typename K::Raw kr[2][2];
   int64_t jmax = e_cap - 1;
   int32_t gblk = 0;
@@ -309,7 +309,22 @@ __device__ __forceinline__ void index_stream_block(
     }
   };
   const bool early = !kPaged && e_cap > 0;
-  if (early) load(0, 0);
+  if (early) {
+    load(0, 0);
+    load(1, 2);
+  }
+  v8bf aq[4];
+  K::q_operands(n < Hi ? q + (static_cast<int64_t>(row) * Hi + n) * 128 : nullptr, g, aq);
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    wv[i] = 0.f;
+    if (h < Hi) {
+      const int64_t o = static_cast<int64_t>(row) * Hi + h;
+      wv[i] = w[o] * (q_scale ? q_scale[o] : 1.0f);
+    }
+  }
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, status, bx == 0 && tid == 0);
   const int64_t nv = ri.nv;
   // each lane keeps the keys of groups 4i + 2 (g & 1) + (g >> 1), i < kKeep
@@ -325,23 +340,11 @@ __device__ __forceinline__ void index_stream_block(
         gblk = static_cast<int32_t>(
             paged_row(pm, b, min<int64_t>(wbase + lane * 16, jmax), status) >> pm.shift);
     if (!early) load(0, 0);
-    v8bf aq[4];
-    K::q_operands(n < Hi ? q + (static_cast<int64_t>(row) * Hi + n) * 128 : nullptr, g, aq);
-    float wv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g + i;
-      wv[i] = 0.f;
-      if (h < Hi) {
-        const int64_t o = static_cast<int64_t>(row) * Hi + h;
-        wv[i] = w[o] * (q_scale ? q_scale[o] : 1.0f);
-      }
-    }
     float* srow = scores + static_cast<int64_t>(row) * ld_scores;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int sl = st & 1;
-      if (st + 1 < kSteps) load(sl ^ 1, 2 * (st + 1));
+      if (st + 1 < kSteps && !(early && st == 0)) load(sl ^ 1, 2 * (st + 1));
       float part[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {

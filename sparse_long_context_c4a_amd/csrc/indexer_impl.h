@@ -379,32 +379,33 @@ __device__ __forceinline__ void index_stream_block(
     }
   }
   if constexpr (kCand) {
-    // wave candidates: the keys above the (cap+1)-th largest of the wave's 256
+    // wave candidates: the keys above the (cap+1)-th largest of the wave's
+    // 256.  Each lane sorts its keys (descending) once, so a lane holding
+    // the wave's maximum holds it first; the maximum is then taken cap + 1
+    // times, each time one instance leaving the lowest lane that has it
+    // (its keys move up one place)
     uint32_t work[kKeep];
 #pragma unroll
     for (int i = 0; i < kKeep; ++i) work[i] = kk[i];
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i)
+#pragma unroll
+      for (int j = 0; j + 1 < kKeep - i; ++j) {
+        const uint32_t hi = max(work[j], work[j + 1]), lo = min(work[j], work[j + 1]);
+        work[j] = hi;
+        work[j + 1] = lo;
+      }
     uint32_t next = 0;
     for (int it = 0; it <= cap; ++it) {
-      uint32_t m = work[0];
-#pragma unroll
-      for (int i = 1; i < kKeep; ++i) m = max(m, work[i]);
-      m = wave_max_u32(m);
+      const uint32_t m =
+          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(wave_max_u32(work[0]))));
       next = m;
       if (m == 0u || it == cap) break;
-      // drop one instance of m (from the lowest lane that holds it)
-      bool has = false;
+      const uint64_t bal = __ballot(work[0] == m);
+      const bool me = lane == __ffsll(static_cast<long long>(bal)) - 1;
 #pragma unroll
-      for (int i = 0; i < kKeep; ++i) has |= work[i] == m;
-      const uint64_t bal = __ballot(has);
-      if (lane == __ffsll(static_cast<long long>(bal)) - 1) {
-        bool done = false;
-#pragma unroll
-        for (int i = 0; i < kKeep; ++i)
-          if (!done && work[i] == m) {
-            work[i] = 0u;
-            done = true;
-          }
-      }
+      for (int i = 0; i + 1 < kKeep; ++i) work[i] = me ? work[i + 1] : work[i];
+      work[kKeep - 1] = me ? 0u : work[kKeep - 1];
     }
     // threshold: strictly above the (cap+1)-th largest (1 if fewer keys)
     const uint32_t tw = next == 0u ? 1u : (next == 0xffffffffu ? next : next + 1u);

@@ -427,14 +427,27 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
   const int total = g.k + g.W;
   const int a_begin = run * g.slots_per_run;
   const int a_end = min(total, a_begin + g.slots_per_run);
-  for (int a = a_begin + tid; a < min(a_end, g.k); a += 512)
-    idx_s[a - a_begin] = g.idx[static_cast<int64_t>(row) * g.k + a];
+  // the run's cache indices (at most kMRunSlots = 4 x 512) are loaded into
+  // registers and stored to LDS after the rotation table's arithmetic, which
+  // covers their latency
+  int32_t ix[kMRunSlots / 512];
+  const int a_idx = min(a_end, g.k);
+#pragma unroll
+  for (int u = 0; u < kMRunSlots / 512; ++u) {
+    const int a = a_begin + tid + 512 * u;
+    ix[u] = a < a_idx ? g.idx[static_cast<int64_t>(row) * g.k + a] : -1;
+  }
   const int64_t c0 = chunk_win ? g.chunk_pos0[b] : 0;
   for (int i = tid; i < half; i += 512) {
     float c = 1.f, sn = 0.f;
     if (ok) rope_cs1(m + g.off, i, g.theta1, &c, &sn);
     cs_s[i][0] = c;
     cs_s[i][1] = sn;
+  }
+#pragma unroll
+  for (int u = 0; u < kMRunSlots / 512; ++u) {
+    const int a = a_begin + tid + 512 * u;
+    if (a < a_idx) idx_s[a - a_begin] = ix[u];
   }
   __syncthreads();
   // query head h as the B operand, this wave's dim half: chunks c = 8 dh +
@@ -543,6 +556,18 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
       __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
       if (cc < 6) __builtin_amdgcn_sched_group_barrier(0x100, kNB, 0);
     }
+    // the first weighted-sum step's V^T fragments (the tile stays in LDS
+    // until the next tile's first barrier): read now, so that they land while
+    // the partial logits are exchanged and the softmax runs
+    lds_u8* const lds_base = (lds_u8*)v_lds;
+    v4s lo0[16], hi0[16];
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      lo0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s_ptr)(lds_base + (4 * gq + te) * kMPitch + tq * 8 + dh * 512 + db * 32));
+      hi0[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s_ptr)(lds_base + (16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512 + db * 32));
+    }
 #pragma unroll
     for (int i = 0; i < kNB; ++i) spart[wave][i][lane] = sv[i];
     __syncthreads();
@@ -585,7 +610,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
                        static_cast<__bf16>(p[8 * u + 2]), static_cast<__bf16>(p[8 * u + 3]),
                        static_cast<__bf16>(p[8 * u + 4]), static_cast<__bf16>(p[8 * u + 5]),
                        static_cast<__bf16>(p[8 * u + 6]), static_cast<__bf16>(p[8 * u + 7])};
-      lds_u8* lds_base = (lds_u8*)v_lds;
+      if (u == 0) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          const v8bf va =
+              __builtin_bit_cast(v8bf, __builtin_shufflevector(lo0[db], hi0[db], 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+        }
+        continue;
+      }
       lds_u8* r_lo = lds_base + (32 * u + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
       lds_u8* r_hi = lds_base + (32 * u + 16 + 4 * gq + te) * kMPitch + tq * 8 + dh * 512;
       v4s lo[16], hi[16];

@@ -665,11 +665,16 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
       lse[static_cast<int64_t>(row) * g.H + h] =
           l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
+    // the run's own attention output (normalised by its sum), rounded to
+    // bf16 like the layer's output, and its (max, sum) in f32: half the
+    // bytes of f32 accumulators for the merge to read
     const int64_t pi = (static_cast<int64_t>(row) * g.n_runs + run) * g.H + h;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    uint16_t* prow = reinterpret_cast<uint16_t*>(part_acc) + pi * kMD;
 #pragma unroll
     for (int db = 0; db < 16; ++db)
-      *reinterpret_cast<float4*>(part_acc + pi * kMD + 256 * dh + 16 * db + 4 * gq) =
-          float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+      *reinterpret_cast<uint2*>(prow + 256 * dh + 16 * db + 4 * gq) =
+          uint2{pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
     if (gq == 0 && dh == 0) {
       part_ml[2 * pi] = m_run * kLn2;  // natural-log units for the merge
       part_ml[2 * pi + 1] = l_run;
@@ -1246,9 +1251,11 @@ __global__ __launch_bounds__(128) void k_attn_dcombine(AttnGeom g, const float* 
 }
 
 // Merge the runs of one (row, head) of the matrix-core path (partials
-// (row, run, head)) and apply R_m^{-1}: workgroup -> (head blockIdx.x, row
-// blockIdx.y), thread -> dims 4 tid .. +3, up to kCombR runs' partials
-// loaded per memory round trip.  The (cos, sin) of R_m come from the
+// (row, run, head): each run's normalised output o_r in bf16 and its max
+// m_r and sum l_r, so out = sum_r e^(m_r - M) l_r o_r / sum_r e^(m_r - M) l_r)
+// and apply R_m^{-1}: workgroup -> (head blockIdx.x, row blockIdx.y),
+// thread -> dims 4 tid .. +3, up to kCombR runs' partials loaded per memory
+// round trip.  The (cos, sin) of R_m come from the
 // step's table when the caller has one, else are computed here.
 __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
@@ -1283,11 +1290,12 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
     // an empty run left max -inf, sum 0 and acc 0; runs past the end are
     // empty.  Every partial's load goes out before any result is used.
     float mr[kCombR], lr[kCombR];
-    float4 u[kCombR];
+    uint2 u[kCombR];
+    const uint16_t* pacc = reinterpret_cast<const uint16_t*>(part_acc);
 #pragma unroll
     for (int q = 0; q < kCombR; ++q) {
-      u[q] = float4{0.f, 0.f, 0.f, 0.f};
-      if (q < nr) u[q] = reinterpret_cast<const float4*>(part_acc + ((p0 + r0 + q) * g.H + h) * kMD)[d4];
+      u[q] = uint2{0u, 0u};
+      if (q < nr) u[q] = reinterpret_cast<const uint2*>(pacc + ((p0 + r0 + q) * g.H + h) * kMD)[d4];
     }
 #pragma unroll
     for (int q = 0; q < kCombR; ++q) {
@@ -1308,12 +1316,12 @@ __global__ __launch_bounds__(128) void k_attn_mcombine(AttnGeom g, const float* 
     t.w *= c;
 #pragma unroll
     for (int q = 0; q < kCombR; ++q) {
-      const float wgt = mr[q] == -INFINITY ? 0.f : expf(mr[q] - Mn);
-      L = fmaf(wgt, lr[q], L);
-      t.x = fmaf(wgt, u[q].x, t.x);
-      t.y = fmaf(wgt, u[q].y, t.y);
-      t.z = fmaf(wgt, u[q].z, t.z);
-      t.w = fmaf(wgt, u[q].w, t.w);
+      const float wl = mr[q] == -INFINITY ? 0.f : expf(mr[q] - Mn) * lr[q];
+      L += wl;
+      t.x = fmaf(wl, bf16_to_f32(static_cast<uint16_t>(u[q].x & 0xffffu)), t.x);
+      t.y = fmaf(wl, bf16_to_f32(static_cast<uint16_t>(u[q].x >> 16)), t.y);
+      t.z = fmaf(wl, bf16_to_f32(static_cast<uint16_t>(u[q].y & 0xffffu)), t.z);
+      t.w = fmaf(wl, bf16_to_f32(static_cast<uint16_t>(u[q].y >> 16)), t.w);
     }
     M = Mn;
   }
@@ -1397,7 +1405,9 @@ Plan plan(const dsa_attn_args& a) {
   p.part = p.n_runs > 1 || a.out_fp8;
   size_t off = 0;
   p.off_acc = off;
-  if (p.part) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * 4);
+  // partial outputs: bf16 on the matrix-core path, f32 accumulators elsewhere
+  const size_t acc_el = p.mfma ? 2 : 4;
+  if (p.part) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * a.dim * acc_el);
   p.off_ml = off;
   if (p.part) off = align_up(off + static_cast<size_t>(rows) * p.n_runs * a.heads * 2 * 4);
   p.off_cs = off;

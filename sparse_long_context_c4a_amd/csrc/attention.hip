@@ -686,14 +686,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma8(
 // bf16, D = 512, heads in groups of 16, few rows.  A workgroup takes one
 // row, 16 heads and a run of slots; its kDecWaves waves take interleaved
 // groups of 32 slots.  Each wave gathers its own 32 vectors (16 bytes per
-// lane of each, through registers into its LDS tile), computes S^T = K Q^T
-// and O^T += V^T P^T for its 16 heads exactly as the MFMA path above, and
-// keeps its own online-softmax state.  The waves then merge in LDS.  A row
-// whose slots span several runs leaves one un-normalised partial
-// (max, sum, acc) per run, merged by k_attn_dcombine with the R_m table the
-// run-0 workgroup leaves.  (Merging in the same launch by the last workgroup
-// to arrive needs agent-scope release/acquire fences, whose L2 write-back
-// and invalidate cost more than the second launch.)
+// lane of each, through registers into its LDS tile) and computes S^T =
+// K Q^T for the 16 heads; the waves agree on each step's max per head and
+// leave their probabilities in LDS; then wave w accumulates O^T += V^T P^T
+// over dims kWD w .. +kWD-1 for all the step's tiles, so the waves never
+// merge.  A row whose slots span several runs leaves one un-normalised
+// partial (max, sum, acc in f32) per run, merged by k_attn_dcombine with the
+// R_m table the run-0 workgroup leaves.  (Merging in the same launch by the
+// last workgroup to arrive needs agent-scope release/acquire fences, whose
+// L2 write-back and invalidate cost more than the second launch.)
 //
 // Workgroup order: the head groups of one (row, run) read the same vectors,
 // so they are placed on one XCD (workgroup ids congruent mod 8; the

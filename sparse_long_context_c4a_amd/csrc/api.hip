@@ -341,11 +341,6 @@ LayerWs layer_plan(const dsa_layer_args* a, void* ws) {
   return L;
 }
 
-__global__ void k_row_positions(const int64_t* __restrict__ pos0, int T, int B, int64_t* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B * T) out[i] = pos0[i / T] + (i % T);
-}
-
 dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStream_t st, bool decode) {
   dsa_status rc = validate_layer(a, decode);
   if (rc == DSA_OK && a->main_fp8 && !decode)
@@ -380,10 +375,6 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     if (rc != DSA_OK) return rc;
     return early ? DSA_OK : launch_decode_window_insert(*a, st);
   }
-  hipLaunchKernelGGL(k_row_positions, dim3((B * T + 255) / 256), dim3(256), 0, st, a->pos0, T, B,
-                     const_cast<int64_t*>(L.ia.q_pos));
-  rc = hip_check(hipGetLastError(), "k_row_positions launch");
-  if (rc != DSA_OK) return rc;
   // S1: compress entries completing in the chunk (reads the old rings)
   const int rows_logits = static_cast<int>(ceil_div(T, a->main.stride));
   dsa_compress_args c{};
@@ -425,27 +416,26 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     rc = launch_compress(ci, st);
     if (rc != DSA_OK) return rc;
   }
-  // rings take the chunk's raw tokens
-  rc = launch_ring_update(a->x, a->dtype, a->main.dim, T, a->main_ring, a->main.span, a->pos0, B,
-                          a->max_pos_end, a->paging, a->status, st);
+  // the rings take the chunk's raw tokens; the rows' positions (for the
+  // indexer and attention) and, without a Q-norm, the chunk's tokens rotated
+  // for the window, in the same launch
+  rc = launch_chunk_tasks(a->x, a->dtype, a->main.dim, a->main_ring, a->kx, raw_idx_dt,
+                          a->idx_dim, a->idx_heads > 0 ? a->idx_ring : nullptr, T, a->main.span,
+                          a->pos0, B, a->max_pos_end, a->paging, a->status,
+                          const_cast<int64_t*>(L.ia.q_pos),
+                          a->q_norm_gamma ? nullptr : base + L.off_rot, a->main.rope_dim,
+                          a->main.rope_base, a->main.rope_pos_offset, st);
   if (rc != DSA_OK) return rc;
-  if (a->idx_heads > 0) {
-    rc = launch_ring_update(a->kx, raw_idx_dt, a->idx_dim, T, a->idx_ring, a->main.span, a->pos0,
-                            B, a->max_pos_end, a->paging, a->status, st);
-    if (rc != DSA_OK) return rc;
-  }
   // S3 + S4
   rc = launch_index_topk(L.ia, base + L.off_idx_ws, st);
   if (rc != DSA_OK) return rc;
-  // rotated chunk tokens: the window of the chunk's own queries, then the
-  // ring; with a Q-norm, the queries prepared in the same launch
-  if (a->q_norm_gamma)
+  // with a Q-norm: the queries prepared and the chunk's tokens rotated for
+  // the window (the window of the chunk's own queries, then the ring) in one
+  // launch
+  if (a->q_norm_gamma) {
     rc = launch_qk_prep(*a, base + L.off_qrot, base + L.off_rot, st);
-  else
-    rc = launch_rotate_chunk(a->x, a->dtype, a->main.dim, T, a->main.rope_dim, a->main.rope_base,
-                             a->main.rope_pos_offset, a->pos0, B, base + L.off_rot,
-                             a->max_pos_end, st);
-  if (rc != DSA_OK) return rc;
+    if (rc != DSA_OK) return rc;
+  }
   // S5
   AttnLaunch lx;
   lx.ev0 = call_timing().attn0;

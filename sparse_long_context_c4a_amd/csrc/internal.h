@@ -69,12 +69,16 @@ dsa_status launch_attn(const dsa_attn_args& a, void* ws, hipStream_t st,
                        const AttnLaunch& lx = AttnLaunch{});
 
 // Layer helpers: ring and window maintenance, chunk rotation.
-dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
-                              const int64_t* pos0, int B, int64_t max_pos_end,
-                              const dsa_paging& pg, uint32_t* status, hipStream_t st);
-dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, int r, double base,
-                               int64_t off, const int64_t* pos0, int B, void* out,
-                               int64_t max_pos_end, hipStream_t st);
+// In one launch after the compressor: the chunk's tail into the main ring
+// (raw0, ring0) and, with ring1, the indexer's ring; every row's position
+// into qpos; with rot_out, the chunk's main tokens (raw0) rotated for the
+// window.
+dsa_status launch_chunk_tasks(const void* raw0, dsa_dtype dt0, int D0, void* ring0,
+                              const void* raw1, dsa_dtype dt1, int D1, void* ring1, int64_t T,
+                              int S, const int64_t* pos0, int B, int64_t max_pos_end,
+                              const dsa_paging& pg, uint32_t* status, int64_t* qpos,
+                              void* rot_out, int rope_dim, double rope_base, int64_t rope_off,
+                              hipStream_t st);
 dsa_status launch_window_update(const void* rot_chunk, dsa_dtype dt, int D, int64_t T, void* win,
                                 int w_cap, int window_size, const int64_t* pos0, int B,
                                 int64_t max_pos_end, const dsa_paging& pg, uint32_t* status,

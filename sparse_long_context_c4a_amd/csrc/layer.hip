@@ -22,48 +22,87 @@ __global__ void k_zero(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-// Copy the last min(T, S) raw tokens of the chunk into the ring.  Grid:
-// (min(T, S), B); element size in 2-byte units.
-__global__ void k_ring_update(const uint16_t* __restrict__ raw, int units, int64_t T,
-                              uint16_t* __restrict__ ring, int S, const int64_t* __restrict__ pos0,
-                              int64_t max_pos_end, Paging pg, uint32_t* status) {
+// One ring's copy source and destination (element size in 2-byte units).
+struct RingCopy {
+  const uint16_t* raw;
+  uint16_t* ring;
+  int units;
+};
+
+// The chunk's tokens rotated for the window: out[b, t] = R_{p0 + t + off}
+// x[b, t] in the storage dtype.
+template <typename T>
+struct RotateJob {
+  const T* x;
+  T* out;
+  int D, r;
+  double theta1;  // base^(-2 / r): pair i turns by (p + off) theta1^i
+  int64_t off;
+};
+
+template <typename T>
+__device__ __forceinline__ void rotate_token(const RotateJob<T>& j, int b, int64_t t, int64_t Tn,
+                                             int64_t p0) {
+  const int64_t o = (static_cast<int64_t>(b) * Tn + t) * j.D;
+  const int first_rot = (j.D - j.r) / 2;
+  for (int pr = threadIdx.x; pr < j.D / 2; pr += blockDim.x) {
+    float a0 = load_as_f32(j.x, o + 2 * pr), a1 = load_as_f32(j.x, o + 2 * pr + 1);
+    if (pr >= first_rot) {
+      float c, s;
+      rope_cs1(p0 + t + j.off, pr - first_rot, j.theta1, &c, &s);
+      const float t0 = a0 * c - a1 * s, t1 = a0 * s + a1 * c;
+      a0 = t0;
+      a1 = t1;
+    }
+    store_from_f32(j.out, o + 2 * pr, a0);
+    store_from_f32(j.out, o + 2 * pr + 1, a1);
+  }
+}
+
+// A chunk's bookkeeping after the compressor, in one launch, no role
+// waiting on another (grid (X, B, roles)): for blockIdx.z < n_rings, ring z
+// (0 the main ring, 1 the indexer's) takes the last min(T, S) raw tokens of
+// the chunk (blocks x < min(T, S)); blockIdx.z = n_rings writes every row's
+// position pos0[b] + t to qpos; with rot.out, blockIdx.z = n_rings + 1
+// rotates the chunk's tokens for the window (token t by block t mod X).
+template <typename RT>
+__global__ void k_chunk_tasks(RingCopy r0, RingCopy r1, int n_rings, int64_t T, int S,
+                              const int64_t* __restrict__ pos0, int B, int64_t max_pos_end,
+                              Paging pg, uint32_t* status, int64_t* __restrict__ qpos,
+                              RotateJob<RT> rot) {
+  const int z = static_cast<int>(blockIdx.z);
+  if (z == n_rings) {
+    const int64_t nrow = static_cast<int64_t>(B) * T;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * gridDim.y * blockDim.x;
+    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x +
+                     threadIdx.x;
+         i < nrow; i += stride)
+      qpos[i] = pos0[i / T] + i % T;
+    return;
+  }
+  if (z > n_rings) {
+    const int b = blockIdx.y;
+    const int64_t p0 = pos0[b];
+    if (p0 < 0 || p0 + T > max_pos_end) return;
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) rotate_token(rot, b, t, T, p0);
+    return;
+  }
+  const int64_t keep = T < S ? T : S;
+  if (static_cast<int64_t>(blockIdx.x) >= keep) return;
+  const uint16_t* raw = blockIdx.z == 0 ? r0.raw : r1.raw;
+  uint16_t* ring = blockIdx.z == 0 ? r0.ring : r1.ring;
+  const int units = blockIdx.z == 0 ? r0.units : r1.units;
   const int b = blockIdx.y;
   const int64_t p0 = pos0[b];
   if (p0 < 0 || p0 + T > max_pos_end) return;
   bool ok = true;
   const int64_t sq = state_seq(pg, b, threadIdx.x == 0 ? status : nullptr, &ok);
   if (!ok) return;
-  const int64_t keep = T < S ? T : S;
   const int64_t t = T - keep + blockIdx.x;  // chunk offset of the token
   const int64_t p = p0 + t;
   const uint16_t* src = raw + (static_cast<int64_t>(b) * T + t) * units;
   uint16_t* dst = ring + (sq * S + (p % S)) * units;
   for (int i = threadIdx.x; i < units; i += blockDim.x) dst[i] = src[i];
-}
-
-// out[b, t] = R_{p0 + t + off} x[b, t] in the storage dtype.  Grid (T, B).
-template <typename T>
-__global__ void k_rotate_chunk(const T* __restrict__ x, int D, int64_t Tn, int r, double base,
-                               int64_t off, const int64_t* __restrict__ pos0, T* __restrict__ out,
-                               int64_t max_pos_end) {
-  const int b = blockIdx.y;
-  const int64_t t = blockIdx.x;
-  const int64_t p0 = pos0[b];
-  if (p0 < 0 || p0 + Tn > max_pos_end) return;
-  const int64_t o = (static_cast<int64_t>(b) * Tn + t) * D;
-  const int first_rot = (D - r) / 2;
-  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) {
-    float a0 = load_as_f32(x, o + 2 * pr), a1 = load_as_f32(x, o + 2 * pr + 1);
-    if (pr >= first_rot) {
-      float c, s;
-      rope_cs(p0 + t + off, pr - first_rot, r, base, &c, &s);
-      const float t0 = a0 * c - a1 * s, t1 = a0 * s + a1 * c;
-      a0 = t0;
-      a1 = t1;
-    }
-    store_from_f32(out, o + 2 * pr, a0);
-    store_from_f32(out, o + 2 * pr + 1, a1);
-  }
 }
 
 // The pre-attention step of a chunk, horizontally fused ("DeepSeek V4 稀疏注意力
@@ -160,29 +199,33 @@ dsa_status launch_zero(void* p, size_t bytes, hipStream_t st) {
   return hip_check(hipGetLastError(), "k_zero launch");
 }
 
-dsa_status launch_ring_update(const void* raw, dsa_dtype dt, int D, int64_t T, void* ring, int S,
-                              const int64_t* pos0, int B, int64_t max_pos_end,
-                              const dsa_paging& pg, uint32_t* status, hipStream_t st) {
-  const int units = static_cast<int>(D * dtype_size(dt) / 2);
+dsa_status launch_chunk_tasks(const void* raw0, dsa_dtype dt0, int D0, void* ring0,
+                              const void* raw1, dsa_dtype dt1, int D1, void* ring1, int64_t T,
+                              int S, const int64_t* pos0, int B, int64_t max_pos_end,
+                              const dsa_paging& pg, uint32_t* status, int64_t* qpos,
+                              void* rot_out, int rope_dim, double rope_base, int64_t rope_off,
+                              hipStream_t st) {
+  const RingCopy r0{static_cast<const uint16_t*>(raw0), static_cast<uint16_t*>(ring0),
+                    static_cast<int>(D0 * dtype_size(dt0) / 2)};
+  const RingCopy r1{static_cast<const uint16_t*>(raw1), static_cast<uint16_t*>(ring1),
+                    ring1 ? static_cast<int>(D1 * dtype_size(dt1) / 2) : 0};
+  const int n_rings = ring1 ? 2 : 1;
   const int64_t keep = T < S ? T : S;
-  hipLaunchKernelGGL(k_ring_update, dim3(static_cast<unsigned>(keep), B), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(raw), units, T, static_cast<uint16_t*>(ring), S,
-                     pos0, max_pos_end, make_paging(pg), status);
-  return hip_check(hipGetLastError(), "k_ring_update launch");
-}
-
-dsa_status launch_rotate_chunk(const void* x, dsa_dtype dt, int D, int64_t T, int r, double base,
-                               int64_t off, const int64_t* pos0, int B, void* out,
-                               int64_t max_pos_end, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(T), B);
-  if (dt == DSA_F32)
-    hipLaunchKernelGGL(k_rotate_chunk<float>, grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       D, T, r, base, off, pos0, static_cast<float*>(out), max_pos_end);
-  else
-    hipLaunchKernelGGL(k_rotate_chunk<uint16_t>, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), D, T, r, base, off, pos0,
-                       static_cast<uint16_t*>(out), max_pos_end);
-  return hip_check(hipGetLastError(), "k_rotate_chunk launch");
+  const int64_t rot_blocks = rot_out ? std::min<int64_t>(T, 2048) : 0;
+  const double theta1 = rope_dim > 0 ? std::pow(rope_base, -2.0 / rope_dim) : 1.0;
+  const dim3 grid(static_cast<unsigned>(std::max(keep, rot_blocks)), B, n_rings + 1 + (rot_out ? 1 : 0));
+  if (dt0 == DSA_F32) {
+    const RotateJob<float> rj{static_cast<const float*>(raw0), static_cast<float*>(rot_out), D0,
+                              rope_dim, theta1, rope_off};
+    hipLaunchKernelGGL(k_chunk_tasks<float>, grid, dim3(256), 0, st, r0, r1, n_rings, T, S, pos0, B,
+                       max_pos_end, make_paging(pg), status, qpos, rj);
+  } else {
+    const RotateJob<uint16_t> rj{static_cast<const uint16_t*>(raw0), static_cast<uint16_t*>(rot_out),
+                                 D0, rope_dim, theta1, rope_off};
+    hipLaunchKernelGGL(k_chunk_tasks<uint16_t>, grid, dim3(256), 0, st, r0, r1, n_rings, T, S, pos0,
+                       B, max_pos_end, make_paging(pg), status, qpos, rj);
+  }
+  return hip_check(hipGetLastError(), "k_chunk_tasks launch");
 }
 
 dsa_status launch_qk_prep(const dsa_layer_args& a, void* q_rot, void* rot_chunk, hipStream_t st) {

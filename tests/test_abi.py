@@ -239,7 +239,7 @@ def test_layer_decode_noalloc_refuses_steps_beyond_its_scratch():
     any device call -- here without a GPU."""
     cap = _lib._lib.dsa_layer_decode_noalloc_capacity()
     assert cap == 64 << 20
-    big = _layer_args(main=_lib.geom(128, 128, 512, 64), idx_heads=0, k=8192, n_seqs=128,
+    big = _layer_args(main=_lib.geom(128, 128, 512, 64), idx_heads=0, k=8192, n_seqs=256,
                       max_pos_end=1 << 20, e_cap=8192, w_cap=256)
     need = _lib.layer_workspace(big)
     assert need > cap

@@ -396,10 +396,11 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
   c.max_pos_end = a->max_pos_end;
   c.status = a->status;
   c.paging = a->paging;
-  rc = launch_compress(c, st);
-  if (rc != DSA_OK) return rc;
   const dsa_dtype raw_idx_dt = a->idx_dtype == DSA_F32 ? DSA_F32 : DSA_BF16;
-  if (a->idx_heads > 0) {
+  if (a->idx_heads == 0) {
+    rc = launch_compress(c, st);
+    if (rc != DSA_OK) return rc;
+  } else {
     dsa_compress_args ci = c;
     ci.geom.dim = a->idx_dim;
     ci.geom.rope_dim = a->idx_rope_dim;
@@ -413,7 +414,7 @@ dsa_status run_layer(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStre
     ci.out_dtype = a->idx_dtype;
     ci.out_scale = a->idx_scale;
     ci.out_mx_scale = a->idx_mx_scale;
-    rc = launch_compress(ci, st);
+    rc = launch_compress_pair(c, ci, st);
     if (rc != DSA_OK) return rc;
   }
   // the rings take the chunk's raw tokens; the rows' positions (for the

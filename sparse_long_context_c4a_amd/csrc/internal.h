@@ -40,6 +40,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Kernel launchers (one per step); arguments already validated.
 dsa_status launch_compress(const dsa_compress_args& a, hipStream_t st);
+// Two compressions of one chunk (the main entries a, the indexer keys b) in
+// one launch where their types allow, else one after the other.
+dsa_status launch_compress_pair(const dsa_compress_args& a, const dsa_compress_args& b,
+                                hipStream_t st);
 dsa_status launch_zero(void* p, size_t bytes, hipStream_t st);
 
 // Indexer + Top-k.  Workspace layout is owned by indexer.hip.

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
   const uint32_t* mrow = meta + static_cast<int64_t>(row) * nw;
   const uint64_t* crow = cand + static_cast<int64_t>(row) * slots;
   // two candidates per 16-byte load: v[2 i + h] is slot 2 t + 2 kSel i + h
-  // (slots is even: cap >= 8; the row's start is 16-byte aligned)
+  // (slots is even: nw is a multiple of 4; the row's start is 16-byte aligned)
   constexpr int kPer = kFinalCap / kSel;
   uint64_t v[kPer];
 #pragma unroll
@@ -194,8 +194,7 @@ __global__ __launch_bounds__(kSel) void k_topk_cand_final(
     v[2 * i] = static_cast<uint64_t>(w.x) | (static_cast<uint64_t>(w.y) << 32);
     v[2 * i + 1] = static_cast<uint64_t>(w.z) | (static_cast<uint64_t>(w.w) << 32);
   }
-  // wave thresholds: nw <= kSel (nw * cap <= kFinalCap with cap >= 8), one
-  // per thread
+  // wave thresholds: nw <= kSel (the plan's condition), one per thread
   const uint32_t mw = t < nw ? mrow[t] : 0u;
   uint32_t tm = mw;
   const RowInfo ri = row_info(q_pos, row, s, S, nv_cap, max_pos_end, nullptr, false);
@@ -456,12 +455,15 @@ Plan plan(const dsa_index_args& a) {
   p.ent = 1024;
   p.nb = static_cast<int>(ceil_div(p.nv_cap, p.ent));
   p.nw = 4 * p.nb;  // waves per row, ent / 4 entries each
-  // Candidates per wave: the union holds >= 2k and fits the final LDS pass.
-  // A wave of 256 entries at 1M context holds ~0.5 of the row's top 512;
-  // more than 8 of them has probability ~3e-8 for unstructured scores.
+  // Candidates per wave: the union holds >= 2k and fits the final LDS pass
+  // (one wave threshold per thread there: nw <= kSel).  A wave of 256
+  // entries at 1M context holds ~0.5 of the row's top 512; more than 6 of
+  // them has probability ~1e-6 per wave for unstructured scores (~1e-3 per
+  // row), and such a wave is scored again in full by the final pass.
   p.cap = static_cast<int>(std::min<int64_t>(
-      32, std::max<int64_t>(8, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nw)))));
-  p.cand = p.mfma && p.nv_cap > a.k && static_cast<int64_t>(p.nw) * p.cap <= kFinalCap &&
+      32, std::max<int64_t>(6, ceil_div(4 * static_cast<int64_t>(a.k), std::max(1, p.nw)))));
+  p.cand = p.mfma && p.nv_cap > a.k && p.nw <= kSel &&
+           static_cast<int64_t>(p.nw) * p.cap <= kFinalCap &&
            static_cast<int64_t>(p.nw) * p.cap >= 2 * static_cast<int64_t>(a.k);
   // many rows per sequence: the fp8 contraction with exact correction
   p.pre = prefill_index_applies(a, p.nv_cap);

@@ -700,6 +700,17 @@ __global__ __launch_bounds__(kThreads, 3) void k_pidx_main(PArgs a) {
   uint32_t* mst = reinterpret_cast<uint32_t*>(a.masks + (row0 + wr0 + (lane >> 2)) * a.ld_t);
   int buf = 0;
   for (int s = 0; s < nst; ++s) {
+    // the three workgroups sharing a compute unit keep pace: a wave's
+    // priority falls with each quarter of its stages (left alone, the
+    // oldest workgroup takes most issue slots and the last one runs its
+    // final stretch with one wave per SIMD)
+    {
+      const int qtr = (4 * s) / nst;
+      if (qtr == 0) __builtin_amdgcn_s_setprio(3);
+      else if (qtr == 1) __builtin_amdgcn_s_setprio(2);
+      else if (qtr == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     u32x4 rk[4];
     float rks;
     gload(min(s + 2, nst - 1), rk, rks);

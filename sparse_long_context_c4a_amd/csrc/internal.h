@@ -44,7 +44,6 @@ dsa_status launch_compress(const dsa_compress_args& a, hipStream_t st);
 // one launch where their types allow, else one after the other.
 dsa_status launch_compress_pair(const dsa_compress_args& a, const dsa_compress_args& b,
                                 hipStream_t st);
-dsa_status launch_zero(void* p, size_t bytes, hipStream_t st);
 
 // Indexer + Top-k.  Workspace layout is owned by indexer.hip.
 size_t index_topk_ws_bytes(const dsa_index_args& a);

@@ -16,12 +16,6 @@
 namespace dsa {
 namespace {
 
-__global__ void k_zero(uint32_t* p, size_t n) {
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = 0u;
-}
-
 // One ring's copy source and destination (element size in 2-byte units).
 struct RingCopy {
   const uint16_t* raw;
@@ -190,14 +184,6 @@ __global__ void k_decode_window_insert(const MainT* __restrict__ x, MainT* __res
 }
 
 }  // namespace
-
-dsa_status launch_zero(void* p, size_t bytes, hipStream_t st) {
-  const size_t n = bytes / 4;
-  if (n == 0) return DSA_OK;
-  const unsigned blocks = static_cast<unsigned>(std::min<size_t>(1024, (n + 255) / 256));
-  hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), n);
-  return hip_check(hipGetLastError(), "k_zero launch");
-}
 
 dsa_status launch_chunk_tasks(const void* raw0, dsa_dtype dt0, int D0, void* ring0,
                               const void* raw1, dsa_dtype dt1, int D1, void* ring1, int64_t T,

@@ -107,14 +107,14 @@ def build_sets(w, n_sets, device):
 
 
 def time_layer(w, sets, steps, warmup, decode, out_fp8=False, q_norm=False):
-    """Two timed passes of `steps` layer steps each, after `warmup` untimed
-    ones.  The first pass gives the step time: nothing but the layer's own
-    launches on the stream, bracketed by events.  The second pass hands the
-    library HIP events (dsa_set_timing_events) that it attaches to the
-    dispatch packets of the scoring kernel and of the attention kernels
-    (hipExtLaunchKernel), which gives their own durations on the stream they
-    run on.  With out_fp8 the
-    layer stores its output as fp8 codes with one scale per (row, head)."""
+    """Two timed passes after `warmup` untimed steps.  The first, of `steps`
+    steps, gives the step time: nothing but the layer's own launches on the
+    stream, bracketed by events.  The second (`steps` steps, at least 100 for
+    decode) hands the library HIP events (dsa_set_timing_events) that it
+    attaches to the dispatch packets of the scoring kernel and of the
+    attention kernels (hipExtLaunchKernel), which gives their own mean
+    durations on the stream they run on.  With out_fp8 the layer stores its
+    output as fp8 codes with one scale per (row, head)."""
     import torch
     from sparse_long_context_c4a_amd import _lib
     from sparse_long_context_c4a_amd import layer as Ly
@@ -145,9 +145,13 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False, q_norm=False):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
-    ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(steps)]
-    for i in range(steps):
+    # the kernel durations: a mean over at least 100 consecutive steps (a
+    # mean over 20 moved by +-1.5 us between runs at the headline workload;
+    # over 100 it holds within a few tenths)
+    n_ev = max(steps, 100) if decode else steps
+    ev_i = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(n_ev)]
+    ev_a = [(_lib.HipEvent(), _lib.HipEvent()) for _ in range(n_ev)]
+    for i in range(n_ev):
         _lib.set_timing_events(index=ev_i[i], attn=ev_a[i])
         fn(args[i % len(args)], ws=ws, stream=stream)
     torch.cuda.synchronize()
@@ -155,8 +159,8 @@ def time_layer(w, sets, steps, warmup, decode, out_fp8=False, q_norm=False):
     assert all(s == 0 for s in st), f"device status {st}"
     # (a workload without an indexer, k >= every n_vis, never records the
     # indexer's events)
-    idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / steps if w.Hi else None
-    attn_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_a) / steps
+    idx_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_i) / n_ev if w.Hi else None
+    attn_ms = sum(e[0].elapsed_ms(e[1]) for e in ev_a) / n_ev
     return ms, idx_ms, attn_ms
 
 

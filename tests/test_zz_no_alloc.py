@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 CASES = [
-    # the largest scratch of the decode workloads first (33 MiB), then a
-    # smaller c4a step whose Top-k runs on the candidate path
+    # a large scratch first (c128a at 1M: 18 MiB), then a smaller c4a step
+    # whose Top-k runs on the candidate path
     ("c128a_decode_B16_L1M", configs.C128A_DECODE_1M, {}),
     ("c4a_decode_B2_L40000", configs.C4A_DECODE_64K, dict(B=2, L=40000)),
 ]

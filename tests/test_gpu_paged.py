@@ -41,6 +41,9 @@ CASES = [
     ("c128a_decode_B2_L5120", configs.C128A_DECODE_1M, dict(B=2, L=5120, k=64), None, None),
     ("c4a_prefill_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077), 2000, 77),
     ("c4a_prefill_contraction_B2_T300", configs.C4A_PREFILL_128K, dict(B=2, L=4300), 4000, 300),
+    # MXFP4 keys: the chunk's two compressions in one launch, both paged
+    ("c4a_prefill_fp4_ragged_T77", configs.C4A_PREFILL_128K, dict(L=2077, idx_dtype="fp4"), 2000,
+     77),
     ("c128a_prefill_T300", configs.C128A_DECODE_1M, dict(B=2, L=1300, k=64, mode="prefill"), 1000,
      300),
 ]

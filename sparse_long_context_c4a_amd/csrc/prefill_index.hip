@@ -855,7 +855,13 @@ __global__ __launch_bounds__(kPSelT) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         const uint4* rm = reinterpret_cast<const uint4*>(krm + jj * 128);
         blo[u] = rm[g];
         bhi[u] = rm[4 + g];
-        ks[u] = ksb[jj];
+        ks[u] = 0.f;
+      }
+      // the score is whole in every lane and lanes g == 0 keep it, so only
+      // they load the key scales (a gather's cost follows its active lanes)
+      if (g == 0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) ks[u] = ksb[j[u] >= 0 ? j[u] : 0];
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
